@@ -1,0 +1,304 @@
+"""Seeded synthetic inputs for the block-diffusion decode step and the
+dual-stream training attention.
+
+This module only draws random numbers and lays them out: it computes no
+attention, no logits, no softmax and no commit/accept/certificate decision.
+Both the GPU library's tests/benchmark and the CPU oracle's tests read their
+inputs from here, so that the two sides see the same values.
+
+Every tensor is returned as a NumPy array: float32 for the float32 workload,
+raw bfloat16 bit patterns (uint16, round-to-nearest-even from float32) for the
+bfloat16 workloads.
+
+Shapes follow the workloads on the pages: batch 1, a mostly visual prefix
+(visual tokens are 89-97 % of the input in the LOWN article, 'research
+motivation'), block 16/32 and threshold 0.9 (Fast-dVLM overview, §4.1 and
+§2.3.1), Qwen2.5-VL-3B geometry (16 query heads, 2 KV heads, head_dim 128,
+hidden 2048, vocabulary 151936).  Synthetic values stand in for the pages'
+benchmarks and trained weights, which are not available.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+BASE_SEED = 20261203
+N_CONFIGS = 5
+
+
+# ---------------------------------------------------------------------------
+# Random streams and number formats
+# ---------------------------------------------------------------------------
+
+def config_rng(cfg: int, seed: int | None = None) -> np.random.Generator:
+    """PCG64 stream for workload ``cfg`` (1..5): child ``cfg-1`` of
+    SeedSequence(seed or BASE_SEED)."""
+    ss = np.random.SeedSequence(BASE_SEED if seed is None else seed)
+    return np.random.Generator(np.random.PCG64(ss.spawn(N_CONFIGS)[cfg - 1]))
+
+
+def bf16_bits(x) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest, ties to even
+    (the rounding torch's .to(torch.bfloat16) performs).  Inputs are finite."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact value of bfloat16 bit patterns, as float64 (used to plant
+    hidden states against the rounded weights)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def normal(rng, shape, std=1.0, trunc=None) -> np.ndarray:
+    """float32 N(0, std^2); with ``trunc`` every |x| > trunc is redrawn."""
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if trunc is not None:
+        bad = np.abs(x) > trunc
+        while bad.any():
+            x[bad] = rng.standard_normal(int(bad.sum()), dtype=np.float32)
+            bad = np.abs(x) > trunc
+    if std != 1.0:
+        x *= np.float32(std)
+    return x
+
+
+def normal_bf16(rng, shape, std=1.0, trunc=None, chunk_rows=8192) -> np.ndarray:
+    """bfloat16 bits of N(0, std^2) (optionally truncated to |x| <= trunc
+    before scaling), generated in row chunks to bound host memory."""
+    shape = tuple(shape)
+    out = np.empty(shape, dtype=np.uint16)
+    rows = shape[0]
+    for s in range(0, rows, chunk_rows):
+        e = min(rows, s + chunk_rows)
+        out[s:e] = bf16_bits(normal(rng, (e - s,) + shape[1:], std, trunc))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Hidden-state planting for the LM head
+# ---------------------------------------------------------------------------
+
+def plant_hidden(rng, W_bits, targets, target_conf, sigma_w) -> np.ndarray:
+    """Hidden rows h_i = e_i + alpha_i * u_i, where u_i is the unit direction
+    of the (bf16-rounded) weight row of target token t_i and e_i ~ N(0, I) is
+    drawn and then made orthogonal to u_i.
+
+    alpha_i comes from a statistical model of the weights, not from the
+    logits: with W entries i.i.d. N(0, sigma_w^2), the target logit is
+    alpha * |W_t| and every other logit is ~ N(0, sigma_w^2 |h|^2), whose
+    exponential has mean exp(sigma_w^2 |h|^2 / 2).  Setting
+        alpha |W_t| - log(V-1) - sigma_w^2 (|e|^2 + alpha^2) / 2 = logit(c_i)
+    places the top probability near the requested c_i (within about half a
+    percent at the sizes used), with t_i ahead of every other token by a
+    wide logit gap.  Returns float32 rows (round them to bf16 with
+    ``bf16_bits``)."""
+    V, d = W_bits.shape
+    targets = np.asarray(targets)
+    c = np.asarray(target_conf, dtype=np.float64)
+    out = np.empty((targets.size, d), dtype=np.float32)
+    s2 = float(sigma_w) ** 2
+    for i, t in enumerate(targets):
+        w = bf16_to_f64(W_bits[int(t)])
+        nw = float(np.sqrt(w @ w))
+        u = w / nw
+        e = rng.standard_normal(d)
+        e -= (e @ u) * u
+        ee = float(e @ e)
+        C = np.log(V - 1.0) + 0.5 * s2 * ee + np.log(c[i] / (1.0 - c[i]))
+        disc = nw * nw - 2.0 * s2 * C
+        alpha = (nw - np.sqrt(max(disc, 0.0))) / s2 if s2 > 0 else C / nw
+        out[i] = (e + alpha * u).astype(np.float32)
+    return out
+
+
+def _commit_band_conf(rng, n, p_commit=0.4, hi=(0.92, 0.999), lo=(0.02, 0.88)):
+    """Target top probabilities: with probability p_commit in ``hi`` (above
+    the 0.9 threshold with a margin), else in ``lo`` (below it with a margin)."""
+    z = rng.random(n) < p_commit
+    c = np.where(z, rng.uniform(hi[0], hi[1], n), rng.uniform(lo[0], lo[1], n))
+    return c, z
+
+
+def _different_token(rng, tok, V):
+    """A uniform token id different from ``tok``."""
+    x = int(rng.integers(0, V - 1))
+    return x + (x >= tok)
+
+
+# ---------------------------------------------------------------------------
+# Workloads
+# ---------------------------------------------------------------------------
+
+def tiny(seed: int | None = None) -> dict:
+    """Tiny float32 case.  Dual-stream attention over 4 visual + 4 clean +
+    4 noisy tokens, block 2, one head, head_dim 16; one decode block of B=4
+    queries over a 32-token prefix; LM head d=16 x V=64; threshold 0.9; every
+    position masked.  Q/K/V, hidden and W ~ N(0, 1); each hidden row gets a
+    planted target token pushed along its weight row by a random amount
+    (alpha ~ U(0, 6) in units of the row direction)."""
+    rng = config_rng(1, seed)
+    n_vis, n_txt, blk, dh = 4, 4, 2, 16
+    n = n_vis + 2 * n_txt
+    B, P, V, d = 4, 32, 64, 16
+    r = {
+        "dtype": "f32", "n_vis": n_vis, "n_txt": n_txt, "block": blk, "H": 1, "dh": dh,
+        "ds_q": normal(rng, (n, 1, dh)), "ds_k": normal(rng, (n, 1, dh)),
+        "ds_v": normal(rng, (n, 1, dh)),
+        "B": B, "P": P, "Hq": 1, "Hkv": 1, "cap": P + B,
+        "q": normal(rng, (B, 1, dh)),
+        "k_cache": normal(rng, (1, P + B, dh)), "v_cache": normal(rng, (1, P + B, dh)),
+        "V": V, "d": d, "W": normal(rng, (V, d)),
+    }
+    t = rng.integers(0, V, B)
+    alpha = rng.uniform(0.0, 6.0, B)
+    h = normal(rng, (B, d))
+    for i in range(B):
+        w = r["W"][t[i]].astype(np.float64)
+        h[i] += (alpha[i] * w / np.sqrt(w @ w)).astype(np.float32)
+    r.update(h=h, targets=t.astype(np.int32), tau=0.9,
+             masked=np.ones(B, np.uint8), tokens=np.zeros(B, np.int32))
+    return r
+
+
+def qwen_decode(seed: int | None = None, B=16, n_vis=1024, n_prompt=256, Hq=16, Hkv=2,
+                dh=128, d=2048, V=151936, p_commit=0.4, sigma_w=0.02) -> dict:
+    """One MDM block-decode step shaped like Qwen2.5-VL-3B, bf16.  Prefix KV of
+    n_vis visual + n_prompt prompt tokens, then the block's B rows; bidirectional
+    intra-block mask.  q, K ~ N(0,1); V ~ N(0,1) truncated to |v| <= 4.  W ~
+    N(0, sigma_w^2).  Hidden rows planted so that about p_commit of them have top
+    probability in [0.92, 0.999] and the rest in [0.02, 0.88].  Position 0 holds
+    the block's AR seed token (already unmasked); 1..B-1 are masked."""
+    rng = config_rng(2, seed)
+    P = n_vis + n_prompt
+    cap = P + B
+    W = normal_bf16(rng, (V, d), std=sigma_w)
+    t = rng.integers(0, V, B)
+    c, z = _commit_band_conf(rng, B, p_commit)
+    h = bf16_bits(plant_hidden(rng, W, t, c, sigma_w))
+    masked = np.ones(B, np.uint8)
+    masked[0] = 0
+    tokens = np.zeros(B, np.int32)
+    tokens[0] = int(rng.integers(0, V))
+    return {
+        "dtype": "bf16", "B": B, "P": P, "n_vis": n_vis, "n_prompt": n_prompt, "cap": cap,
+        "Hq": Hq, "Hkv": Hkv, "dh": dh, "d": d, "V": V, "tau": 0.9,
+        "q": normal_bf16(rng, (B, Hq, dh)),
+        "k_cache": normal_bf16(rng, (Hkv * cap, dh)).reshape(Hkv, cap, dh),
+        "v_cache": normal_bf16(rng, (Hkv * cap, dh), trunc=4.0).reshape(Hkv, cap, dh),
+        "W": W, "h": h, "targets": t.astype(np.int32), "target_conf": c, "planted_commit": z,
+        "masked": masked, "tokens": tokens,
+    }
+
+
+def linear_spec(seed: int | None = None, B=32, n_vis=1024, n_prompt=256, Hq=16, Hkv=2,
+                dh=128, d=2048, V=151936, p_geo=0.15, sigma_w=0.02) -> dict:
+    """Linear self-speculative step, bf16: a bidirectional draft pass and a
+    causal verify pass of the same B queries over the prefix.  Draft targets
+    d_i ~ U{V}; verify targets equal d_i for i < L_true, differ at L_true, and
+    are uniform after it; L_true = min(Geometric(p_geo), B) (support >= 1, the
+    first token being the AR seed).  Each pass has its own q and its own block
+    K/V rows (rows P..P+B-1 of its cache)."""
+    rng = config_rng(3, seed)
+    P = n_vis + n_prompt
+    cap = P + B
+    W = normal_bf16(rng, (V, d), std=sigma_w)
+    L_true = int(min(rng.geometric(p_geo), B))
+    draft_t = rng.integers(0, V, B)
+    ver_t = rng.integers(0, V, B)
+    ver_t[:L_true] = draft_t[:L_true]
+    if L_true < B:
+        ver_t[L_true] = _different_token(rng, int(draft_t[L_true]), V)
+    c_d = rng.uniform(0.3, 0.999, B)
+    c_v = rng.uniform(0.3, 0.999, B)
+    h_d = bf16_bits(plant_hidden(rng, W, draft_t, c_d, sigma_w))
+    h_v = bf16_bits(plant_hidden(rng, W, ver_t, c_v, sigma_w))
+    kp = normal_bf16(rng, (Hkv * P, dh)).reshape(Hkv, P, dh)
+    vp = normal_bf16(rng, (Hkv * P, dh), trunc=4.0).reshape(Hkv, P, dh)
+
+    def cache(kblk, vblk):
+        kc = np.concatenate([kp, kblk], axis=1)
+        vc = np.concatenate([vp, vblk], axis=1)
+        return kc, vc
+
+    kd, vd = cache(normal_bf16(rng, (Hkv * B, dh)).reshape(Hkv, B, dh),
+                   normal_bf16(rng, (Hkv * B, dh), trunc=4.0).reshape(Hkv, B, dh))
+    kv_, vv_ = cache(normal_bf16(rng, (Hkv * B, dh)).reshape(Hkv, B, dh),
+                     normal_bf16(rng, (Hkv * B, dh), trunc=4.0).reshape(Hkv, B, dh))
+    return {
+        "dtype": "bf16", "B": B, "P": P, "cap": cap, "Hq": Hq, "Hkv": Hkv, "dh": dh,
+        "d": d, "V": V, "W": W, "L_true": L_true,
+        "draft_targets": draft_t.astype(np.int32), "verify_targets": ver_t.astype(np.int32),
+        "q_draft": normal_bf16(rng, (B, Hq, dh)), "q_verify": normal_bf16(rng, (B, Hq, dh)),
+        "k_draft": kd, "v_draft": vd, "k_verify": kv_, "v_verify": vv_,
+        "h_draft": h_d, "h_verify": h_v,
+    }
+
+
+def fused_spec(seed: int | None = None, B=16, n_vis=4096, n_prompt=512, Hq=16, Hkv=2,
+               dh=128, d=2048, V=151936, p_geo=0.15, sigma_w=0.02, n_cert=64,
+               k_cert=4, p_agree=0.83) -> dict:
+    """Fused (quadratic) speculative step, bf16: 2B query rows under the
+    SPEC_FUSED mask over a 4096-visual + 512-text prefix, one LM-head pass over
+    the 2B rows.  The draft tokens fed to the verify half are uniform; verify
+    rows 0..B-1 are planted to agree with them over a Geometric(p_geo) prefix
+    (capped at B); draft-half rows B..2B-1 get uniform targets.
+    Certificate inputs: n_cert anchor confidences ~ U(0,1) (float32), anchor
+    tokens ~ U{V}, text-only tokens equal to the anchor with probability
+    p_agree (83.4 % agreement in the LOWN article), else a different uniform
+    token; k_cert is the per-step unmask quota k."""
+    rng = config_rng(4, seed)
+    P = n_vis + n_prompt
+    bq = 2 * B
+    cap = P + bq
+    W = normal_bf16(rng, (V, d), std=sigma_w)
+    L_true = int(min(rng.geometric(p_geo), B))
+    draft_in = rng.integers(0, V, B)
+    ver_t = rng.integers(0, V, B)
+    ver_t[:L_true] = draft_in[:L_true]
+    if L_true < B:
+        ver_t[L_true] = _different_token(rng, int(draft_in[L_true]), V)
+    next_t = rng.integers(0, V, B)
+    tgt = np.concatenate([ver_t, next_t])
+    c = rng.uniform(0.3, 0.999, bq)
+    h = bf16_bits(plant_hidden(rng, W, tgt, c, sigma_w))
+    anchor_conf = rng.random(n_cert, dtype=np.float32)
+    anchor_tok = rng.integers(0, V, n_cert)
+    agree = rng.random(n_cert) < p_agree
+    text_tok = anchor_tok.copy()
+    for i in np.nonzero(~agree)[0]:
+        text_tok[i] = _different_token(rng, int(anchor_tok[i]), V)
+    return {
+        "dtype": "bf16", "B": B, "Bq": bq, "P": P, "cap": cap, "Hq": Hq, "Hkv": Hkv,
+        "dh": dh, "d": d, "V": V, "W": W, "h": h, "L_true": L_true,
+        "draft_in": draft_in.astype(np.int32), "targets": tgt.astype(np.int32),
+        "q": normal_bf16(rng, (bq, Hq, dh)),
+        "k_cache": normal_bf16(rng, (Hkv * cap, dh)).reshape(Hkv, cap, dh),
+        "v_cache": normal_bf16(rng, (Hkv * cap, dh), trunc=4.0).reshape(Hkv, cap, dh),
+        "anchor_conf": anchor_conf, "anchor_tok": anchor_tok.astype(np.int32),
+        "text_tok": text_tok.astype(np.int32), "k_cert": k_cert,
+    }
+
+
+def dualstream(seed: int | None = None, n_vis=1024, n_txt=2048, block=32, H=16, dh=128,
+               dtype="bf16") -> dict:
+    """Training-time dual-stream attention input, token order
+    [visual | clean text | noisy text].  Q, K ~ N(0,1), V ~ N(0,1) truncated
+    to |v| <= 4.  A mask probability t ~ U(0,1) is drawn once; each noisy
+    position is replaced by [MASK] with probability t, and every [MASK]
+    position carries the same Q/K/V row (one shared embedding)."""
+    rng = config_rng(5, seed)
+    n = n_vis + 2 * n_txt
+    q = normal(rng, (n, H, dh))
+    k = normal(rng, (n, H, dh))
+    v = normal(rng, (n, H, dh), trunc=4.0)
+    t = float(rng.random())
+    is_mask = rng.random(n_txt) < t
+    mq, mk, mv = normal(rng, (H, dh)), normal(rng, (H, dh)), normal(rng, (H, dh), trunc=4.0)
+    rows = n_vis + n_txt + np.nonzero(is_mask)[0]
+    q[rows], k[rows], v[rows] = mq, mk, mv
+    conv = bf16_bits if dtype == "bf16" else (lambda x: x)
+    return {"dtype": dtype, "n_vis": n_vis, "n_txt": n_txt, "block": block, "H": H, "dh": dh,
+            "N": n, "t": t, "is_mask": is_mask, "q": conv(q), "k": conv(k), "v": conv(v)}

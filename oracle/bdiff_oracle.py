@@ -1,0 +1,342 @@
+"""Plain CPU oracle for the block-diffusion decode step and the dual-stream
+training attention of Fast-dVLM.
+
+TEST INFRASTRUCTURE ONLY.  This module exists so that tests, the smoke check
+and the CPU-baseline leg of the benchmark can compute what the method defines,
+slowly and in float64, and compare the GPU library against it.  Nothing on the
+product path may import it, and it shares no code with the HIP library.
+
+Sources (web pages on the method; cited by page and section):
+  [OV]   Fast-dVLM engineering overview, ocdem.com/news/1032714
+         - §1.2: blocks decoded left to right, parallel denoising inside a
+           block, KV cache reused across blocks.
+         - §2.2.1: dual noisy/clean streams and the three attention masks
+           N2N / N2C / C2C, with printed 4x4 matrices for block size 2.
+         - §2.2.2: visual tokens kept once, in the clean stream, reached from
+           the noisy stream only through N2C; causal-context decoding.
+         - §2.3.1: self-speculative decoding, longest verified prefix kept and
+           the KV cache truncated; linear (two forwards) and quadratic
+           (one forward, O(B^2)) variants.
+         - §4.1: recommended block_size 16 and denoising threshold 0.9.
+  [TH]   Fast-dVLM article (itsolotime.com, Thai), §4.1 "Causal context
+         attention": noisy tokens attend bidirectionally inside their block and
+         to the preceding clean context including visual tokens; the clean
+         stream keeps token-level causal attention.
+  [LOWN] LOWN article (paper.rainbus.top/paper/2610.36671), section
+         "method step details": anchor confidence s = max_w p(y_i = w | .),
+         scan of masked positions in descending anchor confidence, longest
+         prefix where the text-only top-1 equals the anchor top-1, and the
+         branch rule |U_text| >= k.
+
+Readings where the pages are silent (each one is listed with its reason in the
+design notes of the repository):
+  R1  N2C is token-level and includes the diagonal (clean j <= noisy i), as in
+      the printed matrix; every visual key is visible to every noisy query.
+  R2  N2N blocks tile the noisy stream from its first token.
+  R3  C2C is causal over [visual | clean text], visual tokens included.
+  R4  No clean query sees a noisy key.
+  R5  Commit rule: masked positions with conf > tau (strict); if none
+      qualifies and some position is masked, the single most confident masked
+      position is committed (lowest index on ties).
+  R6  Argmax ties resolve to the lowest vocabulary index.
+  R7  Attention scale is 1/sqrt(dh); queries/keys are taken post-RoPE.
+  R8  A query row with no visible key produces a zero output row.
+  R9  Speculative accept compares index-aligned draft and verify arrays and
+      accepts exactly L tokens (no bonus token).
+  R10 SPEC_FUSED (the quadratic variant's one-forward mask, whose layout the
+      pages do not print) is the dual-stream mask restricted to one block:
+      rows 0..B-1 (verify half, draft tokens as input) are causal among
+      themselves; rows B..2B-1 (draft half) see verify row j iff j <= i-B and
+      see all of the draft half.  Both halves see the whole prefix.
+  R11 Certificate order: stable sort by anchor confidence, descending, lower
+      index first on ties.
+
+Every function below takes float64 (or integer) arrays and returns new arrays;
+bfloat16 inputs are passed as raw uint16 bit patterns and widened exactly.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "widen", "mask_n2n", "mask_n2c", "mask_c2c", "dualstream_mask",
+    "intra_block_mask", "masked_attention", "block_attn", "dualstream_attn",
+    "lm_logits", "lmhead_conf", "commit", "spec_accept", "cert_scan",
+    "decode_step", "linear_spec_step", "fused_spec_step",
+]
+
+
+# ---------------------------------------------------------------------------
+# Input widening
+# ---------------------------------------------------------------------------
+
+def widen(x) -> np.ndarray:
+    """Return ``x`` as float64.  uint16 arrays are bfloat16 bit patterns: the
+    16 bits are the top half of an IEEE float32, so shifting them into place
+    gives the exact value, which float64 then holds exactly."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Masks  [OV §2.2.1, §2.2.2; TH §4.1]
+# ---------------------------------------------------------------------------
+
+def mask_n2n(n_txt: int, block: int) -> np.ndarray:
+    """Noisy -> noisy: bidirectional inside a block of ``block`` tokens, blocks
+    tiling the noisy stream from its first token (R2).  [OV §2.2.1 'N2N']"""
+    i = np.arange(n_txt)[:, None]
+    j = np.arange(n_txt)[None, :]
+    return (i // block) == (j // block)
+
+
+def mask_n2c(n_txt: int) -> np.ndarray:
+    """Noisy text i -> clean text j, visible iff j <= i (R1).
+    [OV §2.2.1 'N2C', printed lower-triangular matrix]"""
+    i = np.arange(n_txt)[:, None]
+    j = np.arange(n_txt)[None, :]
+    return j <= i
+
+
+def mask_c2c(n: int) -> np.ndarray:
+    """Clean -> clean: token-level causal attention.  [OV §2.2.1 'C2C';
+    TH §4.1 item 3]"""
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    return j <= i
+
+
+def dualstream_mask(n_vis: int, n_txt: int, block: int) -> np.ndarray:
+    """Full boolean mask over the token order [visual | clean text | noisy
+    text] (vision-efficient concatenation: one copy of the visual tokens,
+    in the clean stream).  Row = query, column = key.  [OV §2.2.1, §2.2.2]"""
+    ctx = n_vis + n_txt
+    n = ctx + n_txt
+    m = np.zeros((n, n), dtype=bool)
+    m[:ctx, :ctx] = mask_c2c(ctx)                 # C2C over [vis | clean] (R3)
+    m[ctx:, :n_vis] = True                        # noisy -> every visual key (R1)
+    m[ctx:, n_vis:ctx] = mask_n2c(n_txt)          # N2C
+    m[ctx:, ctx:] = mask_n2n(n_txt, block)        # N2N
+    # clean -> noisy stays False (R4)
+    return m
+
+
+def intra_block_mask(kind: str, bq: int) -> np.ndarray:
+    """Visibility among the Bq block queries at decode time.
+    'bidir'      - all ones (N2N over one block)          [OV §1.2]
+    'causal'     - j <= i (the AR verify pass)             [OV §2.3.1]
+    'spec_fused' - reading R10, Bq = 2B                    [OV §2.3.1]"""
+    i = np.arange(bq)[:, None]
+    j = np.arange(bq)[None, :]
+    if kind == "bidir":
+        return np.ones((bq, bq), dtype=bool)
+    if kind == "causal":
+        return j <= i
+    if kind == "spec_fused":
+        if bq % 2:
+            raise ValueError("spec_fused needs an even number of rows")
+        b = bq // 2
+        m = np.zeros((bq, bq), dtype=bool)
+        m[:b, :b] = mask_c2c(b)          # verify half: causal
+        m[b:, :b] = mask_n2c(b)          # draft half -> verify half: j <= i - B
+        m[b:, b:] = mask_n2n(b, b)       # draft half: one bidirectional block
+        return m
+    raise ValueError(f"unknown mask kind {kind!r}")
+
+
+# ---------------------------------------------------------------------------
+# Attention (scaled dot-product over the allowed keys; R7, R8)
+# ---------------------------------------------------------------------------
+
+def masked_attention(q, k, v, allowed, scale: float) -> np.ndarray:
+    """o_i = sum_j softmax_j(scale * q_i . k_j) v_j over the keys j with
+    allowed[i, j]; a row with no allowed key is zero (R8).
+    q [Nq][dh], k/v [Nk][dh], allowed [Nq][Nk] bool."""
+    q = widen(q)
+    k = widen(k)
+    v = widen(v)
+    allowed = np.asarray(allowed, dtype=bool)
+    s = scale * (q @ k.T)
+    s = np.where(allowed, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    w = np.exp(s - m)                      # exp(-inf) = 0 for hidden keys
+    den = w.sum(axis=1, keepdims=True)
+    return (w @ v) / np.where(den > 0.0, den, 1.0)
+
+
+def block_attn(q, k_cache, v_cache, P: int, intra, scale: float | None = None) -> np.ndarray:
+    """Block queries over the cached prefix plus the block itself.
+    q [Bq][Hq][dh]; k_cache/v_cache [Hkv][cap][dh] with the block's own keys at
+    rows P..P+Bq-1.  Prefix keys are always visible; block key j is visible to
+    query i iff intra[i, j].  Query head h reads KV head h // (Hq / Hkv).
+    [OV §1.2: cached visual+prompt prefix, bidirectional block]"""
+    q = widen(q)
+    k_cache = widen(k_cache)
+    v_cache = widen(v_cache)
+    bq, hq, dh = q.shape
+    hkv = k_cache.shape[0]
+    if hq % hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if scale is None:
+        scale = 1.0 / np.sqrt(dh)
+    allowed = np.zeros((bq, P + bq), dtype=bool)
+    allowed[:, :P] = True
+    allowed[:, P:] = np.asarray(intra, dtype=bool)
+    group = hq // hkv
+    out = np.zeros((bq, hq, dh))
+    for h in range(hq):
+        g = h // group
+        out[:, h, :] = masked_attention(q[:, h, :], k_cache[g, :P + bq], v_cache[g, :P + bq],
+                                        allowed, scale)
+    return out
+
+
+def dualstream_attn(q, k, v, n_vis: int, n_txt: int, block: int,
+                    scale: float | None = None, rows=None) -> np.ndarray:
+    """Training-time attention over [visual | clean text | noisy text] with the
+    N2N / N2C / C2C masks.  q/k/v [N][H][dh].  If ``rows`` is given, only those
+    query rows are computed (returned in that order), for spot checks at large
+    N.  [OV §2.2.1, §2.2.2; TH §4.1]"""
+    q = widen(q)
+    k = widen(k)
+    v = widen(v)
+    n, nh, dh = q.shape
+    if n != n_vis + 2 * n_txt:
+        raise ValueError("N must equal n_vis + 2 * n_txt")
+    if scale is None:
+        scale = 1.0 / np.sqrt(dh)
+    allowed = dualstream_mask(n_vis, n_txt, block)
+    rows = np.arange(n) if rows is None else np.asarray(rows)
+    out = np.zeros((rows.size, nh, dh))
+    for h in range(nh):
+        out[:, h, :] = masked_attention(q[rows, h, :], k[:, h, :], v[:, h, :],
+                                        allowed[rows], scale)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# LM head confidence  [LOWN 'method step details': s = max_w p(y = w | .)]
+# ---------------------------------------------------------------------------
+
+def lm_logits(h, W, chunk: int = 16384) -> np.ndarray:
+    """logits[b, v] = sum_k h[b, k] W[v, k], in float64 (W widened in row
+    chunks to bound memory; the sum over k is not reordered)."""
+    h = widen(h)
+    W = np.asarray(W)
+    V = W.shape[0]
+    out = np.empty((h.shape[0], V))
+    for s in range(0, V, chunk):
+        out[:, s:s + chunk] = h @ widen(W[s:s + chunk]).T
+    return out
+
+
+def lmhead_conf(h, W):
+    """Per position: argmax token (lowest index on ties, R6) and confidence =
+    the largest softmax probability = 1 / sum_v exp(l_v - max l)."""
+    logits = lm_logits(h, W)
+    m = logits.max(axis=1)
+    a = np.argmax(logits, axis=1)          # numpy returns the first maximum
+    s = np.exp(logits - m[:, None]).sum(axis=1)
+    return 1.0 / s, a.astype(np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Commit, accept, certificate
+# ---------------------------------------------------------------------------
+
+def commit(conf, argmax, masked, tokens, tau: float):
+    """Threshold unmasking [OV §4.1 threshold 0.9] with the always-one rule
+    (R5).  Returns (masked_out, tokens_out, n_committed)."""
+    conf = np.asarray(conf, dtype=np.float64)
+    masked = np.asarray(masked).astype(np.uint8).copy()
+    tokens = np.asarray(tokens).astype(np.int64).copy()
+    b = conf.shape[0]
+    chosen = [i for i in range(b) if masked[i] and conf[i] > tau]
+    if not chosen:
+        best = None
+        for i in range(b):
+            if masked[i] and (best is None or conf[i] > conf[best]):
+                best = i
+        if best is not None:
+            chosen = [best]
+    for i in chosen:
+        tokens[i] = int(argmax[i])
+        masked[i] = 0
+    return masked, tokens, len(chosen)
+
+
+def spec_accept(draft, verify, P: int):
+    """Longest prefix where the diffusion draft equals the causal verify pass;
+    the KV cache is truncated to P + L and the L accepted tokens are appended.
+    [OV §2.3.1]  Returns (L, kv_len, accepted_tokens)."""
+    draft = np.asarray(draft).astype(np.int64)
+    verify = np.asarray(verify).astype(np.int64)
+    L = 0
+    while L < draft.shape[0] and draft[L] == verify[L]:
+        L += 1
+    return L, P + L, draft[:L].copy()
+
+
+def cert_scan(anchor_conf, anchor_tok, text_tok, k: int):
+    """LOWN certificate: order the masked positions by anchor confidence
+    (descending, R11), walk that order while the text-only top-1 equals the
+    anchor top-1; the walk length is |U_text|, and the image forward can be
+    skipped iff |U_text| >= k.  [LOWN 'method step details' (2), (3)]
+    Returns (order, L, skip_full)."""
+    conf = np.asarray(anchor_conf, dtype=np.float64)
+    anchor_tok = np.asarray(anchor_tok)
+    text_tok = np.asarray(text_tok)
+    n = conf.shape[0]
+    order = sorted(range(n), key=lambda i: (-conf[i], i))
+    L = 0
+    while L < n and text_tok[order[L]] == anchor_tok[order[L]]:
+        L += 1
+    return np.asarray(order, dtype=np.int64), L, int(L >= k)
+
+
+# ---------------------------------------------------------------------------
+# Compositions
+# ---------------------------------------------------------------------------
+
+def decode_step(q, k_cache, v_cache, P, h, W, masked, tokens, tau, kind="bidir"):
+    """One threshold (MDM) block-decode step: block attention over the prefix,
+    LM-head confidence, commit.  The attention output and the LM-head input are
+    separate tensors because the remaining transformer layers sit between them.
+    [OV §1.2, §4.1]"""
+    bq = q.shape[0]
+    o = block_attn(q, k_cache, v_cache, P, intra_block_mask(kind, bq))
+    conf, a = lmhead_conf(h, W)
+    m2, t2, n = commit(conf, a, masked, tokens, tau)
+    return {"attn": o, "conf": conf, "argmax": a, "masked": m2, "tokens": t2, "n_committed": n}
+
+
+def linear_spec_step(q_draft, kc_draft, vc_draft, q_verify, kc_verify, vc_verify, P,
+                     h_draft, h_verify, W):
+    """Linear self-speculative step: a bidirectional draft forward, a causal
+    verify forward, then longest-prefix accept.  [OV §2.3.1, two forwards]"""
+    bq = q_draft.shape[0]
+    o_d = block_attn(q_draft, kc_draft, vc_draft, P, intra_block_mask("bidir", bq))
+    _, draft = lmhead_conf(h_draft, W)
+    o_v = block_attn(q_verify, kc_verify, vc_verify, P, intra_block_mask("causal", bq))
+    _, verify = lmhead_conf(h_verify, W)
+    L, kv_len, acc = spec_accept(draft, verify, P)
+    return {"attn_draft": o_d, "attn_verify": o_v, "draft": draft, "verify": verify,
+            "accepted": L, "kv_len": kv_len, "out_tokens": acc}
+
+
+def fused_spec_step(q, k_cache, v_cache, P, h, W, draft_in):
+    """Quadratic (fused) speculative step: one forward of 2B rows under the
+    SPEC_FUSED mask (R10), one LM-head pass over the 2B rows; rows 0..B-1 give
+    the verify tokens for the draft tokens that were fed in; rows B..2B-1 give
+    the next draft.  [OV §2.3.1, one forward]"""
+    bq = q.shape[0]
+    b = bq // 2
+    o = block_attn(q, k_cache, v_cache, P, intra_block_mask("spec_fused", bq))
+    conf, a = lmhead_conf(h, W)
+    L, kv_len, acc = spec_accept(draft_in, a[:b], P)
+    return {"attn": o, "conf": conf, "argmax": a, "accepted": L, "kv_len": kv_len,
+            "out_tokens": acc, "next_draft": a[b:]}

@@ -1,0 +1,35 @@
+"""Checks that a generated LM-head input keeps every integer decision away
+from floating-point ties (test infrastructure only).
+
+A commit decision (conf > tau) or an argmax can only be compared bit-exactly
+between a float64 oracle and a float32 GPU kernel if no input sits on the
+boundary.  The guards used throughout the tests: the top-2 logit gap of every
+row exceeds 1e-2, and every confidence is at least 1e-3 away from tau.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .bdiff_oracle import lm_logits
+
+GAP_MIN = 1e-2
+TAU_DIST_MIN = 1e-3
+
+
+def lmhead_margins(h, W, tau=None):
+    """Return (top-2 logit gap per row, |conf - tau| per row or None)."""
+    logits = lm_logits(h, W)
+    top2 = np.sort(logits, axis=1)[:, -2:]
+    gap = top2[:, 1] - top2[:, 0]
+    if tau is None:
+        return gap, None
+    conf = 1.0 / np.exp(logits - top2[:, 1:2]).sum(axis=1)
+    return gap, np.abs(conf - tau)
+
+
+def lmhead_guarded(h, W, tau=None) -> bool:
+    gap, dist = lmhead_margins(h, W, tau)
+    ok = bool((gap > GAP_MIN).all())
+    if dist is not None:
+        ok = ok and bool((dist >= TAU_DIST_MIN).all())
+    return ok

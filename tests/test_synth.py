@@ -1,0 +1,70 @@
+"""The seeded input generators: determinism, number format, shapes, and the
+guards the parity tests rely on (checked with the oracle at full size)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_diffusion_vlm_amd import synth
+from oracle.guards import lmhead_margins
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 10,
+                        np.array([1.0, -1.0, 0.0, 1.00390625, 1.01171875, 3e38, -2e-39],
+                                 np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(synth.bf16_bits(x), ref)
+
+
+def test_same_seed_same_inputs_and_streams_differ():
+    a, b = synth.tiny(), synth.tiny()
+    for k in ("ds_q", "W", "h", "k_cache"):
+        assert np.array_equal(a[k], b[k])
+    c = synth.tiny(seed=5)
+    assert not np.array_equal(a["W"], c["W"])
+    d1 = synth.dualstream(n_vis=8, n_txt=8, H=2, dh=16)
+    d2 = synth.dualstream(n_vis=8, n_txt=8, H=2, dh=16)
+    assert np.array_equal(d1["q"], d2["q"])
+
+
+def test_truncated_values_and_shared_mask_rows():
+    r = synth.dualstream(n_vis=16, n_txt=64, H=2, dh=16, dtype="f32")
+    assert np.abs(r["v"]).max() <= 4.0
+    rows = r["n_vis"] + r["n_txt"] + np.nonzero(r["is_mask"])[0]
+    if rows.size > 1:
+        assert (r["q"][rows] == r["q"][rows[0]]).all()
+        assert (r["v"][rows] == r["v"][rows[0]]).all()
+
+
+def test_decode_shapes_full_size_metadata():
+    r = synth.qwen_decode(V=2000, d=256)
+    assert r["q"].shape == (16, 16, 128) and r["q"].dtype == np.uint16
+    assert r["k_cache"].shape == (2, 1296, 128) and r["P"] == 1280
+    assert r["masked"][0] == 0 and r["masked"][1:].all()
+
+
+def test_full_size_decode_guards_hold():
+    """The Qwen-shaped decode step at its real size: the planted hidden rows
+    keep the top-2 logit gap above 1e-2 and every confidence at least 1e-3
+    away from tau, so float32 and float64 take the same decisions."""
+    r = synth.qwen_decode()
+    gap, dist = lmhead_margins(r["h"], r["W"], r["tau"])
+    assert gap.min() > 1e-2 and dist.min() >= 1e-3
+    conf, a = oracle.lmhead_conf(r["h"], r["W"])
+    assert np.array_equal(a, r["targets"])
+    assert 0 < (conf[1:] > r["tau"]).sum() < 15
+
+
+@pytest.mark.parametrize("which", ["linear", "fused"])
+def test_full_size_spec_guards_hold(which):
+    if which == "linear":
+        r = synth.linear_spec()
+        hs = [r["h_draft"], r["h_verify"]]
+    else:
+        r = synth.fused_spec()
+        hs = [r["h"]]
+    for h in hs:
+        gap, _ = lmhead_margins(h, r["W"])
+        assert gap.min() > 1e-2
