@@ -1,0 +1,162 @@
+"""Python binding of libbdiff (include/bdiff.h): the same entry points under
+the same names, with argument marshalling only.
+
+Tensor arguments may be torch tensors (their data pointer is passed) or raw
+integer device addresses.  ``stream=None`` means torch's current stream on
+the current device.  Each call returns the bd_status code; a non-zero status
+raises BdError unless ``check=False``.  The library must be built
+(``python -m block_diffusion_vlm_amd.build``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import numpy as np
+
+LIB_PATH = Path(__file__).resolve().parent / "libbdiff.so"
+
+BD_OK, BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_ALIGN, BD_E_WORKSPACE, BD_E_DEVICE, BD_E_LAUNCH = range(8)
+BD_F32, BD_BF16 = 0, 1
+BD_MASK_BIDIR, BD_MASK_CAUSAL, BD_MASK_SPEC_FUSED = 0, 1, 2
+
+# Every symbol include/bdiff.h declares.
+EXPORTS = (
+    "bd_status_str", "bd_device_check", "bd_make_intra_mask",
+    "bd_block_attn_ws_bytes", "bd_block_attn",
+    "bd_lmhead_conf_ws_bytes", "bd_lmhead_conf",
+    "bd_commit", "bd_spec_accept", "bd_cert_scan", "bd_dualstream_attn",
+)
+
+
+class BdError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {bd_status_str(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "bd_status_str": ([_I], ctypes.c_char_p),
+    "bd_device_check": ([ctypes.c_int], _I),
+    "bd_make_intra_mask": ([_I, _I, _P], _I),
+    "bd_block_attn_ws_bytes": ([_I, _I, _I, _I, _I], _SZ),
+    "bd_block_attn": ([_I, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _F, _P, _P, _SZ, _P], _I),
+    "bd_lmhead_conf_ws_bytes": ([_I, _I, _I], _SZ),
+    "bd_lmhead_conf": ([_I, _P, _P, _I, _I, _I, _P, _P, _P, _SZ, _P], _I),
+    "bd_commit": ([_P, _P, _I, _F, _P, _P, _P, _P], _I),
+    "bd_spec_accept": ([_P, _P, _I, _I, _P, _P, _P, _P], _I),
+    "bd_cert_scan": ([_P, _P, _P, _I, _I, _P, _P, _P, _P], _I),
+    "bd_dualstream_attn": ([_I, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P], _I),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbdiff.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_diffusion_vlm_amd.build`")
+        L = ctypes.CDLL(str(LIB_PATH))
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    raise TypeError(f"expected a tensor or an integer address, got {type(x)!r}")
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ret(fn: str, status: int, check: bool) -> int:
+    if check and status != BD_OK:
+        raise BdError(fn, status)
+    return status
+
+
+def bd_status_str(status: int) -> str:
+    return lib().bd_status_str(int(status)).decode()
+
+
+def bd_device_check(device: int = 0) -> int:
+    return int(lib().bd_device_check(int(device)))
+
+
+def bd_make_intra_mask(kind: int, Bq: int, check: bool = True) -> np.ndarray:
+    rows = np.zeros(max(int(Bq), 1), dtype=np.uint64)
+    st = lib().bd_make_intra_mask(int(kind), int(Bq), rows.ctypes.data)
+    _ret("bd_make_intra_mask", st, check)
+    return rows[: max(int(Bq), 0)]
+
+
+def bd_block_attn_ws_bytes(P, Bq, Hq, Hkv, dh) -> int:
+    return int(lib().bd_block_attn_ws_bytes(P, Bq, Hq, Hkv, dh))
+
+
+def bd_block_attn(dt, q, k_cache, v_cache, P, cap, intra_mask, Bq, Hq, Hkv, dh, scale, out, ws,
+                  ws_bytes, stream=None, check=True) -> int:
+    st = lib().bd_block_attn(dt, _ptr(q), _ptr(k_cache), _ptr(v_cache), P, cap, _ptr(intra_mask),
+                             Bq, Hq, Hkv, dh, scale, _ptr(out), _ptr(ws), ws_bytes,
+                             _stream(stream))
+    return _ret("bd_block_attn", st, check)
+
+
+def bd_lmhead_conf_ws_bytes(B, d, V) -> int:
+    return int(lib().bd_lmhead_conf_ws_bytes(B, d, V))
+
+
+def bd_lmhead_conf(dt, h, W, B, d, V, conf, argmax, ws, ws_bytes, stream=None, check=True) -> int:
+    st = lib().bd_lmhead_conf(dt, _ptr(h), _ptr(W), B, d, V, _ptr(conf), _ptr(argmax), _ptr(ws),
+                              ws_bytes, _stream(stream))
+    return _ret("bd_lmhead_conf", st, check)
+
+
+def bd_commit(conf, argmax, B, tau, masked, tokens, n_committed, stream=None, check=True) -> int:
+    st = lib().bd_commit(_ptr(conf), _ptr(argmax), B, tau, _ptr(masked), _ptr(tokens),
+                         _ptr(n_committed), _stream(stream))
+    return _ret("bd_commit", st, check)
+
+
+def bd_spec_accept(draft, verify, B, P, accepted, kv_len, out_tokens, stream=None,
+                   check=True) -> int:
+    st = lib().bd_spec_accept(_ptr(draft), _ptr(verify), B, P, _ptr(accepted), _ptr(kv_len),
+                              _ptr(out_tokens), _stream(stream))
+    return _ret("bd_spec_accept", st, check)
+
+
+def bd_cert_scan(anchor_conf, anchor_tok, text_tok, n, k, order, accepted, skip_full,
+                 stream=None, check=True) -> int:
+    st = lib().bd_cert_scan(_ptr(anchor_conf), _ptr(anchor_tok), _ptr(text_tok), n, k,
+                            _ptr(order), _ptr(accepted), _ptr(skip_full), _stream(stream))
+    return _ret("bd_cert_scan", st, check)
+
+
+def bd_dualstream_attn(dt, q, k, v, n_vis, n_txt, block, H, dh, scale, out, stream=None,
+                       check=True) -> int:
+    st = lib().bd_dualstream_attn(dt, _ptr(q), _ptr(k), _ptr(v), n_vis, n_txt, block, H, dh,
+                                  scale, _ptr(out), _stream(stream))
+    return _ret("bd_dualstream_attn", st, check)

@@ -1,0 +1,181 @@
+// C ABI of libbdiff: argument validation on the host, then the kernel
+// launchers.  Nothing is enqueued unless every check passes; no call touches
+// the HIP runtime before its arguments are validated, so the error paths run
+// (and are tested) on machines without a GPU.
+#include <math.h>
+#include <string.h>
+
+#include "bd_internal.h"
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bd_status launch_status(hipError_t e) { return e == hipSuccess ? BD_OK : BD_E_LAUNCH; }
+
+inline float default_scale(float scale, int dh) {
+    return scale != 0.f ? scale : 1.0f / sqrtf(static_cast<float>(dh));
+}
+
+bool dh_ok(bd_dtype dt, int dh) {
+    if (dt == BD_BF16) return dh == 128;
+    return dh >= 4 && dh <= 128 && dh % 4 == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bd_status_str(bd_status s) {
+    switch (s) {
+        case BD_OK: return "ok";
+        case BD_E_NULL: return "a required pointer is NULL";
+        case BD_E_SHAPE: return "size out of range or inconsistent sizes";
+        case BD_E_DTYPE: return "unsupported dtype for this call";
+        case BD_E_ALIGN: return "pointer not 16-byte aligned";
+        case BD_E_WORKSPACE: return "workspace missing or too small";
+        case BD_E_DEVICE: return "device is not gfx950";
+        case BD_E_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+bd_status bd_device_check(int device) {
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || device < 0 || device >= count)
+        return BD_E_DEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return BD_E_DEVICE;
+    return strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? BD_OK : BD_E_DEVICE;
+}
+
+bd_status bd_make_intra_mask(bd_mask_kind kind, int32_t Bq, uint64_t* host_rows) {
+    if (!host_rows) return BD_E_NULL;
+    if (Bq < 1 || Bq > 64) return BD_E_SHAPE;
+    if (kind == BD_MASK_SPEC_FUSED && (Bq & 1)) return BD_E_SHAPE;
+    const uint64_t ones = (Bq == 64) ? ~0ull : ((1ull << Bq) - 1ull);
+    for (int i = 0; i < Bq; ++i) {
+        uint64_t row = 0;
+        switch (kind) {
+            case BD_MASK_BIDIR: row = ones; break;
+            case BD_MASK_CAUSAL: row = (i == 63) ? ~0ull : ((1ull << (i + 1)) - 1ull); break;
+            case BD_MASK_SPEC_FUSED: {
+                const int B = Bq / 2;
+                const uint64_t half = (1ull << B) - 1ull;
+                if (i < B) {
+                    row = (1ull << (i + 1)) - 1ull;                  // verify half: causal
+                } else {
+                    const int r = i - B;
+                    row = ((1ull << (r + 1)) - 1ull) | (half << B);   // j <= i-B, all drafts
+                }
+                break;
+            }
+            default: return BD_E_SHAPE;
+        }
+        host_rows[i] = row;
+    }
+    return BD_OK;
+}
+
+size_t bd_block_attn_ws_bytes(int32_t P, int32_t Bq, int32_t Hq, int32_t Hkv, int32_t dh) {
+    if (P < 0 || Bq < 1 || Bq > 64 || Hq < 1 || Hkv < 1 || dh < 1) return 0;
+    return bd::block_attn_ws_bytes(P, Bq, Hq, Hkv, dh);
+}
+
+bd_status bd_block_attn(bd_dtype dt, const void* q, const void* k_cache, const void* v_cache,
+                        int32_t P, int32_t cap, const uint64_t* intra_mask, int32_t Bq,
+                        int32_t Hq, int32_t Hkv, int32_t dh, float scale, void* out, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+    if (!q || !k_cache || !v_cache || !intra_mask || !out) return BD_E_NULL;
+    if (dt != BD_F32 && dt != BD_BF16) return BD_E_DTYPE;
+    if (Bq < 1 || Bq > 64 || P < 0 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0) return BD_E_SHAPE;
+    if ((int64_t)P + Bq > cap) return BD_E_SHAPE;
+    if (!dh_ok(dt, dh)) return BD_E_SHAPE;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return BD_E_ALIGN;
+    if (!(scale == scale) || isinf(scale)) return BD_E_SHAPE;
+    const float sc = default_scale(scale, dh);
+    if (dt == BD_F32)
+        return launch_status(bd::launch_block_attn_f32(
+            static_cast<const float*>(q), static_cast<const float*>(k_cache),
+            static_cast<const float*>(v_cache), P, cap, intra_mask, Bq, Hq, Hkv, dh, sc,
+            static_cast<float*>(out), stream));
+    const size_t need = bd::block_attn_ws_bytes(P, Bq, Hq, Hkv, dh);
+    if (!ws || ws_bytes < need) return BD_E_WORKSPACE;
+    if (!aligned16(ws)) return BD_E_ALIGN;
+    return launch_status(bd::launch_block_attn_bf16(q, k_cache, v_cache, P, cap, intra_mask, Bq,
+                                                    Hq, Hkv, sc, out, ws, stream));
+}
+
+size_t bd_lmhead_conf_ws_bytes(int32_t B, int32_t d, int32_t V) {
+    if (B < 1 || B > 64 || d < 1 || V < 1) return 0;
+    return bd::lmhead_ws_bytes(B, d, V);
+}
+
+bd_status bd_lmhead_conf(bd_dtype dt, const void* h, const void* W, int32_t B, int32_t d,
+                         int32_t V, float* conf, int32_t* argmax, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+    if (!h || !W || !conf || !argmax) return BD_E_NULL;
+    if (dt != BD_F32 && dt != BD_BF16) return BD_E_DTYPE;
+    if (B < 1 || B > 64 || d < 1 || V < 1) return BD_E_SHAPE;
+    if (dt == BD_BF16 && (d % 128 != 0 || d > 16384)) return BD_E_SHAPE;
+    if (!aligned16(h) || !aligned16(W)) return BD_E_ALIGN;
+    if (!ws || ws_bytes < bd::lmhead_ws_bytes(B, d, V)) return BD_E_WORKSPACE;
+    if (!aligned16(ws)) return BD_E_ALIGN;
+    if (dt == BD_F32)
+        return launch_status(bd::launch_lmhead_f32(static_cast<const float*>(h),
+                                                   static_cast<const float*>(W), B, d, V, conf,
+                                                   argmax, ws, stream));
+    return launch_status(bd::launch_lmhead_bf16(h, W, B, d, V, conf, argmax, ws, stream));
+}
+
+bd_status bd_commit(const float* conf, const int32_t* argmax, int32_t B, float tau,
+                    uint8_t* masked, int32_t* tokens, int32_t* n_committed, hipStream_t stream) {
+    if (!conf || !argmax || !masked || !tokens || !n_committed) return BD_E_NULL;
+    if (B < 0 || B > 64) return BD_E_SHAPE;
+    if (!(tau == tau)) return BD_E_SHAPE;
+    return launch_status(bd::launch_commit(conf, argmax, B, tau, masked, tokens, n_committed,
+                                           stream));
+}
+
+bd_status bd_spec_accept(const int32_t* draft, const int32_t* verify, int32_t B, int32_t P,
+                         int32_t* accepted, int32_t* kv_len, int32_t* out_tokens,
+                         hipStream_t stream) {
+    if (!draft || !verify || !accepted || !kv_len || !out_tokens) return BD_E_NULL;
+    if (B < 0 || B > 64 || P < 0 || (int64_t)P + B > INT32_MAX) return BD_E_SHAPE;
+    return launch_status(
+        bd::launch_spec_accept(draft, verify, B, P, accepted, kv_len, out_tokens, stream));
+}
+
+bd_status bd_cert_scan(const float* anchor_conf, const int32_t* anchor_tok,
+                       const int32_t* text_tok, int32_t n, int32_t k, int32_t* order,
+                       int32_t* accepted, int32_t* skip_full, hipStream_t stream) {
+    if (!anchor_conf || !anchor_tok || !text_tok || !order || !accepted || !skip_full)
+        return BD_E_NULL;
+    if (n < 0 || n > 1024) return BD_E_SHAPE;
+    return launch_status(bd::launch_cert_scan(anchor_conf, anchor_tok, text_tok, n, k, order,
+                                              accepted, skip_full, stream));
+}
+
+bd_status bd_dualstream_attn(bd_dtype dt, const void* q, const void* k, const void* v,
+                             int32_t n_vis, int32_t n_txt, int32_t block, int32_t H, int32_t dh,
+                             float scale, void* out, hipStream_t stream) {
+    if (!q || !k || !v || !out) return BD_E_NULL;
+    if (dt != BD_F32 && dt != BD_BF16) return BD_E_DTYPE;
+    if (n_vis < 0 || n_txt < 0 || block < 1 || H < 1) return BD_E_SHAPE;
+    const int64_t N = (int64_t)n_vis + 2 * (int64_t)n_txt;
+    if (N < 1 || N > (1 << 24)) return BD_E_SHAPE;
+    if (!dh_ok(dt, dh)) return BD_E_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return BD_E_ALIGN;
+    if (!(scale == scale) || isinf(scale)) return BD_E_SHAPE;
+    const float sc = default_scale(scale, dh);
+    if (dt == BD_F32)
+        return launch_status(bd::launch_dualstream_f32(
+            static_cast<const float*>(q), static_cast<const float*>(k),
+            static_cast<const float*>(v), n_vis, n_txt, block, H, dh, sc,
+            static_cast<float*>(out), stream));
+    return launch_status(
+        bd::launch_dualstream_bf16(q, k, v, n_vis, n_txt, block, H, sc, out, stream));
+}
+
+}  // extern "C"

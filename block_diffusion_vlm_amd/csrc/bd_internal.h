@@ -1,0 +1,96 @@
+// Internal declarations shared by the libbdiff translation units: vector
+// types for gfx950 MFMA operands, small device helpers, and the kernel
+// launchers that the C ABI layer calls after validating its arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bdiff.h"
+
+namespace bd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWave = 64;
+
+// bfloat16 bits -> float32 (exact).
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float32 -> bfloat16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Two floats -> two packed bfloat16 (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+// Softmax partial state (max in log2 units, sum of 2^(x - max), index).
+struct ArgSoft {
+    float m;
+    float s;
+    int a;
+};
+
+// Merge two partial states: larger max wins the index, equal maxima keep the
+// smaller index, sums are rescaled to the common max.
+__device__ __forceinline__ ArgSoft merge(ArgSoft x, ArgSoft y) {
+    if (y.m > x.m || (y.m == x.m && y.a < x.a)) {
+        ArgSoft t = x;
+        x = y;
+        y = t;
+    }
+    // x now holds the winner
+    if (y.s > 0.f) x.s += y.s * exp2f(y.m - x.m);
+    return x;
+}
+
+// Kernel launchers (defined next to their kernels).  They assume validated
+// arguments and return the HIP launch status.
+hipError_t launch_commit(const float* conf, const int32_t* argmax, int B, float tau,
+                         uint8_t* masked, int32_t* tokens, int32_t* n_committed, hipStream_t st);
+hipError_t launch_spec_accept(const int32_t* draft, const int32_t* verify, int B, int P,
+                              int32_t* accepted, int32_t* kv_len, int32_t* out_tokens,
+                              hipStream_t st);
+hipError_t launch_cert_scan(const float* conf, const int32_t* atok, const int32_t* ttok, int n,
+                            int k, int32_t* order, int32_t* accepted, int32_t* skip,
+                            hipStream_t st);
+
+// LM head
+int lmhead_grid(int B, int d, int V);           // workgroups used for a shape
+size_t lmhead_ws_bytes(int B, int d, int V);
+hipError_t launch_lmhead_bf16(const void* h, const void* W, int B, int d, int V, float* conf,
+                              int32_t* argmax, void* ws, hipStream_t st);
+hipError_t launch_lmhead_f32(const float* h, const float* W, int B, int d, int V, float* conf,
+                             int32_t* argmax, void* ws, hipStream_t st);
+
+// Block attention
+size_t block_attn_ws_bytes(int P, int Bq, int Hq, int Hkv, int dh);
+hipError_t launch_block_attn_bf16(const void* q, const void* kc, const void* vc, int P, int cap,
+                                  const uint64_t* mask, int Bq, int Hq, int Hkv, float scale,
+                                  void* out, void* ws, hipStream_t st);
+hipError_t launch_block_attn_f32(const float* q, const float* kc, const float* vc, int P, int cap,
+                                 const uint64_t* mask, int Bq, int Hq, int Hkv, int dh,
+                                 float scale, float* out, hipStream_t st);
+
+// Dual-stream attention
+hipError_t launch_dualstream_bf16(const void* q, const void* k, const void* v, int n_vis,
+                                  int n_txt, int block, int H, float scale, void* out,
+                                  hipStream_t st);
+hipError_t launch_dualstream_f32(const float* q, const float* k, const float* v, int n_vis,
+                                 int n_txt, int block, int H, int dh, float scale, float* out,
+                                 hipStream_t st);
+
+}  // namespace bd

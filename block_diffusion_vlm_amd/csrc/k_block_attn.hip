@@ -1,0 +1,247 @@
+// Block attention at decode time: Bq block queries attend the KV-cached
+// prefix (visual + prompt + earlier blocks, always visible) and the block's
+// own keys under an intra-block bitmask (Fast-dVLM overview §1.2: blocks in
+// order with a reusable KV cache, bidirectional denoising inside a block;
+// §2.3.1 for the causal verify pass and the fused draft+verify mask).
+//
+// bf16 path: split-K over the keys (flash-decoding).  Grouped-query heads are
+// packed so that all Bq x (Hq/Hkv) query rows of one KV head form the rows of
+// one tile; workgroup (split, kv head, row block) handles 64 keys for up to
+// 128 rows (4 waves x 32 rows) and writes an unnormalised partial
+// (max, sum, O) per row; a second kernel merges the splits in a fixed order.
+#include "attn_common.h"
+
+namespace bd {
+
+namespace {
+
+using namespace attn;
+
+constexpr int kRowsPerWg = 128;
+
+struct Partials {
+    float* m;   // [rows][nsplit]
+    float* l;   // [rows][nsplit]
+    float* o;   // [rows][nsplit][128]
+};
+
+__host__ __device__ inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+__host__ __device__ inline Partials partials(void* ws, int rows, int nsplit) {
+    uint8_t* p = static_cast<uint8_t*>(ws);
+    Partials r;
+    r.m = reinterpret_cast<float*>(p);
+    size_t off = al256(size_t(rows) * nsplit * 4);
+    r.l = reinterpret_cast<float*>(p + off);
+    off += al256(size_t(rows) * nsplit * 4);
+    r.o = reinterpret_cast<float*>(p + off);
+    return r;
+}
+
+inline size_t partials_bytes(int rows, int nsplit) {
+    return 2 * al256(size_t(rows) * nsplit * 4) + al256(size_t(rows) * nsplit * kDh * 4);
+}
+
+__global__ __launch_bounds__(256) void block_attn_split_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, int P, int cap, const uint64_t* __restrict__ mask, int Bq,
+    int Hq, int Hkv, float scale_log2, void* __restrict__ ws, int nsplit) {
+    __shared__ __align__(16) Tiles tiles;
+    const int split = blockIdx.x;
+    const int g = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int group = Hq / Hkv;
+    const int R = Bq * group;                       // query rows of this KV head
+    const int Nk = P + Bq;
+    const int j0 = split * kBN;
+
+    load_tile(tiles, kc + size_t(g) * cap * kDh, vc + size_t(g) * cap * kDh, kDh, j0, Nk);
+
+    // Query row of this lane: r -> (block query i, head g*group + r % group).
+    const int r = blockIdx.z * kRowsPerWg + wave * 32 + (lane & 31);
+    const bool row_ok = r < R;
+    const int qi = row_ok ? r / group : 0;
+    const int qh = g * group + (row_ok ? r % group : 0);
+    bf16x8 qf[8];
+    load_q(qf, row_ok ? q + (size_t(qi) * Hq + qh) * kDh : nullptr, lane);
+    const uint64_t mbits = row_ok ? mask[qi] : 0;
+    __syncthreads();
+
+    f32x16 sacc[2];
+    scores(sacc, tiles, qf, lane);
+
+    float x[2][16];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int j = j0 + 32 * kb + acc_row(e, lane);
+            const bool vis = (j < P) || (j < Nk && ((mbits >> (j - P)) & 1ull));
+            x[kb][e] = vis ? sacc[kb][e] * scale_log2 : -INFINITY;
+            mx = fmaxf(mx, x[kb][e]);
+        }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mref = (mx == -INFINITY) ? 0.f : mx;
+    float p[2][16];
+    float l = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            p[kb][e] = exp2f(x[kb][e] - mref);
+            l += p[kb][e];
+        }
+    l += __shfl_xor(l, 32);
+
+    f32x16 oacc[4] = {};
+    accumulate_pv(oacc, tiles, p, lane);
+
+    if (row_ok) {
+        const size_t rg = size_t(g) * R + r;        // global row
+        const Partials pt = partials(ws, Hkv * R, nsplit);
+        if (lane < 32) {
+            pt.m[rg * nsplit + split] = mx;
+            pt.l[rg * nsplit + split] = l;
+        }
+        float* o = pt.o + (rg * nsplit + split) * kDh;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const int dh = 32 * db + acc_row(4 * e4, lane);
+                *reinterpret_cast<f32x4*>(o + dh) =
+                    f32x4{oacc[db][4 * e4], oacc[db][4 * e4 + 1], oacc[db][4 * e4 + 2],
+                          oacc[db][4 * e4 + 3]};
+            }
+    }
+}
+
+// One wave per query row: merge the splits in order and normalise.
+__global__ __launch_bounds__(64) void block_attn_combine_kernel(const void* __restrict__ ws,
+                                                                int Bq, int Hq, int Hkv,
+                                                                int nsplit,
+                                                                uint16_t* __restrict__ out) {
+    const int rg = blockIdx.x;                      // global row = g * R + r
+    const int group = Hq / Hkv;
+    const int R = Bq * group;
+    const int g = rg / R;
+    const int r = rg % R;
+    const int qi = r / group;
+    const int qh = g * group + r % group;
+    const Partials pt = partials(const_cast<void*>(ws), Hkv * R, nsplit);
+    const float* m = pt.m + size_t(rg) * nsplit;
+    const float* l = pt.l + size_t(rg) * nsplit;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, m[s]);
+    const int dh = 2 * threadIdx.x;
+    float o0 = 0.f, o1 = 0.f, L = 0.f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < nsplit; ++s) {
+            if (m[s] == -INFINITY) continue;
+            const float w = exp2f(m[s] - M);
+            const float* o = pt.o + (size_t(rg) * nsplit + s) * kDh;
+            L += w * l[s];
+            o0 += w * o[dh];
+            o1 += w * o[dh + 1];
+        }
+        o0 /= L;
+        o1 /= L;
+    }
+    uint16_t* dst = out + (size_t(qi) * Hq + qh) * kDh + dh;
+    *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(o0, o1);
+}
+
+// ---------------------------------------------------------------------------
+// float32 path: one wave per (query, head) row, keys in chunks of 64 with an
+// online softmax; lanes own keys for the scores and dims for the output.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void block_attn_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
+    int P, int cap, const uint64_t* __restrict__ mask, int Bq, int Hq, int Hkv, int dh,
+    float scale_log2, float* __restrict__ out) {
+    __shared__ float qs[128];
+    const int qi = blockIdx.x / Hq;
+    const int h = blockIdx.x % Hq;
+    const int g = h / (Hq / Hkv);
+    const int lane = threadIdx.x;
+    const float* qr = q + (size_t(qi) * Hq + h) * dh;
+    for (int d = lane; d < dh; d += 64) qs[d] = qr[d];
+    __syncthreads();
+    const uint64_t mbits = mask[qi];
+    const float* kb = kc + size_t(g) * cap * dh;
+    const float* vb = vc + size_t(g) * cap * dh;
+    const int Nk = P + Bq;
+    float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int j0 = 0; j0 < Nk; j0 += 64) {
+        const int j = j0 + lane;
+        float x = -INFINITY;
+        if (j < Nk && (j < P || ((mbits >> (j - P)) & 1ull))) {
+            const float* kr = kb + size_t(j) * dh;
+            float acc = 0.f;
+            for (int d = 0; d < dh; ++d) acc = fmaf(qs[d], kr[d], acc);
+            x = acc * scale_log2;
+        }
+        float cm = x;
+        for (int off = 32; off > 0; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
+        const float mn = fmaxf(m, cm);
+        if (mn == -INFINITY) continue;
+        const float alpha = exp2f(m - mn);
+        const float p = exp2f(x - mn);
+        float ps = p;
+        for (int off = 32; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
+        l = l * alpha + ps;
+        o0 *= alpha;
+        o1 *= alpha;
+        const int cnt = Nk - j0 < 64 ? Nk - j0 : 64;
+        for (int t = 0; t < cnt; ++t) {
+            const float pt = __shfl(p, t);
+            const float* vr = vb + size_t(j0 + t) * dh;
+            if (lane < dh) o0 = fmaf(pt, vr[lane], o0);
+            if (lane + 64 < dh) o1 = fmaf(pt, vr[lane + 64], o1);
+        }
+        m = mn;
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float* orow = out + (size_t(qi) * Hq + h) * dh;
+    if (lane < dh) orow[lane] = o0 * inv;
+    if (lane + 64 < dh) orow[lane + 64] = o1 * inv;
+}
+
+}  // namespace
+
+size_t block_attn_ws_bytes(int P, int Bq, int Hq, int Hkv, int dh) {
+    (void)dh;
+    const int nsplit = (P + Bq + kBN - 1) / kBN;
+    const int rows = Bq * Hq;      // = Hkv * R
+    (void)Hkv;
+    return partials_bytes(rows, nsplit);
+}
+
+hipError_t launch_block_attn_bf16(const void* q, const void* kc, const void* vc, int P, int cap,
+                                  const uint64_t* mask, int Bq, int Hq, int Hkv, float scale,
+                                  void* out, void* ws, hipStream_t st) {
+    const int nsplit = (P + Bq + kBN - 1) / kBN;
+    const int R = Bq * (Hq / Hkv);
+    const dim3 grid(nsplit, Hkv, (R + kRowsPerWg - 1) / kRowsPerWg);
+    hipLaunchKernelGGL(block_attn_split_kernel, grid, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
+                       static_cast<const uint16_t*>(vc), P, cap, mask, Bq, Hq, Hkv,
+                       scale * kLog2e, ws, nsplit);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(block_attn_combine_kernel, dim3(Bq * Hq), dim3(64), 0, st, ws, Bq, Hq, Hkv,
+                       nsplit, static_cast<uint16_t*>(out));
+    return hipGetLastError();
+}
+
+hipError_t launch_block_attn_f32(const float* q, const float* kc, const float* vc, int P, int cap,
+                                 const uint64_t* mask, int Bq, int Hq, int Hkv, int dh,
+                                 float scale, float* out, hipStream_t st) {
+    hipLaunchKernelGGL(block_attn_f32_kernel, dim3(Bq * Hq), dim3(64), 0, st, q, kc, vc, P, cap,
+                       mask, Bq, Hq, Hkv, dh, scale * kLog2e, out);
+    return hipGetLastError();
+}
+
+}  // namespace bd

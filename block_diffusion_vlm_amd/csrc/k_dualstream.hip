@@ -1,0 +1,247 @@
+// Training-time dual-stream attention (Fast-dVLM overview §2.2.1-§2.2.2;
+// Thai article §4.1, §4.4) over the vision-efficient token order
+// [visual | clean text | noisy text]:
+//   C2C  clean stream (visual + clean text) is token-level causal;
+//   N2C  a noisy token sees every visual token and the clean text up to its
+//        own position (the printed N2C matrix includes the diagonal);
+//   N2N  noisy tokens attend bidirectionally inside their block;
+//   no clean token sees a noisy one.
+//
+// bf16 path: flash attention forward on v_mfma_f32_32x32x16_bf16.  A
+// workgroup owns 128 query rows of one head (4 waves x 32 rows) and streams
+// 64-key tiles of K and V^T through LDS with an online softmax.  The mask is
+// never materialised: for each query tile the visible key ranges follow in
+// closed form from the three rules, every tile outside them is skipped, tiles
+// that are visible for every (query, key) pair skip the per-element test,
+// and only tiles crossing a rule boundary evaluate it.  Query tiles are
+// launched heaviest first so that the long rows do not form a tail.
+#include "attn_common.h"
+
+namespace bd {
+
+namespace {
+
+using namespace attn;
+
+constexpr int kBM = 128;
+
+struct Geometry {
+    int n_vis, n_txt, ctx, N, block;
+};
+
+// Visibility of key j for query i (both < N).
+__device__ __forceinline__ bool visible(const Geometry& G, int i, int j) {
+    if (i < G.ctx) return j <= i;                      // C2C (j <= i < ctx)
+    const int r = i - G.ctx;
+    if (j < G.n_vis) return true;                      // N2C, visual keys
+    if (j < G.ctx) return (j - G.n_vis) <= r;          // N2C, clean text
+    return (j - G.ctx) / G.block == r / G.block;       // N2N
+}
+
+// Key ranges a query tile [i0, i1) must visit: range A = [0, a_end) (visual +
+// clean keys), range B = [b_beg, b_end) (noisy keys, possibly empty).
+__host__ __device__ inline void key_ranges(const Geometry& G, int i0, int i1, int* a_end,
+                                           int* b_beg, int* b_end) {
+    int ae = 0;
+    if (i0 < G.ctx) ae = (i1 < G.ctx ? i1 : G.ctx);                 // clean rows: j <= i
+    if (i1 > G.ctx) {
+        const int r_last = i1 - 1 - G.ctx;
+        const int noisy_reach = G.n_vis + r_last + 1;                // visual + clean <= r
+        ae = ae > noisy_reach ? ae : noisy_reach;
+        const int r_first = (i0 > G.ctx ? i0 : G.ctx) - G.ctx;
+        *b_beg = G.ctx + (r_first / G.block) * G.block;
+        int be = G.ctx + (r_last / G.block + 1) * G.block;
+        *b_end = be < G.N ? be : G.N;
+    } else {
+        *b_beg = *b_end = 0;
+    }
+    *a_end = ae;
+}
+
+// True when every (query, key) pair of the tile is visible.
+__device__ __forceinline__ bool tile_full(const Geometry& G, int i0, int i1, int j0, int j1) {
+    if (i1 > G.N) i1 = G.N;
+    if (j1 > G.N) return false;
+    if (i1 <= G.ctx) return j1 - 1 <= i0;                            // causal, below diagonal
+    if (i0 >= G.ctx) {
+        const int r0 = i0 - G.ctx, r1 = i1 - 1 - G.ctx;
+        if (j1 <= G.ctx) return j1 - 1 <= G.n_vis + r0;               // visual / clean text
+        if (j0 >= G.ctx) {                                            // noisy keys
+            const int b0 = r0 / G.block;
+            return b0 == r1 / G.block && (j0 - G.ctx) / G.block == b0 &&
+                   (j1 - 1 - G.ctx) / G.block == b0;
+        }
+    }
+    return false;
+}
+
+__global__ __launch_bounds__(256) void dualstream_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, Geometry G, int H, float scale_log2,
+    uint16_t* __restrict__ out, int nqt) {
+    __shared__ __align__(16) Tiles tiles;
+    const int h = blockIdx.x;
+    // Later query tiles see more keys (causal context, then the visual prefix
+    // plus clean text for the noisy stream), so tiles are issued last-first.
+    const int qt = nqt - 1 - blockIdx.y;
+    const int i0 = qt * kBM;
+    const int i1 = (i0 + kBM < G.N) ? i0 + kBM : G.N;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row = i0 + wave * 32 + (lane & 31);
+    const bool row_ok = row < G.N;
+    const size_t rs = size_t(H) * kDh;               // element stride between tokens
+
+    bf16x8 qf[8];
+    load_q(qf, row_ok ? q + size_t(row) * rs + size_t(h) * kDh : nullptr, lane);
+
+    int a_end, b_beg, b_end;
+    key_ranges(G, i0, i1, &a_end, &b_beg, &b_end);
+    const int na = (a_end + kBN - 1) / kBN;
+    const int nb = b_end > b_beg ? (b_end - b_beg + kBN - 1) / kBN : 0;
+
+    float m = -INFINITY, l = 0.f;
+    f32x16 oacc[4] = {};
+    const uint16_t* kb = k + size_t(h) * kDh;
+    const uint16_t* vb = v + size_t(h) * kDh;
+
+    for (int t = 0; t < na + nb; ++t) {
+        int j0, jend;
+        if (t < na) {
+            j0 = t * kBN;
+            jend = a_end;
+        } else {
+            j0 = b_beg + (t - na) * kBN;
+            jend = b_end;
+        }
+        const int j1 = j0 + kBN < jend ? j0 + kBN : jend;
+        __syncthreads();                               // previous tile fully consumed
+        load_tile(tiles, kb, vb, rs, j0, jend);
+        __syncthreads();
+
+        f32x16 sacc[2];
+        scores(sacc, tiles, qf, lane);
+
+        const bool full = (j1 - j0 == kBN) && tile_full(G, i0, i1, j0, j1);
+        float x[2][16];
+        float mx = m;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int j = j0 + 32 * kb2 + acc_row(e, lane);
+                const bool vis = full || (row_ok && j < j1 && visible(G, row, j));
+                x[kb2][e] = vis ? sacc[kb2][e] * scale_log2 : -INFINITY;
+                mx = fmaxf(mx, x[kb2][e]);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mref = (mx == -INFINITY) ? 0.f : mx;
+        const float alpha = exp2f(m - mref);
+        float p[2][16];
+        float ls = 0.f;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                p[kb2][e] = exp2f(x[kb2][e] - mref);
+                ls += p[kb2][e];
+            }
+        ls += __shfl_xor(ls, 32);
+        l = l * alpha + ls;
+        m = mx;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+        accumulate_pv(oacc, tiles, p, lane);
+    }
+
+    if (row_ok) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        uint16_t* orow = out + size_t(row) * rs + size_t(h) * kDh;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const int dh = 32 * db + acc_row(4 * e4, lane);
+                u32x2 w = {pack_bf16x2(oacc[db][4 * e4] * inv, oacc[db][4 * e4 + 1] * inv),
+                           pack_bf16x2(oacc[db][4 * e4 + 2] * inv, oacc[db][4 * e4 + 3] * inv)};
+                *reinterpret_cast<u32x2*>(orow + dh) = w;
+            }
+    }
+}
+
+// float32 path: one wave per (token, head) row, online softmax over the
+// visible keys in chunks of 64.
+__global__ __launch_bounds__(64) void dualstream_f32_kernel(const float* __restrict__ q,
+                                                            const float* __restrict__ k,
+                                                            const float* __restrict__ v,
+                                                            Geometry G, int H, int dh,
+                                                            float scale_log2,
+                                                            float* __restrict__ out) {
+    __shared__ float qs[128];
+    const int i = blockIdx.x / H;
+    const int h = blockIdx.x % H;
+    const int lane = threadIdx.x;
+    const size_t rs = size_t(H) * dh;
+    for (int d = lane; d < dh; d += 64) qs[d] = q[size_t(i) * rs + size_t(h) * dh + d];
+    __syncthreads();
+    float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int j0 = 0; j0 < G.N; j0 += 64) {
+        const int j = j0 + lane;
+        float x = -INFINITY;
+        if (j < G.N && visible(G, i, j)) {
+            const float* kr = k + size_t(j) * rs + size_t(h) * dh;
+            float acc = 0.f;
+            for (int d = 0; d < dh; ++d) acc = fmaf(qs[d], kr[d], acc);
+            x = acc * scale_log2;
+        }
+        float cm = x;
+        for (int off = 32; off > 0; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
+        const float mn = fmaxf(m, cm);
+        if (mn == -INFINITY) continue;
+        const float alpha = exp2f(m - mn);
+        const float p = exp2f(x - mn);
+        float ps = p;
+        for (int off = 32; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
+        l = l * alpha + ps;
+        o0 *= alpha;
+        o1 *= alpha;
+        const int cnt = G.N - j0 < 64 ? G.N - j0 : 64;
+        for (int t = 0; t < cnt; ++t) {
+            const float pt = __shfl(p, t);
+            const float* vr = v + size_t(j0 + t) * rs + size_t(h) * dh;
+            if (lane < dh) o0 = fmaf(pt, vr[lane], o0);
+            if (lane + 64 < dh) o1 = fmaf(pt, vr[lane + 64], o1);
+        }
+        m = mn;
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float* orow = out + size_t(i) * rs + size_t(h) * dh;
+    if (lane < dh) orow[lane] = o0 * inv;
+    if (lane + 64 < dh) orow[lane + 64] = o1 * inv;
+}
+
+}  // namespace
+
+hipError_t launch_dualstream_bf16(const void* q, const void* k, const void* v, int n_vis,
+                                  int n_txt, int block, int H, float scale, void* out,
+                                  hipStream_t st) {
+    Geometry G{n_vis, n_txt, n_vis + n_txt, n_vis + 2 * n_txt, block};
+    const int nqt = (G.N + kBM - 1) / kBM;
+    const dim3 grid(H, nqt);
+    hipLaunchKernelGGL(dualstream_bf16_kernel, grid, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), G, H, scale * kLog2e,
+                       static_cast<uint16_t*>(out), nqt);
+    return hipGetLastError();
+}
+
+hipError_t launch_dualstream_f32(const float* q, const float* k, const float* v, int n_vis,
+                                 int n_txt, int block, int H, int dh, float scale, float* out,
+                                 hipStream_t st) {
+    Geometry G{n_vis, n_txt, n_vis + n_txt, n_vis + 2 * n_txt, block};
+    hipLaunchKernelGGL(dualstream_f32_kernel, dim3(G.N * H), dim3(64), 0, st, q, k, v, G, H, dh,
+                       scale * kLog2e, out);
+    return hipGetLastError();
+}
+
+}  // namespace bd

@@ -1,0 +1,487 @@
+// LM-head confidence: logits = h W^T fused with a split-vocabulary softmax
+// maximum, so no logit ever reaches memory.  Per position b it yields the
+// argmax token and conf = max_w p(w) = 1 / sum_v exp(l_v - max l) (the anchor
+// confidence of the LOWN article, 'method step details' (1)).
+//
+// bf16 path (gfx950 MFMA).  The contraction is W[V][d] x h^T[d][B] with the
+// vocabulary as the M dimension and the positions as N, on
+// v_mfma_f32_16x16x32_bf16.  W is streamed exactly once, straight from HBM
+// into the A operand (no LDS): lane l of a wave reads 64 contiguous bytes of
+// vocabulary row (l % 16) per 128-element K chunk, so a wave instruction
+// group covers 16 rows x 256 B.  The K index inside a chunk is permuted
+// identically for A and B (lane group g, MFMA j, element e <-> k = 32g + 8j + e),
+// which leaves the dot product unchanged.  h is tiny and is held in
+// registers as ready-made B fragments for the wave's K range.
+//
+// A workgroup has `ks` waves that split K; per 16-row vocabulary tile they
+// add their partial logits through LDS and one wave (rotating) folds the 16
+// rows into running (max, sum, argmax) states in the log2 domain.  Tiles are
+// dealt round-robin to a persistent grid, so the load is even to within one
+// tile per workgroup.  Each workgroup writes one partial state per position;
+// the last workgroup to finish (completion counter) merges all partials in a
+// fixed order, so the result is deterministic.
+#include "bd_internal.h"
+
+namespace bd {
+
+namespace {
+
+constexpr int kMaxGrid = 512;       // persistent workgroups for the bf16 path
+constexpr int kCtrBytes = 256;      // completion counter area at the start of ws
+
+struct WsView {
+    unsigned* ctr;
+    float* m;
+    float* s;
+    int* a;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+__host__ __device__ inline WsView ws_view(void* ws, int G, int B) {
+    uint8_t* p = static_cast<uint8_t*>(ws);
+    WsView v;
+    v.ctr = reinterpret_cast<unsigned*>(p);
+    size_t off = kCtrBytes;
+    v.m = reinterpret_cast<float*>(p + off);
+    off += align256(size_t(G) * B * sizeof(float));
+    v.s = reinterpret_cast<float*>(p + off);
+    off += align256(size_t(G) * B * sizeof(float));
+    v.a = reinterpret_cast<int*>(p + off);
+    return v;
+}
+
+inline size_t ws_size(int G, int B) {
+    return kCtrBytes + 3 * align256(size_t(G) * B * 4);
+}
+
+// Fold four logits (rows row0..row0+3, already in log2 units) into a state.
+// Rows are visited in increasing order, so a strict '>' keeps the lowest
+// index among equal maxima.
+__device__ __forceinline__ void fold4(ArgSoft& st, const float x[4], int row0, int V) {
+    float mx = st.m;
+    int ax = st.a;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (row0 + i < V && x[i] > mx) {
+            mx = x[i];
+            ax = row0 + i;
+        }
+    }
+    float s = (st.s > 0.f) ? st.s * exp2f(st.m - mx) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (row0 + i < V) s += exp2f(x[i] - mx);
+    st.m = mx;
+    st.s = s;
+    st.a = ax;
+}
+
+__device__ __forceinline__ ArgSoft shfl_xor_state(ArgSoft x, int off) {
+    ArgSoft y;
+    y.m = __shfl_xor(x.m, off);
+    y.s = __shfl_xor(x.s, off);
+    y.a = __shfl_xor(x.a, off);
+    return y;
+}
+
+// Arrival on the completion counter; returns true in the last workgroup.
+// Partials written before the call are visible to the last workgroup after
+// it returns (device-scope release/acquire fences around the atomic).
+__device__ __forceinline__ bool arrive_last(unsigned* ctr, unsigned nblocks) {
+    __shared__ unsigned s_last;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned old = atomicInc(ctr, nblocks - 1);   // wraps back to 0
+        s_last = (old == nblocks - 1) ? 1u : 0u;
+    }
+    __syncthreads();
+    const bool last = s_last != 0;
+    if (last) __threadfence();
+    return last;
+}
+
+// Merge G partial states per position in a fixed order and write the
+// outputs.  Called by every thread of the last workgroup (blockDim.x >= 64,
+// a multiple of 64).
+__device__ void final_combine(const WsView& w, int G, int B, float* conf, int32_t* argmax) {
+    int bp = 1;
+    while (bp < B) bp <<= 1;
+    const int nthr = blockDim.x;
+    int T = nthr / bp;                  // threads per position (power of two)
+    if (T > 64) T = 64;
+    const int col = threadIdx.x / T;
+    const int sub = threadIdx.x % T;
+    for (int c0 = 0; c0 < B; c0 += nthr / T) {
+        const int c = c0 + col;
+        ArgSoft st{-INFINITY, 0.f, 0x7fffffff};
+        if (c < B) {
+            int p = sub;
+            for (; p + 7 * T < G; p += 8 * T) {
+                float mm[8], ss[8];
+                int aa[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const size_t idx = size_t(p + u * T) * B + c;
+                    mm[u] = w.m[idx];
+                    ss[u] = w.s[idx];
+                    aa[u] = w.a[idx];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) st = merge(st, ArgSoft{mm[u], ss[u], aa[u]});
+            }
+            for (; p < G; p += T) {
+                const size_t idx = size_t(p) * B + c;
+                st = merge(st, ArgSoft{w.m[idx], w.s[idx], w.a[idx]});
+            }
+        }
+        for (int off = 1; off < T; off <<= 1) st = merge(st, shfl_xor_state(st, off));
+        if (c < B && sub == 0) {
+            conf[c] = 1.0f / st.s;
+            argmax[c] = st.a;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel.  NB = number of 16-position column blocks (ceil(B/16));
+// NCH = 128-element K chunks per wave.  blockDim.x = 64 * ks, d = 128*NCH*ks.
+// ---------------------------------------------------------------------------
+template <int NB, int NCH>
+__global__ __launch_bounds__(256) void lmhead_bf16_kernel(const uint16_t* __restrict__ h,
+                                                          const uint16_t* __restrict__ W,
+                                                          int B, int d, int V, int ntiles,
+                                                          float* __restrict__ conf,
+                                                          int32_t* __restrict__ argmax,
+                                                          void* __restrict__ ws) {
+    constexpr int NL = NCH * 4;                       // 16-byte loads per lane per tile
+    __shared__ f32x4 red[2][4][NB][64];               // per-wave partial logits, 2 buffers
+    __shared__ ArgSoft fin[4][NB][16];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int nwave = blockDim.x >> 6;
+    const int r16 = lane & 15;
+    const int g = lane >> 4;
+    const int k0 = wave * NCH * 128 + g * 32;         // this lane's K start (elements)
+    const int G = gridDim.x;
+
+    // B fragments of h for this wave's K range, kept in registers.
+    bf16x8 hf[NCH][4][NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int row = nb * 16 + r16;
+        const u32x4* hp = reinterpret_cast<const u32x4*>(h + size_t(row < B ? row : 0) * d + k0);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                u32x4 v = (row < B) ? hp[c * 16 + j] : u32x4{0, 0, 0, 0};
+                hf[c][j][nb] = __builtin_bit_cast(bf16x8, v);
+            }
+    }
+
+    ArgSoft st[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) st[nb] = ArgSoft{-INFINITY, 0.f, 0x7fffffff};
+
+    auto load_tile = [&](u32x4 (&buf)[NL], int tile) {
+        int row = tile * 16 + r16;
+        row = row < V ? row : V - 1;
+        const u32x4* p = reinterpret_cast<const u32x4*>(W + size_t(row) * d + k0);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) buf[c * 4 + j] = p[c * 16 + j];
+    };
+
+    u32x4 cur[NL];
+    int tile = blockIdx.x;
+    if (tile < ntiles) load_tile(cur, tile);
+    int it = 0;
+    while (tile < ntiles) {
+        const int next = tile + G;
+        u32x4 nxt[NL];
+        if (next < ntiles) load_tile(nxt, next);
+
+        f32x4 acc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, cur[c * 4 + j]);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, hf[c][j][nb], acc[nb],
+                                                                      0, 0, 0);
+            }
+
+        bool mine = true;
+        if (nwave > 1) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) red[it & 1][wave][nb][lane] = acc[nb];
+            __syncthreads();
+            mine = (wave == it % nwave);
+            if (mine) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    f32x4 t = red[it & 1][0][nb][lane];
+                    for (int w = 1; w < nwave; ++w) t += red[it & 1][w][nb][lane];
+                    acc[nb] = t;
+                }
+            }
+        }
+        if (mine) {
+            const int row0 = tile * 16 + g * 4;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const float x[4] = {acc[nb][0] * kLog2e, acc[nb][1] * kLog2e,
+                                    acc[nb][2] * kLog2e, acc[nb][3] * kLog2e};
+                fold4(st[nb], x, row0, V);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NL; ++i) cur[i] = nxt[i];
+        tile = next;
+        ++it;
+    }
+
+    // Merge the four lane groups that hold the same position, then the waves.
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        st[nb] = merge(st[nb], shfl_xor_state(st[nb], 16));
+        st[nb] = merge(st[nb], shfl_xor_state(st[nb], 32));
+        if (lane < 16) fin[wave][nb][lane] = st[nb];
+    }
+    __syncthreads();
+    const WsView wv = ws_view(ws, G, B);
+    if (wave == 0 && lane < 16) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            ArgSoft s = fin[0][nb][lane];
+            for (int w = 1; w < nwave; ++w) s = merge(s, fin[w][nb][lane]);
+            const int col = nb * 16 + lane;
+            if (col < B) {
+                const size_t idx = size_t(blockIdx.x) * B + col;
+                wv.m[idx] = s.m;
+                wv.s[idx] = s.s;
+                wv.a[idx] = s.a;
+            }
+        }
+    }
+    if (arrive_last(wv.ctr, G)) final_combine(wv, G, B, conf, argmax);
+}
+
+// Generic bf16 fallback for shapes whose h fragments do not fit in
+// registers (large B x d): one wave per 16-row tile over the whole K range,
+// h fragments re-read (from cache) per chunk.
+template <int NB>
+__global__ __launch_bounds__(256) void lmhead_bf16_generic_kernel(
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int B, int d, int V,
+    int ntiles, float* __restrict__ conf, int32_t* __restrict__ argmax, void* __restrict__ ws) {
+    __shared__ ArgSoft fin[4][NB][16];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int nwave = blockDim.x >> 6;
+    const int r16 = lane & 15;
+    const int g = lane >> 4;
+    const int G = gridDim.x;
+
+    ArgSoft st[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) st[nb] = ArgSoft{-INFINITY, 0.f, 0x7fffffff};
+
+    for (int tile = blockIdx.x * nwave + wave; tile < ntiles; tile += G * nwave) {
+        int row = tile * 16 + r16;
+        row = row < V ? row : V - 1;
+        const u32x4* wp = reinterpret_cast<const u32x4*>(W + size_t(row) * d + g * 32);
+        f32x4 acc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < d / 128; ++c) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, wp[c * 16 + j]);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int hrow = nb * 16 + r16;
+                    const u32x4* hp =
+                        reinterpret_cast<const u32x4*>(h + size_t(hrow < B ? hrow : 0) * d + g * 32);
+                    const u32x4 hv = (hrow < B) ? hp[c * 16 + j] : u32x4{0, 0, 0, 0};
+                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        a, __builtin_bit_cast(bf16x8, hv), acc[nb], 0, 0, 0);
+                }
+            }
+        }
+        const int row0 = tile * 16 + g * 4;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const float x[4] = {acc[nb][0] * kLog2e, acc[nb][1] * kLog2e, acc[nb][2] * kLog2e,
+                                acc[nb][3] * kLog2e};
+            fold4(st[nb], x, row0, V);
+        }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        st[nb] = merge(st[nb], shfl_xor_state(st[nb], 16));
+        st[nb] = merge(st[nb], shfl_xor_state(st[nb], 32));
+        if (lane < 16) fin[wave][nb][lane] = st[nb];
+    }
+    __syncthreads();
+    const WsView wv = ws_view(ws, G, B);
+    if (wave == 0 && lane < 16) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            ArgSoft s = fin[0][nb][lane];
+            for (int w = 1; w < nwave; ++w) s = merge(s, fin[w][nb][lane]);
+            const int col = nb * 16 + lane;
+            if (col < B) {
+                const size_t idx = size_t(blockIdx.x) * B + col;
+                wv.m[idx] = s.m;
+                wv.s[idx] = s.s;
+                wv.a[idx] = s.a;
+            }
+        }
+    }
+    if (arrive_last(wv.ctr, G)) final_combine(wv, G, B, conf, argmax);
+}
+
+// ---------------------------------------------------------------------------
+// float32 path (small problems): workgroup (x, b) scans vocabulary slice x
+// for position b, one row per thread, h[b] staged in LDS.
+// ---------------------------------------------------------------------------
+constexpr int kF32Rows = 256;
+
+__global__ __launch_bounds__(256) void lmhead_f32_kernel(const float* __restrict__ h,
+                                                         const float* __restrict__ W, int B,
+                                                         int d, int V, float* __restrict__ conf,
+                                                         int32_t* __restrict__ argmax,
+                                                         void* __restrict__ ws) {
+    extern __shared__ float hs[];
+    __shared__ ArgSoft wst[4];
+    const int b = blockIdx.y;
+    for (int k = threadIdx.x; k < d; k += blockDim.x) hs[k] = h[size_t(b) * d + k];
+    __syncthreads();
+    const int v = blockIdx.x * kF32Rows + threadIdx.x;
+    ArgSoft st{-INFINITY, 0.f, 0x7fffffff};
+    if (v < V) {
+        const float* wr = W + size_t(v) * d;
+        float acc = 0.f;
+        for (int k = 0; k < d; ++k) acc = fmaf(hs[k], wr[k], acc);
+        st = ArgSoft{acc * kLog2e, 1.f, v};
+    }
+    for (int off = 1; off < 64; off <<= 1) st = merge(st, shfl_xor_state(st, off));
+    if ((threadIdx.x & 63) == 0) wst[threadIdx.x >> 6] = st;
+    __syncthreads();
+    const int G = gridDim.x * gridDim.y;
+    const int blk = blockIdx.y * gridDim.x + blockIdx.x;   // partial index
+    // Partials are laid out [slice][b] so final_combine sees G' = gridDim.x
+    // slices per position.
+    const WsView wv = ws_view(ws, gridDim.x, B);
+    if (threadIdx.x == 0) {
+        ArgSoft s = wst[0];
+        for (int w = 1; w < 4; ++w) s = merge(s, wst[w]);
+        const size_t idx = size_t(blockIdx.x) * B + b;
+        wv.m[idx] = s.m;
+        wv.s[idx] = s.s;
+        wv.a[idx] = s.a;
+    }
+    (void)blk;
+    if (arrive_last(wv.ctr, G)) final_combine(wv, gridDim.x, B, conf, argmax);
+}
+
+// Host-side plan for the bf16 kernel: waves per workgroup (K split) and
+// chunks per wave.  Returns false when the register-resident variant does not
+// apply (then the generic kernel runs).
+bool plan_bf16(int B, int d, int* ks, int* nch) {
+    const int NB = (B + 15) / 16;
+    const int c = d / 128;
+    const int max_nch = 8 / NB;       // h fragments: 16 * NCH * NB VGPRs <= 128
+    const int order[3] = {4, 2, 1};
+    for (int i = 0; i < 3; ++i) {
+        const int k = order[i];
+        if (c % k == 0 && c / k <= max_nch) {
+            *ks = k;
+            *nch = c / k;
+            return true;
+        }
+    }
+    return false;
+}
+
+template <int NB>
+hipError_t launch_nb(const void* h, const void* W, int B, int d, int V, float* conf,
+                     int32_t* argmax, void* ws, hipStream_t st) {
+    const int ntiles = (V + 15) / 16;
+    const int G = ntiles < kMaxGrid ? ntiles : kMaxGrid;
+    const auto* hh = static_cast<const uint16_t*>(h);
+    const auto* ww = static_cast<const uint16_t*>(W);
+    int ks = 0, nch = 0;
+    if (!plan_bf16(B, d, &ks, &nch)) {
+        hipLaunchKernelGGL(lmhead_bf16_generic_kernel<NB>, dim3(G), dim3(256), 0, st, hh, ww, B,
+                           d, V, ntiles, conf, argmax, ws);
+        return hipGetLastError();
+    }
+#define BD_LMH_CASE(N)                                                                     \
+    case N:                                                                                \
+        if constexpr (N * NB <= 8) {                                                       \
+            hipLaunchKernelGGL((lmhead_bf16_kernel<NB, N>), dim3(G), dim3(64 * ks), 0, st, \
+                               hh, ww, B, d, V, ntiles, conf, argmax, ws);                 \
+        }                                                                                  \
+        break;
+    switch (nch) {
+        BD_LMH_CASE(1)
+        BD_LMH_CASE(2)
+        BD_LMH_CASE(3)
+        BD_LMH_CASE(4)
+        BD_LMH_CASE(5)
+        BD_LMH_CASE(6)
+        BD_LMH_CASE(7)
+        BD_LMH_CASE(8)
+        default:
+            return hipErrorInvalidValue;
+    }
+#undef BD_LMH_CASE
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int lmhead_grid(int B, int d, int V) {
+    (void)B;
+    (void)d;
+    const int ntiles = (V + 15) / 16;
+    return ntiles < kMaxGrid ? ntiles : kMaxGrid;
+}
+
+size_t lmhead_ws_bytes(int B, int d, int V) {
+    // bf16: one partial per workgroup; f32: one per 256-row slice.
+    const int g_bf16 = lmhead_grid(B, d, V);
+    const int g_f32 = (V + kF32Rows - 1) / kF32Rows;
+    const int G = g_bf16 > g_f32 ? g_bf16 : g_f32;
+    return ws_size(G, B);
+}
+
+hipError_t launch_lmhead_bf16(const void* h, const void* W, int B, int d, int V, float* conf,
+                              int32_t* argmax, void* ws, hipStream_t st) {
+    switch ((B + 15) / 16) {
+        case 1: return launch_nb<1>(h, W, B, d, V, conf, argmax, ws, st);
+        case 2: return launch_nb<2>(h, W, B, d, V, conf, argmax, ws, st);
+        case 3: return launch_nb<3>(h, W, B, d, V, conf, argmax, ws, st);
+        case 4: return launch_nb<4>(h, W, B, d, V, conf, argmax, ws, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_lmhead_f32(const float* h, const float* W, int B, int d, int V, float* conf,
+                             int32_t* argmax, void* ws, hipStream_t st) {
+    const dim3 grid((V + kF32Rows - 1) / kF32Rows, B);
+    hipLaunchKernelGGL(lmhead_f32_kernel, grid, dim3(kF32Rows), size_t(d) * sizeof(float), st, h,
+                       W, B, d, V, conf, argmax, ws);
+    return hipGetLastError();
+}
+
+}  // namespace bd

@@ -1,0 +1,130 @@
+// Latency-bound decisions of the decode step: threshold commit, speculative
+// accept and the LOWN certificate scan.  Each runs in a single workgroup; a
+// block holds at most 64 positions, so commit and accept are one wavefront
+// with ballots instead of loops.
+#include "bd_internal.h"
+
+namespace bd {
+
+// Threshold unmasking with the always-one rule (Fast-dVLM overview §4.1:
+// denoising threshold 0.9).  Lane i owns position i.
+__global__ __launch_bounds__(64) void commit_kernel(const float* __restrict__ conf,
+                                                    const int32_t* __restrict__ argmax, int B,
+                                                    float tau, uint8_t* __restrict__ masked,
+                                                    int32_t* __restrict__ tokens,
+                                                    int32_t* __restrict__ n_committed) {
+    const int i = threadIdx.x;
+    const bool in = i < B;
+    const float c = in ? conf[i] : 0.f;
+    const bool m = in && masked[i] != 0;
+    const bool above = m && (c > tau);
+    const uint64_t above_bits = __ballot(above);
+    const uint64_t masked_bits = __ballot(m);
+    bool take = above;
+    int n = __popcll(above_bits);
+    if (above_bits == 0 && masked_bits != 0) {
+        // Most confident masked position, lowest index on ties.
+        float bc = c;
+        int bi = m ? i : 64;
+        for (int off = 32; off > 0; off >>= 1) {
+            const float oc = __shfl_xor(bc, off);
+            const int oi = __shfl_xor(bi, off);
+            const bool other_valid = oi < 64;
+            const bool mine_valid = bi < 64;
+            if (other_valid && (!mine_valid || oc > bc || (oc == bc && oi < bi))) {
+                bc = oc;
+                bi = oi;
+            }
+        }
+        take = (i == bi);
+        n = 1;
+    }
+    if (take) {
+        tokens[i] = argmax[i];
+        masked[i] = 0;
+    }
+    if (i == 0) *n_committed = n;
+}
+
+// Longest verified prefix (overview §2.3.1): the first disagreement is the
+// lowest set bit of a ballot.
+__global__ __launch_bounds__(64) void spec_accept_kernel(const int32_t* __restrict__ draft,
+                                                         const int32_t* __restrict__ verify,
+                                                         int B, int P,
+                                                         int32_t* __restrict__ accepted,
+                                                         int32_t* __restrict__ kv_len,
+                                                         int32_t* __restrict__ out_tokens) {
+    const int i = threadIdx.x;
+    const int32_t d = i < B ? draft[i] : 0;
+    const bool differ = i < B && d != verify[i];
+    const uint64_t bits = __ballot(differ);
+    const int L = bits ? __builtin_ctzll(bits) : B;
+    if (i < L) out_tokens[i] = d;
+    if (i == 0) {
+        *accepted = L;
+        *kv_len = P + L;
+    }
+}
+
+// LOWN certificate (method step details (2)-(3)).  Thread i computes the
+// rank of position i in the stable descending order of anchor confidence;
+// the certified prefix ends at the smallest rank whose text-only token
+// disagrees with the anchor token, so no explicit sort is needed for L.
+__global__ __launch_bounds__(1024) void cert_scan_kernel(const float* __restrict__ conf,
+                                                         const int32_t* __restrict__ atok,
+                                                         const int32_t* __restrict__ ttok, int n,
+                                                         int k, int32_t* __restrict__ order,
+                                                         int32_t* __restrict__ accepted,
+                                                         int32_t* __restrict__ skip) {
+    __shared__ float sc[1024];
+    __shared__ int wave_min[16];
+    const int i = threadIdx.x;
+    if (i < n) sc[i] = conf[i];
+    __syncthreads();
+    int first_bad = n;
+    if (i < n) {
+        const float c = sc[i];
+        int rank = 0;
+        for (int j = 0; j < n; ++j) {
+            const float o = sc[j];
+            rank += (o > c) || (o == c && j < i);
+        }
+        order[rank] = i;
+        if (ttok[i] != atok[i]) first_bad = rank;
+    }
+    for (int off = 32; off > 0; off >>= 1) first_bad = min(first_bad, __shfl_xor(first_bad, off));
+    if ((i & 63) == 0) wave_min[i >> 6] = first_bad;
+    __syncthreads();
+    if (i == 0) {
+        int L = n;
+        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) L = min(L, wave_min[w]);
+        *accepted = L;
+        *skip = (L >= k) ? 1 : 0;
+    }
+}
+
+hipError_t launch_commit(const float* conf, const int32_t* argmax, int B, float tau,
+                         uint8_t* masked, int32_t* tokens, int32_t* n_committed, hipStream_t st) {
+    hipLaunchKernelGGL(commit_kernel, dim3(1), dim3(64), 0, st, conf, argmax, B, tau, masked,
+                       tokens, n_committed);
+    return hipGetLastError();
+}
+
+hipError_t launch_spec_accept(const int32_t* draft, const int32_t* verify, int B, int P,
+                              int32_t* accepted, int32_t* kv_len, int32_t* out_tokens,
+                              hipStream_t st) {
+    hipLaunchKernelGGL(spec_accept_kernel, dim3(1), dim3(64), 0, st, draft, verify, B, P,
+                       accepted, kv_len, out_tokens);
+    return hipGetLastError();
+}
+
+hipError_t launch_cert_scan(const float* conf, const int32_t* atok, const int32_t* ttok, int n,
+                            int k, int32_t* order, int32_t* accepted, int32_t* skip,
+                            hipStream_t st) {
+    const int threads = n <= 64 ? 64 : ((n + 63) / 64) * 64;
+    hipLaunchKernelGGL(cert_scan_kernel, dim3(1), dim3(threads), 0, st, conf, atok, ttok, n, k,
+                       order, accepted, skip);
+    return hipGetLastError();
+}
+
+}  // namespace bd

@@ -1,0 +1,201 @@
+"""Device-side plumbing around libbdiff: upload seeded inputs into torch
+device tensors, allocate outputs and workspaces, and run the compositions the
+pages describe (one MDM decode step, the linear and the fused speculative
+steps) as sequences of C-ABI calls.  Every arithmetic step runs in libbdiff;
+this module only moves buffers and arguments.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from . import bdiff as bd
+
+
+def to_dev(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """Copy a NumPy array to the GPU; uint16 arrays are bfloat16 bit
+    patterns and become bfloat16 tensors, uint64 becomes a bit-identical int64."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    if a.dtype == np.uint64:
+        return torch.from_numpy(a.view(np.int64)).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    """Inverse of to_dev (bfloat16 -> uint16 bit patterns)."""
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def dtype_code(name: str) -> int:
+    return {"f32": bd.BD_F32, "bf16": bd.BD_BF16}[name]
+
+
+def mask_dev(kind: int, bq: int, device="cuda") -> torch.Tensor:
+    return to_dev(bd.bd_make_intra_mask(kind, bq), device)
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """Zero-filled device workspace (the LM head needs its counter at 0)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+class LMHead:
+    """bd_lmhead_conf over fixed device buffers."""
+
+    def __init__(self, dt: int, W: torch.Tensor, B: int, d: int, V: int, device="cuda"):
+        self.dt, self.W, self.B, self.d, self.V = dt, W, B, d, V
+        self.conf = torch.empty(B, dtype=torch.float32, device=device)
+        self.argmax = torch.empty(B, dtype=torch.int32, device=device)
+        self.ws_bytes = bd.bd_lmhead_conf_ws_bytes(B, d, V)
+        self.ws = workspace(self.ws_bytes, device)
+
+    def __call__(self, h: torch.Tensor, stream=None):
+        bd.bd_lmhead_conf(self.dt, h, self.W, self.B, self.d, self.V, self.conf, self.argmax,
+                          self.ws, self.ws_bytes, stream)
+
+
+class BlockAttn:
+    """bd_block_attn over fixed device buffers."""
+
+    def __init__(self, dt: int, kind: int, Bq: int, P: int, cap: int, Hq: int, Hkv: int, dh: int,
+                 device="cuda"):
+        self.dt, self.Bq, self.P, self.cap, self.Hq, self.Hkv, self.dh = dt, Bq, P, cap, Hq, Hkv, dh
+        self.mask = mask_dev(kind, Bq, device)
+        tdt = torch.float32 if dt == bd.BD_F32 else torch.bfloat16
+        self.out = torch.empty((Bq, Hq, dh), dtype=tdt, device=device)
+        self.ws_bytes = bd.bd_block_attn_ws_bytes(P, Bq, Hq, Hkv, dh)
+        self.ws = workspace(self.ws_bytes, device)
+
+    def __call__(self, q, k_cache, v_cache, stream=None, scale=0.0):
+        bd.bd_block_attn(self.dt, q, k_cache, v_cache, self.P, self.cap, self.mask, self.Bq,
+                         self.Hq, self.Hkv, self.dh, scale, self.out, self.ws, self.ws_bytes,
+                         stream)
+
+
+class DecodeStep:
+    """One threshold (MDM) block-decode step: bd_block_attn (bidirectional
+    block) -> bd_lmhead_conf -> bd_commit.  Inputs from synth.qwen_decode or
+    synth.tiny.  ``reset()`` restores the block state (masked flags, tokens)
+    so that repeated steps do identical work."""
+
+    def __init__(self, inp: dict, device="cuda"):
+        self.inp = inp
+        dt = dtype_code(inp["dtype"])
+        B = inp["B"]
+        self.q = to_dev(inp["q"], device)
+        self.k_cache = to_dev(inp["k_cache"], device)
+        self.v_cache = to_dev(inp["v_cache"], device)
+        self.h = to_dev(inp["h"], device)
+        self.W = to_dev(inp["W"], device)
+        self.attn = BlockAttn(dt, bd.BD_MASK_BIDIR, B, inp["P"], inp["cap"], inp["Hq"],
+                              inp["Hkv"], inp["q"].shape[-1], device)
+        self.lm = LMHead(dt, self.W, B, inp["d"], inp["V"], device)
+        self.masked0 = to_dev(inp["masked"], device)
+        self.tokens0 = to_dev(inp["tokens"], device)
+        self.masked = self.masked0.clone()
+        self.tokens = self.tokens0.clone()
+        self.n_committed = torch.zeros(1, dtype=torch.int32, device=device)
+        self.tau = float(inp["tau"])
+        self.B = B
+
+    def reset(self):
+        self.masked.copy_(self.masked0)
+        self.tokens.copy_(self.tokens0)
+
+    def run(self, stream=None):
+        self.attn(self.q, self.k_cache, self.v_cache, stream)
+        self.lm(self.h, stream)
+        bd.bd_commit(self.lm.conf, self.lm.argmax, self.B, self.tau, self.masked, self.tokens,
+                     self.n_committed, stream)
+
+
+class LinearSpecStep:
+    """Linear self-speculative step: draft (bidirectional) and verify (causal)
+    passes, each block attention + LM head, then bd_spec_accept."""
+
+    def __init__(self, inp: dict, device="cuda"):
+        self.inp = inp
+        B, P = inp["B"], inp["P"]
+        dh = inp["q_draft"].shape[-1]
+        self.t = {k: to_dev(inp[k], device) for k in
+                  ("q_draft", "q_verify", "k_draft", "v_draft", "k_verify", "v_verify",
+                   "h_draft", "h_verify", "W")}
+        self.attn_d = BlockAttn(bd.BD_BF16, bd.BD_MASK_BIDIR, B, P, inp["cap"], inp["Hq"],
+                                inp["Hkv"], dh, device)
+        self.attn_v = BlockAttn(bd.BD_BF16, bd.BD_MASK_CAUSAL, B, P, inp["cap"], inp["Hq"],
+                                inp["Hkv"], dh, device)
+        self.lm_d = LMHead(bd.BD_BF16, self.t["W"], B, inp["d"], inp["V"], device)
+        self.lm_v = LMHead(bd.BD_BF16, self.t["W"], B, inp["d"], inp["V"], device)
+        self.accepted = torch.zeros(1, dtype=torch.int32, device=device)
+        self.kv_len = torch.zeros(1, dtype=torch.int32, device=device)
+        self.out_tokens = torch.full((B,), -1, dtype=torch.int32, device=device)
+        self.B, self.P = B, P
+
+    def run(self, stream=None):
+        t = self.t
+        self.attn_d(t["q_draft"], t["k_draft"], t["v_draft"], stream)
+        self.lm_d(t["h_draft"], stream)
+        self.attn_v(t["q_verify"], t["k_verify"], t["v_verify"], stream)
+        self.lm_v(t["h_verify"], stream)
+        bd.bd_spec_accept(self.lm_d.argmax, self.lm_v.argmax, self.B, self.P, self.accepted,
+                          self.kv_len, self.out_tokens, stream)
+
+
+class FusedSpecStep:
+    """Fused (quadratic) speculative step: one block attention over 2B rows
+    under the SPEC_FUSED mask, one LM head over the 2B rows, bd_spec_accept on
+    the verify half; plus the LOWN certificate scan."""
+
+    def __init__(self, inp: dict, device="cuda"):
+        self.inp = inp
+        B, bq, P = inp["B"], inp["Bq"], inp["P"]
+        dh = inp["q"].shape[-1]
+        self.t = {k: to_dev(inp[k], device) for k in
+                  ("q", "k_cache", "v_cache", "h", "W", "draft_in", "anchor_conf",
+                   "anchor_tok", "text_tok")}
+        self.attn = BlockAttn(bd.BD_BF16, bd.BD_MASK_SPEC_FUSED, bq, P, inp["cap"], inp["Hq"],
+                              inp["Hkv"], dh, device)
+        self.lm = LMHead(bd.BD_BF16, self.t["W"], bq, inp["d"], inp["V"], device)
+        self.accepted = torch.zeros(1, dtype=torch.int32, device=device)
+        self.kv_len = torch.zeros(1, dtype=torch.int32, device=device)
+        self.out_tokens = torch.full((B,), -1, dtype=torch.int32, device=device)
+        n = inp["anchor_conf"].shape[0]
+        self.order = torch.full((n,), -1, dtype=torch.int32, device=device)
+        self.cert_L = torch.zeros(1, dtype=torch.int32, device=device)
+        self.skip = torch.zeros(1, dtype=torch.int32, device=device)
+        self.B, self.P, self.n, self.k = B, P, n, int(inp["k_cert"])
+
+    def run(self, stream=None):
+        t = self.t
+        self.attn(t["q"], t["k_cache"], t["v_cache"], stream)
+        self.lm(t["h"], stream)
+        bd.bd_spec_accept(t["draft_in"], self.lm.argmax, self.B, self.P, self.accepted,
+                          self.kv_len, self.out_tokens, stream)
+        bd.bd_cert_scan(t["anchor_conf"], t["anchor_tok"], t["text_tok"], self.n, self.k,
+                        self.order, self.cert_L, self.skip, stream)
+
+
+class DualStream:
+    """bd_dualstream_attn over device buffers from synth.dualstream."""
+
+    def __init__(self, inp: dict, device="cuda"):
+        self.inp = inp
+        self.dt = dtype_code(inp["dtype"])
+        self.q, self.k, self.v = (to_dev(inp[x], device) for x in ("q", "k", "v"))
+        self.out = torch.empty_like(self.q)
+
+    def run(self, stream=None):
+        i = self.inp
+        bd.bd_dualstream_attn(self.dt, self.q, self.k, self.v, i["n_vis"], i["n_txt"], i["block"],
+                              i["H"], i["dh"], 0.0, self.out, stream)
+
+
+def default_scale(dh: int) -> float:
+    return 1.0 / math.sqrt(dh)

@@ -1,0 +1,204 @@
+/*
+ * bdiff.h - C ABI of libbdiff, the block-diffusion decode step and the
+ * dual-stream training attention of Fast-dVLM, for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Sources (web pages on the method, cited by page and section):
+ *   [OV]   Fast-dVLM engineering overview (ocdem.com/news/1032714)
+ *   [TH]   Fast-dVLM article, Thai translation (itsolotime.com/th/archives/34466)
+ *   [LOWN] LOWN article (paper.rainbus.top/paper/2610.36671)
+ *
+ * Conventions shared by every call
+ *   - Pointers are DEVICE pointers unless the argument says "host".
+ *   - Every compute call is asynchronous on `stream` (0 = the null stream)
+ *     and returns as soon as its kernels are enqueued.
+ *   - The caller owns every buffer.  The library allocates no device memory
+ *     and keeps no global mutable state; scratch space comes in as a
+ *     caller-provided workspace sized by the matching *_ws_bytes query.
+ *   - Arguments are checked on the host before anything is enqueued; on an
+ *     error nothing is launched and the outputs are untouched.  A failed
+ *     launch returns BD_E_LAUNCH.  No call aborts or throws.
+ *   - Tensors are dense, row-major, in the layouts given below.  bf16 means
+ *     IEEE bfloat16 storage with float32 accumulation inside the kernels.
+ *   - Vector-loaded tensors (q, k, v, caches, h, W, outputs, workspaces)
+ *     must be 16-byte aligned (BD_E_ALIGN otherwise).
+ *   - Two calls that share a workspace must be ordered on one stream.
+ */
+#ifndef BDIFF_H
+#define BDIFF_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BD_OK = 0,
+    BD_E_NULL = 1,       /* a required pointer is NULL                        */
+    BD_E_SHAPE = 2,      /* a size is out of range or sizes are inconsistent  */
+    BD_E_DTYPE = 3,      /* unknown dtype, or dtype not supported for the call */
+    BD_E_ALIGN = 4,      /* a vector-loaded pointer is not 16-byte aligned    */
+    BD_E_WORKSPACE = 5,  /* workspace missing or smaller than *_ws_bytes      */
+    BD_E_DEVICE = 6,     /* current device is not gfx950                      */
+    BD_E_LAUNCH = 7      /* the HIP runtime rejected a kernel launch          */
+} bd_status;
+
+typedef enum { BD_F32 = 0, BD_BF16 = 1 } bd_dtype;
+
+/* Visibility among the Bq block queries (block key j for block query i). */
+typedef enum {
+    BD_MASK_BIDIR = 0,      /* all ones: parallel denoising inside a block [OV §1.2] */
+    BD_MASK_CAUSAL = 1,     /* j <= i: the AR verify pass [OV §2.3.1]               */
+    BD_MASK_SPEC_FUSED = 2  /* draft+verify in one forward [OV §2.3.1], Bq = 2B:
+                               rows 0..B-1 causal among themselves; rows B..2B-1
+                               see row j < B iff j <= i-B, and all of B..2B-1 */
+} bd_mask_kind;
+
+/* Static description of a status code; never NULL. */
+const char* bd_status_str(bd_status s);
+
+/* BD_OK iff `device` exists and is a gfx950 GPU; BD_E_DEVICE otherwise
+ * (including when no GPU is present).  There is no fallback path. */
+bd_status bd_device_check(int device);
+
+/* Host helper: fills host_rows[i] (i < Bq) with the intra-block bitmask of
+ * block query i (bit j set = block key j visible) for `kind`.
+ * Bq in [1, 64]; BD_MASK_SPEC_FUSED needs an even Bq.  host_rows: host array
+ * of Bq words.  Errors: BD_E_NULL, BD_E_SHAPE. */
+bd_status bd_make_intra_mask(bd_mask_kind kind, int32_t Bq, uint64_t* host_rows);
+
+/*
+ * bd_block_attn - attention of a block of Bq queries over a KV-cached prefix
+ * plus the block itself.  [OV §1.2: blocks decoded in order, each block's
+ * tokens denoised in parallel with bidirectional attention, the prefix
+ * (visual + prompt + earlier blocks) kept in the KV cache; TH §1]
+ *
+ *   o[i][h] = sum_j softmax_j(scale * q[i][h] . k[g][j]) v[g][j]
+ *   over j in [0, P) (always visible) and j = P + jb for block key jb with
+ *   bit jb of intra_mask[i] set; g = h / (Hq / Hkv) (grouped-query heads).
+ *   A query row with no visible key gets a zero output row.
+ *
+ *   q           [Bq][Hq][dh]   dtype dt
+ *   k_cache,
+ *   v_cache     [Hkv][cap][dh] dtype dt; rows P..P+Bq-1 hold the block's keys
+ *                              and values (written by the caller)
+ *   intra_mask  [Bq] uint64 (device), e.g. from bd_make_intra_mask
+ *   out         [Bq][Hq][dh]   dtype dt
+ *   scale       softmax scale; 0 selects 1/sqrt(dh)
+ *   ws          workspace of at least bd_block_attn_ws_bytes(...) bytes
+ * Limits: 1 <= Bq <= 64, 0 <= P, P + Bq <= cap, Hkv >= 1, Hq % Hkv == 0,
+ *   BD_BF16: dh == 128;  BD_F32: dh % 4 == 0 and 4 <= dh <= 128.
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_ALIGN, BD_E_WORKSPACE,
+ *   BD_E_LAUNCH.
+ */
+size_t bd_block_attn_ws_bytes(int32_t P, int32_t Bq, int32_t Hq, int32_t Hkv, int32_t dh);
+bd_status bd_block_attn(bd_dtype dt, const void* q, const void* k_cache, const void* v_cache,
+                        int32_t P, int32_t cap, const uint64_t* intra_mask,
+                        int32_t Bq, int32_t Hq, int32_t Hkv, int32_t dh, float scale,
+                        void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * bd_lmhead_conf - LM-head contraction fused with the softmax maximum:
+ * per position b, logits l[v] = h[b] . W[v] (never written to memory),
+ *   argmax[b] = smallest v with l[v] = max l,
+ *   conf[b]   = 1 / sum_v exp(l[v] - max l) = the largest softmax probability.
+ * [LOWN 'method step details' (1): confidence = max_w p(y_i = w | .);
+ *  OV §1.1: batch-1 decode is bound by reloading the weights every step]
+ *
+ *   h       [B][d]  dtype dt
+ *   W       [V][d]  dtype dt (row-major: one row per vocabulary entry)
+ *   conf    [B] float32 out;  argmax [B] int32 out
+ *   ws      workspace of at least bd_lmhead_conf_ws_bytes(B, d, V) bytes.
+ *           Its first 256 bytes hold a completion counter that must be zero
+ *           before the first call; every call leaves it at zero again, so a
+ *           zero-filled workspace can be reused across calls.
+ * Limits: 1 <= B <= 64, V >= 1, d >= 1;  BD_BF16 needs d % 128 == 0 and
+ *   d <= 16384.  The result is deterministic (fixed reduction order).
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_ALIGN, BD_E_WORKSPACE,
+ *   BD_E_LAUNCH.
+ */
+size_t bd_lmhead_conf_ws_bytes(int32_t B, int32_t d, int32_t V);
+bd_status bd_lmhead_conf(bd_dtype dt, const void* h, const void* W,
+                         int32_t B, int32_t d, int32_t V,
+                         float* conf, int32_t* argmax,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * bd_commit - threshold unmasking with the always-one rule.
+ * [OV §4.1: denoising confidence threshold 0.9; OV §1.2 parallel unmasking]
+ * Every position i with masked[i] != 0 and conf[i] > tau is committed.  If
+ * none qualifies and some position is masked, the masked position with the
+ * largest conf (lowest index on ties) is committed alone.  Committing i sets
+ * tokens[i] = argmax[i] and masked[i] = 0; other positions are untouched.
+ *
+ *   conf [B] float32, argmax [B] int32   (e.g. from bd_lmhead_conf)
+ *   masked [B] uint8 in/out, tokens [B] int32 in/out
+ *   n_committed [1] int32 out
+ * Limits: 0 <= B <= 64; conf values must not be NaN.
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_LAUNCH.
+ */
+bd_status bd_commit(const float* conf, const int32_t* argmax, int32_t B, float tau,
+                    uint8_t* masked, int32_t* tokens, int32_t* n_committed,
+                    hipStream_t stream);
+
+/*
+ * bd_spec_accept - self-speculative verification: keep the longest prefix
+ * of the diffusion draft that the causal (AR) pass reproduces, truncate the
+ * KV cache to it and append the accepted tokens.  [OV §2.3.1; TH §5.3]
+ *   L = max { l <= B : draft[0..l) == verify[0..l) }   (index-aligned)
+ *   accepted[0] = L;  kv_len[0] = P + L;  out_tokens[0..L) = draft[0..L)
+ * The KV truncation is the length update: cache rows below P + L stay valid,
+ * rows from P + L on are free to be overwritten.  out_tokens[L..B) are left
+ * untouched.  Used by both the linear (two forwards) and the fused quadratic
+ * (one forward, rows 0..B-1 of the fused block give `verify`) variants.
+ *   draft, verify [B] int32;  accepted [1], kv_len [1], out_tokens [B] int32 out
+ * Limits: 0 <= B <= 64, P >= 0, P + B must fit in int32.
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_LAUNCH.
+ */
+bd_status bd_spec_accept(const int32_t* draft, const int32_t* verify, int32_t B, int32_t P,
+                         int32_t* accepted, int32_t* kv_len, int32_t* out_tokens,
+                         hipStream_t stream);
+
+/*
+ * bd_cert_scan - LOWN certificate over n masked positions.
+ * [LOWN 'method step details' (2)-(3)]  order = the positions sorted by
+ * anchor_conf descending (stable: lower index first on ties);
+ * L = the longest prefix of `order` on which text_tok == anchor_tok;
+ * skip_full = (L >= k): the image forward can be skipped this step.
+ *   anchor_conf [n] float32 (finite), anchor_tok [n] int32, text_tok [n] int32
+ *   order [n] int32 out, accepted [1] int32 out (= L), skip_full [1] int32 out
+ * Limits: 0 <= n <= 1024.
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_LAUNCH.
+ */
+bd_status bd_cert_scan(const float* anchor_conf, const int32_t* anchor_tok,
+                       const int32_t* text_tok, int32_t n, int32_t k,
+                       int32_t* order, int32_t* accepted, int32_t* skip_full,
+                       hipStream_t stream);
+
+/*
+ * bd_dualstream_attn - training-time attention over the vision-efficient
+ * dual-stream sequence [visual (n_vis) | clean text (n_txt) | noisy text
+ * (n_txt)], N = n_vis + 2 n_txt.  [OV §2.2.1-§2.2.2; TH §4.1, §4.4]
+ * Query row i sees key j iff
+ *   C2C: i, j < n_vis + n_txt and j <= i             (clean stream, causal)
+ *   N2C: i noisy (r = i - n_vis - n_txt), j visual, or j clean text with
+ *        j - n_vis <= r                               (printed N2C matrix)
+ *   N2N: i, j noisy with (r / block) == (r_j / block) (bidirectional block)
+ * and no clean query sees a noisy key.  Softmax scaled dot-product per head.
+ *   q, k, v, out [N][H][dh] dtype dt;  scale 0 selects 1/sqrt(dh)
+ * Limits: n_vis >= 0, n_txt >= 0, N >= 1, block >= 1, H >= 1,
+ *   BD_BF16: dh == 128;  BD_F32: dh % 4 == 0 and 4 <= dh <= 128.
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_ALIGN, BD_E_LAUNCH.
+ */
+bd_status bd_dualstream_attn(bd_dtype dt, const void* q, const void* k, const void* v,
+                             int32_t n_vis, int32_t n_txt, int32_t block, int32_t H,
+                             int32_t dh, float scale, void* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BDIFF_H */

@@ -1,0 +1,175 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads and
+exports every entry point include/bdiff.h declares, argument validation
+returns the documented status before anything is launched, and the host mask
+helper agrees with the oracle's masks."""
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import oracle
+from block_diffusion_vlm_amd import bdiff as bd
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "bdiff.h"
+FAKE = 0x10000          # a 16-byte-aligned non-null address; never dereferenced
+MISALIGNED = 0x10008
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|bd_status|size_t)\s+(bd_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def test_header_declares_exactly_the_bound_entry_points():
+    assert declared_functions() == sorted(bd.EXPORTS)
+
+
+def test_library_loads_and_exports_every_symbol():
+    L = bd.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    for s in range(8):
+        assert isinstance(bd.bd_status_str(s), str) and bd.bd_status_str(s)
+    assert bd.bd_status_str(99) == "unknown status"
+
+
+def test_device_check_reports_no_gfx950_here():
+    # On a machine without a GPU the check must fail cleanly, not crash.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert bd.bd_device_check(0) == bd.BD_E_DEVICE
+    assert bd.bd_device_check(-1) == bd.BD_E_DEVICE
+
+
+@pytest.mark.parametrize("kind,name", [(bd.BD_MASK_BIDIR, "bidir"), (bd.BD_MASK_CAUSAL, "causal"),
+                                       (bd.BD_MASK_SPEC_FUSED, "spec_fused")])
+def test_intra_mask_matches_oracle(kind, name):
+    for bq in range(1, 65):
+        if name == "spec_fused" and bq % 2:
+            assert bd.bd_make_intra_mask(kind, bq, check=False).size == bq  # status checked below
+            continue
+        rows = bd.bd_make_intra_mask(kind, bq)
+        bits = ((rows[:, None] >> np.arange(bq, dtype=np.uint64)[None, :]) & np.uint64(1)).astype(bool)
+        assert np.array_equal(bits, oracle.intra_block_mask(name, bq)), bq
+        if bq < 64:
+            assert not (rows >> np.uint64(bq)).any()      # no bits beyond the block
+
+
+def test_intra_mask_errors():
+    L = bd.lib()
+    assert L.bd_make_intra_mask(0, 4, None) == bd.BD_E_NULL
+    buf = np.zeros(70, np.uint64)
+    assert L.bd_make_intra_mask(0, 0, buf.ctypes.data) == bd.BD_E_SHAPE
+    assert L.bd_make_intra_mask(0, 65, buf.ctypes.data) == bd.BD_E_SHAPE
+    assert L.bd_make_intra_mask(2, 5, buf.ctypes.data) == bd.BD_E_SHAPE
+    assert L.bd_make_intra_mask(7, 4, buf.ctypes.data) == bd.BD_E_SHAPE
+
+
+def test_workspace_queries():
+    assert bd.bd_block_attn_ws_bytes(1280, 16, 16, 2, 128) > 0
+    assert bd.bd_block_attn_ws_bytes(-1, 16, 16, 2, 128) == 0
+    assert bd.bd_lmhead_conf_ws_bytes(16, 2048, 151936) >= 256
+    assert bd.bd_lmhead_conf_ws_bytes(0, 2048, 151936) == 0
+    assert bd.bd_lmhead_conf_ws_bytes(65, 2048, 151936) == 0
+
+
+def _attn(**kw):
+    a = dict(dt=bd.BD_BF16, q=FAKE, k_cache=FAKE, v_cache=FAKE, P=32, cap=64, intra_mask=FAKE,
+             Bq=16, Hq=16, Hkv=2, dh=128, scale=0.0, out=FAKE, ws=FAKE, ws_bytes=1 << 30,
+             stream=0, check=False)
+    a.update(kw)
+    return bd.bd_block_attn(**a)
+
+
+def test_block_attn_validation():
+    assert _attn(q=None) == bd.BD_E_NULL
+    assert _attn(intra_mask=None) == bd.BD_E_NULL
+    assert _attn(dt=5) == bd.BD_E_DTYPE
+    assert _attn(Bq=0) == bd.BD_E_SHAPE
+    assert _attn(Bq=65, cap=200) == bd.BD_E_SHAPE
+    assert _attn(Hq=15) == bd.BD_E_SHAPE
+    assert _attn(Hkv=0) == bd.BD_E_SHAPE
+    assert _attn(P=49) == bd.BD_E_SHAPE          # P + Bq > cap
+    assert _attn(P=-1) == bd.BD_E_SHAPE
+    assert _attn(dh=64) == bd.BD_E_SHAPE         # bf16 needs dh == 128
+    assert _attn(dt=bd.BD_F32, dh=130) == bd.BD_E_SHAPE
+    assert _attn(scale=float("nan")) == bd.BD_E_SHAPE
+    assert _attn(q=MISALIGNED) == bd.BD_E_ALIGN
+    assert _attn(out=MISALIGNED) == bd.BD_E_ALIGN
+    assert _attn(ws=None) == bd.BD_E_WORKSPACE
+    need = bd.bd_block_attn_ws_bytes(32, 16, 16, 2, 128)
+    assert _attn(ws_bytes=need - 1) == bd.BD_E_WORKSPACE
+    assert _attn(ws=MISALIGNED) == bd.BD_E_ALIGN
+
+
+def _lm(**kw):
+    a = dict(dt=bd.BD_BF16, h=FAKE, W=FAKE, B=16, d=2048, V=151936, conf=FAKE, argmax=FAKE,
+             ws=FAKE, ws_bytes=1 << 30, stream=0, check=False)
+    a.update(kw)
+    return bd.bd_lmhead_conf(**a)
+
+
+def test_lmhead_validation():
+    assert _lm(W=None) == bd.BD_E_NULL
+    assert _lm(conf=None) == bd.BD_E_NULL
+    assert _lm(dt=9) == bd.BD_E_DTYPE
+    assert _lm(B=0) == bd.BD_E_SHAPE
+    assert _lm(B=65) == bd.BD_E_SHAPE
+    assert _lm(V=0) == bd.BD_E_SHAPE
+    assert _lm(d=2000) == bd.BD_E_SHAPE          # bf16 needs d % 128 == 0
+    assert _lm(d=16512) == bd.BD_E_SHAPE
+    assert _lm(h=MISALIGNED) == bd.BD_E_ALIGN
+    assert _lm(ws=None) == bd.BD_E_WORKSPACE
+    assert _lm(ws_bytes=bd.bd_lmhead_conf_ws_bytes(16, 2048, 151936) - 1) == bd.BD_E_WORKSPACE
+
+
+def test_small_calls_validation():
+    c = lambda **kw: bd.bd_commit(**{**dict(conf=FAKE, argmax=FAKE, B=16, tau=0.9, masked=FAKE,
+                                            tokens=FAKE, n_committed=FAKE, stream=0,
+                                            check=False), **kw})
+    assert c(conf=None) == bd.BD_E_NULL
+    assert c(n_committed=None) == bd.BD_E_NULL
+    assert c(B=-1) == bd.BD_E_SHAPE
+    assert c(B=65) == bd.BD_E_SHAPE
+    assert c(tau=float("nan")) == bd.BD_E_SHAPE
+    a = lambda **kw: bd.bd_spec_accept(**{**dict(draft=FAKE, verify=FAKE, B=16, P=10,
+                                                 accepted=FAKE, kv_len=FAKE, out_tokens=FAKE,
+                                                 stream=0, check=False), **kw})
+    assert a(verify=None) == bd.BD_E_NULL
+    assert a(B=65) == bd.BD_E_SHAPE
+    assert a(P=-3) == bd.BD_E_SHAPE
+    assert a(P=2 ** 31 - 5) == bd.BD_E_SHAPE
+    s = lambda **kw: bd.bd_cert_scan(**{**dict(anchor_conf=FAKE, anchor_tok=FAKE, text_tok=FAKE,
+                                               n=64, k=4, order=FAKE, accepted=FAKE,
+                                               skip_full=FAKE, stream=0, check=False), **kw})
+    assert s(order=None) == bd.BD_E_NULL
+    assert s(n=-1) == bd.BD_E_SHAPE
+    assert s(n=1025) == bd.BD_E_SHAPE
+
+
+def test_dualstream_validation():
+    d = lambda **kw: bd.bd_dualstream_attn(**{**dict(dt=bd.BD_BF16, q=FAKE, k=FAKE, v=FAKE,
+                                                     n_vis=16, n_txt=16, block=4, H=2, dh=128,
+                                                     scale=0.0, out=FAKE, stream=0,
+                                                     check=False), **kw})
+    assert d(v=None) == bd.BD_E_NULL
+    assert d(dt=3) == bd.BD_E_DTYPE
+    assert d(block=0) == bd.BD_E_SHAPE
+    assert d(H=0) == bd.BD_E_SHAPE
+    assert d(n_vis=0, n_txt=0) == bd.BD_E_SHAPE
+    assert d(n_txt=-1) == bd.BD_E_SHAPE
+    assert d(dh=16) == bd.BD_E_SHAPE
+    assert d(k=MISALIGNED) == bd.BD_E_ALIGN
+    assert d(scale=float("inf")) == bd.BD_E_SHAPE
+
+
+def test_python_binding_raises_on_error():
+    with pytest.raises(bd.BdError) as e:
+        bd.bd_commit(FAKE, FAKE, 99, 0.9, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == bd.BD_E_SHAPE
