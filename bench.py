@@ -1,0 +1,272 @@
+"""Benchmark of the block-diffusion decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one threshold (MDM) block-decode step of the Qwen2.5-VL-3B-shaped
+workload: bd_block_attn (16 block queries, bidirectional block, over a
+1024-visual + 256-prompt KV prefix; 16 query / 2 KV heads, head_dim 128) ->
+bd_lmhead_conf (hidden 2048 x vocabulary 151936, bf16) -> bd_commit
+(threshold 0.9), plus the restore of the block state so that every step does
+the same work.  Inputs are seeded synthetic tensors already resident in HBM;
+the step is captured once as a HIP graph and replayed K times between HIP
+events.  One JSON line is printed.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "block decode steps/s + committed tok/s (B=16, 1280-tok prefix); % peak HBM GB/s"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published peak
+PROFILE_DIR = ROOT / "profiles"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        h.update((ROOT / "block_diffusion_vlm_amd" / "csrc" / n).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def timed(fn, iters, warmup, stream):
+    """Average ms per call of fn() (launching on `stream`), HIP events on it."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def traffic_from_profile(kernel_hash: str):
+    """HBM bytes per LM-head call from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    f = PROFILE_DIR / "lmhead_qwen_decode_pmc.json"
+    if not f.exists():
+        return None
+    try:
+        d = json.loads(f.read_text())
+    except ValueError:
+        return None
+    if d.get("kernel_source_sha") != kernel_hash:
+        return None
+    return d.get("hbm_bytes_per_call")
+
+
+def cpu_baseline(inp, budget_s):
+    """The oracle's decode step on the same inputs, timed on the host cores."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    tau = float(np.float32(0.9))
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode_step(inp["q"], inp["k_cache"], inp["v_cache"], inp["P"], inp["h"],
+                           inp["W"], inp["masked"], inp["tokens"], tau)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 50:
+            break
+    return {"value": n / el, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} full decode steps of the same workload (float64 NumPy oracle: "
+                      f"block attention, LM head over all 151936 rows, commit), {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_diffusion_vlm_amd import bdiff as bd
+    from block_diffusion_vlm_amd import runner, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if bd.bd_device_check(0) != bd.BD_OK:
+        raise SystemExit("device 0 is not gfx950")
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    inp = synth.qwen_decode()
+    step = runner.DecodeStep(inp)
+    B, P, Hq, Hkv, dh, d, V = (inp[k] for k in ("B", "P", "Hq", "Hkv", "dh", "d", "V"))
+
+    # Eager reference step (and the commit count that every replay repeats).
+    step.reset()
+    step.run()
+    torch.cuda.synchronize()
+    n_commit = int(step.n_committed.item())
+    tokens_ref = step.tokens.clone()
+
+    # Capture reset + step as one graph.
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step.reset()
+        step.run()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step.reset()
+        step.run()
+    torch.cuda.synchronize()
+
+    ms_step = timed(graph.replay, args.steps, args.warmup, stream)
+    torch.cuda.synchronize()
+    assert torch.equal(step.tokens, tokens_ref), "graph replay diverged from the eager step"
+    assert int(step.n_committed.item()) == n_commit
+
+    # Dominant kernel: the LM head (its two dispatches), timed alone.
+    ms_lm = timed(lambda: step.lm(step.h), args.steps, args.warmup, stream)
+    ms_attn = timed(lambda: step.attn(step.q, step.k_cache, step.v_cache), args.steps,
+                    args.warmup, stream)
+
+    # Algorithmic bytes (each byte the step must touch once).
+    b_W = V * d * 2
+    b_lm = b_W + B * d * 2 + B * 8
+    b_kv = 2 * Hkv * (P + B) * dh * 2
+    b_attn = b_kv + 2 * B * Hq * dh * 2
+    b_commit = B * (4 + 4 + 1 + 4) + B * (1 + 4) + 4
+    b_step = b_lm + b_attn + b_commit
+    steps_per_s = 1e3 / ms_step
+    kernel_hash = source_hash("k_lmhead.hip")
+    achieved = b_lm / (ms_lm * 1e-3) / 1e9
+
+    # Plain device copy of known size (calibrates the HBM byte counters in a
+    # profiled run of this same command).
+    cal = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda")
+    cal2 = torch.empty_like(cal)
+    ms_copy = timed(lambda: cal2.copy_(cal), 20, 3, stream)
+    del cal, cal2
+
+    out = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 1),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Qwen2.5-VL-3B-shaped MDM block-decode step", "block": B,
+                   "prefix": P, "prefix_visual": inp["n_vis"], "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": dh, "hidden": d, "vocab": V, "threshold": 0.9,
+                   "global_batch": 1, "parallelism": "none (1 GPU)"},
+        "committed_tok_per_s": round(steps_per_s * n_commit, 1),
+        "committed_per_step": n_commit,
+        "step_hbm_gbs": round(b_step / (ms_step * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(b_step / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": "bd_lmhead_conf (contraction + merge)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile(kernel_hash),
+                     "us_per_launch": round(ms_lm * 1e3, 2), "bytes_per_launch": b_lm},
+        "kernels_us": {"bd_block_attn": round(ms_attn * 1e3, 2),
+                       "bd_lmhead_conf": round(ms_lm * 1e3, 2),
+                       "copy_256MiB_GBs": round(2 * 256 * 2 ** 20 / (ms_copy * 1e-3) / 1e9, 1)},
+    }
+
+    if not args.no_secondary:
+        out["secondary"] = secondary(args, stream)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def dualstream_pairs(n_vis, n_txt, block):
+    """Visible (query, key) pairs of one head under the N2N/N2C/C2C masks, in
+    closed form: causal clean stream, then per noisy row every visual key, the
+    clean text up to its position and its own (possibly ragged) block."""
+    ctx = n_vis + n_txt
+    full, rem = divmod(n_txt, block)
+    n2n = full * block * block + rem * rem
+    return ctx * (ctx + 1) // 2 + n_txt * n_vis + n_txt * (n_txt + 1) // 2 + n2n
+
+
+def secondary(args, stream):
+    """The other workloads, each timed on its own (not part of `value`)."""
+    import torch
+    from block_diffusion_vlm_amd import runner, synth
+    res = {}
+    iters = max(20, args.steps // 5)
+    warm = max(3, args.warmup // 5)
+
+    r5 = synth.dualstream()
+    ds = runner.DualStream(r5)
+    ms = timed(ds.run, iters, warm, stream)
+    flops = dualstream_pairs(r5["n_vis"], r5["n_txt"], r5["block"]) * r5["H"] * 4 * r5["dh"]
+    res["dualstream_fwd"] = {"us": round(ms * 1e3, 2),
+                             "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                             "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "shape": "1024 vis + 2048 clean + 2048 noisy, block 32, 16 heads x 128"}
+    del ds
+
+    r3 = synth.linear_spec()
+    lin = runner.LinearSpecStep(r3)
+    ms = timed(lin.run, iters, warm, stream)
+    torch.cuda.synchronize()
+    L = int(lin.accepted.item())
+    b = 2 * (r3["V"] * r3["d"] * 2 + 2 * r3["Hkv"] * r3["cap"] * r3["dh"] * 2)
+    res["linear_spec_step"] = {"us": round(ms * 1e3, 2), "accepted": L,
+                               "accepted_tok_per_s": round(L / (ms * 1e-3), 1),
+                               "hbm_frac": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del lin, r3
+
+    r4 = synth.fused_spec()
+    fu = runner.FusedSpecStep(r4)
+    ms = timed(fu.run, iters, warm, stream)
+    torch.cuda.synchronize()
+    b = r4["V"] * r4["d"] * 2 + 2 * r4["Hkv"] * r4["cap"] * r4["dh"] * 2
+    res["fused_spec_step"] = {"us": round(ms * 1e3, 2), "accepted": int(fu.accepted.item()),
+                              "cert_accepted": int(fu.cert_L.item()),
+                              "hbm_frac": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    ms_attn = timed(lambda: fu.attn(fu.t["q"], fu.t["k_cache"], fu.t["v_cache"]), iters, warm,
+                    stream)
+    res["fused_spec_step"]["attn_us"] = round(ms_attn * 1e3, 2)
+    del fu, r4
+    return res
+
+
+if __name__ == "__main__":
+    main()

@@ -18,8 +18,11 @@
 // rows into running (max, sum, argmax) states in the log2 domain.  Tiles are
 // dealt round-robin to a persistent grid, so the load is even to within one
 // tile per workgroup.  Each workgroup writes one partial state per position;
-// the last workgroup to finish (completion counter) merges all partials in a
-// fixed order, so the result is deterministic.
+// a second, small kernel (one workgroup per position) merges the partials in
+// a fixed order, so the result is deterministic.  The kernel boundary makes
+// the partials visible to the merge; an in-kernel "last workgroup" merge
+// would need a device-scope release fence per workgroup, which on gfx950
+// writes back the L2 and costs far more than the second launch.
 #include "bd_internal.h"
 
 namespace bd {
@@ -27,10 +30,11 @@ namespace bd {
 namespace {
 
 constexpr int kMaxGrid = 512;       // persistent workgroups for the bf16 path
-constexpr int kCtrBytes = 256;      // completion counter area at the start of ws
+constexpr int kCombineThreads = 256;
 
+// Partial states live column-major, [position][partial], so that the merge
+// kernel reads each position's partials with coalesced loads.
 struct WsView {
-    unsigned* ctr;
     float* m;
     float* s;
     int* a;
@@ -40,20 +44,15 @@ __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_
 
 __host__ __device__ inline WsView ws_view(void* ws, int G, int B) {
     uint8_t* p = static_cast<uint8_t*>(ws);
+    const size_t one = align256(size_t(G) * B * sizeof(float));
     WsView v;
-    v.ctr = reinterpret_cast<unsigned*>(p);
-    size_t off = kCtrBytes;
-    v.m = reinterpret_cast<float*>(p + off);
-    off += align256(size_t(G) * B * sizeof(float));
-    v.s = reinterpret_cast<float*>(p + off);
-    off += align256(size_t(G) * B * sizeof(float));
-    v.a = reinterpret_cast<int*>(p + off);
+    v.m = reinterpret_cast<float*>(p);
+    v.s = reinterpret_cast<float*>(p + one);
+    v.a = reinterpret_cast<int*>(p + 2 * one);
     return v;
 }
 
-inline size_t ws_size(int G, int B) {
-    return kCtrBytes + 3 * align256(size_t(G) * B * 4);
-}
+inline size_t ws_size(int G, int B) { return 3 * align256(size_t(G) * B * 4); }
 
 // Fold four logits (rows row0..row0+3, already in log2 units) into a state.
 // Rows are visited in increasing order, so a strict '>' keeps the lowest
@@ -85,63 +84,49 @@ __device__ __forceinline__ ArgSoft shfl_xor_state(ArgSoft x, int off) {
     return y;
 }
 
-// Arrival on the completion counter; returns true in the last workgroup.
-// Partials written before the call are visible to the last workgroup after
-// it returns (device-scope release/acquire fences around the atomic).
-__device__ __forceinline__ bool arrive_last(unsigned* ctr, unsigned nblocks) {
-    __shared__ unsigned s_last;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned old = atomicInc(ctr, nblocks - 1);   // wraps back to 0
-        s_last = (old == nblocks - 1) ? 1u : 0u;
-    }
-    __syncthreads();
-    const bool last = s_last != 0;
-    if (last) __threadfence();
-    return last;
+__device__ __forceinline__ void store_partial(const WsView& w, int G, int col, int part, ArgSoft s) {
+    const size_t idx = size_t(col) * G + part;
+    w.m[idx] = s.m;
+    w.s[idx] = s.s;
+    w.a[idx] = s.a;
 }
 
-// Merge G partial states per position in a fixed order and write the
-// outputs.  Called by every thread of the last workgroup (blockDim.x >= 64,
-// a multiple of 64).
-__device__ void final_combine(const WsView& w, int G, int B, float* conf, int32_t* argmax) {
-    int bp = 1;
-    while (bp < B) bp <<= 1;
-    const int nthr = blockDim.x;
-    int T = nthr / bp;                  // threads per position (power of two)
-    if (T > 64) T = 64;
-    const int col = threadIdx.x / T;
-    const int sub = threadIdx.x % T;
-    for (int c0 = 0; c0 < B; c0 += nthr / T) {
-        const int c = c0 + col;
-        ArgSoft st{-INFINITY, 0.f, 0x7fffffff};
-        if (c < B) {
-            int p = sub;
-            for (; p + 7 * T < G; p += 8 * T) {
-                float mm[8], ss[8];
-                int aa[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const size_t idx = size_t(p + u * T) * B + c;
-                    mm[u] = w.m[idx];
-                    ss[u] = w.s[idx];
-                    aa[u] = w.a[idx];
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u) st = merge(st, ArgSoft{mm[u], ss[u], aa[u]});
-            }
-            for (; p < G; p += T) {
-                const size_t idx = size_t(p) * B + c;
-                st = merge(st, ArgSoft{w.m[idx], w.s[idx], w.a[idx]});
-            }
-        }
-        for (int off = 1; off < T; off <<= 1) st = merge(st, shfl_xor_state(st, off));
-        if (c < B && sub == 0) {
-            conf[c] = 1.0f / st.s;
-            argmax[c] = st.a;
-        }
+// Merge of the G partial states of position blockIdx.x, in a fixed order:
+// thread t folds partials t, t + 256, ... (one round of independent loads
+// for G <= 512), then a fixed shuffle tree and a fixed cross-wave order.
+__global__ __launch_bounds__(kCombineThreads) void lmhead_combine_kernel(
+    const void* __restrict__ ws, int G, int B, float* __restrict__ conf,
+    int32_t* __restrict__ argmax) {
+    __shared__ ArgSoft wred[kCombineThreads / 64];
+    const WsView w = ws_view(const_cast<void*>(ws), G, B);
+    const int col = blockIdx.x;
+    const float* m = w.m + size_t(col) * G;
+    const float* s = w.s + size_t(col) * G;
+    const int* a = w.a + size_t(col) * G;
+    ArgSoft st{-INFINITY, 0.f, 0x7fffffff};
+    int p = threadIdx.x;
+    for (; p + kCombineThreads < G; p += 2 * kCombineThreads) {
+        const ArgSoft x{m[p], s[p], a[p]};
+        const int q = p + kCombineThreads;
+        const ArgSoft y{m[q], s[q], a[q]};
+        st = merge(merge(st, x), y);
     }
+    if (p < G) st = merge(st, ArgSoft{m[p], s[p], a[p]});
+    for (int off = 1; off < 64; off <<= 1) st = merge(st, shfl_xor_state(st, off));
+    if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = st;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        ArgSoft r = wred[0];
+        for (int i = 1; i < kCombineThreads / 64; ++i) r = merge(r, wred[i]);
+        conf[col] = 1.0f / r.s;
+        argmax[col] = r.a;
+    }
+}
+
+hipError_t launch_combine(void* ws, int G, int B, float* conf, int32_t* argmax, hipStream_t st) {
+    hipLaunchKernelGGL(lmhead_combine_kernel, dim3(B), dim3(kCombineThreads), 0, st, ws, G, B,
+                       conf, argmax);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -152,8 +137,6 @@ template <int NB, int NCH>
 __global__ __launch_bounds__(256) void lmhead_bf16_kernel(const uint16_t* __restrict__ h,
                                                           const uint16_t* __restrict__ W,
                                                           int B, int d, int V, int ntiles,
-                                                          float* __restrict__ conf,
-                                                          int32_t* __restrict__ argmax,
                                                           void* __restrict__ ws) {
     constexpr int NL = NCH * 4;                       // 16-byte loads per lane per tile
     __shared__ f32x4 red[2][4][NB][64];               // per-wave partial logits, 2 buffers
@@ -264,15 +247,9 @@ __global__ __launch_bounds__(256) void lmhead_bf16_kernel(const uint16_t* __rest
             ArgSoft s = fin[0][nb][lane];
             for (int w = 1; w < nwave; ++w) s = merge(s, fin[w][nb][lane]);
             const int col = nb * 16 + lane;
-            if (col < B) {
-                const size_t idx = size_t(blockIdx.x) * B + col;
-                wv.m[idx] = s.m;
-                wv.s[idx] = s.s;
-                wv.a[idx] = s.a;
-            }
+            if (col < B) store_partial(wv, G, col, blockIdx.x, s);
         }
     }
-    if (arrive_last(wv.ctr, G)) final_combine(wv, G, B, conf, argmax);
 }
 
 // Generic bf16 fallback for shapes whose h fragments do not fit in
@@ -281,7 +258,7 @@ __global__ __launch_bounds__(256) void lmhead_bf16_kernel(const uint16_t* __rest
 template <int NB>
 __global__ __launch_bounds__(256) void lmhead_bf16_generic_kernel(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int B, int d, int V,
-    int ntiles, float* __restrict__ conf, int32_t* __restrict__ argmax, void* __restrict__ ws) {
+    int ntiles, void* __restrict__ ws) {
     __shared__ ArgSoft fin[4][NB][16];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -338,15 +315,9 @@ __global__ __launch_bounds__(256) void lmhead_bf16_generic_kernel(
             ArgSoft s = fin[0][nb][lane];
             for (int w = 1; w < nwave; ++w) s = merge(s, fin[w][nb][lane]);
             const int col = nb * 16 + lane;
-            if (col < B) {
-                const size_t idx = size_t(blockIdx.x) * B + col;
-                wv.m[idx] = s.m;
-                wv.s[idx] = s.s;
-                wv.a[idx] = s.a;
-            }
+            if (col < B) store_partial(wv, G, col, blockIdx.x, s);
         }
     }
-    if (arrive_last(wv.ctr, G)) final_combine(wv, G, B, conf, argmax);
 }
 
 // ---------------------------------------------------------------------------
@@ -357,9 +328,7 @@ constexpr int kF32Rows = 256;
 
 __global__ __launch_bounds__(256) void lmhead_f32_kernel(const float* __restrict__ h,
                                                          const float* __restrict__ W, int B,
-                                                         int d, int V, float* __restrict__ conf,
-                                                         int32_t* __restrict__ argmax,
-                                                         void* __restrict__ ws) {
+                                                         int d, int V, void* __restrict__ ws) {
     extern __shared__ float hs[];
     __shared__ ArgSoft wst[4];
     const int b = blockIdx.y;
@@ -376,21 +345,11 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(const float* __restrict
     for (int off = 1; off < 64; off <<= 1) st = merge(st, shfl_xor_state(st, off));
     if ((threadIdx.x & 63) == 0) wst[threadIdx.x >> 6] = st;
     __syncthreads();
-    const int G = gridDim.x * gridDim.y;
-    const int blk = blockIdx.y * gridDim.x + blockIdx.x;   // partial index
-    // Partials are laid out [slice][b] so final_combine sees G' = gridDim.x
-    // slices per position.
-    const WsView wv = ws_view(ws, gridDim.x, B);
     if (threadIdx.x == 0) {
         ArgSoft s = wst[0];
         for (int w = 1; w < 4; ++w) s = merge(s, wst[w]);
-        const size_t idx = size_t(blockIdx.x) * B + b;
-        wv.m[idx] = s.m;
-        wv.s[idx] = s.s;
-        wv.a[idx] = s.a;
+        store_partial(ws_view(ws, gridDim.x, B), gridDim.x, b, blockIdx.x, s);
     }
-    (void)blk;
-    if (arrive_last(wv.ctr, G)) final_combine(wv, gridDim.x, B, conf, argmax);
 }
 
 // Host-side plan for the bf16 kernel: waves per workgroup (K split) and
@@ -422,14 +381,17 @@ hipError_t launch_nb(const void* h, const void* W, int B, int d, int V, float* c
     int ks = 0, nch = 0;
     if (!plan_bf16(B, d, &ks, &nch)) {
         hipLaunchKernelGGL(lmhead_bf16_generic_kernel<NB>, dim3(G), dim3(256), 0, st, hh, ww, B,
-                           d, V, ntiles, conf, argmax, ws);
-        return hipGetLastError();
+                           d, V, ntiles, ws);
+        const hipError_t e = hipGetLastError();
+        return e != hipSuccess ? e : launch_combine(ws, G, B, conf, argmax, st);
     }
 #define BD_LMH_CASE(N)                                                                     \
     case N:                                                                                \
         if constexpr (N * NB <= 8) {                                                       \
             hipLaunchKernelGGL((lmhead_bf16_kernel<NB, N>), dim3(G), dim3(64 * ks), 0, st, \
-                               hh, ww, B, d, V, ntiles, conf, argmax, ws);                 \
+                               hh, ww, B, d, V, ntiles, ws);                               \
+        } else {                                                                           \
+            return hipErrorInvalidValue;                                                   \
         }                                                                                  \
         break;
     switch (nch) {
@@ -445,7 +407,8 @@ hipError_t launch_nb(const void* h, const void* W, int B, int d, int V, float* c
             return hipErrorInvalidValue;
     }
 #undef BD_LMH_CASE
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : launch_combine(ws, G, B, conf, argmax, st);
 }
 
 }  // namespace
@@ -458,7 +421,8 @@ int lmhead_grid(int B, int d, int V) {
 }
 
 size_t lmhead_ws_bytes(int B, int d, int V) {
-    // bf16: one partial per workgroup; f32: one per 256-row slice.
+    // bf16: one partial per workgroup and position; f32: one per 256-row
+    // vocabulary slice and position.
     const int g_bf16 = lmhead_grid(B, d, V);
     const int g_f32 = (V + kF32Rows - 1) / kF32Rows;
     const int G = g_bf16 > g_f32 ? g_bf16 : g_f32;
@@ -480,8 +444,9 @@ hipError_t launch_lmhead_f32(const float* h, const float* W, int B, int d, int V
                              int32_t* argmax, void* ws, hipStream_t st) {
     const dim3 grid((V + kF32Rows - 1) / kF32Rows, B);
     hipLaunchKernelGGL(lmhead_f32_kernel, grid, dim3(kF32Rows), size_t(d) * sizeof(float), st, h,
-                       W, B, d, V, conf, argmax, ws);
-    return hipGetLastError();
+                       W, B, d, V, ws);
+    const hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : launch_combine(ws, grid.x, B, conf, argmax, st);
 }
 
 }  // namespace bd

@@ -42,7 +42,7 @@ def mask_dev(kind: int, bq: int, device="cuda") -> torch.Tensor:
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    """Zero-filled device workspace (the LM head needs its counter at 0)."""
+    """Zero-filled device workspace of at least 256 bytes."""
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 

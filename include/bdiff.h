@@ -111,10 +111,10 @@ bd_status bd_block_attn(bd_dtype dt, const void* q, const void* k_cache, const v
  *   h       [B][d]  dtype dt
  *   W       [V][d]  dtype dt (row-major: one row per vocabulary entry)
  *   conf    [B] float32 out;  argmax [B] int32 out
- *   ws      workspace of at least bd_lmhead_conf_ws_bytes(B, d, V) bytes.
- *           Its first 256 bytes hold a completion counter that must be zero
- *           before the first call; every call leaves it at zero again, so a
- *           zero-filled workspace can be reused across calls.
+ *   ws      workspace of at least bd_lmhead_conf_ws_bytes(B, d, V) bytes
+ *           (per-workgroup partial maxima, sums and indices; no initial
+ *           contents required).  Two kernels run: the streaming contraction
+ *           and a small merge of the partials.
  * Limits: 1 <= B <= 64, V >= 1, d >= 1;  BD_BF16 needs d % 128 == 0 and
  *   d <= 16384.  The result is deterministic (fixed reduction order).
  * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_ALIGN, BD_E_WORKSPACE,

@@ -139,11 +139,11 @@ def test_lmhead_bf16_matches_oracle(B, d, V):
     oc, oa = oracle.lmhead_conf(r["h"], r["W"])
     assert np.array_equal(a0, oa)
     assert rel_err(conf0, oc) <= 1e-4 or np.abs(conf0 / oc - 1).max() <= 1e-4
-    # Deterministic, and the workspace counter is back at zero for reuse.
+    # Deterministic: a second call on a dirty workspace gives identical bits.
     lm(h)
     torch.cuda.synchronize()
     assert np.array_equal(lm.conf.cpu().numpy(), conf0)
-    assert int(lm.ws[:4].view(torch.int32).item()) == 0
+    assert np.array_equal(lm.argmax.cpu().numpy(), a0)
 
 
 def test_lmhead_workspace_reuse_across_shapes():
