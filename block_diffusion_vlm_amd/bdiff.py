@@ -24,7 +24,7 @@ BD_MASK_BIDIR, BD_MASK_CAUSAL, BD_MASK_SPEC_FUSED = 0, 1, 2
 EXPORTS = (
     "bd_status_str", "bd_device_check", "bd_make_intra_mask",
     "bd_block_attn_ws_bytes", "bd_block_attn",
-    "bd_lmhead_conf_ws_bytes", "bd_lmhead_conf",
+    "bd_lmhead_conf_ws_bytes", "bd_lmhead_conf", "bd_lmhead_conf_commit",
     "bd_commit", "bd_spec_accept", "bd_cert_scan", "bd_dualstream_attn",
 )
 
@@ -50,6 +50,7 @@ _SIGS = {
     "bd_block_attn": ([_I, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _F, _P, _P, _SZ, _P], _I),
     "bd_lmhead_conf_ws_bytes": ([_I, _I, _I], _SZ),
     "bd_lmhead_conf": ([_I, _P, _P, _I, _I, _I, _P, _P, _P, _SZ, _P], _I),
+    "bd_lmhead_conf_commit": ([_I, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "bd_commit": ([_P, _P, _I, _F, _P, _P, _P, _P], _I),
     "bd_spec_accept": ([_P, _P, _I, _I, _P, _P, _P, _P], _I),
     "bd_cert_scan": ([_P, _P, _P, _I, _I, _P, _P, _P, _P], _I),
@@ -133,6 +134,14 @@ def bd_lmhead_conf(dt, h, W, B, d, V, conf, argmax, ws, ws_bytes, stream=None, c
     st = lib().bd_lmhead_conf(dt, _ptr(h), _ptr(W), B, d, V, _ptr(conf), _ptr(argmax), _ptr(ws),
                               ws_bytes, _stream(stream))
     return _ret("bd_lmhead_conf", st, check)
+
+
+def bd_lmhead_conf_commit(dt, h, W, B, d, V, tau, conf, argmax, masked, tokens, n_committed, ws,
+                          ws_bytes, stream=None, check=True) -> int:
+    st = lib().bd_lmhead_conf_commit(dt, _ptr(h), _ptr(W), B, d, V, tau, _ptr(conf), _ptr(argmax),
+                                     _ptr(masked), _ptr(tokens), _ptr(n_committed), _ptr(ws),
+                                     ws_bytes, _stream(stream))
+    return _ret("bd_lmhead_conf_commit", st, check)
 
 
 def bd_commit(conf, argmax, B, tau, masked, tokens, n_committed, stream=None, check=True) -> int:

@@ -100,6 +100,7 @@ bd_status bd_block_attn(bd_dtype dt, const void* q, const void* k_cache, const v
             static_cast<const float*>(q), static_cast<const float*>(k_cache),
             static_cast<const float*>(v_cache), P, cap, intra_mask, Bq, Hq, Hkv, dh, sc,
             static_cast<float*>(out), stream));
+    if ((int64_t)P + Bq > 65536) return BD_E_SHAPE;   // at most 1024 key tiles
     const size_t need = bd::block_attn_ws_bytes(P, Bq, Hq, Hkv, dh);
     if (!ws || ws_bytes < need) return BD_E_WORKSPACE;
     if (!aligned16(ws)) return BD_E_ALIGN;
@@ -112,21 +113,42 @@ size_t bd_lmhead_conf_ws_bytes(int32_t B, int32_t d, int32_t V) {
     return bd::lmhead_ws_bytes(B, d, V);
 }
 
-bd_status bd_lmhead_conf(bd_dtype dt, const void* h, const void* W, int32_t B, int32_t d,
-                         int32_t V, float* conf, int32_t* argmax, void* ws, size_t ws_bytes,
-                         hipStream_t stream) {
-    if (!h || !W || !conf || !argmax) return BD_E_NULL;
+namespace {
+
+bd_status lmhead_common(bd_dtype dt, const void* h, const void* W, int32_t B, int32_t d,
+                        int32_t V, const bd::Finish& f, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+    if (!h || !W || !f.conf || !f.argmax) return BD_E_NULL;
+    if (f.commit && (!f.masked || !f.tokens || !f.n_committed)) return BD_E_NULL;
     if (dt != BD_F32 && dt != BD_BF16) return BD_E_DTYPE;
     if (B < 1 || B > 64 || d < 1 || V < 1) return BD_E_SHAPE;
     if (dt == BD_BF16 && (d % 128 != 0 || d > 16384)) return BD_E_SHAPE;
+    if (f.commit && !(f.tau == f.tau)) return BD_E_SHAPE;
     if (!aligned16(h) || !aligned16(W)) return BD_E_ALIGN;
     if (!ws || ws_bytes < bd::lmhead_ws_bytes(B, d, V)) return BD_E_WORKSPACE;
     if (!aligned16(ws)) return BD_E_ALIGN;
     if (dt == BD_F32)
         return launch_status(bd::launch_lmhead_f32(static_cast<const float*>(h),
-                                                   static_cast<const float*>(W), B, d, V, conf,
-                                                   argmax, ws, stream));
-    return launch_status(bd::launch_lmhead_bf16(h, W, B, d, V, conf, argmax, ws, stream));
+                                                   static_cast<const float*>(W), B, d, V, f, ws,
+                                                   stream));
+    return launch_status(bd::launch_lmhead_bf16(h, W, B, d, V, f, ws, stream));
+}
+
+}  // namespace
+
+bd_status bd_lmhead_conf(bd_dtype dt, const void* h, const void* W, int32_t B, int32_t d,
+                         int32_t V, float* conf, int32_t* argmax, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+    const bd::Finish f{conf, argmax, false, 0.f, nullptr, nullptr, nullptr};
+    return lmhead_common(dt, h, W, B, d, V, f, ws, ws_bytes, stream);
+}
+
+bd_status bd_lmhead_conf_commit(bd_dtype dt, const void* h, const void* W, int32_t B, int32_t d,
+                                int32_t V, float tau, float* conf, int32_t* argmax,
+                                uint8_t* masked, int32_t* tokens, int32_t* n_committed, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+    const bd::Finish f{conf, argmax, true, tau, masked, tokens, n_committed};
+    return lmhead_common(dt, h, W, B, d, V, f, ws, ws_bytes, stream);
 }
 
 bd_status bd_commit(const float* conf, const int32_t* argmax, int32_t B, float tau,

@@ -40,30 +40,56 @@ __device__ __forceinline__ int acc_row(int r, int lane) {
     return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-// Cooperative load of keys [j0, j0 + 64) of one head into LDS (K as is, V
-// transposed).  Rows at or beyond `jend` are filled with zeros; `row_stride`
-// is the distance between consecutive keys in elements.  256 threads.
-__device__ __forceinline__ void load_tile(Tiles& t, const uint16_t* __restrict__ kbase,
-                                          const uint16_t* __restrict__ vbase, size_t row_stride,
-                                          int j0, int jend) {
+// A 64-key tile of K and V in flight through registers: thread t holds keys
+// t/16 + 16u (u = 0..3), dims 8*(t%16) .. +7, of both K and V.  256 threads.
+struct TileRegs {
+    u32x4 k[4];
+    u32x4 v[4];
+};
+
+// Global -> registers for keys [j0, j0 + 64); keys at or beyond `jend` read
+// as zeros.  `row_stride` is the distance between consecutive keys in elements.
+__device__ __forceinline__ void fetch_tile(TileRegs& r, const uint16_t* __restrict__ kbase,
+                                           const uint16_t* __restrict__ vbase, size_t row_stride,
+                                           int j0, int jend) {
+    const int tid = threadIdx.x;
+    const int col = (tid & 15) * 8;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int j = j0 + (tid >> 4) + 16 * u;
+        r.k[u] = u32x4{0, 0, 0, 0};
+        r.v[u] = u32x4{0, 0, 0, 0};
+        if (j < jend) {
+            r.k[u] = *reinterpret_cast<const u32x4*>(kbase + size_t(j) * row_stride + col);
+            r.v[u] = *reinterpret_cast<const u32x4*>(vbase + size_t(j) * row_stride + col);
+        }
+    }
+}
+
+// Registers -> LDS: K as is, V transposed.
+__device__ __forceinline__ void store_tile(Tiles& t, const TileRegs& r) {
     const int tid = threadIdx.x;
     const int col = (tid & 15) * 8;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int key = (tid >> 4) + 16 * u;
-        const int j = j0 + key;
-        u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-        if (j < jend) {
-            kv = *reinterpret_cast<const u32x4*>(kbase + size_t(j) * row_stride + col);
-            vv = *reinterpret_cast<const u32x4*>(vbase + size_t(j) * row_stride + col);
-        }
-        *reinterpret_cast<u32x4*>(&t.k[key * kKPitch + col]) = kv;
+        *reinterpret_cast<u32x4*>(&t.k[key * kKPitch + col]) = r.k[u];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            t.vt[(col + 2 * e) * kVPitch + key] = static_cast<uint16_t>(vv[e] & 0xFFFFu);
-            t.vt[(col + 2 * e + 1) * kVPitch + key] = static_cast<uint16_t>(vv[e] >> 16);
+            t.vt[(col + 2 * e) * kVPitch + key] = static_cast<uint16_t>(r.v[u][e] & 0xFFFFu);
+            t.vt[(col + 2 * e + 1) * kVPitch + key] = static_cast<uint16_t>(r.v[u][e] >> 16);
         }
     }
+}
+
+// Cooperative load of keys [j0, j0 + 64) of one head into LDS (K as is, V
+// transposed).
+__device__ __forceinline__ void load_tile(Tiles& t, const uint16_t* __restrict__ kbase,
+                                          const uint16_t* __restrict__ vbase, size_t row_stride,
+                                          int j0, int jend) {
+    TileRegs r;
+    fetch_tile(r, kbase, vbase, row_stride, j0, jend);
+    store_tile(t, r);
 }
 
 // Q fragments (B operand of S^T) for 32 rows; rowptr == nullptr gives zeros.

@@ -68,13 +68,23 @@ hipError_t launch_cert_scan(const float* conf, const int32_t* atok, const int32_
                             int k, int32_t* order, int32_t* accepted, int32_t* skip,
                             hipStream_t st);
 
-// LM head
+// LM head.  The merge of the per-workgroup partials writes conf/argmax and,
+// when `commit` is set, also applies the threshold commit to the block.
+struct Finish {
+    float* conf;
+    int32_t* argmax;
+    bool commit;
+    float tau;
+    uint8_t* masked;
+    int32_t* tokens;
+    int32_t* n_committed;
+};
 int lmhead_grid(int B, int d, int V);           // workgroups used for a shape
 size_t lmhead_ws_bytes(int B, int d, int V);
-hipError_t launch_lmhead_bf16(const void* h, const void* W, int B, int d, int V, float* conf,
-                              int32_t* argmax, void* ws, hipStream_t st);
-hipError_t launch_lmhead_f32(const float* h, const float* W, int B, int d, int V, float* conf,
-                             int32_t* argmax, void* ws, hipStream_t st);
+hipError_t launch_lmhead_bf16(const void* h, const void* W, int B, int d, int V, const Finish& f,
+                              void* ws, hipStream_t st);
+hipError_t launch_lmhead_f32(const float* h, const float* W, int B, int d, int V,
+                             const Finish& f, void* ws, hipStream_t st);
 
 // Block attention
 size_t block_attn_ws_bytes(int P, int Bq, int Hq, int Hkv, int dh);

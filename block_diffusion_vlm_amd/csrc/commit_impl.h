@@ -1,0 +1,50 @@
+// Threshold commit of one block, executed by one full wavefront (lane i owns
+// position i, B <= 64).  Shared by the standalone commit kernel and the
+// LM-head merge kernel that commits right after it.
+#pragma once
+
+#include "bd_internal.h"
+
+namespace bd {
+
+// Every masked position with conf > tau is committed; if none qualifies and
+// some position is masked, the most confident masked position (lowest index
+// on ties) is committed alone.  Committing sets tokens[i] = argmax and
+// masked[i] = 0.  Must be called by all 64 lanes of a wave; c/a are lane i's
+// confidence and token (ignored for i >= B).
+__device__ __forceinline__ void commit_wave(float c, int32_t a, int B, float tau,
+                                            uint8_t* __restrict__ masked,
+                                            int32_t* __restrict__ tokens,
+                                            int32_t* __restrict__ n_committed) {
+    const int i = threadIdx.x & 63;
+    const bool in = i < B;
+    const bool m = in && masked[i] != 0;
+    const bool above = m && (c > tau);
+    const uint64_t above_bits = __ballot(above);
+    const uint64_t masked_bits = __ballot(m);
+    bool take = above;
+    int n = __popcll(above_bits);
+    if (above_bits == 0 && masked_bits != 0) {
+        float bc = c;
+        int bi = m ? i : 64;
+        for (int off = 32; off > 0; off >>= 1) {
+            const float oc = __shfl_xor(bc, off);
+            const int oi = __shfl_xor(bi, off);
+            const bool other_valid = oi < 64;
+            const bool mine_valid = bi < 64;
+            if (other_valid && (!mine_valid || oc > bc || (oc == bc && oi < bi))) {
+                bc = oc;
+                bi = oi;
+            }
+        }
+        take = (i == bi);
+        n = 1;
+    }
+    if (take) {
+        tokens[i] = a;
+        masked[i] = 0;
+    }
+    if (i == 0) *n_committed = n;
+}
+
+}  // namespace bd

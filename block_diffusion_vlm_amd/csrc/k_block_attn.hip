@@ -45,7 +45,7 @@ inline size_t partials_bytes(int rows, int nsplit) {
 __global__ __launch_bounds__(256) void block_attn_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int P, int cap, const uint64_t* __restrict__ mask, int Bq,
-    int Hq, int Hkv, float scale_log2, void* __restrict__ ws, int nsplit) {
+    int Hq, int Hkv, float scale_log2, void* __restrict__ ws, int nsplit, int kt) {
     __shared__ __align__(16) Tiles tiles;
     const int split = blockIdx.x;
     const int g = blockIdx.y;
@@ -54,9 +54,14 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
     const int group = Hq / Hkv;
     const int R = Bq * group;                       // query rows of this KV head
     const int Nk = P + Bq;
-    const int j0 = split * kBN;
+    const uint16_t* kb = kc + size_t(g) * cap * kDh;
+    const uint16_t* vb = vc + size_t(g) * cap * kDh;
+    const int t_beg = split * kt;
+    const int ntiles = (Nk + kBN - 1) / kBN;
+    const int t_end = t_beg + kt < ntiles ? t_beg + kt : ntiles;
 
-    load_tile(tiles, kc + size_t(g) * cap * kDh, vc + size_t(g) * cap * kDh, kDh, j0, Nk);
+    TileRegs nxt;
+    fetch_tile(nxt, kb, vb, kDh, t_beg * kBN, Nk);
 
     // Query row of this lane: r -> (block query i, head g*group + r % group).
     const int r = blockIdx.z * kRowsPerWg + wave * 32 + (lane & 31);
@@ -66,43 +71,54 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
     bf16x8 qf[8];
     load_q(qf, row_ok ? q + (size_t(qi) * Hq + qh) * kDh : nullptr, lane);
     const uint64_t mbits = row_ok ? mask[qi] : 0;
-    __syncthreads();
 
-    f32x16 sacc[2];
-    scores(sacc, tiles, qf, lane);
-
-    float x[2][16];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int j = j0 + 32 * kb + acc_row(e, lane);
-            const bool vis = (j < P) || (j < Nk && ((mbits >> (j - P)) & 1ull));
-            x[kb][e] = vis ? sacc[kb][e] * scale_log2 : -INFINITY;
-            mx = fmaxf(mx, x[kb][e]);
-        }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mref = (mx == -INFINITY) ? 0.f : mx;
-    float p[2][16];
-    float l = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            p[kb][e] = exp2f(x[kb][e] - mref);
-            l += p[kb][e];
-        }
-    l += __shfl_xor(l, 32);
-
+    float m = -INFINITY, l = 0.f;
     f32x16 oacc[4] = {};
-    accumulate_pv(oacc, tiles, p, lane);
+    for (int t = t_beg; t < t_end; ++t) {
+        const int j0 = t * kBN;
+        if (t > t_beg) __syncthreads();             // previous tile fully consumed
+        store_tile(tiles, nxt);
+        __syncthreads();
+        if (t + 1 < t_end) fetch_tile(nxt, kb, vb, kDh, j0 + kBN, Nk);
+
+        f32x16 sacc[2];
+        scores(sacc, tiles, qf, lane);
+        float x[2][16];
+        float mx = m;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int j = j0 + 32 * kb2 + acc_row(e, lane);
+                const bool vis = (j < P) || (j < Nk && ((mbits >> (j - P)) & 1ull));
+                x[kb2][e] = vis ? sacc[kb2][e] * scale_log2 : -INFINITY;
+                mx = fmaxf(mx, x[kb2][e]);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mref = (mx == -INFINITY) ? 0.f : mx;
+        const float alpha = exp2f(m - mref);
+        float p[2][16];
+        float ls = 0.f;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                p[kb2][e] = exp2f(x[kb2][e] - mref);
+                ls += p[kb2][e];
+            }
+        ls += __shfl_xor(ls, 32);
+        l = l * alpha + ls;
+        m = mx;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+        accumulate_pv(oacc, tiles, p, lane);
+    }
 
     if (row_ok) {
         const size_t rg = size_t(g) * R + r;        // global row
         const Partials pt = partials(ws, Hkv * R, nsplit);
         if (lane < 32) {
-            pt.m[rg * nsplit + split] = mx;
+            pt.m[rg * nsplit + split] = m;
             pt.l[rg * nsplit + split] = l;
         }
         float* o = pt.o + (rg * nsplit + split) * kDh;
@@ -118,11 +134,16 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
     }
 }
 
-// One wave per query row: merge the splits in order and normalise.
-__global__ __launch_bounds__(64) void block_attn_combine_kernel(const void* __restrict__ ws,
-                                                                int Bq, int Hq, int Hkv,
-                                                                int nsplit,
-                                                                uint16_t* __restrict__ out) {
+// One workgroup of 128 threads per query row: the split weights
+// 2^(m_s - M) are formed once (thread s owns split s), then thread t
+// accumulates output dim t over the splits in a fixed order, with the loads
+// of consecutive splits independent of each other.
+constexpr int kCombineThreads = 128;
+
+__global__ __launch_bounds__(kCombineThreads) void block_attn_combine_kernel(
+    const void* __restrict__ ws, int Bq, int Hq, int Hkv, int nsplit, uint16_t* __restrict__ out) {
+    __shared__ float wsh[1024];
+    __shared__ float red[kCombineThreads / 64];
     const int rg = blockIdx.x;                      // global row = g * R + r
     const int group = Hq / Hkv;
     const int R = Bq * group;
@@ -130,27 +151,50 @@ __global__ __launch_bounds__(64) void block_attn_combine_kernel(const void* __re
     const int r = rg % R;
     const int qi = r / group;
     const int qh = g * group + r % group;
+    const int t = threadIdx.x;
     const Partials pt = partials(const_cast<void*>(ws), Hkv * R, nsplit);
     const float* m = pt.m + size_t(rg) * nsplit;
     const float* l = pt.l + size_t(rg) * nsplit;
+
+    // Row maximum over the splits.
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, m[s]);
-    const int dh = 2 * threadIdx.x;
-    float o0 = 0.f, o1 = 0.f, L = 0.f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < nsplit; ++s) {
-            if (m[s] == -INFINITY) continue;
-            const float w = exp2f(m[s] - M);
-            const float* o = pt.o + (size_t(rg) * nsplit + s) * kDh;
-            L += w * l[s];
-            o0 += w * o[dh];
-            o1 += w * o[dh + 1];
-        }
-        o0 /= L;
-        o1 /= L;
+    for (int s = t; s < nsplit; s += kCombineThreads) M = fmaxf(M, m[s]);
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    if ((t & 63) == 0) red[t >> 6] = M;
+    __syncthreads();
+    M = fmaxf(red[0], red[1]);
+    __syncthreads();
+
+    // Split weights (0 for splits without a visible key) and their sum.
+    float L = 0.f;
+    for (int s = t; s < nsplit; s += kCombineThreads) {
+        const float ms = m[s];
+        const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+        wsh[s] = w;
+        L += w * l[s];
     }
-    uint16_t* dst = out + (size_t(qi) * Hq + qh) * kDh + dh;
-    *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(o0, o1);
+    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+    if ((t & 63) == 0) red[t >> 6] = L;
+    __syncthreads();
+    L = red[0] + red[1];
+
+    float acc = 0.f;
+    const float* o = pt.o + size_t(rg) * nsplit * kDh + t;
+    int s = 0;
+    for (; s + 8 <= nsplit; s += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = o[size_t(s + u) * kDh];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += wsh[s + u] * v[u];
+    }
+    for (; s < nsplit; ++s) acc += wsh[s] * o[size_t(s) * kDh];
+    const float res = (M == -INFINITY) ? 0.f : acc / L;
+    const float nb = __shfl_down(res, 1);
+    if ((t & 1) == 0) {
+        uint16_t* dst = out + (size_t(qi) * Hq + qh) * kDh + t;
+        *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(res, nb);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -209,30 +253,48 @@ __global__ __launch_bounds__(64) void block_attn_f32_kernel(
     if (lane + 64 < dh) orow[lane + 64] = o1 * inv;
 }
 
+// Key tiles per workgroup.  A split writes a partial output row of 128 floats
+// for each of the R = Bq * Hq / Hkv query rows of its KV head, while it reads
+// 64 keys x 512 bytes of K and V per tile; grouping tiles keeps the partial
+// traffic near the KV traffic when R is large (R / 128 tiles per split), and
+// one tile per split keeps the most workgroups busy when R is small.
+int tiles_per_split(int P, int Bq, int Hq, int Hkv) {
+    const int R = Bq * (Hq / Hkv);
+    const int ntiles = (P + Bq + kBN - 1) / kBN;
+    int kt = (R + 127) / 128;
+    if (kt < 1) kt = 1;
+    if (kt > ntiles) kt = ntiles;
+    return kt;
+}
+
+int num_splits(int P, int Bq, int Hq, int Hkv) {
+    const int ntiles = (P + Bq + kBN - 1) / kBN;
+    const int kt = tiles_per_split(P, Bq, Hq, Hkv);
+    return (ntiles + kt - 1) / kt;
+}
+
 }  // namespace
 
 size_t block_attn_ws_bytes(int P, int Bq, int Hq, int Hkv, int dh) {
     (void)dh;
-    const int nsplit = (P + Bq + kBN - 1) / kBN;
-    const int rows = Bq * Hq;      // = Hkv * R
-    (void)Hkv;
-    return partials_bytes(rows, nsplit);
+    return partials_bytes(Bq * Hq, num_splits(P, Bq, Hq, Hkv));
 }
 
 hipError_t launch_block_attn_bf16(const void* q, const void* kc, const void* vc, int P, int cap,
                                   const uint64_t* mask, int Bq, int Hq, int Hkv, float scale,
                                   void* out, void* ws, hipStream_t st) {
-    const int nsplit = (P + Bq + kBN - 1) / kBN;
+    const int kt = tiles_per_split(P, Bq, Hq, Hkv);
+    const int nsplit = num_splits(P, Bq, Hq, Hkv);
     const int R = Bq * (Hq / Hkv);
     const dim3 grid(nsplit, Hkv, (R + kRowsPerWg - 1) / kRowsPerWg);
     hipLaunchKernelGGL(block_attn_split_kernel, grid, dim3(256), 0, st,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                        static_cast<const uint16_t*>(vc), P, cap, mask, Bq, Hq, Hkv,
-                       scale * kLog2e, ws, nsplit);
+                       scale * kLog2e, ws, nsplit, kt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(block_attn_combine_kernel, dim3(Bq * Hq), dim3(64), 0, st, ws, Bq, Hq, Hkv,
-                       nsplit, static_cast<uint16_t*>(out));
+    hipLaunchKernelGGL(block_attn_combine_kernel, dim3(Bq * Hq), dim3(kCombineThreads), 0, st, ws,
+                       Bq, Hq, Hkv, nsplit, static_cast<uint16_t*>(out));
     return hipGetLastError();
 }
 

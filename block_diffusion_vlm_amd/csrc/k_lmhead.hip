@@ -18,19 +18,20 @@
 // rows into running (max, sum, argmax) states in the log2 domain.  Tiles are
 // dealt round-robin to a persistent grid, so the load is even to within one
 // tile per workgroup.  Each workgroup writes one partial state per position;
-// a second, small kernel (one workgroup per position) merges the partials in
-// a fixed order, so the result is deterministic.  The kernel boundary makes
+// a second, small kernel (one wave per position) merges the partials in a
+// fixed order, so the result is deterministic; the same merge, followed by
+// the threshold commit, runs as a single workgroup when the caller asks for
+// both.  The kernel boundary makes
 // the partials visible to the merge; an in-kernel "last workgroup" merge
 // would need a device-scope release fence per workgroup, which on gfx950
 // writes back the L2 and costs far more than the second launch.
-#include "bd_internal.h"
+#include "commit_impl.h"
 
 namespace bd {
 
 namespace {
 
 constexpr int kMaxGrid = 512;       // persistent workgroups for the bf16 path
-constexpr int kCombineThreads = 256;
 
 // Partial states live column-major, [position][partial], so that the merge
 // kernel reads each position's partials with coalesced loads.
@@ -91,41 +92,81 @@ __device__ __forceinline__ void store_partial(const WsView& w, int G, int col, i
     w.a[idx] = s.a;
 }
 
-// Merge of the G partial states of position blockIdx.x, in a fixed order:
-// thread t folds partials t, t + 256, ... (one round of independent loads
-// for G <= 512), then a fixed shuffle tree and a fixed cross-wave order.
-__global__ __launch_bounds__(kCombineThreads) void lmhead_combine_kernel(
-    const void* __restrict__ ws, int G, int B, float* __restrict__ conf,
-    int32_t* __restrict__ argmax) {
-    __shared__ ArgSoft wred[kCombineThreads / 64];
-    const WsView w = ws_view(const_cast<void*>(ws), G, B);
-    const int col = blockIdx.x;
+// Merge of the G partial states of one position by one wave, in a fixed
+// order: lane l folds partials l, l + 64, ... (loads issued eight at a time,
+// independent of each other), then a fixed xor-shuffle tree.  The result is
+// valid in every lane.
+__device__ ArgSoft reduce_column(const WsView& w, int G, int col) {
+    const int lane = threadIdx.x & 63;
     const float* m = w.m + size_t(col) * G;
     const float* s = w.s + size_t(col) * G;
     const int* a = w.a + size_t(col) * G;
     ArgSoft st{-INFINITY, 0.f, 0x7fffffff};
-    int p = threadIdx.x;
-    for (; p + kCombineThreads < G; p += 2 * kCombineThreads) {
-        const ArgSoft x{m[p], s[p], a[p]};
-        const int q = p + kCombineThreads;
-        const ArgSoft y{m[q], s[q], a[q]};
-        st = merge(merge(st, x), y);
+    int p = lane;
+    for (; p + 7 * 64 < G; p += 8 * 64) {
+        float mm[8], ss[8];
+        int aa[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            mm[u] = m[p + 64 * u];
+            ss[u] = s[p + 64 * u];
+            aa[u] = a[p + 64 * u];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) st = merge(st, ArgSoft{mm[u], ss[u], aa[u]});
     }
-    if (p < G) st = merge(st, ArgSoft{m[p], s[p], a[p]});
+    for (; p < G; p += 64) st = merge(st, ArgSoft{m[p], s[p], a[p]});
     for (int off = 1; off < 64; off <<= 1) st = merge(st, shfl_xor_state(st, off));
-    if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = st;
-    __syncthreads();
+    return st;
+}
+
+// One wave per position: merged confidence and argmax.
+__global__ __launch_bounds__(64) void lmhead_combine_kernel(const void* __restrict__ ws, int G,
+                                                            int B, float* __restrict__ conf,
+                                                            int32_t* __restrict__ argmax) {
+    const WsView w = ws_view(const_cast<void*>(ws), G, B);
+    const int col = blockIdx.x;
+    const ArgSoft r = reduce_column(w, G, col);
     if (threadIdx.x == 0) {
-        ArgSoft r = wred[0];
-        for (int i = 1; i < kCombineThreads / 64; ++i) r = merge(r, wred[i]);
         conf[col] = 1.0f / r.s;
         argmax[col] = r.a;
     }
 }
 
-hipError_t launch_combine(void* ws, int G, int B, float* conf, int32_t* argmax, hipStream_t st) {
-    hipLaunchKernelGGL(lmhead_combine_kernel, dim3(B), dim3(kCombineThreads), 0, st, ws, G, B,
-                       conf, argmax);
+// One workgroup of 16 waves: wave w merges positions w, w + 16, ... exactly
+// as lmhead_combine_kernel does, then wave 0 commits the block.
+__global__ __launch_bounds__(1024) void lmhead_combine_commit_kernel(
+    const void* __restrict__ ws, int G, int B, float* __restrict__ conf,
+    int32_t* __restrict__ argmax, float tau, uint8_t* __restrict__ masked,
+    int32_t* __restrict__ tokens, int32_t* __restrict__ n_committed) {
+    __shared__ float sconf[64];
+    __shared__ int sarg[64];
+    const WsView w = ws_view(const_cast<void*>(ws), G, B);
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    for (int col = wave; col < B; col += 16) {
+        const ArgSoft r = reduce_column(w, G, col);
+        if (lane == 0) {
+            const float c = 1.0f / r.s;
+            conf[col] = c;
+            argmax[col] = r.a;
+            sconf[col] = c;
+            sarg[col] = r.a;
+        }
+    }
+    __syncthreads();
+    if (wave == 0)
+        commit_wave(lane < B ? sconf[lane] : 0.f, lane < B ? sarg[lane] : 0, B, tau, masked,
+                    tokens, n_committed);
+}
+
+hipError_t launch_combine(void* ws, int G, int B, const Finish& f, hipStream_t st) {
+    if (f.commit)
+        hipLaunchKernelGGL(lmhead_combine_commit_kernel, dim3(1), dim3(1024), 0, st, ws, G, B,
+                           f.conf, f.argmax, f.tau, f.masked, f.tokens, f.n_committed);
+    else
+        hipLaunchKernelGGL(lmhead_combine_kernel, dim3(B), dim3(64), 0, st, ws, G, B, f.conf,
+                           f.argmax);
     return hipGetLastError();
 }
 
@@ -372,8 +413,8 @@ bool plan_bf16(int B, int d, int* ks, int* nch) {
 }
 
 template <int NB>
-hipError_t launch_nb(const void* h, const void* W, int B, int d, int V, float* conf,
-                     int32_t* argmax, void* ws, hipStream_t st) {
+hipError_t launch_nb(const void* h, const void* W, int B, int d, int V, const Finish& f,
+                     void* ws, hipStream_t st) {
     const int ntiles = (V + 15) / 16;
     const int G = ntiles < kMaxGrid ? ntiles : kMaxGrid;
     const auto* hh = static_cast<const uint16_t*>(h);
@@ -383,7 +424,7 @@ hipError_t launch_nb(const void* h, const void* W, int B, int d, int V, float* c
         hipLaunchKernelGGL(lmhead_bf16_generic_kernel<NB>, dim3(G), dim3(256), 0, st, hh, ww, B,
                            d, V, ntiles, ws);
         const hipError_t e = hipGetLastError();
-        return e != hipSuccess ? e : launch_combine(ws, G, B, conf, argmax, st);
+        return e != hipSuccess ? e : launch_combine(ws, G, B, f, st);
     }
 #define BD_LMH_CASE(N)                                                                     \
     case N:                                                                                \
@@ -408,7 +449,7 @@ hipError_t launch_nb(const void* h, const void* W, int B, int d, int V, float* c
     }
 #undef BD_LMH_CASE
     const hipError_t e = hipGetLastError();
-    return e != hipSuccess ? e : launch_combine(ws, G, B, conf, argmax, st);
+    return e != hipSuccess ? e : launch_combine(ws, G, B, f, st);
 }
 
 }  // namespace
@@ -429,24 +470,24 @@ size_t lmhead_ws_bytes(int B, int d, int V) {
     return ws_size(G, B);
 }
 
-hipError_t launch_lmhead_bf16(const void* h, const void* W, int B, int d, int V, float* conf,
-                              int32_t* argmax, void* ws, hipStream_t st) {
+hipError_t launch_lmhead_bf16(const void* h, const void* W, int B, int d, int V, const Finish& f,
+                              void* ws, hipStream_t st) {
     switch ((B + 15) / 16) {
-        case 1: return launch_nb<1>(h, W, B, d, V, conf, argmax, ws, st);
-        case 2: return launch_nb<2>(h, W, B, d, V, conf, argmax, ws, st);
-        case 3: return launch_nb<3>(h, W, B, d, V, conf, argmax, ws, st);
-        case 4: return launch_nb<4>(h, W, B, d, V, conf, argmax, ws, st);
+        case 1: return launch_nb<1>(h, W, B, d, V, f, ws, st);
+        case 2: return launch_nb<2>(h, W, B, d, V, f, ws, st);
+        case 3: return launch_nb<3>(h, W, B, d, V, f, ws, st);
+        case 4: return launch_nb<4>(h, W, B, d, V, f, ws, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_lmhead_f32(const float* h, const float* W, int B, int d, int V, float* conf,
-                             int32_t* argmax, void* ws, hipStream_t st) {
+hipError_t launch_lmhead_f32(const float* h, const float* W, int B, int d, int V,
+                             const Finish& f, void* ws, hipStream_t st) {
     const dim3 grid((V + kF32Rows - 1) / kF32Rows, B);
     hipLaunchKernelGGL(lmhead_f32_kernel, grid, dim3(kF32Rows), size_t(d) * sizeof(float), st, h,
                        W, B, d, V, ws);
     const hipError_t e = hipGetLastError();
-    return e != hipSuccess ? e : launch_combine(ws, grid.x, B, conf, argmax, st);
+    return e != hipSuccess ? e : launch_combine(ws, grid.x, B, f, st);
 }
 
 }  // namespace bd

@@ -2,7 +2,7 @@
 // accept and the LOWN certificate scan.  Each runs in a single workgroup; a
 // block holds at most 64 positions, so commit and accept are one wavefront
 // with ballots instead of loops.
-#include "bd_internal.h"
+#include "commit_impl.h"
 
 namespace bd {
 
@@ -14,36 +14,9 @@ __global__ __launch_bounds__(64) void commit_kernel(const float* __restrict__ co
                                                     int32_t* __restrict__ tokens,
                                                     int32_t* __restrict__ n_committed) {
     const int i = threadIdx.x;
-    const bool in = i < B;
-    const float c = in ? conf[i] : 0.f;
-    const bool m = in && masked[i] != 0;
-    const bool above = m && (c > tau);
-    const uint64_t above_bits = __ballot(above);
-    const uint64_t masked_bits = __ballot(m);
-    bool take = above;
-    int n = __popcll(above_bits);
-    if (above_bits == 0 && masked_bits != 0) {
-        // Most confident masked position, lowest index on ties.
-        float bc = c;
-        int bi = m ? i : 64;
-        for (int off = 32; off > 0; off >>= 1) {
-            const float oc = __shfl_xor(bc, off);
-            const int oi = __shfl_xor(bi, off);
-            const bool other_valid = oi < 64;
-            const bool mine_valid = bi < 64;
-            if (other_valid && (!mine_valid || oc > bc || (oc == bc && oi < bi))) {
-                bc = oc;
-                bi = oi;
-            }
-        }
-        take = (i == bi);
-        n = 1;
-    }
-    if (take) {
-        tokens[i] = argmax[i];
-        masked[i] = 0;
-    }
-    if (i == 0) *n_committed = n;
+    const float c = i < B ? conf[i] : 0.f;
+    const int32_t a = i < B ? argmax[i] : 0;
+    commit_wave(c, a, B, tau, masked, tokens, n_committed);
 }
 
 // Longest verified prefix (overview §2.3.1): the first disagreement is the

@@ -81,11 +81,14 @@ class BlockAttn:
 
 class DecodeStep:
     """One threshold (MDM) block-decode step: bd_block_attn (bidirectional
-    block) -> bd_lmhead_conf -> bd_commit.  Inputs from synth.qwen_decode or
+    block) -> bd_lmhead_conf_commit (LM head, then commit).  With
+    ``fused=False`` the LM head and the commit are the two separate calls
+    bd_lmhead_conf and bd_commit.  Inputs from synth.qwen_decode or
     synth.tiny.  ``reset()`` restores the block state (masked flags, tokens)
     so that repeated steps do identical work."""
 
-    def __init__(self, inp: dict, device="cuda"):
+    def __init__(self, inp: dict, device="cuda", fused=True):
+        self.fused = fused
         self.inp = inp
         dt = dtype_code(inp["dtype"])
         B = inp["B"]
@@ -97,23 +100,34 @@ class DecodeStep:
         self.attn = BlockAttn(dt, bd.BD_MASK_BIDIR, B, inp["P"], inp["cap"], inp["Hq"],
                               inp["Hkv"], inp["q"].shape[-1], device)
         self.lm = LMHead(dt, self.W, B, inp["d"], inp["V"], device)
-        self.masked0 = to_dev(inp["masked"], device)
-        self.tokens0 = to_dev(inp["tokens"], device)
-        self.masked = self.masked0.clone()
-        self.tokens = self.tokens0.clone()
+        # Block state (tokens int32[B], then masked uint8[B]) in one buffer, so
+        # that restoring it between repeated steps is a single copy.
+        nbytes = 4 * B + 16 * ((B + 15) // 16)
+        host = np.zeros(nbytes, np.uint8)
+        host[:4 * B] = np.asarray(inp["tokens"], np.int32).view(np.uint8)
+        host[4 * B:5 * B] = np.asarray(inp["masked"], np.uint8)
+        self.state0 = to_dev(host, device)
+        self.state = self.state0.clone()
+        self.tokens = self.state[:4 * B].view(torch.int32)
+        self.masked = self.state[4 * B:5 * B]
         self.n_committed = torch.zeros(1, dtype=torch.int32, device=device)
         self.tau = float(inp["tau"])
         self.B = B
 
     def reset(self):
-        self.masked.copy_(self.masked0)
-        self.tokens.copy_(self.tokens0)
+        self.state.copy_(self.state0)
 
     def run(self, stream=None):
         self.attn(self.q, self.k_cache, self.v_cache, stream)
-        self.lm(self.h, stream)
-        bd.bd_commit(self.lm.conf, self.lm.argmax, self.B, self.tau, self.masked, self.tokens,
-                     self.n_committed, stream)
+        lm = self.lm
+        if self.fused:
+            bd.bd_lmhead_conf_commit(lm.dt, self.h, lm.W, lm.B, lm.d, lm.V, self.tau, lm.conf,
+                                     lm.argmax, self.masked, self.tokens, self.n_committed, lm.ws,
+                                     lm.ws_bytes, stream)
+        else:
+            lm(self.h, stream)
+            bd.bd_commit(lm.conf, lm.argmax, self.B, self.tau, self.masked, self.tokens,
+                         self.n_committed, stream)
 
 
 class LinearSpecStep:

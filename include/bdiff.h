@@ -90,7 +90,8 @@ bd_status bd_make_intra_mask(bd_mask_kind kind, int32_t Bq, uint64_t* host_rows)
  *   scale       softmax scale; 0 selects 1/sqrt(dh)
  *   ws          workspace of at least bd_block_attn_ws_bytes(...) bytes
  * Limits: 1 <= Bq <= 64, 0 <= P, P + Bq <= cap, Hkv >= 1, Hq % Hkv == 0,
- *   BD_BF16: dh == 128;  BD_F32: dh % 4 == 0 and 4 <= dh <= 128.
+ *   BD_BF16: dh == 128 and P + Bq <= 65536;  BD_F32: dh % 4 == 0 and
+ *   4 <= dh <= 128.
  * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_ALIGN, BD_E_WORKSPACE,
  *   BD_E_LAUNCH.
  */
@@ -125,6 +126,25 @@ bd_status bd_lmhead_conf(bd_dtype dt, const void* h, const void* W,
                          int32_t B, int32_t d, int32_t V,
                          float* conf, int32_t* argmax,
                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * bd_lmhead_conf_commit - bd_lmhead_conf followed by bd_commit on its
+ * outputs, as one call: the merge of the LM-head partials and the threshold
+ * commit run in the same small kernel, saving a launch per decode step.
+ * [OV §1.2 parallel denoising inside a block; OV §4.1 threshold 0.9;
+ *  LOWN 'method step details' (1) for the confidence]
+ * Arguments as in bd_lmhead_conf and bd_commit; conf and argmax are written
+ * exactly as bd_lmhead_conf writes them (bit-identical), then positions are
+ * committed exactly as bd_commit would commit them.  The workspace size is
+ * bd_lmhead_conf_ws_bytes(B, d, V).
+ * Errors: those of bd_lmhead_conf, plus BD_E_NULL for masked, tokens or
+ *   n_committed and BD_E_SHAPE for a NaN tau.
+ */
+bd_status bd_lmhead_conf_commit(bd_dtype dt, const void* h, const void* W,
+                                int32_t B, int32_t d, int32_t V, float tau,
+                                float* conf, int32_t* argmax,
+                                uint8_t* masked, int32_t* tokens, int32_t* n_committed,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * bd_commit - threshold unmasking with the always-one rule.

@@ -129,6 +129,21 @@ def test_lmhead_validation():
     assert _lm(ws_bytes=bd.bd_lmhead_conf_ws_bytes(16, 2048, 151936) - 1) == bd.BD_E_WORKSPACE
 
 
+def test_lmhead_conf_commit_validation():
+    f = lambda **kw: bd.bd_lmhead_conf_commit(**{**dict(
+        dt=bd.BD_BF16, h=FAKE, W=FAKE, B=16, d=2048, V=151936, tau=0.9, conf=FAKE, argmax=FAKE,
+        masked=FAKE, tokens=FAKE, n_committed=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=0,
+        check=False), **kw})
+    assert f(masked=None) == bd.BD_E_NULL
+    assert f(n_committed=None) == bd.BD_E_NULL
+    assert f(argmax=None) == bd.BD_E_NULL
+    assert f(tau=float("nan")) == bd.BD_E_SHAPE
+    assert f(B=0) == bd.BD_E_SHAPE
+    assert f(d=100) == bd.BD_E_SHAPE
+    assert f(W=MISALIGNED) == bd.BD_E_ALIGN
+    assert f(ws_bytes=10) == bd.BD_E_WORKSPACE
+
+
 def test_small_calls_validation():
     c = lambda **kw: bd.bd_commit(**{**dict(conf=FAKE, argmax=FAKE, B=16, tau=0.9, masked=FAKE,
                                             tokens=FAKE, n_committed=FAKE, stream=0,

@@ -315,6 +315,47 @@ def test_decode_step_full_size():
     assert np.array_equal(runner.to_host(step.tokens), o["tokens"])
 
 
+@pytest.mark.parametrize("B,d,V", [(1, 128, 1000), (16, 2048, 30011), (33, 384, 999),
+                                   (64, 2048, 3001)])
+def test_lmhead_conf_commit_equals_separate_calls(B, d, V):
+    r = synth.qwen_decode(seed=B + V, B=B, d=d, V=V, n_vis=4, n_prompt=4, Hq=2, Hkv=1)
+    h, W = runner.to_dev(r["h"]), runner.to_dev(r["W"])
+    masked0 = (np.random.default_rng(B).random(B) < 0.8).astype(np.uint8)
+    tokens0 = np.arange(B, dtype=np.int32) + 7
+    out = {}
+    for fused in (False, True):
+        lm = runner.LMHead(bd.BD_BF16, W, B, d, V)
+        masked, tokens = runner.to_dev(masked0), runner.to_dev(tokens0)
+        n = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+        if fused:
+            bd.bd_lmhead_conf_commit(bd.BD_BF16, h, W, B, d, V, TAU32, lm.conf, lm.argmax, masked,
+                                     tokens, n, lm.ws, lm.ws_bytes)
+        else:
+            lm(h)
+            bd.bd_commit(lm.conf, lm.argmax, B, TAU32, masked, tokens, n)
+        torch.cuda.synchronize()
+        out[fused] = (lm.conf.cpu().numpy(), lm.argmax.cpu().numpy(), runner.to_host(masked),
+                      runner.to_host(tokens), int(n.item()))
+    for a, b in zip(out[False], out[True]):
+        assert np.array_equal(a, b)
+    oc, oa = oracle.lmhead_conf(r["h"], r["W"])
+    m2, t2, nc = oracle.commit(oc, oa, masked0, tokens0, TAU32)
+    assert np.array_equal(out[True][2], m2) and np.array_equal(out[True][3], t2)
+    assert out[True][4] == nc
+
+
+def test_decode_step_full_size_separate_calls():
+    r = synth.qwen_decode()
+    step = runner.DecodeStep(r, fused=False)
+    step.run()
+    torch.cuda.synchronize()
+    o = oracle.decode_step(r["q"], r["k_cache"], r["v_cache"], r["P"], r["h"], r["W"],
+                           r["masked"], r["tokens"], TAU32)
+    assert np.array_equal(runner.to_host(step.masked), o["masked"])
+    assert np.array_equal(runner.to_host(step.tokens), o["tokens"])
+    assert int(step.n_committed.item()) == o["n_committed"]
+
+
 def test_tiny_decode_step_f32():
     r = synth.tiny()
     step = runner.DecodeStep(r)
