@@ -6,18 +6,17 @@
 // bf16 path (gfx950 MFMA).  The contraction is W[V][d] x h^T[d][B] with the
 // vocabulary as the M dimension and the positions as N, on
 // v_mfma_f32_16x16x32_bf16.  W is streamed exactly once, straight from HBM
-// into the A operand (no LDS): lane l of a wave reads 64 contiguous bytes of
-// vocabulary row (l % 16) per 128-element K chunk, so a wave instruction
-// group covers 16 rows x 256 B.  The K index inside a chunk is permuted
-// identically for A and B (lane group g, MFMA j, element e <-> k = 32g + 8j + e),
-// which leaves the dot product unchanged.  h is tiny and is held in
-// registers as ready-made B fragments for the wave's K range.
+// with non-temporal loads and staged through LDS into the A operand (see the
+// kernel).  The K index inside a 128-element chunk is permuted identically
+// for A and B (lane group g, MFMA j, element e <-> k = 32g + 8j + e), which
+// leaves the dot product unchanged.  h is tiny and is held in registers as
+// ready-made B fragments for the wave's K range.
 //
 // A workgroup has `ks` waves that split K; per 16-row vocabulary tile they
 // add their partial logits through LDS and one wave (rotating) folds the 16
-// rows into running (max, sum, argmax) states in the log2 domain.  Tiles are
-// dealt round-robin to a persistent grid, so the load is even to within one
-// tile per workgroup.  Each workgroup writes one partial state per position;
+// rows into running (max, sum, argmax) states in the log2 domain.  Each
+// workgroup of a persistent grid streams one contiguous range of tiles (the
+// ranges differ by at most one tile).  Each workgroup writes one partial state per position;
 // a second, small kernel (one wave per position) merges the partials in a
 // fixed order, so the result is deterministic; the same merge, followed by
 // the threshold commit, runs as a single workgroup when the caller asks for
@@ -31,7 +30,7 @@ namespace bd {
 
 namespace {
 
-constexpr int kMaxGrid = 512;       // persistent workgroups for the bf16 path
+constexpr int kMaxGrid = 256;       // persistent workgroups for the bf16 path
 
 // Partial states live column-major, [position][partial], so that the merge
 // kernel reads each position's partials with coalesced loads.
@@ -173,6 +172,17 @@ hipError_t launch_combine(void* ws, int G, int B, const Finish& f, hipStream_t s
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel.  NB = number of 16-position column blocks (ceil(B/16));
 // NCH = 128-element K chunks per wave.  blockDim.x = 64 * ks, d = 128*NCH*ks.
+//
+// Load path.  Wave w owns the K range [w*NCH*128, (w+1)*NCH*128) of every
+// tile, i.e. a 16-row x NCH*256-byte region.  It reads that region with
+// 4*NCH non-temporal 16-byte loads per lane, where consecutive lanes read
+// consecutive 16-byte pieces (each instruction covers 1 KB of contiguous
+// memory, whole cache lines; the weights are used once, so they bypass the
+// caches), stages it in a wave-private LDS buffer and reads the MFMA A
+// fragments from there.  Row r's 16-byte piece p sits in LDS slot p ^ (r % 16)
+// of that row, so the 16 rows read by one fragment load fall in 16 distinct
+// banks.  The next tile's loads are in flight while the current tile is
+// multiplied.
 // ---------------------------------------------------------------------------
 template <int NB, int NCH>
 __global__ __launch_bounds__(256) void lmhead_bf16_kernel(const uint16_t* __restrict__ h,
@@ -180,23 +190,27 @@ __global__ __launch_bounds__(256) void lmhead_bf16_kernel(const uint16_t* __rest
                                                           int B, int d, int V, int ntiles,
                                                           void* __restrict__ ws) {
     constexpr int NL = NCH * 4;                       // 16-byte loads per lane per tile
+    constexpr int PIECES = NCH * 16;                  // 16-byte pieces per row segment
     __shared__ f32x4 red[2][4][NB][64];               // per-wave partial logits, 2 buffers
     __shared__ ArgSoft fin[4][NB][16];
+    __shared__ __align__(16) u32x4 stage[4][16 * PIECES];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nwave = blockDim.x >> 6;
     const int r16 = lane & 15;
     const int g = lane >> 4;
-    const int k0 = wave * NCH * 128 + g * 32;         // this lane's K start (elements)
+    const int kw = wave * NCH * 128;                  // this wave's K start (elements)
     const int G = gridDim.x;
 
-    // B fragments of h for this wave's K range, kept in registers.
+    // B fragments of h for this wave's K range, kept in registers: fragment
+    // (c, j) of lane (r16, g) holds k = kw + 128c + 32g + 8j .. +7.
     bf16x8 hf[NCH][4][NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int row = nb * 16 + r16;
-        const u32x4* hp = reinterpret_cast<const u32x4*>(h + size_t(row < B ? row : 0) * d + k0);
+        const u32x4* hp =
+            reinterpret_cast<const u32x4*>(h + size_t(row < B ? row : 0) * d + kw + g * 32);
 #pragma unroll
         for (int c = 0; c < NCH; ++c)
 #pragma unroll
@@ -210,24 +224,34 @@ __global__ __launch_bounds__(256) void lmhead_bf16_kernel(const uint16_t* __rest
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) st[nb] = ArgSoft{-INFINITY, 0.f, 0x7fffffff};
 
+    // Load i of a lane covers slot q = 64 i + lane of the row-major
+    // [16 rows][PIECES] region: row q / PIECES, slot q % PIECES, holding
+    // piece (slot ^ row % 16).
     auto load_tile = [&](u32x4 (&buf)[NL], int tile) {
-        int row = tile * 16 + r16;
-        row = row < V ? row : V - 1;
-        const u32x4* p = reinterpret_cast<const u32x4*>(W + size_t(row) * d + k0);
 #pragma unroll
-        for (int c = 0; c < NCH; ++c)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) buf[c * 4 + j] = p[c * 16 + j];
+        for (int i = 0; i < NL; ++i) {
+            const int q = 64 * i + lane;
+            const int r = q / PIECES;
+            const int piece = (q % PIECES) ^ (r & 15);
+            int row = tile * 16 + r;
+            row = row < V ? row : V - 1;
+            buf[i] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(W + size_t(row) * d + kw) + piece);
+        }
     };
 
-    u32x4 cur[NL];
-    int tile = blockIdx.x;
-    if (tile < ntiles) load_tile(cur, tile);
+    // Contiguous range of tiles per workgroup.
+    const int t_beg = int(int64_t(ntiles) * blockIdx.x / G);
+    const int t_end = int(int64_t(ntiles) * (blockIdx.x + 1) / G);
+    u32x4 nxt[NL];
+    if (t_beg < t_end) load_tile(nxt, t_beg);
     int it = 0;
-    while (tile < ntiles) {
-        const int next = tile + G;
-        u32x4 nxt[NL];
-        if (next < ntiles) load_tile(nxt, next);
+    for (int tile = t_beg; tile < t_end; ++tile, ++it) {
+        // The previous tile's fragment reads precede these writes in this
+        // wave's program order, so the wave-private buffer can be refilled.
+#pragma unroll
+        for (int i = 0; i < NL; ++i) stage[wave][64 * i + lane] = nxt[i];
+        if (tile + 1 < t_end) load_tile(nxt, tile + 1);
 
         f32x4 acc[NB];
 #pragma unroll
@@ -236,7 +260,9 @@ __global__ __launch_bounds__(256) void lmhead_bf16_kernel(const uint16_t* __rest
         for (int c = 0; c < NCH; ++c)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const bf16x8 a = __builtin_bit_cast(bf16x8, cur[c * 4 + j]);
+                const int piece = c * 16 + g * 4 + j;
+                const bf16x8 a =
+                    __builtin_bit_cast(bf16x8, stage[wave][r16 * PIECES + (piece ^ r16)]);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
                     acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, hf[c][j][nb], acc[nb],
@@ -267,10 +293,6 @@ __global__ __launch_bounds__(256) void lmhead_bf16_kernel(const uint16_t* __rest
                 fold4(st[nb], x, row0, V);
             }
         }
-#pragma unroll
-        for (int i = 0; i < NL; ++i) cur[i] = nxt[i];
-        tile = next;
-        ++it;
     }
 
     // Merge the four lane groups that hold the same position, then the waves.
