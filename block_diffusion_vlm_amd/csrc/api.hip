@@ -93,7 +93,7 @@ bd_status bd_block_attn(bd_dtype dt, const void* q, const void* k_cache, const v
     if (!dh_ok(dt, dh)) return BD_E_SHAPE;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
         return BD_E_ALIGN;
-    if (!(scale == scale) || isinf(scale)) return BD_E_SHAPE;
+    if (!(scale >= 0.f) || isinf(scale)) return BD_E_SHAPE;
     const float sc = default_scale(scale, dh);
     if (dt == BD_F32)
         return launch_status(bd::launch_block_attn_f32(
@@ -189,7 +189,7 @@ bd_status bd_dualstream_attn(bd_dtype dt, const void* q, const void* k, const vo
     if (N < 1 || N > (1 << 24)) return BD_E_SHAPE;
     if (!dh_ok(dt, dh)) return BD_E_SHAPE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return BD_E_ALIGN;
-    if (!(scale == scale) || isinf(scale)) return BD_E_SHAPE;
+    if (!(scale >= 0.f) || isinf(scale)) return BD_E_SHAPE;
     const float sc = default_scale(scale, dh);
     if (dt == BD_F32)
         return launch_status(bd::launch_dualstream_f32(

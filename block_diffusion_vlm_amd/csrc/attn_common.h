@@ -2,14 +2,15 @@
 // the KV cache and dual-stream training attention), on gfx950
 // v_mfma_f32_32x32x16_bf16.
 //
-// Formulation.  A wave owns 32 query rows.  Scores are computed transposed,
-// S^T[key][q] = K[key][:] . Q[q][:], with K as the A operand (read from LDS)
-// and Q as the B operand (held in registers), and the output transposed as
-// well, O^T[dh][q] = V^T[dh][key] . P^T[key][q], with V^T read from LDS and P
-// taken straight from the score accumulators.  In the 32x32 accumulator layout
-// lane l holds query column l % 32 for both products, so every per-row
-// softmax quantity (max, sum, rescale factor) lives in the lane that needs it;
-// only lanes l and l ^ 32 share a row.
+// Formulation.  A wave owns RB blocks of 32 query rows.  Scores are computed
+// transposed, S^T[key][q] = K[key][:] . Q[q][:], with K as the A operand (read
+// from LDS) and Q as the B operand (held in registers), and the output
+// transposed as well, O^T[dh][q] = V^T[dh][key] . P^T[key][q], with V^T read
+// from LDS by transposing loads and P taken straight from the score
+// accumulators.  In the 32x32 accumulator layout lane l holds query column
+// l % 32 for both products, so every per-row softmax quantity (max, sum,
+// rescale factor) lives in the lane that needs it; only lanes l and l ^ 32
+// share a row.  Each A fragment read from LDS feeds RB MFMAs.
 //
 // Accumulator layout (32x32, 16 floats per lane): register r of lane l holds
 // row 8*(r/4) + 4*(l/32) + (r%4), column l % 32.  Operand layout (A and B,
@@ -18,9 +19,20 @@
 // block are taken from accumulator registers 8*s2 .. 8*s2+7, i.e. keys
 // 16*s2 + 4*(l/32) + {0,1,2,3} and 16*s2 + 8 + 4*(l/32) + {0,1,2,3}; V^T is
 // read with exactly that key permutation, so the sum over keys is unchanged.
+//
+// LDS tiles.  K and V are both stored row-major ([key][dh]) with 16-byte
+// stores.  K rows are padded to 272 bytes, so the 16 keys of one fragment
+// load fall in distinct banks.  V^T fragments come from ds_read_b64_tr_b16:
+// within each 16-lane group, lane i of the result receives element
+// (i % 4) of the 8 bytes addressed by lane 4k + i/4, for k = 0..3; with lane
+// L addressing V[key0 + L/4][dh0 + 4 (L%4)], lane i therefore receives
+// V[key0 + k][dh0 + i], k = 0..3 - four keys of one dh column.  V rows are
+// padded to 288 bytes, so the four rows read by one group use distinct banks.
 #pragma once
 
 #include "bd_internal.h"
+
+#define BD_LDS __attribute__((address_space(3)))
 
 namespace bd {
 namespace attn {
@@ -28,11 +40,11 @@ namespace attn {
 constexpr int kDh = 128;           // head dimension of the bf16 kernels
 constexpr int kBN = 64;            // keys per tile
 constexpr int kKPitch = kDh + 8;   // LDS row pitch of K tiles (elements): 272 B
-constexpr int kVPitch = kBN + 4;   // LDS row pitch of V^T tiles (elements): 136 B
+constexpr int kVPitch = kDh + 16;  // LDS row pitch of V tiles (elements): 288 B
 
 struct Tiles {
     uint16_t k[kBN * kKPitch];      // K tile, [key][dh]
-    uint16_t vt[kDh * kVPitch];     // V tile transposed, [dh][key]
+    uint16_t v[kBN * kVPitch];      // V tile, [key][dh]
 };
 
 // Key held by accumulator register r of lane l inside a 32-key block.
@@ -40,56 +52,56 @@ __device__ __forceinline__ int acc_row(int r, int lane) {
     return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-// A 64-key tile of K and V in flight through registers: thread t holds keys
-// t/16 + 16u (u = 0..3), dims 8*(t%16) .. +7, of both K and V.  256 threads.
+// A 64-key tile of K and V in flight through registers.  With T threads,
+// thread t holds 16-byte pieces p = t + T u (u < 1024 / T) of both K and V:
+// key p / 16, dims 8 (p % 16) .. +7.
+template <int T>
 struct TileRegs {
-    u32x4 k[4];
-    u32x4 v[4];
+    static constexpr int N = 1024 / T;
+    u32x4 k[N];
+    u32x4 v[N];
 };
 
 // Global -> registers for keys [j0, j0 + 64); keys at or beyond `jend` read
 // as zeros.  `row_stride` is the distance between consecutive keys in elements.
-__device__ __forceinline__ void fetch_tile(TileRegs& r, const uint16_t* __restrict__ kbase,
+template <int T>
+__device__ __forceinline__ void fetch_tile(TileRegs<T>& r, const uint16_t* __restrict__ kbase,
                                            const uint16_t* __restrict__ vbase, size_t row_stride,
                                            int j0, int jend) {
-    const int tid = threadIdx.x;
-    const int col = (tid & 15) * 8;
+    constexpr int KEYS_PER_U = T / 16;               // key rows between consecutive u
+    const int key = threadIdx.x >> 4;
+    const int col = (threadIdx.x & 15) * 8;
+    const size_t off = size_t(j0 + key) * row_stride + col;
+    const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + off);
+    const u32x4* vp = reinterpret_cast<const u32x4*>(vbase + off);
+    const size_t step = size_t(KEYS_PER_U) * row_stride / 8;   // in 16-byte units
+    if (j0 + kBN <= jend) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int j = j0 + (tid >> 4) + 16 * u;
-        r.k[u] = u32x4{0, 0, 0, 0};
-        r.v[u] = u32x4{0, 0, 0, 0};
-        if (j < jend) {
-            r.k[u] = *reinterpret_cast<const u32x4*>(kbase + size_t(j) * row_stride + col);
-            r.v[u] = *reinterpret_cast<const u32x4*>(vbase + size_t(j) * row_stride + col);
+        for (int u = 0; u < TileRegs<T>::N; ++u) {
+            r.k[u] = kp[u * step];
+            r.v[u] = vp[u * step];
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < TileRegs<T>::N; ++u) {
+            const bool ok = j0 + key + KEYS_PER_U * u < jend;
+            r.k[u] = ok ? kp[u * step] : u32x4{0, 0, 0, 0};
+            r.v[u] = ok ? vp[u * step] : u32x4{0, 0, 0, 0};
         }
     }
 }
 
-// Registers -> LDS: K as is, V transposed.
-__device__ __forceinline__ void store_tile(Tiles& t, const TileRegs& r) {
-    const int tid = threadIdx.x;
-    const int col = (tid & 15) * 8;
+// Registers -> LDS (both row-major).
+template <int T>
+__device__ __forceinline__ void store_tile(Tiles& t, const TileRegs<T>& r) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int key = (tid >> 4) + 16 * u;
+    for (int u = 0; u < TileRegs<T>::N; ++u) {
+        const int p = threadIdx.x + T * u;
+        const int key = p >> 4;
+        const int col = (p & 15) * 8;
         *reinterpret_cast<u32x4*>(&t.k[key * kKPitch + col]) = r.k[u];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            t.vt[(col + 2 * e) * kVPitch + key] = static_cast<uint16_t>(r.v[u][e] & 0xFFFFu);
-            t.vt[(col + 2 * e + 1) * kVPitch + key] = static_cast<uint16_t>(r.v[u][e] >> 16);
-        }
+        *reinterpret_cast<u32x4*>(&t.v[key * kVPitch + col]) = r.v[u];
     }
-}
-
-// Cooperative load of keys [j0, j0 + 64) of one head into LDS (K as is, V
-// transposed).
-__device__ __forceinline__ void load_tile(Tiles& t, const uint16_t* __restrict__ kbase,
-                                          const uint16_t* __restrict__ vbase, size_t row_stride,
-                                          int j0, int jend) {
-    TileRegs r;
-    fetch_tile(r, kbase, vbase, row_stride, j0, jend);
-    store_tile(t, r);
 }
 
 // Q fragments (B operand of S^T) for 32 rows; rowptr == nullptr gives zeros.
@@ -102,52 +114,75 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[8], const uint16_t* rowptr, 
     }
 }
 
-// S^T for the 64 keys of a tile: sacc[kb] covers keys 32*kb .. 32*kb+31.
-__device__ __forceinline__ void scores(f32x16 (&sacc)[2], const Tiles& t, const bf16x8 (&qf)[8],
-                                       int lane) {
+// S^T for the 64 keys of a tile and RB row blocks: sacc[rb][kb] covers keys
+// 32*kb .. 32*kb+31 of row block rb.
+template <int RB>
+__device__ __forceinline__ void scores(f32x16 (&sacc)[RB][2], const Tiles& t,
+                                       const bf16x8 (&qf)[RB][8], int lane) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-        f32x16 acc = {};
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = f32x16{};
         const uint16_t* kr = &t.k[(32 * kb + (lane & 31)) * kKPitch + 8 * (lane >> 5)];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kr + 16 * s));
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], acc, 0, 0, 0);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                sacc[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rb][s], sacc[rb][kb],
+                                                                       0, 0, 0);
         }
-        sacc[kb] = acc;
     }
 }
 
-// O^T += V^T P^T for one tile; p[kb][r] are the probabilities of the keys in
-// sacc layout.
-__device__ __forceinline__ void accumulate_pv(f32x16 (&oacc)[4], const Tiles& t,
-                                              const float (&p)[2][16], int lane) {
-    bf16x8 pf[2][2];
+// Eight consecutive probabilities as a bf16 B fragment (hardware RNE).
+__device__ __forceinline__ bf16x8 to_bf16x8(const float* p) {
+    bf16x8 r;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int e = 0; e < 8; ++e) r[e] = static_cast<__bf16>(p[e]);
+    return r;
+}
+
+// Transposing LDS load of four keys of one dh column (see the file comment).
+__device__ __forceinline__ bf16x4 read_vt4(const uint16_t* p) {
+    typedef __bf16 lds_bf16x4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (BD_LDS lds_bf16x4*)(const_cast<uint16_t*>(p)));
+}
+
+// O^T += V^T P^T for one tile; p[rb][kb][r] are the probabilities of the
+// keys in sacc layout.
+template <int RB>
+__device__ __forceinline__ void accumulate_pv(f32x16 (&oacc)[RB][4], const Tiles& t,
+                                              const float (&p)[RB][2][16], int lane) {
+    bf16x8 pf[RB][2][2];
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            u32x4 w;
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[kb][8 * s2 + 2 * e], p[kb][8 * s2 + 2 * e + 1]);
-            pf[kb][s2] = __builtin_bit_cast(bf16x8, w);
-        }
-    const int g4 = 4 * (lane >> 5);
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-        const uint16_t* vr = &t.vt[(32 * db + (lane & 31)) * kVPitch];
+            for (int s2 = 0; s2 < 2; ++s2) pf[rb][kb][s2] = to_bf16x8(&p[rb][kb][8 * s2]);
+    // Supplier lane L of 16-lane group q addresses V[key0 + L/4][dh0 + 4 (L%4)]
+    // with key0 = 32 kb + 16 s2 + 4 (q / 2) (+ 8 for the upper four keys) and
+    // dh0 = 32 db + 16 (q % 2).
+    const int q = lane >> 4;
+    const int L = lane & 15;
+    const uint16_t* vbase = &t.v[(4 * (q >> 1) + (L >> 2)) * kVPitch + 16 * (q & 1) + 4 * (L & 3)];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                const int key0 = 32 * kb + 16 * s2 + g4;
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(vr + key0);
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + key0 + 8);
-                const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, a), pf[kb][s2], oacc[db], 0, 0, 0);
+                const uint16_t* vp = vbase + (32 * kb + 16 * s2) * kVPitch + 32 * db;
+                const bf16x4 lo = read_vt4(vp);
+                const bf16x4 hi = read_vt4(vp + 8 * kVPitch);
+                const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[rb][kb][s2],
+                                                                           oacc[rb][db], 0, 0, 0);
             }
-    }
 }
 
 }  // namespace attn

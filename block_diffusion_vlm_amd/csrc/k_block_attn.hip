@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int P, int cap, const uint64_t* __restrict__ mask, int Bq,
     int Hq, int Hkv, float scale_log2, void* __restrict__ ws, int nsplit, int kt) {
-    __shared__ __align__(16) Tiles tiles;
+    __shared__ __align__(16) Tiles tiles[2];
     const int split = blockIdx.x;
     const int g = blockIdx.y;
     const int lane = threadIdx.x & 63;
@@ -60,30 +60,31 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
     const int ntiles = (Nk + kBN - 1) / kBN;
     const int t_end = t_beg + kt < ntiles ? t_beg + kt : ntiles;
 
-    TileRegs nxt;
-    fetch_tile(nxt, kb, vb, kDh, t_beg * kBN, Nk);
+    TileRegs<256> regs;
+    fetch_tile<256>(regs, kb, vb, kDh, t_beg * kBN, Nk);
 
     // Query row of this lane: r -> (block query i, head g*group + r % group).
     const int r = blockIdx.z * kRowsPerWg + wave * 32 + (lane & 31);
     const bool row_ok = r < R;
     const int qi = row_ok ? r / group : 0;
     const int qh = g * group + (row_ok ? r % group : 0);
-    bf16x8 qf[8];
-    load_q(qf, row_ok ? q + (size_t(qi) * Hq + qh) * kDh : nullptr, lane);
+    bf16x8 qf[1][8];
+    load_q(qf[0], row_ok ? q + (size_t(qi) * Hq + qh) * kDh : nullptr, lane);
     const uint64_t mbits = row_ok ? mask[qi] : 0;
 
+    store_tile<256>(tiles[0], regs);
+    __syncthreads();
+
     float m = -INFINITY, l = 0.f;
-    f32x16 oacc[4] = {};
+    f32x16 oacc[1][4] = {};
     for (int t = t_beg; t < t_end; ++t) {
         const int j0 = t * kBN;
-        if (t > t_beg) __syncthreads();             // previous tile fully consumed
-        store_tile(tiles, nxt);
-        __syncthreads();
-        if (t + 1 < t_end) fetch_tile(nxt, kb, vb, kDh, j0 + kBN, Nk);
+        if (t + 1 < t_end) fetch_tile<256>(regs, kb, vb, kDh, j0 + kBN, Nk);
+        const Tiles& cur = tiles[(t - t_beg) & 1];
 
-        f32x16 sacc[2];
-        scores(sacc, tiles, qf, lane);
-        float x[2][16];
+        f32x16 sacc[1][2];
+        scores<1>(sacc, cur, qf, lane);
+        float p[1][2][16];
         float mx = m;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
@@ -91,27 +92,31 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
             for (int e = 0; e < 16; ++e) {
                 const int j = j0 + 32 * kb2 + acc_row(e, lane);
                 const bool vis = (j < P) || (j < Nk && ((mbits >> (j - P)) & 1ull));
-                x[kb2][e] = vis ? sacc[kb2][e] * scale_log2 : -INFINITY;
-                mx = fmaxf(mx, x[kb2][e]);
+                p[0][kb2][e] = vis ? sacc[0][kb2][e] * scale_log2 : -INFINITY;
+                mx = fmaxf(mx, p[0][kb2][e]);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mref = (mx == -INFINITY) ? 0.f : mx;
-        const float alpha = exp2f(m - mref);
-        float p[2][16];
         float ls = 0.f;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                p[kb2][e] = exp2f(x[kb2][e] - mref);
-                ls += p[kb2][e];
+                p[0][kb2][e] = __builtin_amdgcn_exp2f(p[0][kb2][e] - mref);
+                ls += p[0][kb2][e];
             }
         ls += __shfl_xor(ls, 32);
+        const float alpha = __builtin_amdgcn_exp2f(m - mref);
         l = l * alpha + ls;
         m = mx;
+        if (__ballot(alpha != 1.f)) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-        accumulate_pv(oacc, tiles, p, lane);
+            for (int db = 0; db < 4; ++db) oacc[0][db] *= alpha;
+        }
+        accumulate_pv<1>(oacc, cur, p, lane);
+
+        if (t + 1 < t_end) store_tile<256>(tiles[(t + 1 - t_beg) & 1], regs);
+        __syncthreads();
     }
 
     if (row_ok) {
@@ -128,8 +133,8 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
             for (int e4 = 0; e4 < 4; ++e4) {
                 const int dh = 32 * db + acc_row(4 * e4, lane);
                 *reinterpret_cast<f32x4*>(o + dh) =
-                    f32x4{oacc[db][4 * e4], oacc[db][4 * e4 + 1], oacc[db][4 * e4 + 2],
-                          oacc[db][4 * e4 + 3]};
+                    f32x4{oacc[0][db][4 * e4], oacc[0][db][4 * e4 + 1], oacc[0][db][4 * e4 + 2],
+                          oacc[0][db][4 * e4 + 3]};
             }
     }
 }

@@ -75,38 +75,58 @@ __device__ __forceinline__ bool tile_full(const Geometry& G, int i0, int i1, int
     return false;
 }
 
-__global__ __launch_bounds__(256) void dualstream_bf16_kernel(
+// Visibility of keys for one query row as two intervals: key j is visible
+// iff j <= lim or lo <= j < hi.  Clean row i: lim = i (C2C), no interval.
+// Noisy row r: lim = n_vis + r (every visual key, clean text up to r: N2C),
+// interval = the keys of its N2N block.
+struct RowVis {
+    int lim, lo, hi;
+};
+
+__device__ __forceinline__ RowVis row_vis(const Geometry& G, int i) {
+    RowVis v;
+    if (i < G.ctx) {
+        v.lim = i;
+        v.lo = v.hi = 0;
+    } else {
+        const int r = i - G.ctx;
+        v.lim = G.n_vis + r;
+        v.lo = G.ctx + (r / G.block) * G.block;
+        v.hi = v.lo + G.block < G.N ? v.lo + G.block : G.N;
+    }
+    return v;
+}
+
+// WAVES waves per workgroup, each owning RB blocks of 32 query rows.  K/V
+// tiles are double-buffered in LDS; the next tile's global loads are issued
+// before the current tile is multiplied and land in the other buffer, so one
+// barrier per tile suffices.
+template <int WAVES, int RB, int OCC = 1>
+__global__ __launch_bounds__(WAVES * 64, OCC) void dualstream_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, Geometry G, int H, float scale_log2,
     uint16_t* __restrict__ out, int nqt) {
-    __shared__ __align__(16) Tiles tiles;
+    constexpr int T = WAVES * 64;
+    constexpr int BM = WAVES * 32 * RB;
+    __shared__ __align__(16) Tiles tiles[2];
     const int h = blockIdx.x;
     // Later query tiles see more keys (causal context, then the visual prefix
     // plus clean text for the noisy stream), so tiles are issued last-first.
     const int qt = nqt - 1 - blockIdx.y;
-    const int i0 = qt * kBM;
-    const int i1 = (i0 + kBM < G.N) ? i0 + kBM : G.N;
+    const int i0 = qt * BM;
+    const int i1 = (i0 + BM < G.N) ? i0 + BM : G.N;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int row = i0 + wave * 32 + (lane & 31);
-    const bool row_ok = row < G.N;
     const size_t rs = size_t(H) * kDh;               // element stride between tokens
-
-    bf16x8 qf[8];
-    load_q(qf, row_ok ? q + size_t(row) * rs + size_t(h) * kDh : nullptr, lane);
 
     int a_end, b_beg, b_end;
     key_ranges(G, i0, i1, &a_end, &b_beg, &b_end);
     const int na = (a_end + kBN - 1) / kBN;
     const int nb = b_end > b_beg ? (b_end - b_beg + kBN - 1) / kBN : 0;
-
-    float m = -INFINITY, l = 0.f;
-    f32x16 oacc[4] = {};
+    const int ntile = na + nb;
     const uint16_t* kb = k + size_t(h) * kDh;
     const uint16_t* vb = v + size_t(h) * kDh;
-
-    for (int t = 0; t < na + nb; ++t) {
-        int j0, jend;
+    auto tile_range = [&](int t, int& j0, int& jend) {
         if (t < na) {
             j0 = t * kBN;
             jend = a_end;
@@ -114,57 +134,126 @@ __global__ __launch_bounds__(256) void dualstream_bf16_kernel(
             j0 = b_beg + (t - na) * kBN;
             jend = b_end;
         }
-        const int j1 = j0 + kBN < jend ? j0 + kBN : jend;
-        __syncthreads();                               // previous tile fully consumed
-        load_tile(tiles, kb, vb, rs, j0, jend);
-        __syncthreads();
+    };
 
-        f32x16 sacc[2];
-        scores(sacc, tiles, qf, lane);
-
-        const bool full = (j1 - j0 == kBN) && tile_full(G, i0, i1, j0, j1);
-        float x[2][16];
-        float mx = m;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int j = j0 + 32 * kb2 + acc_row(e, lane);
-                const bool vis = full || (row_ok && j < j1 && visible(G, row, j));
-                x[kb2][e] = vis ? sacc[kb2][e] * scale_log2 : -INFINITY;
-                mx = fmaxf(mx, x[kb2][e]);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mref = (mx == -INFINITY) ? 0.f : mx;
-        const float alpha = exp2f(m - mref);
-        float p[2][16];
-        float ls = 0.f;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                p[kb2][e] = exp2f(x[kb2][e] - mref);
-                ls += p[kb2][e];
-            }
-        ls += __shfl_xor(ls, 32);
-        l = l * alpha + ls;
-        m = mx;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-        accumulate_pv(oacc, tiles, p, lane);
+    TileRegs<T> regs;
+    if (ntile > 0) {
+        int j0, jend;
+        tile_range(0, j0, jend);
+        fetch_tile<T>(regs, kb, vb, rs, j0, jend);
     }
 
-    if (row_ok) {
-        const float inv = l > 0.f ? 1.f / l : 0.f;
+    bf16x8 qf[RB][8];
+    RowVis rv[RB];
+    int rows[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int row = i0 + (wave * RB + rb) * 32 + (lane & 31);
+        rows[rb] = row;
+        const bool ok = row < G.N;
+        load_q(qf[rb], ok ? q + size_t(row) * rs + size_t(h) * kDh : nullptr, lane);
+        rv[rb] = ok ? row_vis(G, row) : RowVis{-1, 0, 0};
+    }
+
+    if (ntile > 0) store_tile<T>(tiles[0], regs);
+    __syncthreads();
+
+    float m[RB], l[RB];
+    f32x16 oacc[RB][4];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        m[rb] = -INFINITY;
+        l[rb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[rb][db] = f32x16{};
+    }
+
+    for (int t = 0; t < ntile; ++t) {
+        int j0, jend;
+        tile_range(t, j0, jend);
+        const int j1 = j0 + kBN < jend ? j0 + kBN : jend;
+        if (t + 1 < ntile) {
+            int n0, nend;
+            tile_range(t + 1, n0, nend);
+            fetch_tile<T>(regs, kb, vb, rs, n0, nend);
+        }
+        const Tiles& cur = tiles[t & 1];
+
+        f32x16 sacc[RB][2];
+        scores<RB>(sacc, cur, qf, lane);
+
+        const bool full = (j1 - j0 == kBN) && tile_full(G, i0, i1, j0, j1);
+        // Key of accumulator register e of this lane: jl + 8 (e / 4) + e % 4.
+        const int jl = j0 + 4 * (lane >> 5);
+        float p[RB][2][16];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            float mx = -INFINITY;
+            if (full) {
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        p[rb][kb2][e] = sacc[rb][kb2][e];
+                        mx = fmaxf(mx, p[rb][kb2][e]);
+                    }
+            } else {
+                const int lim = rv[rb].lim < j1 - 1 ? rv[rb].lim : j1 - 1;
+                const int hi = rv[rb].hi < j1 ? rv[rb].hi : j1;
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int j = jl + 32 * kb2 + 8 * (e >> 2) + (e & 3);
+                        const bool vis = (j <= lim) || (j >= rv[rb].lo && j < hi);
+                        p[rb][kb2][e] = vis ? sacc[rb][kb2][e] : -INFINITY;
+                        mx = fmaxf(mx, p[rb][kb2][e]);
+                    }
+            }
+            // Raw-score maximum; everything below is in log2 units of the
+            // scaled score: p = 2^(scale_log2 * s - mnew).
+            mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+            const float mnew = fmaxf(m[rb], mx);
+            const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+            float ls = 0.f;
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    p[rb][kb2][e] = __builtin_amdgcn_exp2f(fmaf(p[rb][kb2][e], scale_log2, -mref));
+                    ls += p[rb][kb2][e];
+                }
+            ls += __shfl_xor(ls, 32);
+            const float alpha = __builtin_amdgcn_exp2f(m[rb] - mref);
+            l[rb] = l[rb] * alpha + ls;
+            m[rb] = mnew;
+            // Rescale the running output only when some row's maximum moved.
+            if (__ballot(alpha != 1.f)) {
+#pragma unroll
+                for (int db = 0; db < 4; ++db) oacc[rb][db] *= alpha;
+            }
+        }
+        accumulate_pv<RB>(oacc, cur, p, lane);
+
+        if (t + 1 < ntile) store_tile<T>(tiles[(t + 1) & 1], regs);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int row = rows[rb];
+        if (row >= G.N) continue;
+        const float inv = l[rb] > 0.f ? 1.f / l[rb] : 0.f;
         uint16_t* orow = out + size_t(row) * rs + size_t(h) * kDh;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4) {
                 const int dh = 32 * db + acc_row(4 * e4, lane);
-                u32x2 w = {pack_bf16x2(oacc[db][4 * e4] * inv, oacc[db][4 * e4 + 1] * inv),
-                           pack_bf16x2(oacc[db][4 * e4 + 2] * inv, oacc[db][4 * e4 + 3] * inv)};
-                *reinterpret_cast<u32x2*>(orow + dh) = w;
+                bf16x4 w;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) w[x] = static_cast<__bf16>(oacc[rb][db][4 * e4 + x] * inv);
+                *reinterpret_cast<bf16x4*>(orow + dh) = w;
             }
     }
 }
@@ -222,16 +311,27 @@ __global__ __launch_bounds__(64) void dualstream_f32_kernel(const float* __restr
 
 }  // namespace
 
+#ifndef BD_DS_WAVES
+#define BD_DS_WAVES 4
+#endif
+#ifndef BD_DS_RB
+#define BD_DS_RB 1
+#endif
+#ifndef BD_DS_OCC
+#define BD_DS_OCC 2
+#endif
+
 hipError_t launch_dualstream_bf16(const void* q, const void* k, const void* v, int n_vis,
                                   int n_txt, int block, int H, float scale, void* out,
                                   hipStream_t st) {
+    constexpr int BM = BD_DS_WAVES * 32 * BD_DS_RB;
     Geometry G{n_vis, n_txt, n_vis + n_txt, n_vis + 2 * n_txt, block};
-    const int nqt = (G.N + kBM - 1) / kBM;
+    const int nqt = (G.N + BM - 1) / BM;
     const dim3 grid(H, nqt);
-    hipLaunchKernelGGL(dualstream_bf16_kernel, grid, dim3(256), 0, st,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), G, H, scale * kLog2e,
-                       static_cast<uint16_t*>(out), nqt);
+    hipLaunchKernelGGL((dualstream_bf16_kernel<BD_DS_WAVES, BD_DS_RB, BD_DS_OCC>), grid,
+                       dim3(BD_DS_WAVES * 64), 0, st, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), G, H,
+                       scale * kLog2e, static_cast<uint16_t*>(out), nqt);
     return hipGetLastError();
 }
 

@@ -87,7 +87,7 @@ bd_status bd_make_intra_mask(bd_mask_kind kind, int32_t Bq, uint64_t* host_rows)
  *                              and values (written by the caller)
  *   intra_mask  [Bq] uint64 (device), e.g. from bd_make_intra_mask
  *   out         [Bq][Hq][dh]   dtype dt
- *   scale       softmax scale; 0 selects 1/sqrt(dh)
+ *   scale       softmax scale, > 0; 0 selects 1/sqrt(dh)
  *   ws          workspace of at least bd_block_attn_ws_bytes(...) bytes
  * Limits: 1 <= Bq <= 64, 0 <= P, P + Bq <= cap, Hkv >= 1, Hq % Hkv == 0,
  *   BD_BF16: dh == 128 and P + Bq <= 65536;  BD_F32: dh % 4 == 0 and
@@ -208,7 +208,7 @@ bd_status bd_cert_scan(const float* anchor_conf, const int32_t* anchor_tok,
  *        j - n_vis <= r                               (printed N2C matrix)
  *   N2N: i, j noisy with (r / block) == (r_j / block) (bidirectional block)
  * and no clean query sees a noisy key.  Softmax scaled dot-product per head.
- *   q, k, v, out [N][H][dh] dtype dt;  scale 0 selects 1/sqrt(dh)
+ *   q, k, v, out [N][H][dh] dtype dt;  scale > 0, or 0 for 1/sqrt(dh)
  * Limits: n_vis >= 0, n_txt >= 0, N >= 1, block >= 1, H >= 1,
  *   BD_BF16: dh == 128;  BD_F32: dh % 4 == 0 and 4 <= dh <= 128.
  * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_ALIGN, BD_E_LAUNCH.

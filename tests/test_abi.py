@@ -100,6 +100,7 @@ def test_block_attn_validation():
     assert _attn(dh=64) == bd.BD_E_SHAPE         # bf16 needs dh == 128
     assert _attn(dt=bd.BD_F32, dh=130) == bd.BD_E_SHAPE
     assert _attn(scale=float("nan")) == bd.BD_E_SHAPE
+    assert _attn(scale=-0.5) == bd.BD_E_SHAPE
     assert _attn(q=MISALIGNED) == bd.BD_E_ALIGN
     assert _attn(out=MISALIGNED) == bd.BD_E_ALIGN
     assert _attn(ws=None) == bd.BD_E_WORKSPACE
@@ -182,6 +183,7 @@ def test_dualstream_validation():
     assert d(dh=16) == bd.BD_E_SHAPE
     assert d(k=MISALIGNED) == bd.BD_E_ALIGN
     assert d(scale=float("inf")) == bd.BD_E_SHAPE
+    assert d(scale=-1.0) == bd.BD_E_SHAPE
 
 
 def test_python_binding_raises_on_error():
