@@ -135,14 +135,6 @@ __device__ __forceinline__ void scores(f32x16 (&sacc)[RB][2], const Tiles& t,
     }
 }
 
-// Eight consecutive probabilities as a bf16 B fragment (hardware RNE).
-__device__ __forceinline__ bf16x8 to_bf16x8(const float* p) {
-    bf16x8 r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = static_cast<__bf16>(p[e]);
-    return r;
-}
-
 // Transposing LDS load of four keys of one dh column (see the file comment).
 __device__ __forceinline__ bf16x4 read_vt4(const uint16_t* p) {
     typedef __bf16 lds_bf16x4 __attribute__((ext_vector_type(4)));
@@ -150,18 +142,27 @@ __device__ __forceinline__ bf16x4 read_vt4(const uint16_t* p) {
         (BD_LDS lds_bf16x4*)(const_cast<uint16_t*>(p)));
 }
 
-// O^T += V^T P^T for one tile; p[rb][kb][r] are the probabilities of the
-// keys in sacc layout.
+// bf16 P^T fragments of one tile from probabilities in score-accumulator
+// order: pf[rb][kb][s2] = p[rb][kb][8*s2 .. 8*s2+7].  The probabilities live
+// in their own registers, never in the MFMA accumulators: VALU writes into
+// registers that an MFMA chain also writes are avoided altogether.
 template <int RB>
-__device__ __forceinline__ void accumulate_pv(f32x16 (&oacc)[RB][4], const Tiles& t,
-                                              const float (&p)[RB][2][16], int lane) {
-    bf16x8 pf[RB][2][2];
+__device__ __forceinline__ void pack_p(bf16x8 (&pf)[RB][2][2], const float (&sacc)[RB][2][16]) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) pf[rb][kb][s2] = to_bf16x8(&p[rb][kb][8 * s2]);
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    pf[rb][kb][s2][e] = static_cast<__bf16>(sacc[rb][kb][8 * s2 + e]);
+}
+
+// O^T += V^T P^T for one tile.
+template <int RB>
+__device__ __forceinline__ void accumulate_pv(f32x16 (&oacc)[RB][4], const Tiles& t,
+                                              const bf16x8 (&pf)[RB][2][2], int lane) {
     // Supplier lane L of 16-lane group q addresses V[key0 + L/4][dh0 + 4 (L%4)]
     // with key0 = 32 kb + 16 s2 + 4 (q / 2) (+ 8 for the upper four keys) and
     // dh0 = 32 db + 16 (q % 2).

@@ -84,36 +84,42 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
 
         f32x16 sacc[1][2];
         scores<1>(sacc, cur, qf, lane);
-        float p[1][2][16];
-        float mx = m;
+        float x[1][2][16];
+        float mx = -INFINITY;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int j = j0 + 32 * kb2 + acc_row(e, lane);
-                const bool vis = (j < P) || (j < Nk && ((mbits >> (j - P)) & 1ull));
-                p[0][kb2][e] = vis ? sacc[0][kb2][e] * scale_log2 : -INFINITY;
-                mx = fmaxf(mx, p[0][kb2][e]);
+                const int jb = j - P;            // block key index (negative in the prefix)
+                const bool in_block = (jb >= 0) & (j < Nk);
+                const bool bit = ((mbits >> (jb & 63)) & 1ull) != 0;
+                const bool vis = (j < P) | (in_block & bit);
+                x[0][kb2][e] = vis ? sacc[0][kb2][e] : -INFINITY;
+                mx = fmaxf(mx, x[0][kb2][e]);
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mref = (mx == -INFINITY) ? 0.f : mx;
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+        const float mnew = fmaxf(m, mx);
+        const float mref = (mnew == -INFINITY) ? 0.f : mnew;
         float ls = 0.f;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                p[0][kb2][e] = __builtin_amdgcn_exp2f(p[0][kb2][e] - mref);
-                ls += p[0][kb2][e];
+                x[0][kb2][e] = __builtin_amdgcn_exp2f(fmaf(x[0][kb2][e], scale_log2, -mref));
+                ls += x[0][kb2][e];
             }
         ls += __shfl_xor(ls, 32);
         const float alpha = __builtin_amdgcn_exp2f(m - mref);
         l = l * alpha + ls;
-        m = mx;
+        m = mnew;
         if (__ballot(alpha != 1.f)) {
 #pragma unroll
             for (int db = 0; db < 4; ++db) oacc[0][db] *= alpha;
         }
-        accumulate_pv<1>(oacc, cur, p, lane);
+        bf16x8 pf[1][2][2];
+        pack_p<1>(pf, x);
+        accumulate_pv<1>(oacc, cur, pf, lane);
 
         if (t + 1 < t_end) store_tile<256>(tiles[(t + 1 - t_beg) & 1], regs);
         __syncthreads();

@@ -23,7 +23,9 @@ namespace {
 
 using namespace attn;
 
-constexpr int kBM = 128;
+
+// Headroom (log2 units) before the running maximum of a row is moved.
+constexpr float kLazy = 8.0f;
 
 struct Geometry {
     int n_vis, n_txt, ctx, N, block;
@@ -185,18 +187,14 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void dualstream_bf16_kernel(
         const bool full = (j1 - j0 == kBN) && tile_full(G, i0, i1, j0, j1);
         // Key of accumulator register e of this lane: jl + 8 (e / 4) + e % 4.
         const int jl = j0 + 4 * (lane >> 5);
-        float p[RB][2][16];
+        float x[RB][2][16];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            float mx = -INFINITY;
             if (full) {
 #pragma unroll
                 for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        p[rb][kb2][e] = sacc[rb][kb2][e];
-                        mx = fmaxf(mx, p[rb][kb2][e]);
-                    }
+                    for (int e = 0; e < 16; ++e) x[rb][kb2][e] = sacc[rb][kb2][e];
             } else {
                 const int lim = rv[rb].lim < j1 - 1 ? rv[rb].lim : j1 - 1;
                 const int hi = rv[rb].hi < j1 ? rv[rb].hi : j1;
@@ -205,35 +203,46 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void dualstream_bf16_kernel(
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int j = jl + 32 * kb2 + 8 * (e >> 2) + (e & 3);
-                        const bool vis = (j <= lim) || (j >= rv[rb].lo && j < hi);
-                        p[rb][kb2][e] = vis ? sacc[rb][kb2][e] : -INFINITY;
-                        mx = fmaxf(mx, p[rb][kb2][e]);
+                        const bool vis = (j <= lim) | ((j >= rv[rb].lo) & (j < hi));
+                        x[rb][kb2][e] = vis ? sacc[rb][kb2][e] : -INFINITY;
                     }
             }
-            // Raw-score maximum; everything below is in log2 units of the
-            // scaled score: p = 2^(scale_log2 * s - mnew).
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, x[rb][kb2][e]);
+            // Raw-score maximum, then everything in log2 units of the scaled
+            // score.  The row's reference maximum m only moves when the new
+            // maximum exceeds it by more than kLazy: until then probabilities
+            // 2^(scale_log2 * s - m) stay below 2^kLazy, and skipping the
+            // rescale of the running output leaves the final normalised
+            // result unchanged.
             mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
-            const float mnew = fmaxf(m[rb], mx);
+            const bool move = mx > m[rb] + kLazy;
+            const float mnew = move ? mx : m[rb];
             const float mref = (mnew == -INFINITY) ? 0.f : mnew;
             float ls = 0.f;
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    p[rb][kb2][e] = __builtin_amdgcn_exp2f(fmaf(p[rb][kb2][e], scale_log2, -mref));
-                    ls += p[rb][kb2][e];
+                    x[rb][kb2][e] = __builtin_amdgcn_exp2f(fmaf(x[rb][kb2][e], scale_log2, -mref));
+                    ls += x[rb][kb2][e];
                 }
             ls += __shfl_xor(ls, 32);
-            const float alpha = __builtin_amdgcn_exp2f(m[rb] - mref);
-            l[rb] = l[rb] * alpha + ls;
-            m[rb] = mnew;
-            // Rescale the running output only when some row's maximum moved.
-            if (__ballot(alpha != 1.f)) {
+            if (__ballot(move)) {
+                const float alpha = __builtin_amdgcn_exp2f(m[rb] - mref);
+                l[rb] *= alpha;
 #pragma unroll
                 for (int db = 0; db < 4; ++db) oacc[rb][db] *= alpha;
             }
+            l[rb] += ls;
+            m[rb] = mnew;
         }
-        accumulate_pv<RB>(oacc, cur, p, lane);
+        bf16x8 pf[RB][2][2];
+        pack_p<RB>(pf, x);
+        accumulate_pv<RB>(oacc, cur, pf, lane);
 
         if (t + 1 < ntile) store_tile<T>(tiles[(t + 1) & 1], regs);
         __syncthreads();
