@@ -8,8 +8,10 @@ workload: bd_block_attn (16 block queries, bidirectional block, over a
 bd_lmhead_conf (hidden 2048 x vocabulary 151936, bf16) -> bd_commit
 (threshold 0.9), plus the restore of the block state so that every step does
 the same work.  Inputs are seeded synthetic tensors already resident in HBM;
-S consecutive steps (default 8, each restoring the block state first) are
-captured as one HIP graph, which is replayed K/S times between HIP events.
+S consecutive steps (default 8) are captured as one HIP graph, which is
+replayed K/S times between HIP events.  Each of the S steps of a graph works
+on its own copy of the block state, and one device copy at the head of the
+graph restores all S copies, so that every step starts from the same state.
 One JSON line is printed.
 """
 from __future__ import annotations
@@ -126,7 +128,8 @@ def main():
     stream = torch.cuda.current_stream()
 
     inp = synth.qwen_decode()
-    step = runner.DecodeStep(inp)
+    S = max(1, args.graph_steps)
+    step = runner.DecodeStep(inp, slots=S)
     B, P, Hq, Hkv, dh, d, V = (inp[k] for k in ("B", "P", "Hq", "Hkv", "dh", "d", "V"))
 
     # Eager reference step (and the commit count that every replay repeats).
@@ -136,7 +139,8 @@ def main():
     n_commit = int(step.n_committed.item())
     tokens_ref = step.tokens.clone()
 
-    # Capture reset + step as one graph.
+    # Capture one restore of the S block states + S steps (one per state) as
+    # one graph.
     side = torch.cuda.Stream()
     side.wait_stream(stream)
     with torch.cuda.stream(side):
@@ -144,19 +148,19 @@ def main():
         step.run()
     stream.wait_stream(side)
     torch.cuda.synchronize()
-    S = max(1, args.graph_steps)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        for _ in range(S):
-            step.reset()
-            step.run()
+        step.reset()
+        for i in range(S):
+            step.run(slot=i)
     torch.cuda.synchronize()
 
     reps = max(1, (args.steps + S - 1) // S)
     args.steps = reps * S
     ms_step = timed(graph.replay, reps, max(1, args.warmup // S), stream) / S
     torch.cuda.synchronize()
-    assert torch.equal(step.tokens, tokens_ref), "graph replay diverged from the eager step"
+    for i in range(S):
+        assert torch.equal(step.tokens_slots[i], tokens_ref), "graph replay diverged"
     assert int(step.n_committed.item()) == n_commit
 
     # Dominant kernel: the LM head (its two dispatches), timed alone.

@@ -438,7 +438,7 @@ template <int NB>
 hipError_t launch_nb(const void* h, const void* W, int B, int d, int V, const Finish& f,
                      void* ws, hipStream_t st) {
     const int ntiles = (V + 15) / 16;
-    const int G = ntiles < kMaxGrid ? ntiles : kMaxGrid;
+    const int G = lmhead_grid(B, d, V);
     const auto* hh = static_cast<const uint16_t*>(h);
     const auto* ww = static_cast<const uint16_t*>(W);
     int ks = 0, nch = 0;
@@ -480,7 +480,23 @@ int lmhead_grid(int B, int d, int V) {
     (void)B;
     (void)d;
     const int ntiles = (V + 15) / 16;
-    return ntiles < kMaxGrid ? ntiles : kMaxGrid;
+    if (ntiles <= kMaxGrid) return ntiles;
+    // The kernel is bound by the aggregate HBM bandwidth, so its time follows
+    // the largest per-workgroup share, ceil(ntiles / G), times G.  Between
+    // 7/8 of the chip and all of it, take the grid that wastes the fewest
+    // tile slots (the largest such grid on ties): 9496 tiles, for instance,
+    // go 38 per workgroup to 250 workgroups instead of 37 or 38 to 256, whose
+    // last twenty-four workgroups would run alone at the end.
+    int best = kMaxGrid;
+    long best_slots = long((ntiles + kMaxGrid - 1) / kMaxGrid) * kMaxGrid;
+    for (int g = kMaxGrid - 1; g >= kMaxGrid - kMaxGrid / 8; --g) {
+        const long slots = long((ntiles + g - 1) / g) * g;
+        if (slots < best_slots) {
+            best_slots = slots;
+            best = g;
+        }
+    }
+    return best;
 }
 
 size_t lmhead_ws_bytes(int B, int d, int V) {

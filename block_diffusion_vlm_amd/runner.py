@@ -84,10 +84,15 @@ class DecodeStep:
     block) -> bd_lmhead_conf_commit (LM head, then commit).  With
     ``fused=False`` the LM head and the commit are the two separate calls
     bd_lmhead_conf and bd_commit.  Inputs from synth.qwen_decode or
-    synth.tiny.  ``reset()`` restores the block state (masked flags, tokens)
-    so that repeated steps do identical work."""
+    synth.tiny.
 
-    def __init__(self, inp: dict, device="cuda", fused=True):
+    The block state (committed tokens, masked flags) exists in ``slots``
+    independent copies in one buffer; ``run(slot=i)`` updates copy i and
+    ``reset()`` restores every copy with one device copy, so that repeated
+    steps do identical work and a sequence of steps on different slots needs
+    one restore in all."""
+
+    def __init__(self, inp: dict, device="cuda", fused=True, slots=1):
         self.fused = fused
         self.inp = inp
         dt = dtype_code(inp["dtype"])
@@ -100,16 +105,20 @@ class DecodeStep:
         self.attn = BlockAttn(dt, bd.BD_MASK_BIDIR, B, inp["P"], inp["cap"], inp["Hq"],
                               inp["Hkv"], inp["q"].shape[-1], device)
         self.lm = LMHead(dt, self.W, B, inp["d"], inp["V"], device)
-        # Block state (tokens int32[B], then masked uint8[B]) in one buffer, so
-        # that restoring it between repeated steps is a single copy.
-        nbytes = 4 * B + 16 * ((B + 15) // 16)
-        host = np.zeros(nbytes, np.uint8)
-        host[:4 * B] = np.asarray(inp["tokens"], np.int32).view(np.uint8)
-        host[4 * B:5 * B] = np.asarray(inp["masked"], np.uint8)
-        self.state0 = to_dev(host, device)
+        # One slot: tokens int32[B], then masked uint8[B]; slots 256 bytes apart.
+        used = 5 * B
+        stride = (used + 255) // 256 * 256
+        one = np.zeros(stride, np.uint8)
+        one[:4 * B] = np.asarray(inp["tokens"], np.int32).view(np.uint8)
+        one[4 * B:5 * B] = np.asarray(inp["masked"], np.uint8)
+        self.state0 = to_dev(np.tile(one, slots), device)
         self.state = self.state0.clone()
-        self.tokens = self.state[:4 * B].view(torch.int32)
-        self.masked = self.state[4 * B:5 * B]
+        self.tokens_slots = [self.state[i * stride:i * stride + 4 * B].view(torch.int32)
+                             for i in range(slots)]
+        self.masked_slots = [self.state[i * stride + 4 * B:i * stride + 5 * B]
+                             for i in range(slots)]
+        self.tokens = self.tokens_slots[0]
+        self.masked = self.masked_slots[0]
         self.n_committed = torch.zeros(1, dtype=torch.int32, device=device)
         self.tau = float(inp["tau"])
         self.B = B
@@ -117,16 +126,17 @@ class DecodeStep:
     def reset(self):
         self.state.copy_(self.state0)
 
-    def run(self, stream=None):
+    def run(self, stream=None, slot=0):
+        tokens, masked = self.tokens_slots[slot], self.masked_slots[slot]
         self.attn(self.q, self.k_cache, self.v_cache, stream)
         lm = self.lm
         if self.fused:
             bd.bd_lmhead_conf_commit(lm.dt, self.h, lm.W, lm.B, lm.d, lm.V, self.tau, lm.conf,
-                                     lm.argmax, self.masked, self.tokens, self.n_committed, lm.ws,
+                                     lm.argmax, masked, tokens, self.n_committed, lm.ws,
                                      lm.ws_bytes, stream)
         else:
             lm(self.h, stream)
-            bd.bd_commit(lm.conf, lm.argmax, self.B, self.tau, self.masked, self.tokens,
+            bd.bd_commit(lm.conf, lm.argmax, self.B, self.tau, masked, tokens,
                          self.n_committed, stream)
 
 
