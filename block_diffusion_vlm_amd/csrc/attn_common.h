@@ -2,15 +2,14 @@
 // the KV cache and dual-stream training attention), on gfx950
 // v_mfma_f32_32x32x16_bf16.
 //
-// Formulation.  A wave owns RB blocks of 32 query rows.  Scores are computed
-// transposed, S^T[key][q] = K[key][:] . Q[q][:], with K as the A operand (read
-// from LDS) and Q as the B operand (held in registers), and the output
-// transposed as well, O^T[dh][q] = V^T[dh][key] . P^T[key][q], with V^T read
-// from LDS by transposing loads and P taken straight from the score
-// accumulators.  In the 32x32 accumulator layout lane l holds query column
-// l % 32 for both products, so every per-row softmax quantity (max, sum,
-// rescale factor) lives in the lane that needs it; only lanes l and l ^ 32
-// share a row.  Each A fragment read from LDS feeds RB MFMAs.
+// Formulation.  A wave owns 32 query rows.  Scores are computed transposed,
+// S^T[key][q] = K[key][:] . Q[q][:], with K as the A operand (read from LDS)
+// and Q as the B operand (held in registers), and the output transposed as
+// well, O^T[dh][q] = V^T[dh][key] . P^T[key][q], with V^T read from LDS by
+// transposing loads and P^T packed from the probabilities.  In the 32x32
+// accumulator layout lane l holds query column l % 32 for both products, so
+// every per-row softmax quantity (max, sum, rescale factor) lives in the lane
+// that needs it; only lanes l and l ^ 32 share a row.
 //
 // Accumulator layout (32x32, 16 floats per lane): register r of lane l holds
 // row 8*(r/4) + 4*(l/32) + (r%4), column l % 32.  Operand layout (A and B,
@@ -20,15 +19,27 @@
 // 16*s2 + 4*(l/32) + {0,1,2,3} and 16*s2 + 8 + 4*(l/32) + {0,1,2,3}; V^T is
 // read with exactly that key permutation, so the sum over keys is unchanged.
 //
-// LDS tiles.  K and V are both stored row-major ([key][dh]) with 16-byte
-// stores.  K rows are padded to 272 bytes, so the 16 keys of one fragment
-// load fall in distinct banks.  V^T fragments come from ds_read_b64_tr_b16:
-// within each 16-lane group, lane i of the result receives element
-// (i % 4) of the 8 bytes addressed by lane 4k + i/4, for k = 0..3; with lane
-// L addressing V[key0 + L/4][dh0 + 4 (L%4)], lane i therefore receives
-// V[key0 + k][dh0 + i], k = 0..3 - four keys of one dh column.  V rows are
-// padded to 288 bytes, so the four rows read by one group use distinct banks.
+// LDS tiles.  A K or V tile is 64 keys x 128 dims, row-major (256 bytes per
+// key, no padding), filled straight from global memory by
+// global_load_lds_dwordx4, which writes lane l's 16 bytes at the
+// instruction's LDS base + 16 l; each instruction therefore fills 1 KB (four
+// keys) and the lane chooses which 16-byte piece of its key it fetches.
+// Bank conflicts are avoided with XOR swizzles of the 16-byte piece index:
+//   K: piece p of key r is stored in slot p ^ (r % 16), so the 16
+//      consecutive keys that a quarter-wave reads for one fragment fall in
+//      distinct banks;
+//   V: piece p of key r is stored in slot p ^ 4 (r % 4): a half-wave of one
+//      transposing load (below) reads four aligned pieces of four keys, and
+//      the swizzle sends each key's four pieces to a different quarter of the
+//      banks.
+// V^T fragments come from ds_read_b64_tr_b16: within each 16-lane group,
+// lane i of the result receives element (i % 4) of the 8 bytes addressed by
+// lane 4k + i/4, for k = 0..3; with lane L addressing V[key0 + L/4][dh0 +
+// 4 (L%4)], lane i therefore receives V[key0 + k][dh0 + i], k = 0..3 - four
+// keys of one dh column.
 #pragma once
+
+#include <type_traits>
 
 #include "bd_internal.h"
 
@@ -37,71 +48,119 @@
 namespace bd {
 namespace attn {
 
-constexpr int kDh = 128;           // head dimension of the bf16 kernels
-constexpr int kBN = 64;            // keys per tile
-constexpr int kKPitch = kDh + 8;   // LDS row pitch of K tiles (elements): 272 B
-constexpr int kVPitch = kDh + 16;  // LDS row pitch of V tiles (elements): 288 B
+constexpr int kDh = 128;             // head dimension of the bf16 kernels
+constexpr int kBN = 64;              // keys per tile
+constexpr int kTile = kBN * kDh;     // elements of one K or V tile (16 KB)
 
-struct Tiles {
-    uint16_t k[kBN * kKPitch];      // K tile, [key][dh]
-    uint16_t v[kBN * kVPitch];      // V tile, [key][dh]
-};
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int k_slot(int key, int piece) { return piece ^ (key & 15); }
+__device__ __forceinline__ int v_slot(int key, int piece) { return piece ^ (4 * (key & 3)); }
 
 // Key held by accumulator register r of lane l inside a 32-key block.
 __device__ __forceinline__ int acc_row(int r, int lane) {
     return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-// A 64-key tile of K and V in flight through registers.  With T threads,
-// thread t holds 16-byte pieces p = t + T u (u < 1024 / T) of both K and V:
-// key p / 16, dims 8 (p % 16) .. +7.
-template <int T>
-struct TileRegs {
-    static constexpr int N = 1024 / T;
-    u32x4 k[N];
-    u32x4 v[N];
-};
+// Value of x in lane l ^ 32 (v_permlane32_swap: a VALU exchange of the two
+// half-waves, no LDS round trip).
+__device__ __forceinline__ float other_half(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    // r[0]: lanes < 32 keep x, lanes >= 32 receive lanes 0..31;
+    // r[1]: lanes < 32 receive lanes 32..63, lanes >= 32 keep x.
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
 
-// Global -> registers for keys [j0, j0 + 64); keys at or beyond `jend` read
-// as zeros.  `row_stride` is the distance between consecutive keys in elements.
-template <int T>
-__device__ __forceinline__ void fetch_tile(TileRegs<T>& r, const uint16_t* __restrict__ kbase,
-                                           const uint16_t* __restrict__ vbase, size_t row_stride,
-                                           int j0, int jend) {
-    constexpr int KEYS_PER_U = T / 16;               // key rows between consecutive u
-    const int key = threadIdx.x >> 4;
-    const int col = (threadIdx.x & 15) * 8;
-    const size_t off = size_t(j0 + key) * row_stride + col;
-    const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + off);
-    const u32x4* vp = reinterpret_cast<const u32x4*>(vbase + off);
-    const size_t step = size_t(KEYS_PER_U) * row_stride / 8;   // in 16-byte units
-    if (j0 + kBN <= jend) {
+// Global -> LDS loads of one 64-key K or V tile for a workgroup of WAVES
+// waves (16 / WAVES instructions per wave).  `g` points at the tile's first
+// key, `row_stride` is the distance between consecutive keys in elements
+// (64 row_stride must fit in 31 bits: offsets inside a tile are 32-bit), and
+// keys at or beyond `nkeys` (1 <= nkeys <= 64) repeat key nkeys - 1, so they
+// hold finite values that the callers mask.
+//
+// The loads are issued from inline assembly so that the compiler does not
+// model them: it would otherwise make every later LDS read of any buffer wait
+// for all of them, which defeats prefetching several tiles ahead.  They write
+// no register; the callers order them with dma_wait<N>() (vmcnt counts them,
+// and they complete in issue order) followed by tile_barrier().  M0 holds the
+// wave-uniform LDS address; one wait state separates its write from the load.
+template <int WAVES, bool IS_V>
+__device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* g, int row_stride,
+                                         int nkeys) {
+    constexpr int PER_WAVE = 16 / WAVES;
+    const int lane = threadIdx.x & 63;
+    const unsigned wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int s = lane & 15;
+    const unsigned lofs =
+        static_cast<unsigned>(reinterpret_cast<uintptr_t>((BD_LDS void*)lds));
+    const unsigned rb = 2u * unsigned(row_stride);
 #pragma unroll
-        for (int u = 0; u < TileRegs<T>::N; ++u) {
-            r.k[u] = kp[u * step];
-            r.v[u] = vp[u * step];
-        }
-    } else {
-#pragma unroll
-        for (int u = 0; u < TileRegs<T>::N; ++u) {
-            const bool ok = j0 + key + KEYS_PER_U * u < jend;
-            r.k[u] = ok ? kp[u * step] : u32x4{0, 0, 0, 0};
-            r.v[u] = ok ? vp[u * step] : u32x4{0, 0, 0, 0};
-        }
+    for (int u = 0; u < PER_WAVE; ++u) {
+        const unsigned I = wave * PER_WAVE + u;        // 1 KB instruction index
+        const int key = 4 * int(I) + (lane >> 4);
+        const int kk = key < nkeys ? key : nkeys - 1;
+        const int slot = IS_V ? v_slot(key, s) : k_slot(key, s);
+        const unsigned off = unsigned(kk) * rb + 16u * unsigned(slot);
+        const unsigned m0 = __builtin_amdgcn_readfirstlane(lofs + 1024u * I);
+        __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                         :
+                         : "{m0}"(m0), "v"(off), "s"(g)
+                         : "memory");
     }
 }
 
-// Registers -> LDS (both row-major).
-template <int T>
-__device__ __forceinline__ void store_tile(Tiles& t, const TileRegs<T>& r) {
+// Per-lane global byte offsets of the loads of a complete tile (all 64 keys
+// present), the same for every tile: off[u] for load u of this wave.
+template <int WAVES, bool IS_V>
+__device__ __forceinline__ void dma_offsets(unsigned (&off)[16 / WAVES], int row_stride) {
+    constexpr int PER_WAVE = 16 / WAVES;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int s = lane & 15;
 #pragma unroll
-    for (int u = 0; u < TileRegs<T>::N; ++u) {
-        const int p = threadIdx.x + T * u;
-        const int key = p >> 4;
-        const int col = (p & 15) * 8;
-        *reinterpret_cast<u32x4*>(&t.k[key * kKPitch + col]) = r.k[u];
-        *reinterpret_cast<u32x4*>(&t.v[key * kVPitch + col]) = r.v[u];
+    for (int u = 0; u < PER_WAVE; ++u) {
+        const int key = 4 * (wave * PER_WAVE + u) + (lane >> 4);
+        const int slot = IS_V ? v_slot(key, s) : k_slot(key, s);
+        off[u] = unsigned(key) * 2u * unsigned(row_stride) + 16u * unsigned(slot);
     }
+}
+
+// Loads of a complete tile with precomputed offsets (see dma_tile).
+template <int WAVES>
+__device__ __forceinline__ void dma_tile_full(uint16_t* lds, const uint16_t* g,
+                                              const unsigned (&off)[16 / WAVES]) {
+    constexpr int PER_WAVE = 16 / WAVES;
+    const unsigned wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const unsigned lofs =
+        static_cast<unsigned>(reinterpret_cast<uintptr_t>((BD_LDS void*)lds));
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) {
+        const unsigned m0 = __builtin_amdgcn_readfirstlane(lofs + 1024u * (wave * PER_WAVE + u));
+        __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                         :
+                         : "{m0}"(m0), "v"(off[u]), "s"(g)
+                         : "memory");
+    }
+}
+
+// Waits until at most N of this wave's global memory loads (global -> LDS
+// included) are outstanding; they complete in issue order.
+template <int N = 0>
+__device__ __forceinline__ void dma_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(), whose
+// release side would wait for every outstanding load.  LDS written by the
+// loads above is ordered by dma_wait<N>() before the barrier; LDS reads are
+// complete once their values have been used.  The empty asm statements keep
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void tile_barrier() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
 }
 
 // Q fragments (B operand of S^T) for 32 rows; rowptr == nullptr gives zeros.
@@ -114,25 +173,49 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[8], const uint16_t* rowptr, 
     }
 }
 
-// S^T for the 64 keys of a tile and RB row blocks: sacc[rb][kb] covers keys
-// 32*kb .. 32*kb+31 of row block rb.
-template <int RB>
-__device__ __forceinline__ void scores(f32x16 (&sacc)[RB][2], const Tiles& t,
-                                       const bf16x8 (&qf)[RB][8], int lane) {
+// Per-lane LDS element offsets of the operand reads, the same for every tile:
+// kofs[s] is the K fragment of K-step s for key lane % 32 (add 32 keys for the
+// second key block), vofs[db] the transposing V read of dh block db (add
+// 32 kb + 16 s2 (+ 8) keys).
+struct ReadOffsets {
+    int kofs[8];
+    int vofs[4];
+};
+
+__device__ __forceinline__ ReadOffsets read_offsets(int lane) {
+    ReadOffsets r;
+    const int key = lane & 31;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int s = 0; s < 8; ++s) r.kofs[s] = key * kDh + 8 * k_slot(key, 2 * s + (lane >> 5));
+    // Supplier lane L of 16-lane group q addresses V[key0 + L/4][dh0 + 4 (L%4)]
+    // with key0 = 32 kb + 16 s2 + 4 (q / 2) (+ 8 for the upper four keys) and
+    // dh0 = 32 db + 16 (q % 2); the key's low two bits (L / 4) fix the slot
+    // swizzle, because key0 is a multiple of four.
+    const int q = lane >> 4;
+    const int L = lane & 15;
+    const int kr = 4 * (q >> 1) + (L >> 2);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = f32x16{};
-        const uint16_t* kr = &t.k[(32 * kb + (lane & 31)) * kKPitch + 8 * (lane >> 5)];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kr + 16 * s));
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-                sacc[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rb][s], sacc[rb][kb],
-                                                                       0, 0, 0);
-        }
+    for (int db = 0; db < 4; ++db) {
+        const int piece = 4 * db + 2 * (q & 1) + ((L & 3) >> 1);
+        r.vofs[db] = kr * kDh + 8 * v_slot(kr, piece) + 4 * (L & 1);
     }
+    return r;
+}
+
+// Compile-time loop: f(integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(static_cast<F&&>(f));
+    }
+}
+
+// K fragment (A operand of S^T) of K-step s for key block kb.
+__device__ __forceinline__ bf16x8 read_k(const uint16_t* kt, const ReadOffsets& ro, int kb,
+                                         int s) {
+    return __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const u32x4*>(kt + 32 * kb * kDh + ro.kofs[s]));
 }
 
 // Transposing LDS load of four keys of one dh column (see the file comment).
@@ -142,47 +225,75 @@ __device__ __forceinline__ bf16x4 read_vt4(const uint16_t* p) {
         (BD_LDS lds_bf16x4*)(const_cast<uint16_t*>(p)));
 }
 
-// bf16 P^T fragments of one tile from probabilities in score-accumulator
-// order: pf[rb][kb][s2] = p[rb][kb][8*s2 .. 8*s2+7].  The probabilities live
-// in their own registers, never in the MFMA accumulators: VALU writes into
-// registers that an MFMA chain also writes are avoided altogether.
-template <int RB>
-__device__ __forceinline__ void pack_p(bf16x8 (&pf)[RB][2][2], const float (&sacc)[RB][2][16]) {
+// V^T fragment (A operand of O^T) of dh block db, key block kb, K-step s2.
+__device__ __forceinline__ bf16x8 read_v(const uint16_t* vt, const ReadOffsets& ro, int db,
+                                         int kb, int s2) {
+    const uint16_t* vp = vt + (32 * kb + 16 * s2) * kDh + ro.vofs[db];
+    const bf16x4 lo = read_vt4(vp);
+    const bf16x4 hi = read_vt4(vp + 8 * kDh);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// S^T for the 64 keys of a tile: sacc[kb] covers keys 32*kb .. 32*kb+31.
+__device__ __forceinline__ void scores(f32x16 (&sacc)[2], const uint16_t* kt,
+                                       const bf16x8 (&qf)[8], const ReadOffsets& ro) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int s = 0; s < 8; ++s) {
+            const bf16x8 a = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(kt + 32 * kb * kDh + ro.kofs[s]));
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
+        }
+    }
+}
+
+// Probabilities of one tile, p = 2^(x * scale_log2 - mref) for the values x
+// in score-accumulator order, packed as bf16 P^T fragments,
+// pf[kb][s2] = p[kb][8*s2 .. 8*s2+7]; returns the sum of the rounded
+// probabilities of this lane (the values the P V product uses).  Each pair is
+// exponentiated, packed and summed at once, so the fp32 probabilities are
+// never all live.  They live in their own registers, never in the MFMA
+// accumulators: VALU writes into registers that an MFMA chain also writes are
+// avoided altogether.
+template <typename X>
+__device__ __forceinline__ float exp_pack(bf16x8 (&pf)[2][2], const X& x, float scale_log2,
+                                          float mref) {
+    const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+    float sum = 0.f;
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    pf[rb][kb][s2][e] = static_cast<__bf16>(sacc[rb][kb][8 * s2 + e]);
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const float p0 =
+                    __builtin_amdgcn_exp2f(fmaf(x[kb][8 * s2 + e], scale_log2, -mref));
+                const float p1 =
+                    __builtin_amdgcn_exp2f(fmaf(x[kb][8 * s2 + e + 1], scale_log2, -mref));
+                const bf16x2 two = {static_cast<__bf16>(p0), static_cast<__bf16>(p1)};
+                pf[kb][s2][e] = two[0];
+                pf[kb][s2][e + 1] = two[1];
+                sum = __builtin_amdgcn_fdot2_f32_bf16(two, one, sum, false);
+            }
+    return sum;
 }
 
 // O^T += V^T P^T for one tile.
-template <int RB>
-__device__ __forceinline__ void accumulate_pv(f32x16 (&oacc)[RB][4], const Tiles& t,
-                                              const bf16x8 (&pf)[RB][2][2], int lane) {
-    // Supplier lane L of 16-lane group q addresses V[key0 + L/4][dh0 + 4 (L%4)]
-    // with key0 = 32 kb + 16 s2 + 4 (q / 2) (+ 8 for the upper four keys) and
-    // dh0 = 32 db + 16 (q % 2).
-    const int q = lane >> 4;
-    const int L = lane & 15;
-    const uint16_t* vbase = &t.v[(4 * (q >> 1) + (L >> 2)) * kVPitch + 16 * (q & 1) + 4 * (L & 3)];
+__device__ __forceinline__ void accumulate_pv(f32x16 (&oacc)[4], const uint16_t* vt,
+                                              const bf16x8 (&pf)[2][2], const ReadOffsets& ro) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                const uint16_t* vp = vbase + (32 * kb + 16 * s2) * kVPitch + 32 * db;
+                const uint16_t* vp = vt + (32 * kb + 16 * s2) * kDh + ro.vofs[db];
                 const bf16x4 lo = read_vt4(vp);
-                const bf16x4 hi = read_vt4(vp + 8 * kVPitch);
+                const bf16x4 hi = read_vt4(vp + 8 * kDh);
                 const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-                    oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[rb][kb][s2],
-                                                                           oacc[rb][db], 0, 0, 0);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][s2], oacc[db], 0, 0, 0);
             }
 }
 

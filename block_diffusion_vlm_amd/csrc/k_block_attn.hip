@@ -46,7 +46,8 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int P, int cap, const uint64_t* __restrict__ mask, int Bq,
     int Hq, int Hkv, float scale_log2, void* __restrict__ ws, int nsplit, int kt) {
-    __shared__ __align__(16) Tiles tiles[2];
+    __shared__ __align__(16) uint16_t kbuf[2][kTile];
+    __shared__ __align__(16) uint16_t vbuf[2][kTile];
     const int split = blockIdx.x;
     const int g = blockIdx.y;
     const int lane = threadIdx.x & 63;
@@ -59,32 +60,46 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
     const int t_beg = split * kt;
     const int ntiles = (Nk + kBN - 1) / kBN;
     const int t_end = t_beg + kt < ntiles ? t_beg + kt : ntiles;
-
-    TileRegs<256> regs;
-    fetch_tile<256>(regs, kb, vb, kDh, t_beg * kBN, Nk);
+    unsigned koff[4], voff[4];
+    dma_offsets<4, false>(koff, kDh);
+    dma_offsets<4, true>(voff, kDh);
+    auto load = [&](int t, uint16_t* kd, uint16_t* vd) {
+        const int j0 = t * kBN;
+        const int n = Nk - j0 < kBN ? Nk - j0 : kBN;
+        if (n == kBN) {
+            dma_tile_full<4>(kd, kb + size_t(j0) * kDh, koff);
+            dma_tile_full<4>(vd, vb + size_t(j0) * kDh, voff);
+        } else {
+            dma_tile<4, false>(kd, kb + size_t(j0) * kDh, kDh, n);
+            dma_tile<4, true>(vd, vb + size_t(j0) * kDh, kDh, n);
+        }
+    };
+    load(t_beg, kbuf[0], vbuf[0]);
 
     // Query row of this lane: r -> (block query i, head g*group + r % group).
     const int r = blockIdx.z * kRowsPerWg + wave * 32 + (lane & 31);
     const bool row_ok = r < R;
     const int qi = row_ok ? r / group : 0;
     const int qh = g * group + (row_ok ? r % group : 0);
-    bf16x8 qf[1][8];
-    load_q(qf[0], row_ok ? q + (size_t(qi) * Hq + qh) * kDh : nullptr, lane);
+    bf16x8 qf[8];
+    load_q(qf, row_ok ? q + (size_t(qi) * Hq + qh) * kDh : nullptr, lane);
     const uint64_t mbits = row_ok ? mask[qi] : 0;
+    const ReadOffsets ro = read_offsets(lane);
 
-    store_tile<256>(tiles[0], regs);
-    __syncthreads();
+    dma_wait<0>();
+    tile_barrier();
 
     float m = -INFINITY, l = 0.f;
-    f32x16 oacc[1][4] = {};
-    for (int t = t_beg; t < t_end; ++t) {
+    f32x16 oacc[4] = {};
+    // One tile: the next tile's loads go into the other buffers.
+    auto step = [&](int t, const uint16_t* kcur, const uint16_t* vcur, uint16_t* knxt,
+                    uint16_t* vnxt) {
         const int j0 = t * kBN;
-        if (t + 1 < t_end) fetch_tile<256>(regs, kb, vb, kDh, j0 + kBN, Nk);
-        const Tiles& cur = tiles[(t - t_beg) & 1];
+        if (t + 1 < t_end) load(t + 1, knxt, vnxt);
 
-        f32x16 sacc[1][2];
-        scores<1>(sacc, cur, qf, lane);
-        float x[1][2][16];
+        f32x16 sacc[2];
+        scores(sacc, kcur, qf, ro);
+        float x[2][16];
         float mx = -INFINITY;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
@@ -95,34 +110,32 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
                 const bool in_block = (jb >= 0) & (j < Nk);
                 const bool bit = ((mbits >> (jb & 63)) & 1ull) != 0;
                 const bool vis = (j < P) | (in_block & bit);
-                x[0][kb2][e] = vis ? sacc[0][kb2][e] : -INFINITY;
-                mx = fmaxf(mx, x[0][kb2][e]);
+                x[kb2][e] = vis ? sacc[kb2][e] : -INFINITY;
+                mx = fmaxf(mx, x[kb2][e]);
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+        mx = fmaxf(mx, other_half(mx)) * scale_log2;
         const float mnew = fmaxf(m, mx);
         const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-        float ls = 0.f;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                x[0][kb2][e] = __builtin_amdgcn_exp2f(fmaf(x[0][kb2][e], scale_log2, -mref));
-                ls += x[0][kb2][e];
-            }
-        ls += __shfl_xor(ls, 32);
+        bf16x8 pf[2][2];
+        float ls = exp_pack(pf, x, scale_log2, mref);
+        ls += other_half(ls);
         const float alpha = __builtin_amdgcn_exp2f(m - mref);
         l = l * alpha + ls;
         m = mnew;
         if (__ballot(alpha != 1.f)) {
 #pragma unroll
-            for (int db = 0; db < 4; ++db) oacc[0][db] *= alpha;
+            for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
         }
-        bf16x8 pf[1][2][2];
-        pack_p<1>(pf, x);
-        accumulate_pv<1>(oacc, cur, pf, lane);
-
-        if (t + 1 < t_end) store_tile<256>(tiles[(t + 1 - t_beg) & 1], regs);
-        __syncthreads();
+        accumulate_pv(oacc, vcur, pf, ro);
+    };
+    for (int t = t_beg; t < t_end; t += 2) {
+        step(t, kbuf[0], vbuf[0], kbuf[1], vbuf[1]);
+        dma_wait<0>();
+        tile_barrier();
+        if (t + 1 == t_end) break;
+        step(t + 1, kbuf[1], vbuf[1], kbuf[0], vbuf[0]);
+        dma_wait<0>();
+        tile_barrier();
     }
 
     if (row_ok) {
@@ -139,8 +152,8 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
             for (int e4 = 0; e4 < 4; ++e4) {
                 const int dh = 32 * db + acc_row(4 * e4, lane);
                 *reinterpret_cast<f32x4*>(o + dh) =
-                    f32x4{oacc[0][db][4 * e4], oacc[0][db][4 * e4 + 1], oacc[0][db][4 * e4 + 2],
-                          oacc[0][db][4 * e4 + 3]};
+                    f32x4{oacc[db][4 * e4], oacc[db][4 * e4 + 1], oacc[db][4 * e4 + 2],
+                          oacc[db][4 * e4 + 3]};
             }
     }
 }

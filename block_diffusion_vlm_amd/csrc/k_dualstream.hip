@@ -8,13 +8,16 @@
 //   no clean token sees a noisy one.
 //
 // bf16 path: flash attention forward on v_mfma_f32_32x32x16_bf16.  A
-// workgroup owns 128 query rows of one head (4 waves x 32 rows) and streams
-// 64-key tiles of K and V^T through LDS with an online softmax.  The mask is
-// never materialised: for each query tile the visible key ranges follow in
-// closed form from the three rules, every tile outside them is skipped, tiles
-// that are visible for every (query, key) pair skip the per-element test,
-// and only tiles crossing a rule boundary evaluate it.  Query tiles are
-// launched heaviest first so that the long rows do not form a tail.
+// workgroup owns 128 query rows of one head (4 waves x 32 rows), two
+// workgroups share a CU, and 64-key tiles of K and V stream through LDS with
+// an online softmax.  The mask is never materialised: for each query tile the
+// visible key ranges follow in closed form from the three rules, every tile
+// outside them is skipped, tiles that are visible for every (query, key) pair
+// skip the per-element test, and only tiles crossing a rule boundary
+// evaluate it.  Query tiles are launched heaviest first so that the long
+// rows do not form a tail.
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace bd {
@@ -60,23 +63,6 @@ __host__ __device__ inline void key_ranges(const Geometry& G, int i0, int i1, in
     *a_end = ae;
 }
 
-// True when every (query, key) pair of the tile is visible.
-__device__ __forceinline__ bool tile_full(const Geometry& G, int i0, int i1, int j0, int j1) {
-    if (i1 > G.N) i1 = G.N;
-    if (j1 > G.N) return false;
-    if (i1 <= G.ctx) return j1 - 1 <= i0;                            // causal, below diagonal
-    if (i0 >= G.ctx) {
-        const int r0 = i0 - G.ctx, r1 = i1 - 1 - G.ctx;
-        if (j1 <= G.ctx) return j1 - 1 <= G.n_vis + r0;               // visual / clean text
-        if (j0 >= G.ctx) {                                            // noisy keys
-            const int b0 = r0 / G.block;
-            return b0 == r1 / G.block && (j0 - G.ctx) / G.block == b0 &&
-                   (j1 - 1 - G.ctx) / G.block == b0;
-        }
-    }
-    return false;
-}
-
 // Visibility of keys for one query row as two intervals: key j is visible
 // iff j <= lim or lo <= j < hi.  Clean row i: lim = i (C2C), no interval.
 // Noisy row r: lim = n_vis + r (every visual key, clean text up to r: N2C),
@@ -99,18 +85,26 @@ __device__ __forceinline__ RowVis row_vis(const Geometry& G, int i) {
     return v;
 }
 
-// WAVES waves per workgroup, each owning RB blocks of 32 query rows.  K/V
-// tiles are double-buffered in LDS; the next tile's global loads are issued
-// before the current tile is multiplied and land in the other buffer, so one
-// barrier per tile suffices.
-template <int WAVES, int RB, int OCC = 1>
-__global__ __launch_bounds__(WAVES * 64, OCC) void dualstream_bf16_kernel(
+// One wave per 32 query rows, WAVES waves per workgroup sharing the K/V
+// tiles, two waves per SIMD.  The scores of tile t+1 are computed while the
+// softmax of tile t runs: the score block of an iteration is laid out as 16
+// issue slots separated by scheduling barriers, each issuing one K fragment
+// read (two slots ahead of its use), one score MFMA and a share of the
+// softmax's vector work, so that the vector ALUs work while the MFMAs
+// execute; the P V MFMAs of tile t follow, with their V fragment reads issued
+// two slots ahead.  K runs one tile ahead of V: iteration t reads K(t+1) and
+// V(t) and loads K(t+2) and V(t+1) into the other halves of two double
+// buffers (complete tiles with per-lane offsets computed once); one barrier
+// per iteration separates the loads from their readers.
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 2) void dualstream_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, Geometry G, int H, float scale_log2,
     uint16_t* __restrict__ out, int nqt) {
-    constexpr int T = WAVES * 64;
-    constexpr int BM = WAVES * 32 * RB;
-    __shared__ __align__(16) Tiles tiles[2];
+    constexpr int BM = WAVES * 32;
+    constexpr int kAhead = 2;                        // fragment reads issued ahead
+    __shared__ __align__(16) uint16_t kbuf[2][kTile];
+    __shared__ __align__(16) uint16_t vbuf[2][kTile];
     const int h = blockIdx.x;
     // Later query tiles see more keys (causal context, then the visual prefix
     // plus clean text for the noisy stream), so tiles are issued last-first.
@@ -119,152 +113,217 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void dualstream_bf16_kernel(
     const int i1 = (i0 + BM < G.N) ? i0 + BM : G.N;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const size_t rs = size_t(H) * kDh;               // element stride between tokens
+    const int rs = H * kDh;                          // element stride between tokens
 
     int a_end, b_beg, b_end;
     key_ranges(G, i0, i1, &a_end, &b_beg, &b_end);
     const int na = (a_end + kBN - 1) / kBN;
     const int nb = b_end > b_beg ? (b_end - b_beg + kBN - 1) / kBN : 0;
     const int ntile = na + nb;
-    const uint16_t* kb = k + size_t(h) * kDh;
-    const uint16_t* vb = v + size_t(h) * kDh;
-    auto tile_range = [&](int t, int& j0, int& jend) {
-        if (t < na) {
-            j0 = t * kBN;
-            jend = a_end;
-        } else {
-            j0 = b_beg + (t - na) * kBN;
-            jend = b_end;
-        }
+    // A complete tile of range A is visible for every (query, key) pair when
+    // its last key is at most full_a: below the causal diagonal for clean
+    // rows, inside visual + clean text up to the first row for noisy rows.
+    // A complete tile of range B is when all rows lie in one noisy block
+    // (range B is then exactly that block's keys).
+    const int full_a = i1 <= G.ctx ? i0 : (i0 >= G.ctx ? G.n_vis + (i0 - G.ctx) : -1);
+    const bool full_b = i0 >= G.ctx && (i0 - G.ctx) / G.block == (i1 - 1 - G.ctx) / G.block;
+    const uint16_t* kh = k + size_t(h) * kDh;
+    const uint16_t* vh = v + size_t(h) * kDh;
+    auto tile_j0 = [&](int t) { return t < na ? t * kBN : b_beg + (t - na) * kBN; };
+    auto tile_n = [&](int t) {
+        const int n = (t < na ? a_end : b_end) - tile_j0(t);
+        return n < kBN ? n : kBN;
     };
+    unsigned koff[16 / WAVES], voff[16 / WAVES];
+    dma_offsets<WAVES, false>(koff, rs);
+    dma_offsets<WAVES, true>(voff, rs);
+    // Tiles past the last one are replaced by the last one (their buffers are
+    // not read).
+    auto load_k = [&](int t, uint16_t* dst) {
+        t = t < ntile ? t : ntile - 1;
+        const int n = tile_n(t);
+        if (n == kBN)
+            dma_tile_full<WAVES>(dst, kh + size_t(tile_j0(t)) * rs, koff);
+        else
+            dma_tile<WAVES, false>(dst, kh + size_t(tile_j0(t)) * rs, rs, n);
+    };
+    auto load_v = [&](int t, uint16_t* dst) {
+        t = t < ntile ? t : ntile - 1;
+        const int n = tile_n(t);
+        if (n == kBN)
+            dma_tile_full<WAVES>(dst, vh + size_t(tile_j0(t)) * rs, voff);
+        else
+            dma_tile<WAVES, true>(dst, vh + size_t(tile_j0(t)) * rs, rs, n);
+    };
+    if (ntile <= 0) return;                          // every row sees at least key 0
 
-    TileRegs<T> regs;
-    if (ntile > 0) {
-        int j0, jend;
-        tile_range(0, j0, jend);
-        fetch_tile<T>(regs, kb, vb, rs, j0, jend);
-    }
-
-    bf16x8 qf[RB][8];
-    RowVis rv[RB];
-    int rows[RB];
+    load_k(0, kbuf[0]);
+    load_k(1, kbuf[1]);
+    load_v(0, vbuf[0]);
+    const ReadOffsets ro = read_offsets(lane);
+    const int row = i0 + wave * 32 + (lane & 31);
+    const bool row_ok = row < G.N;
+    bf16x8 qf[8];
+    load_q(qf, row_ok ? q + size_t(row) * rs + size_t(h) * kDh : nullptr, lane);
+    const RowVis rv = row_ok ? row_vis(G, row) : RowVis{-1, 0, 0};
+    float m = -INFINITY, l = 0.f;
+    f32x16 oacc[4];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int row = i0 + (wave * RB + rb) * 32 + (lane & 31);
-        rows[rb] = row;
-        const bool ok = row < G.N;
-        load_q(qf[rb], ok ? q + size_t(row) * rs + size_t(h) * kDh : nullptr, lane);
-        rv[rb] = ok ? row_vis(G, row) : RowVis{-1, 0, 0};
-    }
+    for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
+    dma_wait<0>();
+    tile_barrier();
+    f32x16 sA[2], sB[2];
+    scores(sA, kbuf[0], qf, ro);
+    tile_barrier();           // every wave has read K(0) before K(2) replaces it
 
-    if (ntile > 0) store_tile<T>(tiles[0], regs);
-    __syncthreads();
-
-    float m[RB], l[RB];
-    f32x16 oacc[RB][4];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        m[rb] = -INFINITY;
-        l[rb] = 0.f;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) oacc[rb][db] = f32x16{};
-    }
-
-    for (int t = 0; t < ntile; ++t) {
-        int j0, jend;
-        tile_range(t, j0, jend);
-        const int j1 = j0 + kBN < jend ? j0 + kBN : jend;
-        if (t + 1 < ntile) {
-            int n0, nend;
-            tile_range(t + 1, n0, nend);
-            fetch_tile<T>(regs, kb, vb, rs, n0, nend);
-        }
-        const Tiles& cur = tiles[t & 1];
-
-        f32x16 sacc[RB][2];
-        scores<RB>(sacc, cur, qf, lane);
-
-        const bool full = (j1 - j0 == kBN) && tile_full(G, i0, i1, j0, j1);
+    // Score block of iteration t: S(t+1) from kread into snext, with the
+    // softmax of tile t (scores s) into the bf16 P^T fragments p.  MASKED
+    // evaluates the visibility rules per element (tiles not visible as a
+    // whole).  Slots [0, kMax) take the row maximum, slot kMax decides the
+    // reference maximum, the remaining slots exponentiate pairs of elements,
+    // pack them to bf16 and add them to the row sum (four partial maxima and
+    // sums keep the reduction chains short).  A row's reference maximum m only
+    // moves when the new maximum exceeds it by more than kLazy (log2 units of
+    // the scaled score): until then probabilities stay below 2^kLazy, and
+    // skipping the rescale of the running output leaves the final normalised
+    // result unchanged.
+    auto score_block = [&](auto masked_tag, int j0, int j1, const f32x16 (&s)[2],
+                           f32x16 (&snext)[2], const uint16_t* kread, bf16x8 (&p)[2][2],
+                           float& mnew, float& mref, float& ls, bool& move) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        constexpr int kMax = MASKED ? 4 : 2;
+        constexpr int kExp = 16 - kMax - 1;
+        auto rk = [&](int i) { return read_k(kread, ro, i & 1, i >> 1); };
+        bf16x8 ka[16];
+        static_for<0, kAhead>([&](auto I) { ka[I] = rk(I); });
         // Key of accumulator register e of this lane: jl + 8 (e / 4) + e % 4.
         const int jl = j0 + 4 * (lane >> 5);
-        float x[RB][2][16];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            if (full) {
-#pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) x[rb][kb2][e] = sacc[rb][kb2][e];
+        const int lim = rv.lim < j1 - 1 ? rv.lim : j1 - 1;
+        const int hi = rv.hi < j1 ? rv.hi : j1;
+        auto val = [&](int e) -> float {
+            if constexpr (MASKED) {
+                const int jj = jl + 32 * (e >> 4) + 8 * ((e & 15) >> 2) + (e & 3);
+                const bool vis = (jj <= lim) | ((jj >= rv.lo) & (jj < hi));
+                return vis ? s[e >> 4][e & 15] : -INFINITY;
             } else {
-                const int lim = rv[rb].lim < j1 - 1 ? rv[rb].lim : j1 - 1;
-                const int hi = rv[rb].hi < j1 ? rv[rb].hi : j1;
-#pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int j = jl + 32 * kb2 + 8 * (e >> 2) + (e & 3);
-                        const bool vis = (j <= lim) | ((j >= rv[rb].lo) & (j < hi));
-                        x[rb][kb2][e] = vis ? sacc[rb][kb2][e] : -INFINITY;
-                    }
+                return s[e >> 4][e & 15];
             }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, x[rb][kb2][e]);
-            // Raw-score maximum, then everything in log2 units of the scaled
-            // score.  The row's reference maximum m only moves when the new
-            // maximum exceeds it by more than kLazy: until then probabilities
-            // 2^(scale_log2 * s - m) stay below 2^kLazy, and skipping the
-            // rescale of the running output leaves the final normalised
-            // result unchanged.
-            mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
-            const bool move = mx > m[rb] + kLazy;
-            const float mnew = move ? mx : m[rb];
-            const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-            float ls = 0.f;
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    x[rb][kb2][e] = __builtin_amdgcn_exp2f(fmaf(x[rb][kb2][e], scale_log2, -mref));
-                    ls += x[rb][kb2][e];
+        };
+        float mxp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        float lsp[4] = {0.f, 0.f, 0.f, 0.f};
+        const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+        static_for<0, 16>([&](auto Ic) {
+            constexpr int i = Ic;
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (i + kAhead < 16) ka[i + kAhead] = rk(i + kAhead);
+            // key blocks alternate, so consecutive MFMAs are independent
+            snext[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                ka[i], qf[i >> 1], i < 2 ? f32x16{} : snext[i & 1], 0, 0, 0);
+            if constexpr (i < kMax) {
+                constexpr int per = 32 / kMax;
+                static_for<i * per, (i + 1) * per>(
+                    [&](auto Ec) { mxp[int(Ec) & 3] = fmaxf(mxp[int(Ec) & 3], val(Ec)); });
+            } else if constexpr (i == kMax) {
+                float mx = fmaxf(fmaxf(mxp[0], mxp[1]), fmaxf(mxp[2], mxp[3]));
+                mx = fmaxf(mx, other_half(mx)) * scale_log2;
+                move = mx > m + kLazy;
+                mnew = move ? mx : m;
+                mref = (mnew == -INFINITY) ? 0.f : mnew;
+            } else {
+                constexpr int q0 = i - kMax - 1;
+                constexpr int p_beg = (q0 * 16) / kExp;
+                constexpr int p_end = ((q0 + 1) * 16) / kExp;
+                float pe[32];
+                static_for<2 * p_beg, 2 * p_end>([&](auto Ec) {
+                    pe[int(Ec)] = __builtin_amdgcn_exp2f(fmaf(val(Ec), scale_log2, -mref));
+                });
+                static_for<p_beg, p_end>([&](auto Pc) {
+                    constexpr int e = 2 * int(Pc);
+                    const bf16x2 two = {static_cast<__bf16>(pe[e]),
+                                        static_cast<__bf16>(pe[e + 1])};
+                    constexpr int kb = e >> 4, s2 = (e & 15) >> 3, eo = e & 7;
+                    p[kb][s2][eo] = two[0];
+                    p[kb][s2][eo + 1] = two[1];
+                    lsp[int(Pc) & 3] =
+                        __builtin_amdgcn_fdot2_f32_bf16(two, one, lsp[int(Pc) & 3], false);
+                });
+                if constexpr (i == 15) {
+                    ls = (lsp[0] + lsp[1]) + (lsp[2] + lsp[3]);
+                    ls += other_half(ls);
                 }
-            ls += __shfl_xor(ls, 32);
-            if (__ballot(move)) {
-                const float alpha = __builtin_amdgcn_exp2f(m[rb] - mref);
-                l[rb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < 4; ++db) oacc[rb][db] *= alpha;
             }
-            l[rb] += ls;
-            m[rb] = mnew;
+        });
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // P V of one tile from vread: 16 issue slots, one V fragment read (two
+    // slots ahead of its use) and one MFMA each; dh blocks alternate.
+    auto pv_block = [&](const uint16_t* vread, const bf16x8 (&p)[2][2]) {
+        auto rvv = [&](int j) { return read_v(vread, ro, j & 3, j >> 3, (j >> 2) & 1); };
+        bf16x8 va[16];
+        static_for<0, kAhead>([&](auto J) { va[J] = rvv(J); });
+        static_for<0, 16>([&](auto Jc) {
+            constexpr int j = Jc;
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (j + kAhead < 16) va[j + kAhead] = rvv(j + kAhead);
+            oacc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], p[j >> 3][(j >> 2) & 1],
+                                                                  oacc[j & 3], 0, 0, 0);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // Iteration t: reads K(t+1) and V(t); loads K(t+2) where K(t) was and
+    // V(t+1) where V(t-1) was.
+    auto step = [&](int t, const f32x16 (&s)[2], f32x16 (&snext)[2]) {
+        load_k(t + 2, kbuf[t & 1]);
+        load_v(t + 1, vbuf[(t + 1) & 1]);
+        const int j0 = tile_j0(t);
+        const int n = tile_n(t);
+        const bool full = n == kBN && (t < na ? j0 + kBN - 1 <= full_a : full_b);
+        bf16x8 p[2][2];
+        float mnew, mref, ls;
+        bool move;
+        if (full)
+            score_block(std::false_type{}, j0, j0 + n, s, snext, kbuf[(t + 1) & 1], p, mnew,
+                        mref, ls, move);
+        else
+            score_block(std::true_type{}, j0, j0 + n, s, snext, kbuf[(t + 1) & 1], p, mnew,
+                        mref, ls, move);
+        // Rescale what tiles 0 .. t-1 accumulated when the reference maximum
+        // of a row moved (alpha is 1 for the others).
+        if (__ballot(move)) {
+            const float alpha = __builtin_amdgcn_exp2f(m - mref);
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
         }
-        bf16x8 pf[RB][2][2];
-        pack_p<RB>(pf, x);
-        accumulate_pv<RB>(oacc, cur, pf, lane);
-
-        if (t + 1 < ntile) store_tile<T>(tiles[(t + 1) & 1], regs);
-        __syncthreads();
+        l += ls;
+        m = mnew;
+        pv_block(vbuf[t & 1], p);
+    };
+    int t = 0;
+    for (;;) {
+        step(t, sA, sB);
+        dma_wait<0>();
+        tile_barrier();
+        if (++t == ntile) break;
+        step(t, sB, sA);
+        dma_wait<0>();
+        tile_barrier();
+        if (++t == ntile) break;
     }
 
+    if (!row_ok) return;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* orow = out + size_t(row) * rs + size_t(h) * kDh;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int row = rows[rb];
-        if (row >= G.N) continue;
-        const float inv = l[rb] > 0.f ? 1.f / l[rb] : 0.f;
-        uint16_t* orow = out + size_t(row) * rs + size_t(h) * kDh;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const int d = 32 * db + acc_row(4 * e4, lane);
+            bf16x4 w;
 #pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                const int dh = 32 * db + acc_row(4 * e4, lane);
-                bf16x4 w;
-#pragma unroll
-                for (int x = 0; x < 4; ++x) w[x] = static_cast<__bf16>(oacc[rb][db][4 * e4 + x] * inv);
-                *reinterpret_cast<bf16x4*>(orow + dh) = w;
-            }
-    }
+            for (int x = 0; x < 4; ++x) w[x] = static_cast<__bf16>(oacc[db][4 * e4 + x] * inv);
+            *reinterpret_cast<bf16x4*>(orow + d) = w;
+        }
 }
 
 // float32 path: one wave per (token, head) row, online softmax over the
@@ -320,27 +379,18 @@ __global__ __launch_bounds__(64) void dualstream_f32_kernel(const float* __restr
 
 }  // namespace
 
-#ifndef BD_DS_WAVES
-#define BD_DS_WAVES 4
-#endif
-#ifndef BD_DS_RB
-#define BD_DS_RB 1
-#endif
-#ifndef BD_DS_OCC
-#define BD_DS_OCC 2
-#endif
-
 hipError_t launch_dualstream_bf16(const void* q, const void* k, const void* v, int n_vis,
                                   int n_txt, int block, int H, float scale, void* out,
                                   hipStream_t st) {
-    constexpr int BM = BD_DS_WAVES * 32 * BD_DS_RB;
+    constexpr int kWaves = 4;
+    constexpr int BM = kWaves * 32;
     Geometry G{n_vis, n_txt, n_vis + n_txt, n_vis + 2 * n_txt, block};
     const int nqt = (G.N + BM - 1) / BM;
     const dim3 grid(H, nqt);
-    hipLaunchKernelGGL((dualstream_bf16_kernel<BD_DS_WAVES, BD_DS_RB, BD_DS_OCC>), grid,
-                       dim3(BD_DS_WAVES * 64), 0, st, static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), G, H,
-                       scale * kLog2e, static_cast<uint16_t*>(out), nqt);
+    hipLaunchKernelGGL(dualstream_bf16_kernel<kWaves>, grid, dim3(kWaves * 64), 0, st,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), G, H, scale * kLog2e,
+                       static_cast<uint16_t*>(out), nqt);
     return hipGetLastError();
 }
 
