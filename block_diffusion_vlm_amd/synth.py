@@ -23,7 +23,7 @@ from __future__ import annotations
 import numpy as np
 
 BASE_SEED = 20261203
-N_CONFIGS = 5
+N_CONFIGS = 6
 
 
 # ---------------------------------------------------------------------------
@@ -31,7 +31,7 @@ N_CONFIGS = 5
 # ---------------------------------------------------------------------------
 
 def config_rng(cfg: int, seed: int | None = None) -> np.random.Generator:
-    """PCG64 stream for workload ``cfg`` (1..5): child ``cfg-1`` of
+    """PCG64 stream for workload ``cfg`` (1..6): child ``cfg-1`` of
     SeedSequence(seed or BASE_SEED)."""
     ss = np.random.SeedSequence(BASE_SEED if seed is None else seed)
     return np.random.Generator(np.random.PCG64(ss.spawn(N_CONFIGS)[cfg - 1]))
@@ -81,10 +81,12 @@ def normal_bf16(rng, shape, std=1.0, trunc=None, chunk_rows=8192) -> np.ndarray:
 # Hidden-state planting for the LM head
 # ---------------------------------------------------------------------------
 
-def plant_hidden(rng, W_bits, targets, target_conf, sigma_w) -> np.ndarray:
+def plant_hidden(rng, W_bits, targets, target_conf, sigma_w, row=None) -> np.ndarray:
     """Hidden rows h_i = e_i + alpha_i * u_i, where u_i is the unit direction
     of the (bf16-rounded) weight row of target token t_i and e_i ~ N(0, I) is
-    drawn and then made orthogonal to u_i.
+    drawn and then made orthogonal to u_i.  ``row(t)``, when given, returns
+    the float64 weight row of token t instead (for weights stored in another
+    format; W_bits then only supplies the shape).
 
     alpha_i comes from a statistical model of the weights, not from the
     logits: with W entries i.i.d. N(0, sigma_w^2), the target logit is
@@ -101,7 +103,7 @@ def plant_hidden(rng, W_bits, targets, target_conf, sigma_w) -> np.ndarray:
     out = np.empty((targets.size, d), dtype=np.float32)
     s2 = float(sigma_w) ** 2
     for i, t in enumerate(targets):
-        w = bf16_to_f64(W_bits[int(t)])
+        w = bf16_to_f64(W_bits[int(t)]) if row is None else row(int(t))
         nw = float(np.sqrt(w @ w))
         u = w / nw
         e = rng.standard_normal(d)
@@ -111,6 +113,41 @@ def plant_hidden(rng, W_bits, targets, target_conf, sigma_w) -> np.ndarray:
         disc = nw * nw - 2.0 * s2 * C
         alpha = (nw - np.sqrt(max(disc, 0.0))) / s2 if s2 > 0 else C / nw
         out[i] = (e + alpha * u).astype(np.float32)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# FP8 weights
+# ---------------------------------------------------------------------------
+
+E4M3_CODE_STD = 112.0   # code-domain std of the weights: 4 std = 448, the largest E4M3 value
+
+
+def e4m3_codes(x) -> np.ndarray:
+    """float32 -> OCP E4M3 codes through torch's float8_e4m3fn cast (round to
+    nearest even); the inputs stay within +-448."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def e4m3_row_values(codes) -> np.ndarray:
+    """E4M3 codes -> float64 values through torch's float8_e4m3fn type (used
+    to plant hidden states against the stored weights)."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(
+        torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def normal_e4m3(rng, shape, chunk_rows=8192) -> np.ndarray:
+    """E4M3 codes of 112 x N(0, 1) truncated to |x| <= 4 (so that every value
+    is within the format's range), generated in row chunks."""
+    shape = tuple(shape)
+    out = np.empty(shape, dtype=np.uint8)
+    for s in range(0, shape[0], chunk_rows):
+        e = min(shape[0], s + chunk_rows)
+        x = normal(rng, (e - s,) + shape[1:], 1.0, trunc=4.0) * np.float32(E4M3_CODE_STD)
+        out[s:e] = e4m3_codes(x)
     return out
 
 
@@ -189,6 +226,42 @@ def qwen_decode(seed: int | None = None, B=16, n_vis=1024, n_prompt=256, Hq=16, 
         "k_cache": normal_bf16(rng, (Hkv * cap, dh)).reshape(Hkv, cap, dh),
         "v_cache": normal_bf16(rng, (Hkv * cap, dh), trunc=4.0).reshape(Hkv, cap, dh),
         "W": W, "h": h, "targets": t.astype(np.int32), "target_conf": c, "planted_commit": z,
+        "masked": masked, "tokens": tokens,
+    }
+
+
+def qwen_decode_fp8(seed: int | None = None, B=16, n_vis=1024, n_prompt=256, Hq=16, Hkv=2,
+                    dh=128, d=2048, V=151936, p_commit=0.4, sigma_w=0.02,
+                    scale_spread=0.1) -> dict:
+    """The decode step of ``qwen_decode`` with an FP8 (E4M3, W8A8) LM head.
+    W is stored as E4M3 codes of 112 x N(0,1) (truncated at 4 std) with one
+    float32 scale per vocabulary row, w_scale[v] = sigma_w / 112 x U(1 -
+    spread, 1 + spread), so that the stored weights stand for N(0, sigma_w^2)
+    entries with a per-channel spread.  Hidden rows (bf16) are planted
+    against the stored (decoded and scaled) weight rows as in qwen_decode;
+    the attention inputs and the block state are drawn the same way."""
+    rng = config_rng(6, seed)
+    P = n_vis + n_prompt
+    cap = P + B
+    Wq = normal_e4m3(rng, (V, d))
+    w_scale = (np.float32(sigma_w / E4M3_CODE_STD)
+               * rng.uniform(1 - scale_spread, 1 + scale_spread, V).astype(np.float32))
+    t = rng.integers(0, V, B)
+    c, z = _commit_band_conf(rng, B, p_commit)
+    h = bf16_bits(plant_hidden(rng, Wq, t, c, sigma_w,
+                               row=lambda v: e4m3_row_values(Wq[v]) * float(w_scale[v])))
+    masked = np.ones(B, np.uint8)
+    masked[0] = 0
+    tokens = np.zeros(B, np.int32)
+    tokens[0] = int(rng.integers(0, V))
+    return {
+        "dtype": "fp8", "B": B, "P": P, "n_vis": n_vis, "n_prompt": n_prompt, "cap": cap,
+        "Hq": Hq, "Hkv": Hkv, "dh": dh, "d": d, "V": V, "tau": 0.9,
+        "q": normal_bf16(rng, (B, Hq, dh)),
+        "k_cache": normal_bf16(rng, (Hkv * cap, dh)).reshape(Hkv, cap, dh),
+        "v_cache": normal_bf16(rng, (Hkv * cap, dh), trunc=4.0).reshape(Hkv, cap, dh),
+        "W": Wq, "w_scale": w_scale.astype(np.float32), "h": h,
+        "targets": t.astype(np.int32), "target_conf": c, "planted_commit": z,
         "masked": masked, "tokens": tokens,
     }
 

@@ -17,6 +17,7 @@ Sources (web pages on the method; cited by page and section):
          - §2.3.1: self-speculative decoding, longest verified prefix kept and
            the KV cache truncated; linear (two forwards) and quadratic
            (one forward, O(B^2)) variants.
+         - §2.3.2: the fastest configuration adds FP8 SmoothQuant W8A8.
          - §4.1: recommended block_size 16 and denoising threshold 0.9.
   [TH]   Fast-dVLM article (itsolotime.com, Thai), §4.1 "Causal context
          attention": noisy tokens attend bidirectionally inside their block and
@@ -50,9 +51,16 @@ design notes of the repository):
       see all of the draft half.  Both halves see the whole prefix.
   R11 Certificate order: stable sort by anchor confidence, descending, lower
       index first on ties.
+  R12 FP8 means OCP E4M3 for weights and activations (W8A8), float32
+      accumulation, one float32 scale per vocabulary row of W.
+  R13 Activations are quantized per position with the scale amax/448 (the
+      row maximum maps onto the largest E4M3 value), in float32, rounding to
+      nearest with ties to even.
 
 Every function below takes float64 (or integer) arrays and returns new arrays;
 bfloat16 inputs are passed as raw uint16 bit patterns and widened exactly.
+The FP8 functions follow the OCP 8-bit floating point specification (OFP8)
+for the E4M3 format; their quantization step is taken in float32 (R13).
 """
 
 from __future__ import annotations
@@ -62,7 +70,8 @@ import numpy as np
 __all__ = [
     "widen", "mask_n2n", "mask_n2c", "mask_c2c", "dualstream_mask",
     "intra_block_mask", "masked_attention", "block_attn", "dualstream_attn",
-    "lm_logits", "lmhead_conf", "commit", "spec_accept", "cert_scan",
+    "lm_logits", "conf_argmax", "lmhead_conf", "E4M3_MAX", "e4m3_decode", "e4m3_encode",
+    "quant_fp8_rows", "lm_logits_fp8", "lmhead_conf_fp8", "commit", "spec_accept", "cert_scan",
     "decode_step", "linear_spec_step", "fused_spec_step",
 ]
 
@@ -234,14 +243,120 @@ def lm_logits(h, W, chunk: int = 16384) -> np.ndarray:
     return out
 
 
-def lmhead_conf(h, W):
-    """Per position: argmax token (lowest index on ties, R6) and confidence =
-    the largest softmax probability = 1 / sum_v exp(l_v - max l)."""
-    logits = lm_logits(h, W)
+def conf_argmax(logits):
+    """Per row: argmax token (lowest index on ties, R6) and confidence = the
+    largest softmax probability = 1 / sum_v exp(l_v - max l)."""
     m = logits.max(axis=1)
     a = np.argmax(logits, axis=1)          # numpy returns the first maximum
     s = np.exp(logits - m[:, None]).sum(axis=1)
     return 1.0 / s, a.astype(np.int64)
+
+
+def lmhead_conf(h, W):
+    """Confidence and argmax of the logits h W^T (see conf_argmax)."""
+    return conf_argmax(lm_logits(h, W))
+
+
+# ---------------------------------------------------------------------------
+# FP8 (W8A8) LM head  [OV §2.3.2: FP8 SmoothQuant W8A8 in the fastest
+# configuration; OV §4.1 quant_mode fp8]
+#
+# Number format: OCP 8-bit floating point (OFP8) E4M3.  Bit 7 is the sign,
+# bits 6..3 a biased exponent (bias 7), bits 2..0 the mantissa.  Exponent
+# field 0 encodes subnormals (m/8) 2^-6; the all-ones pattern S.1111.111 is
+# NaN; every other code is (1 + m/8) 2^(e-7).  No infinities; the largest
+# finite magnitude is 448.
+#
+# W8A8 (R12, R13): every vocabulary row of W is stored as E4M3 codes with one
+# float32 scale (per-output-channel weight quantization, done offline); the
+# hidden states are quantized per position at run time (per-token dynamic
+# activation quantization).  SmoothQuant's smoothing factors are folded into
+# the weights and the preceding layer offline, so they do not appear here.
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Exact value of E4M3 codes as float64 (NaN for S.1111.111)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (c & 7 == 7), np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+_E4M3_POS = None
+
+
+def _e4m3_positive_values() -> np.ndarray:
+    """Values of codes 0x00..0x7E (every non-negative finite E4M3 value), which
+    increase with the code."""
+    global _E4M3_POS
+    if _E4M3_POS is None:
+        _E4M3_POS = e4m3_decode(np.arange(0x7F))
+    return _E4M3_POS
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """Round finite values with |y| <= 448 to the nearest E4M3 value, ties to
+    the even code (mantissa bit 0 clear).  The sign bit is taken from y, so a
+    negative value that rounds to zero (and -0.0) gives 0x80."""
+    y = np.asarray(y, dtype=np.float64)
+    if not (np.isfinite(y).all() and (np.abs(y) <= E4M3_MAX).all()):
+        raise ValueError("e4m3_encode needs finite inputs with |y| <= 448")
+    tab = _e4m3_positive_values()
+    a = np.abs(y)
+    hi = np.minimum(np.searchsorted(tab, a, side="left"), tab.size - 1)   # tab[hi] >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - tab[lo]
+    d_hi = tab[hi] - a
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(take_hi, hi, lo)
+    return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def quant_fp8_rows(x):
+    """Per-row dynamic quantization to E4M3 (R13).  The steps are taken in
+    float32, the precision in which the kernels take the same rounding
+    decisions:  amax = max_k |x_k|;  r = 448 / amax and s = amax / 448, each
+    rounded to float32 (r = s = 1 for an all-zero row);  code_k = the E4M3
+    rounding of fl32(x_k * r), clamped to [-448, 448] first (the product can
+    exceed 448 by an ulp).  Then s * decode(code_k) ~ x_k.
+    x: [R][d] bfloat16 bits (uint16) or float32.  Returns (codes uint8 [R][d],
+    s float32 [R])."""
+    x = np.asarray(x)
+    x32 = widen(x).astype(np.float32) if x.dtype == np.uint16 else x.astype(np.float32)
+    amax = np.abs(x32).max(axis=1)
+    nz = amax > 0
+    safe = np.where(nz, amax, np.float32(1))
+    r = np.where(nz, np.float32(E4M3_MAX) / safe, np.float32(1)).astype(np.float32)
+    s = np.where(nz, safe / np.float32(E4M3_MAX), np.float32(1)).astype(np.float32)
+    y = (x32 * r[:, None]).astype(np.float32)
+    y = np.clip(y, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    return e4m3_encode(y.astype(np.float64)), s
+
+
+def lm_logits_fp8(h, Wq, w_scale, chunk: int = 16384) -> np.ndarray:
+    """W8A8 logits in float64: with (qh, sh) = quant_fp8_rows(h),
+        logits[b, v] = sh[b] * w_scale[v] * sum_k dec(qh[b, k]) dec(Wq[v, k]).
+    Wq: [V][d] E4M3 codes (uint8), w_scale: [V] float32."""
+    qh, sh = quant_fp8_rows(h)
+    A = e4m3_decode(qh)
+    Wq = np.asarray(Wq)
+    ws = np.asarray(w_scale, dtype=np.float64)
+    V = Wq.shape[0]
+    out = np.empty((A.shape[0], V))
+    for s in range(0, V, chunk):
+        dot = A @ e4m3_decode(Wq[s:s + chunk]).T
+        out[:, s:s + chunk] = dot * sh.astype(np.float64)[:, None] * ws[None, s:s + chunk]
+    return out
+
+
+def lmhead_conf_fp8(h, Wq, w_scale):
+    """Confidence and argmax of the W8A8 logits (see lm_logits_fp8)."""
+    return conf_argmax(lm_logits_fp8(h, Wq, w_scale))
 
 
 # ---------------------------------------------------------------------------
@@ -302,14 +417,16 @@ def cert_scan(anchor_conf, anchor_tok, text_tok, k: int):
 # Compositions
 # ---------------------------------------------------------------------------
 
-def decode_step(q, k_cache, v_cache, P, h, W, masked, tokens, tau, kind="bidir"):
+def decode_step(q, k_cache, v_cache, P, h, W, masked, tokens, tau, kind="bidir",
+                w_scale=None):
     """One threshold (MDM) block-decode step: block attention over the prefix,
     LM-head confidence, commit.  The attention output and the LM-head input are
     separate tensors because the remaining transformer layers sit between them.
+    With ``w_scale`` given, W holds E4M3 codes and the LM head is the W8A8 one.
     [OV §1.2, §4.1]"""
     bq = q.shape[0]
     o = block_attn(q, k_cache, v_cache, P, intra_block_mask(kind, bq))
-    conf, a = lmhead_conf(h, W)
+    conf, a = lmhead_conf(h, W) if w_scale is None else lmhead_conf_fp8(h, W, w_scale)
     m2, t2, n = commit(conf, a, masked, tokens, tau)
     return {"attn": o, "conf": conf, "argmax": a, "masked": m2, "tokens": t2, "n_committed": n}
 

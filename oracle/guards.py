@@ -10,15 +10,16 @@ from __future__ import annotations
 
 import numpy as np
 
-from .bdiff_oracle import lm_logits
+from .bdiff_oracle import lm_logits, lm_logits_fp8
 
 GAP_MIN = 1e-2
 TAU_DIST_MIN = 1e-3
 
 
-def lmhead_margins(h, W, tau=None):
-    """Return (top-2 logit gap per row, |conf - tau| per row or None)."""
-    logits = lm_logits(h, W)
+def lmhead_margins(h, W, tau=None, w_scale=None):
+    """Return (top-2 logit gap per row, |conf - tau| per row or None).  With
+    ``w_scale`` given, W holds E4M3 codes and the logits are the W8A8 ones."""
+    logits = lm_logits(h, W) if w_scale is None else lm_logits_fp8(h, W, w_scale)
     top2 = np.sort(logits, axis=1)[:, -2:]
     gap = top2[:, 1] - top2[:, 0]
     if tau is None:
@@ -27,8 +28,8 @@ def lmhead_margins(h, W, tau=None):
     return gap, np.abs(conf - tau)
 
 
-def lmhead_guarded(h, W, tau=None) -> bool:
-    gap, dist = lmhead_margins(h, W, tau)
+def lmhead_guarded(h, W, tau=None, w_scale=None) -> bool:
+    gap, dist = lmhead_margins(h, W, tau, w_scale)
     ok = bool((gap > GAP_MIN).all())
     if dist is not None:
         ok = ok and bool((dist >= TAU_DIST_MIN).all())

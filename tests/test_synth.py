@@ -68,3 +68,27 @@ def test_full_size_spec_guards_hold(which):
     for h in hs:
         gap, _ = lmhead_margins(h, r["W"])
         assert gap.min() > 1e-2
+
+
+def test_fp8_weights_format_and_determinism():
+    a = synth.qwen_decode_fp8(V=3000, d=256)
+    b = synth.qwen_decode_fp8(V=3000, d=256)
+    assert np.array_equal(a["W"], b["W"]) and np.array_equal(a["h"], b["h"])
+    assert a["W"].dtype == np.uint8 and a["W"].shape == (3000, 256)
+    assert not ((a["W"] & 0x7F) == 0x7F).any()             # no NaN codes
+    assert a["w_scale"].dtype == np.float32 and (a["w_scale"] > 0).all()
+    ref = torch.from_numpy(np.array([1.0, -3.3, 447.0, 0.01], np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(synth.e4m3_codes(np.array([1.0, -3.3, 447.0, 0.01])), ref)
+    # the stored weights stand for N(0, sigma_w^2) entries
+    w = synth.e4m3_row_values(a["W"]) * a["w_scale"][:, None]
+    assert abs(w.std() / 0.02 - 1) < 0.05
+
+
+def test_full_size_fp8_decode_guards_hold():
+    r = synth.qwen_decode_fp8()
+    gap, dist = lmhead_margins(r["h"], r["W"], r["tau"], w_scale=r["w_scale"])
+    assert gap.min() > 1e-2 and dist.min() >= 1e-3
+    conf, a = oracle.lmhead_conf_fp8(r["h"], r["W"], r["w_scale"])
+    assert np.array_equal(a, r["targets"])
+    assert 0 < (conf[1:] > r["tau"]).sum() < 15
