@@ -85,6 +85,52 @@ def traffic_from_profile(kernel_hash: str):
     return d.get("hbm_bytes_per_call")
 
 
+def step_bytes(inp):
+    """Algorithmic bytes (each byte the step must touch once) of the LM head
+    and of the whole decode step.  FP8 weights take one byte per entry plus
+    one float32 scale per vocabulary row."""
+    B, P, Hq, Hkv, dh, d, V = (inp[k] for k in ("B", "P", "Hq", "Hkv", "dh", "d", "V"))
+    b_W = V * d + 4 * V if inp["dtype"] == "fp8" else V * d * 2
+    b_lm = b_W + B * d * 2 + B * 8
+    b_kv = 2 * Hkv * (P + B) * dh * 2
+    b_attn = b_kv + 2 * B * Hq * dh * 2
+    b_commit = B * (4 + 4 + 1 + 4) + B * (1 + 4) + 4
+    return b_lm, b_lm + b_attn + b_commit
+
+
+def graph_ms_per_step(step, S, reps, warm, stream):
+    """Capture one restore of the S block states + S steps (one per state)
+    as one graph, replay it `reps` times between HIP events, check every
+    state against an eager step, and return (ms per step, commits per step)."""
+    import torch
+    step.reset()
+    step.run()
+    torch.cuda.synchronize()
+    n_commit = int(step.n_committed.item())
+    tokens_ref = step.tokens.clone()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step.reset()
+        step.run()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step.reset()
+        for i in range(S):
+            step.run(slot=i)
+    torch.cuda.synchronize()
+
+    ms = timed(graph.replay, reps, warm, stream) / S
+    torch.cuda.synchronize()
+    for i in range(S):
+        assert torch.equal(step.tokens_slots[i], tokens_ref), "graph replay diverged"
+    assert int(step.n_committed.item()) == n_commit
+    return ms, n_commit
+
+
 def cpu_baseline(inp, budget_s):
     """The oracle's decode step on the same inputs, timed on the host cores."""
     import numpy as np
@@ -115,7 +161,6 @@ def main():
               "(this build has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from block_diffusion_vlm_amd import bdiff as bd
@@ -132,51 +177,18 @@ def main():
     step = runner.DecodeStep(inp, slots=S)
     B, P, Hq, Hkv, dh, d, V = (inp[k] for k in ("B", "P", "Hq", "Hkv", "dh", "d", "V"))
 
-    # Eager reference step (and the commit count that every replay repeats).
-    step.reset()
-    step.run()
-    torch.cuda.synchronize()
-    n_commit = int(step.n_committed.item())
-    tokens_ref = step.tokens.clone()
-
-    # Capture one restore of the S block states + S steps (one per state) as
-    # one graph.
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        step.reset()
-        step.run()
-    stream.wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step.reset()
-        for i in range(S):
-            step.run(slot=i)
-    torch.cuda.synchronize()
-
     reps = max(1, (args.steps + S - 1) // S)
     args.steps = reps * S
-    ms_step = timed(graph.replay, reps, max(1, args.warmup // S), stream) / S
-    torch.cuda.synchronize()
-    for i in range(S):
-        assert torch.equal(step.tokens_slots[i], tokens_ref), "graph replay diverged"
-    assert int(step.n_committed.item()) == n_commit
+    ms_step, n_commit = graph_ms_per_step(step, S, reps, max(1, args.warmup // S), stream)
 
     # Dominant kernel: the LM head (its two dispatches), timed alone.
     ms_lm = timed(lambda: step.lm(step.h), args.steps, args.warmup, stream)
     ms_attn = timed(lambda: step.attn(step.q, step.k_cache, step.v_cache), args.steps,
                     args.warmup, stream)
 
-    # Algorithmic bytes (each byte the step must touch once).
-    b_W = V * d * 2
-    b_lm = b_W + B * d * 2 + B * 8
-    b_kv = 2 * Hkv * (P + B) * dh * 2
-    b_attn = b_kv + 2 * B * Hq * dh * 2
-    b_commit = B * (4 + 4 + 1 + 4) + B * (1 + 4) + 4
-    b_step = b_lm + b_attn + b_commit
+    b_lm, b_step = step_bytes(inp)
     steps_per_s = 1e3 / ms_step
-    kernel_hash = source_hash("k_lmhead.hip")
+    kernel_hash = source_hash("k_lmhead.hip", "lmhead_common.h")
     achieved = b_lm / (ms_lm * 1e-3) / 1e9
 
     # Plain device copy of known size (calibrates the HBM byte counters in a
@@ -242,6 +254,27 @@ def secondary(args, stream):
     res = {}
     iters = max(20, args.steps // 5)
     warm = max(3, args.warmup // 5)
+
+    # The same decode step with the FP8 (E4M3, W8A8) LM head, captured and
+    # replayed like the headline step.
+    r6 = synth.qwen_decode_fp8()
+    S = max(1, args.graph_steps)
+    st8 = runner.DecodeStep(r6, slots=S)
+    reps = max(1, iters // S)
+    ms8, n8 = graph_ms_per_step(st8, S, reps, max(1, warm // S), stream)
+    ms_lm8 = timed(lambda: st8.lm(st8.h), iters, warm, stream)
+    b_lm8, b_step8 = step_bytes(r6)
+    res["decode_step_fp8"] = {
+        "us": round(ms8 * 1e3, 2), "steps_per_s": round(1e3 / ms8, 1),
+        "committed_per_step": n8,
+        "hbm_frac": round(b_step8 / (ms8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "lmhead_us": round(ms_lm8 * 1e3, 2),
+        "lmhead_gbs": round(b_lm8 / (ms_lm8 * 1e-3) / 1e9, 1),
+        "lmhead_hbm_frac": round(b_lm8 / (ms_lm8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "lmhead_bytes": b_lm8,
+        "shape": "the headline step with E4M3 weights (one float32 scale per row) and "
+                 "per-position E4M3 activations"}
+    del st8, r6
 
     r5 = synth.dualstream()
     ds = runner.DualStream(r5)

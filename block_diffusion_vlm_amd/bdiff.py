@@ -25,7 +25,8 @@ EXPORTS = (
     "bd_status_str", "bd_device_check", "bd_make_intra_mask",
     "bd_block_attn_ws_bytes", "bd_block_attn",
     "bd_lmhead_conf_ws_bytes", "bd_lmhead_conf", "bd_lmhead_conf_commit",
-    "bd_commit", "bd_spec_accept", "bd_cert_scan", "bd_dualstream_attn",
+    "bd_lmhead_conf_fp8_ws_bytes", "bd_lmhead_conf_fp8", "bd_lmhead_conf_commit_fp8",
+    "bd_quant_fp8_rows", "bd_commit", "bd_spec_accept", "bd_cert_scan", "bd_dualstream_attn",
 )
 
 
@@ -51,6 +52,11 @@ _SIGS = {
     "bd_lmhead_conf_ws_bytes": ([_I, _I, _I], _SZ),
     "bd_lmhead_conf": ([_I, _P, _P, _I, _I, _I, _P, _P, _P, _SZ, _P], _I),
     "bd_lmhead_conf_commit": ([_I, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
+    "bd_lmhead_conf_fp8_ws_bytes": ([_I, _I, _I], _SZ),
+    "bd_lmhead_conf_fp8": ([_P, _P, _P, _I, _I, _I, _P, _P, _P, _SZ, _P], _I),
+    "bd_lmhead_conf_commit_fp8": ([_P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _SZ,
+                                   _P], _I),
+    "bd_quant_fp8_rows": ([_P, _I, _I, _P, _P, _P], _I),
     "bd_commit": ([_P, _P, _I, _F, _P, _P, _P, _P], _I),
     "bd_spec_accept": ([_P, _P, _I, _I, _P, _P, _P, _P], _I),
     "bd_cert_scan": ([_P, _P, _P, _I, _I, _P, _P, _P, _P], _I),
@@ -142,6 +148,30 @@ def bd_lmhead_conf_commit(dt, h, W, B, d, V, tau, conf, argmax, masked, tokens, 
                                      _ptr(masked), _ptr(tokens), _ptr(n_committed), _ptr(ws),
                                      ws_bytes, _stream(stream))
     return _ret("bd_lmhead_conf_commit", st, check)
+
+
+def bd_lmhead_conf_fp8_ws_bytes(B, d, V) -> int:
+    return int(lib().bd_lmhead_conf_fp8_ws_bytes(B, d, V))
+
+
+def bd_lmhead_conf_fp8(h, Wq, w_scale, B, d, V, conf, argmax, ws, ws_bytes, stream=None,
+                       check=True) -> int:
+    st = lib().bd_lmhead_conf_fp8(_ptr(h), _ptr(Wq), _ptr(w_scale), B, d, V, _ptr(conf),
+                                  _ptr(argmax), _ptr(ws), ws_bytes, _stream(stream))
+    return _ret("bd_lmhead_conf_fp8", st, check)
+
+
+def bd_lmhead_conf_commit_fp8(h, Wq, w_scale, B, d, V, tau, conf, argmax, masked, tokens,
+                              n_committed, ws, ws_bytes, stream=None, check=True) -> int:
+    st = lib().bd_lmhead_conf_commit_fp8(_ptr(h), _ptr(Wq), _ptr(w_scale), B, d, V, tau,
+                                         _ptr(conf), _ptr(argmax), _ptr(masked), _ptr(tokens),
+                                         _ptr(n_committed), _ptr(ws), ws_bytes, _stream(stream))
+    return _ret("bd_lmhead_conf_commit_fp8", st, check)
+
+
+def bd_quant_fp8_rows(x, R, d, q, scale, stream=None, check=True) -> int:
+    st = lib().bd_quant_fp8_rows(_ptr(x), R, d, _ptr(q), _ptr(scale), _stream(stream))
+    return _ret("bd_quant_fp8_rows", st, check)
 
 
 def bd_commit(conf, argmax, B, tau, masked, tokens, n_committed, stream=None, check=True) -> int:

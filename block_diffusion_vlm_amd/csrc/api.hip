@@ -151,6 +151,52 @@ bd_status bd_lmhead_conf_commit(bd_dtype dt, const void* h, const void* W, int32
     return lmhead_common(dt, h, W, B, d, V, f, ws, ws_bytes, stream);
 }
 
+size_t bd_lmhead_conf_fp8_ws_bytes(int32_t B, int32_t d, int32_t V) {
+    if (B < 1 || B > 64 || d < 128 || d > 16384 || d % 128 != 0 || V < 1) return 0;
+    return bd::lmhead_fp8_ws_bytes(B, d, V);
+}
+
+namespace {
+
+bd_status lmhead_fp8_common(const void* h, const uint8_t* Wq, const float* w_scale, int32_t B,
+                            int32_t d, int32_t V, const bd::Finish& f, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+    if (!h || !Wq || !w_scale || !f.conf || !f.argmax) return BD_E_NULL;
+    if (f.commit && (!f.masked || !f.tokens || !f.n_committed)) return BD_E_NULL;
+    if (B < 1 || B > 64 || V < 1 || d < 128 || d > 16384 || d % 128 != 0) return BD_E_SHAPE;
+    if (f.commit && !(f.tau == f.tau)) return BD_E_SHAPE;
+    if (!aligned16(h) || !aligned16(Wq) || !aligned16(w_scale)) return BD_E_ALIGN;
+    if (!ws || ws_bytes < bd::lmhead_fp8_ws_bytes(B, d, V)) return BD_E_WORKSPACE;
+    if (!aligned16(ws)) return BD_E_ALIGN;
+    return launch_status(bd::launch_lmhead_fp8(h, Wq, w_scale, B, d, V, f, ws, stream));
+}
+
+}  // namespace
+
+bd_status bd_lmhead_conf_fp8(const void* h, const uint8_t* Wq, const float* w_scale, int32_t B,
+                             int32_t d, int32_t V, float* conf, int32_t* argmax, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+    const bd::Finish f{conf, argmax, false, 0.f, nullptr, nullptr, nullptr};
+    return lmhead_fp8_common(h, Wq, w_scale, B, d, V, f, ws, ws_bytes, stream);
+}
+
+bd_status bd_lmhead_conf_commit_fp8(const void* h, const uint8_t* Wq, const float* w_scale,
+                                    int32_t B, int32_t d, int32_t V, float tau, float* conf,
+                                    int32_t* argmax, uint8_t* masked, int32_t* tokens,
+                                    int32_t* n_committed, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+    const bd::Finish f{conf, argmax, true, tau, masked, tokens, n_committed};
+    return lmhead_fp8_common(h, Wq, w_scale, B, d, V, f, ws, ws_bytes, stream);
+}
+
+bd_status bd_quant_fp8_rows(const void* x, int32_t R, int32_t d, uint8_t* q, float* scale,
+                            hipStream_t stream) {
+    if (!x || !q || !scale) return BD_E_NULL;
+    if (R < 0 || d < 8 || d % 8 != 0) return BD_E_SHAPE;
+    if (!aligned16(x) || !aligned16(q)) return BD_E_ALIGN;
+    return launch_status(bd::launch_quant_fp8_rows(x, R, d, q, scale, stream));
+}
+
 bd_status bd_commit(const float* conf, const int32_t* argmax, int32_t B, float tau,
                     uint8_t* masked, int32_t* tokens, int32_t* n_committed, hipStream_t stream) {
     if (!conf || !argmax || !masked || !tokens || !n_committed) return BD_E_NULL;

@@ -86,6 +86,14 @@ hipError_t launch_lmhead_bf16(const void* h, const void* W, int B, int d, int V,
 hipError_t launch_lmhead_f32(const float* h, const float* W, int B, int d, int V,
                              const Finish& f, void* ws, hipStream_t st);
 
+// FP8 (E4M3, W8A8) LM head and the per-row quantizer it applies to h.
+int lmhead_fp8_grid(int B, int d, int V);
+size_t lmhead_fp8_ws_bytes(int B, int d, int V);
+hipError_t launch_lmhead_fp8(const void* h, const uint8_t* W, const float* w_scale, int B, int d,
+                             int V, const Finish& f, void* ws, hipStream_t st);
+hipError_t launch_quant_fp8_rows(const void* x, int R, int d, uint8_t* q, float* scale,
+                                 hipStream_t st);
+
 // Block attention
 size_t block_attn_ws_bytes(int P, int Bq, int Hq, int Hkv, int dh);
 hipError_t launch_block_attn_bf16(const void* q, const void* kc, const void* vc, int P, int cap,

@@ -25,71 +25,11 @@
 // would need a device-scope release fence per workgroup, which on gfx950
 // writes back the L2 and costs far more than the second launch.
 #include "commit_impl.h"
+#include "lmhead_common.h"
 
 namespace bd {
 
 namespace {
-
-constexpr int kMaxGrid = 256;       // persistent workgroups for the bf16 path
-
-// Partial states live column-major, [position][partial], so that the merge
-// kernel reads each position's partials with coalesced loads.
-struct WsView {
-    float* m;
-    float* s;
-    int* a;
-};
-
-__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-
-__host__ __device__ inline WsView ws_view(void* ws, int G, int B) {
-    uint8_t* p = static_cast<uint8_t*>(ws);
-    const size_t one = align256(size_t(G) * B * sizeof(float));
-    WsView v;
-    v.m = reinterpret_cast<float*>(p);
-    v.s = reinterpret_cast<float*>(p + one);
-    v.a = reinterpret_cast<int*>(p + 2 * one);
-    return v;
-}
-
-inline size_t ws_size(int G, int B) { return 3 * align256(size_t(G) * B * 4); }
-
-// Fold four logits (rows row0..row0+3, already in log2 units) into a state.
-// Rows are visited in increasing order, so a strict '>' keeps the lowest
-// index among equal maxima.
-__device__ __forceinline__ void fold4(ArgSoft& st, const float x[4], int row0, int V) {
-    float mx = st.m;
-    int ax = st.a;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (row0 + i < V && x[i] > mx) {
-            mx = x[i];
-            ax = row0 + i;
-        }
-    }
-    float s = (st.s > 0.f) ? st.s * exp2f(st.m - mx) : 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        if (row0 + i < V) s += exp2f(x[i] - mx);
-    st.m = mx;
-    st.s = s;
-    st.a = ax;
-}
-
-__device__ __forceinline__ ArgSoft shfl_xor_state(ArgSoft x, int off) {
-    ArgSoft y;
-    y.m = __shfl_xor(x.m, off);
-    y.s = __shfl_xor(x.s, off);
-    y.a = __shfl_xor(x.a, off);
-    return y;
-}
-
-__device__ __forceinline__ void store_partial(const WsView& w, int G, int col, int part, ArgSoft s) {
-    const size_t idx = size_t(col) * G + part;
-    w.m[idx] = s.m;
-    w.s[idx] = s.s;
-    w.a[idx] = s.a;
-}
 
 // Merge of the G partial states of one position by one wave, in a fixed
 // order: lane l folds partials l, l + 64, ... (loads issued eight at a time,
@@ -159,6 +99,8 @@ __global__ __launch_bounds__(1024) void lmhead_combine_commit_kernel(
                     tokens, n_committed);
 }
 
+}  // namespace
+
 hipError_t launch_combine(void* ws, int G, int B, const Finish& f, hipStream_t st) {
     if (f.commit)
         hipLaunchKernelGGL(lmhead_combine_commit_kernel, dim3(1), dim3(1024), 0, st, ws, G, B,
@@ -168,6 +110,9 @@ hipError_t launch_combine(void* ws, int G, int B, const Finish& f, hipStream_t s
                            f.argmax);
     return hipGetLastError();
 }
+
+
+namespace {
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel.  NB = number of 16-position column blocks (ceil(B/16));
@@ -295,24 +240,7 @@ __global__ __launch_bounds__(256) void lmhead_bf16_kernel(const uint16_t* __rest
         }
     }
 
-    // Merge the four lane groups that hold the same position, then the waves.
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        st[nb] = merge(st[nb], shfl_xor_state(st[nb], 16));
-        st[nb] = merge(st[nb], shfl_xor_state(st[nb], 32));
-        if (lane < 16) fin[wave][nb][lane] = st[nb];
-    }
-    __syncthreads();
-    const WsView wv = ws_view(ws, G, B);
-    if (wave == 0 && lane < 16) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            ArgSoft s = fin[0][nb][lane];
-            for (int w = 1; w < nwave; ++w) s = merge(s, fin[w][nb][lane]);
-            const int col = nb * 16 + lane;
-            if (col < B) store_partial(wv, G, col, blockIdx.x, s);
-        }
-    }
+    store_workgroup_partials<NB>(st, fin, ws, B);
 }
 
 // Generic bf16 fallback for shapes whose h fragments do not fit in
@@ -364,23 +292,7 @@ __global__ __launch_bounds__(256) void lmhead_bf16_generic_kernel(
             fold4(st[nb], x, row0, V);
         }
     }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        st[nb] = merge(st[nb], shfl_xor_state(st[nb], 16));
-        st[nb] = merge(st[nb], shfl_xor_state(st[nb], 32));
-        if (lane < 16) fin[wave][nb][lane] = st[nb];
-    }
-    __syncthreads();
-    const WsView wv = ws_view(ws, G, B);
-    if (wave == 0 && lane < 16) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            ArgSoft s = fin[0][nb][lane];
-            for (int w = 1; w < nwave; ++w) s = merge(s, fin[w][nb][lane]);
-            const int col = nb * 16 + lane;
-            if (col < B) store_partial(wv, G, col, blockIdx.x, s);
-        }
-    }
+    store_workgroup_partials<NB>(st, fin, ws, B);
 }
 
 // ---------------------------------------------------------------------------
@@ -479,24 +391,7 @@ hipError_t launch_nb(const void* h, const void* W, int B, int d, int V, const Fi
 int lmhead_grid(int B, int d, int V) {
     (void)B;
     (void)d;
-    const int ntiles = (V + 15) / 16;
-    if (ntiles <= kMaxGrid) return ntiles;
-    // The kernel is bound by the aggregate HBM bandwidth, so its time follows
-    // the largest per-workgroup share, ceil(ntiles / G), times G.  Between
-    // 7/8 of the chip and all of it, take the grid that wastes the fewest
-    // tile slots (the largest such grid on ties): 9496 tiles, for instance,
-    // go 38 per workgroup to 250 workgroups instead of 37 or 38 to 256, whose
-    // last twenty-four workgroups would run alone at the end.
-    int best = kMaxGrid;
-    long best_slots = long((ntiles + kMaxGrid - 1) / kMaxGrid) * kMaxGrid;
-    for (int g = kMaxGrid - 1; g >= kMaxGrid - kMaxGrid / 8; --g) {
-        const long slots = long((ntiles + g - 1) / g) * g;
-        if (slots < best_slots) {
-            best_slots = slots;
-            best = g;
-        }
-    }
-    return best;
+    return persistent_grid((V + 15) / 16);
 }
 
 size_t lmhead_ws_bytes(int B, int d, int V) {

@@ -72,7 +72,7 @@ def _avg(rows, pred):
     return (sum(vals) / len(vals)) if vals else None
 
 
-def traffic(fetch_db: str, write_db: str, out_json: str, source: Path) -> dict:
+def traffic(fetch_db: str, write_db: str, out_json: str, sources) -> dict:
     res = {}
     for kind, db, cname in (("fetch", fetch_db, "FETCH_SIZE"), ("write", write_db, "WRITE_SIZE")):
         rows = pmc_per_dispatch(db, cname)
@@ -93,7 +93,10 @@ def traffic(fetch_db: str, write_db: str, out_json: str, source: Path) -> dict:
                      "merge_kib": merge or 0.0,
                      "bytes_per_call": (lm + (merge or 0.0)) * 1024.0 * scale}
     res["hbm_bytes_per_call"] = res["fetch"]["bytes_per_call"] + res["write"]["bytes_per_call"]
-    res["kernel_source_sha"] = hashlib.sha256(source.read_bytes()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in sources:
+        h.update(Path(f).read_bytes())
+    res["kernel_source_sha"] = h.hexdigest()[:16]
     Path(out_json).write_text(json.dumps(res, indent=1) + "\n")
     return res
 
@@ -104,8 +107,9 @@ def main(argv):
     elif len(argv) >= 3 and argv[0] == "pmc":
         print(pmc(argv[1], argv[2]))
     elif len(argv) >= 4 and argv[0] == "traffic":
-        src = Path(__file__).resolve().parent / "csrc" / "k_lmhead.hip"
-        print(json.dumps(traffic(argv[1], argv[2], argv[3], src), indent=1))
+        csrc = Path(__file__).resolve().parent / "csrc"
+        srcs = [csrc / "k_lmhead.hip", csrc / "lmhead_common.h"]
+        print(json.dumps(traffic(argv[1], argv[2], argv[3], srcs), indent=1))
     else:
         print(__doc__)
         return 2

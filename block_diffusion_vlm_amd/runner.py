@@ -60,6 +60,33 @@ class LMHead:
         bd.bd_lmhead_conf(self.dt, h, self.W, self.B, self.d, self.V, self.conf, self.argmax,
                           self.ws, self.ws_bytes, stream)
 
+    def conf_commit(self, h, tau, masked, tokens, n_committed, stream=None):
+        bd.bd_lmhead_conf_commit(self.dt, h, self.W, self.B, self.d, self.V, tau, self.conf,
+                                 self.argmax, masked, tokens, n_committed, self.ws,
+                                 self.ws_bytes, stream)
+
+
+class LMHeadFP8:
+    """bd_lmhead_conf_fp8 over fixed device buffers: W holds E4M3 codes
+    (uint8 [V][d]) and w_scale one float32 scale per row; h stays bf16."""
+
+    def __init__(self, W: torch.Tensor, w_scale: torch.Tensor, B: int, d: int, V: int,
+                 device="cuda"):
+        self.W, self.w_scale, self.B, self.d, self.V = W, w_scale, B, d, V
+        self.conf = torch.empty(B, dtype=torch.float32, device=device)
+        self.argmax = torch.empty(B, dtype=torch.int32, device=device)
+        self.ws_bytes = bd.bd_lmhead_conf_fp8_ws_bytes(B, d, V)
+        self.ws = workspace(self.ws_bytes, device)
+
+    def __call__(self, h: torch.Tensor, stream=None):
+        bd.bd_lmhead_conf_fp8(h, self.W, self.w_scale, self.B, self.d, self.V, self.conf,
+                              self.argmax, self.ws, self.ws_bytes, stream)
+
+    def conf_commit(self, h, tau, masked, tokens, n_committed, stream=None):
+        bd.bd_lmhead_conf_commit_fp8(h, self.W, self.w_scale, self.B, self.d, self.V, tau,
+                                     self.conf, self.argmax, masked, tokens, n_committed,
+                                     self.ws, self.ws_bytes, stream)
+
 
 class BlockAttn:
     """bd_block_attn over fixed device buffers."""
@@ -83,8 +110,8 @@ class DecodeStep:
     """One threshold (MDM) block-decode step: bd_block_attn (bidirectional
     block) -> bd_lmhead_conf_commit (LM head, then commit).  With
     ``fused=False`` the LM head and the commit are the two separate calls
-    bd_lmhead_conf and bd_commit.  Inputs from synth.qwen_decode or
-    synth.tiny.
+    bd_lmhead_conf and bd_commit.  Inputs from synth.qwen_decode, synth.tiny
+    or synth.qwen_decode_fp8 (bf16 attention, the FP8 LM-head calls).
 
     The block state (committed tokens, masked flags) exists in ``slots``
     independent copies in one buffer; ``run(slot=i)`` updates copy i and
@@ -95,7 +122,8 @@ class DecodeStep:
     def __init__(self, inp: dict, device="cuda", fused=True, slots=1):
         self.fused = fused
         self.inp = inp
-        dt = dtype_code(inp["dtype"])
+        fp8 = inp["dtype"] == "fp8"
+        dt = bd.BD_BF16 if fp8 else dtype_code(inp["dtype"])
         B = inp["B"]
         self.q = to_dev(inp["q"], device)
         self.k_cache = to_dev(inp["k_cache"], device)
@@ -104,7 +132,11 @@ class DecodeStep:
         self.W = to_dev(inp["W"], device)
         self.attn = BlockAttn(dt, bd.BD_MASK_BIDIR, B, inp["P"], inp["cap"], inp["Hq"],
                               inp["Hkv"], inp["q"].shape[-1], device)
-        self.lm = LMHead(dt, self.W, B, inp["d"], inp["V"], device)
+        if fp8:
+            self.w_scale = to_dev(inp["w_scale"], device)
+            self.lm = LMHeadFP8(self.W, self.w_scale, B, inp["d"], inp["V"], device)
+        else:
+            self.lm = LMHead(dt, self.W, B, inp["d"], inp["V"], device)
         # One slot: tokens int32[B], then masked uint8[B]; slots 256 bytes apart.
         used = 5 * B
         stride = (used + 255) // 256 * 256
@@ -131,9 +163,7 @@ class DecodeStep:
         self.attn(self.q, self.k_cache, self.v_cache, stream)
         lm = self.lm
         if self.fused:
-            bd.bd_lmhead_conf_commit(lm.dt, self.h, lm.W, lm.B, lm.d, lm.V, self.tau, lm.conf,
-                                     lm.argmax, masked, tokens, self.n_committed, lm.ws,
-                                     lm.ws_bytes, stream)
+            lm.conf_commit(self.h, self.tau, masked, tokens, self.n_committed, stream)
         else:
             lm(self.h, stream)
             bd.bd_commit(lm.conf, lm.argmax, self.B, self.tau, masked, tokens,

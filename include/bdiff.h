@@ -147,6 +147,64 @@ bd_status bd_lmhead_conf_commit(bd_dtype dt, const void* h, const void* W,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * bd_lmhead_conf_fp8 - bd_lmhead_conf with FP8 weights and activations
+ * (W8A8, the quantization of the fastest configuration: OV §2.3.2 FP8
+ * SmoothQuant W8A8; OV §4.1 quant_mode fp8).  The number format is OCP E4M3
+ * (OFP8 specification: sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * largest finite value 448; S.1111.111 is NaN).
+ *   W8A8 rule.  W is given as E4M3 codes with one float32 dequantization
+ *   scale per vocabulary row.  Each hidden row is quantized when the call
+ *   runs, exactly as bd_quant_fp8_rows quantizes a row (qh[b], s_h[b]); then
+ *     l[v] = s_h[b] * w_scale[v] * sum_k dec(qh[b][k]) dec(Wq[v][k])
+ *   with float32 accumulation, and conf/argmax as in bd_lmhead_conf.
+ *
+ *   h        [B][d] bf16 (finite)
+ *   Wq       [V][d] E4M3 codes (uint8); NaN codes are not allowed
+ *   w_scale  [V] float32
+ *   conf     [B] float32 out;  argmax [B] int32 out
+ *   ws       workspace of at least bd_lmhead_conf_fp8_ws_bytes(B, d, V) bytes
+ *            (no initial contents required)
+ * Limits: 1 <= B <= 64, V >= 1, d % 128 == 0, 128 <= d <= 16384.  h, Wq,
+ *   w_scale and ws must be 16-byte aligned.  Deterministic (fixed reduction
+ *   order).  bd_lmhead_conf_fp8_ws_bytes returns 0 for shapes out of range.
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_ALIGN, BD_E_WORKSPACE, BD_E_LAUNCH.
+ */
+size_t bd_lmhead_conf_fp8_ws_bytes(int32_t B, int32_t d, int32_t V);
+bd_status bd_lmhead_conf_fp8(const void* h, const uint8_t* Wq, const float* w_scale,
+                             int32_t B, int32_t d, int32_t V,
+                             float* conf, int32_t* argmax,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * bd_lmhead_conf_commit_fp8 - bd_lmhead_conf_fp8 followed by bd_commit, as
+ * one call (the same relation as bd_lmhead_conf_commit to bd_lmhead_conf).
+ * [OV §1.2, §2.3.2, §4.1]  Workspace: bd_lmhead_conf_fp8_ws_bytes(B, d, V).
+ * Errors: those of bd_lmhead_conf_fp8, plus BD_E_NULL for masked, tokens or
+ *   n_committed and BD_E_SHAPE for a NaN tau.
+ */
+bd_status bd_lmhead_conf_commit_fp8(const void* h, const uint8_t* Wq, const float* w_scale,
+                                    int32_t B, int32_t d, int32_t V, float tau,
+                                    float* conf, int32_t* argmax,
+                                    uint8_t* masked, int32_t* tokens, int32_t* n_committed,
+                                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * bd_quant_fp8_rows - per-row dynamic quantization to E4M3, the rule that
+ * bd_lmhead_conf_fp8 applies to its hidden rows (and a way to store weights
+ * with per-row scales).  [OV §2.3.2 W8A8]  Per row, in float32:
+ *   amax = max_k |x[k]|;  r = 448 / amax and scale = amax / 448, each
+ *   correctly rounded (r = scale = 1 for an all-zero row);
+ *   q[k] = E4M3(clamp(x[k] * r, -448, 448)), rounded to nearest, ties to the
+ *   even code; a negative value that rounds to zero gives 0x80.
+ *   x [R][d] bf16 (finite);  q [R][d] uint8 out;  scale [R] float32 out
+ * Limits: R >= 0 (R = 0 launches nothing), d % 8 == 0, d >= 8.  x and q must
+ *   be 16-byte aligned.
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_ALIGN, BD_E_LAUNCH.
+ */
+bd_status bd_quant_fp8_rows(const void* x, int32_t R, int32_t d, uint8_t* q, float* scale,
+                            hipStream_t stream);
+
+/*
  * bd_commit - threshold unmasking with the always-one rule.
  * [OV §4.1: denoising confidence threshold 0.9; OV §1.2 parallel unmasking]
  * Every position i with masked[i] != 0 and conf[i] > tau is committed.  If

@@ -145,6 +145,62 @@ def test_lmhead_conf_commit_validation():
     assert f(ws_bytes=10) == bd.BD_E_WORKSPACE
 
 
+def _lm8(commit=False, **kw):
+    a = dict(h=FAKE, Wq=FAKE, w_scale=FAKE, B=16, d=2048, V=151936, conf=FAKE, argmax=FAKE,
+             ws=FAKE, ws_bytes=1 << 30, stream=0, check=False)
+    if commit:
+        a.update(tau=0.9, masked=FAKE, tokens=FAKE, n_committed=FAKE)
+    a.update(kw)
+    return (bd.bd_lmhead_conf_commit_fp8 if commit else bd.bd_lmhead_conf_fp8)(**a)
+
+
+@pytest.mark.parametrize("commit", [False, True])
+def test_lmhead_fp8_validation(commit):
+    f = lambda **kw: _lm8(commit, **kw)  # noqa: E731
+    assert f(h=None) == bd.BD_E_NULL
+    assert f(Wq=None) == bd.BD_E_NULL
+    assert f(w_scale=None) == bd.BD_E_NULL
+    assert f(argmax=None) == bd.BD_E_NULL
+    assert f(B=0) == bd.BD_E_SHAPE
+    assert f(B=65) == bd.BD_E_SHAPE
+    assert f(V=0) == bd.BD_E_SHAPE
+    assert f(d=2000) == bd.BD_E_SHAPE            # d % 128 == 0
+    assert f(d=0) == bd.BD_E_SHAPE
+    assert f(d=16512) == bd.BD_E_SHAPE
+    assert f(h=MISALIGNED) == bd.BD_E_ALIGN
+    assert f(Wq=MISALIGNED) == bd.BD_E_ALIGN
+    assert f(w_scale=MISALIGNED) == bd.BD_E_ALIGN
+    assert f(ws=None) == bd.BD_E_WORKSPACE
+    need = bd.bd_lmhead_conf_fp8_ws_bytes(16, 2048, 151936)
+    assert f(ws_bytes=need - 1) == bd.BD_E_WORKSPACE
+    assert f(ws=MISALIGNED) == bd.BD_E_ALIGN
+    if commit:
+        assert f(masked=None) == bd.BD_E_NULL
+        assert f(n_committed=None) == bd.BD_E_NULL
+        assert f(tau=float("nan")) == bd.BD_E_SHAPE
+
+
+def test_lmhead_fp8_workspace_query():
+    assert bd.bd_lmhead_conf_fp8_ws_bytes(16, 2048, 151936) >= 256
+    # the generic path keeps the quantized hidden rows in the workspace
+    assert bd.bd_lmhead_conf_fp8_ws_bytes(64, 16384, 1000) >= 64 * 16384
+    for bad in ((0, 2048, 10), (65, 2048, 10), (16, 2000, 10), (16, 16512, 10), (16, 2048, 0)):
+        assert bd.bd_lmhead_conf_fp8_ws_bytes(*bad) == 0
+
+
+def test_quant_fp8_rows_validation():
+    q = lambda **kw: bd.bd_quant_fp8_rows(**{**dict(x=FAKE, R=4, d=64, q=FAKE, scale=FAKE,
+                                                    stream=0, check=False), **kw})
+    assert q(x=None) == bd.BD_E_NULL
+    assert q(q=None) == bd.BD_E_NULL
+    assert q(scale=None) == bd.BD_E_NULL
+    assert q(R=-1) == bd.BD_E_SHAPE
+    assert q(d=0) == bd.BD_E_SHAPE
+    assert q(d=12) == bd.BD_E_SHAPE
+    assert q(x=MISALIGNED) == bd.BD_E_ALIGN
+    assert q(q=MISALIGNED) == bd.BD_E_ALIGN
+
+
 def test_small_calls_validation():
     c = lambda **kw: bd.bd_commit(**{**dict(conf=FAKE, argmax=FAKE, B=16, tau=0.9, masked=FAKE,
                                             tokens=FAKE, n_committed=FAKE, stream=0,

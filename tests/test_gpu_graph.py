@@ -16,8 +16,10 @@ def _snapshot(step):
             "argmax": step.lm.argmax.clone(), "attn": step.attn.out.clone()}
 
 
-def test_decode_step_graph_replays_match_eager():
-    r = synth.qwen_decode(V=30011, B=16)
+@pytest.mark.parametrize("workload", ["bf16", "fp8"])
+def test_decode_step_graph_replays_match_eager(workload):
+    gen = synth.qwen_decode if workload == "bf16" else synth.qwen_decode_fp8
+    r = gen(V=30011, B=16)
     step = runner.DecodeStep(r)
     step.reset()
     step.run()
@@ -37,7 +39,7 @@ def test_decode_step_graph_replays_match_eager():
         step.run()
     torch.cuda.synchronize()
 
-    other = runner.DecodeStep(synth.qwen_decode(seed=7, V=30011, B=16))
+    other = runner.DecodeStep(gen(seed=7, V=30011, B=16))
     for rep in range(4):
         # eager work between replays that dirties the step's buffers
         step.tokens.fill_(-5)
