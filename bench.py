@@ -17,7 +17,6 @@ One JSON line is printed.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -42,16 +41,13 @@ def parse():
                     help="decode steps captured per HIP graph (replays = steps / graph-steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--fp8-only", action="store_true",
+                    help="of the secondary workloads, run only the FP8 decode step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     return ap.parse_args()
 
 
-def source_hash(*names) -> str:
-    h = hashlib.sha256()
-    for n in names:
-        h.update((ROOT / "block_diffusion_vlm_amd" / "csrc" / n).read_bytes())
-    return h.hexdigest()[:16]
 
 
 def timed(fn, iters, warmup, stream):
@@ -70,10 +66,13 @@ def timed(fn, iters, warmup, stream):
     return e0.elapsed_time(e1) / iters
 
 
-def traffic_from_profile(kernel_hash: str):
-    """HBM bytes per LM-head call from the committed counter summary, if it
-    was taken on the current kernel source; else None."""
-    f = PROFILE_DIR / "lmhead_qwen_decode_pmc.json"
+def traffic_from_profile(kind: str):
+    """HBM bytes per LM-head call (kind "bf16" or "fp8") from the committed
+    counter summary, if it was taken on the current kernel source; else None."""
+    from block_diffusion_vlm_amd.rocprof_summary import LMHEAD_KINDS, source_sha
+    kernel_hash = source_sha(LMHEAD_KINDS[kind][1])
+    f = PROFILE_DIR / ("lmhead_qwen_decode_pmc.json" if kind == "bf16"
+                       else "lmhead_fp8_qwen_decode_pmc.json")
     if not f.exists():
         return None
     try:
@@ -188,7 +187,6 @@ def main():
 
     b_lm, b_step = step_bytes(inp)
     steps_per_s = 1e3 / ms_step
-    kernel_hash = source_hash("k_lmhead.hip", "lmhead_common.h")
     achieved = b_lm / (ms_lm * 1e-3) / 1e9
 
     # Plain device copy of known size (calibrates the HBM byte counters in a
@@ -222,7 +220,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "bd_lmhead_conf (contraction + merge)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profile(kernel_hash),
+                     "traffic": traffic_from_profile("bf16"),
                      "us_per_launch": round(ms_lm * 1e3, 2), "bytes_per_launch": b_lm},
         "kernels_us": {"bd_block_attn": round(ms_attn * 1e3, 2),
                        "bd_lmhead_conf": round(ms_lm * 1e3, 2),
@@ -272,9 +270,12 @@ def secondary(args, stream):
         "lmhead_gbs": round(b_lm8 / (ms_lm8 * 1e-3) / 1e9, 1),
         "lmhead_hbm_frac": round(b_lm8 / (ms_lm8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "lmhead_bytes": b_lm8,
+        "lmhead_traffic": traffic_from_profile("fp8"),
         "shape": "the headline step with E4M3 weights (one float32 scale per row) and "
                  "per-position E4M3 activations"}
     del st8, r6
+    if args.fp8_only:
+        return res
 
     r5 = synth.dualstream()
     ds = runner.DualStream(r5)

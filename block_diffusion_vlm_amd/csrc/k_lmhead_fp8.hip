@@ -116,10 +116,11 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
 // per lane (consecutive lanes read consecutive 16-byte pieces of a row),
 // staged in a wave-private LDS buffer, and read back as A operands.  Row r's
 // piece p sits in slot p ^ (r & SW), so the 16 rows of one operand read fall
-// in distinct banks.  The next tile's loads (and its 32 row scales) are in
-// flight while the current tile is multiplied.  The waves add their partial
-// logits through LDS; one wave (rotating) scales them and folds them into
-// the running states.
+// in distinct banks.  Two tiles are in flight in registers (with their 32
+// row scales each) while the current tile is multiplied: the tiles carry
+// half the bytes of the bf16 kernel's, so one tile ahead does not cover the
+// memory latency.  The waves add their partial logits through LDS; one wave
+// (rotating) scales them and folds them into the running states.
 //
 // Prologue: each wave loads its K range of h, the workgroup takes the row
 // maxima (lane groups by shuffles, waves through LDS), and each lane keeps
@@ -170,31 +171,33 @@ __global__ __launch_bounds__(256) void lmhead_fp8_kernel(const uint16_t* __restr
 
     const int t_beg = int(int64_t(ntiles) * blockIdx.x / G);
     const int t_end = int(int64_t(ntiles) * (blockIdx.x + 1) / G);
-    u32x4 nxt[NL];
-    f32x4 nsc[RT];
-    if (t_beg < t_end) {
-        load_tile(nxt, t_beg);
-        load_scales(nsc, t_beg);
-    }
+    u32x4 bufA[NL], bufB[NL];                      // two tiles in flight
+    f32x4 scA[RT], scB[RT];
+    auto issue_first_tiles = [&]() {
+        if (t_beg < t_end) {
+            load_tile(bufA, t_beg);
+            load_scales(scA, t_beg);
+        }
+        if (t_beg + 1 < t_end) {
+            load_tile(bufB, t_beg + 1);
+            load_scales(scB, t_beg + 1);
+        }
+    };
 
     // ---- quantize h: lane (r16, g) holds k = kw + 128c + 32g + [0, 32) of
     // position nb*16 + r16, as 32 codes (8 dwords, byte t <-> k offset t).
+    // The h loads are issued before the first tiles' loads (loads return in
+    // order), so the quantization runs while those tiles are in flight; when
+    // the raw values would take too many registers, h is read twice, both
+    // times before the tiles.
     auto h_piece = [&](int nb, int c, int j) -> u32x4 {
         const int row = nb * 16 + r16;
         if (row >= B) return u32x4{0, 0, 0, 0};
         return reinterpret_cast<const u32x4*>(h + size_t(row) * d + kw + c * 128 + g * 32)[j];
     };
-    float shl[NB];                                 // s_h * log2(e) of this lane's position
-    i32x8 hq[NCH][NB];
-    {
-        float m[NB];
+    auto row_amax = [&](float (&m)[NB]) -> void {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            m[nb] = 0.f;
-#pragma unroll
-            for (int c = 0; c < NCH; ++c)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) m[nb] = fmaxf(m[nb], absmax8(h_piece(nb, c, j)));
             m[nb] = fmaxf(m[nb], __shfl_xor(m[nb], 16));
             m[nb] = fmaxf(m[nb], __shfl_xor(m[nb], 32));
             if (g == 0) amx[wave][nb * 16 + r16] = m[nb];
@@ -204,35 +207,83 @@ __global__ __launch_bounds__(256) void lmhead_fp8_kernel(const uint16_t* __restr
         for (int nb = 0; nb < NB; ++nb) {
             float amax = amx[0][nb * 16 + r16];
             for (int w = 1; w < nwave; ++w) amax = fmaxf(amax, amx[w][nb * 16 + r16]);
-            const RowQuant rq = row_quant(amax);
+            m[nb] = amax;
+        }
+    };
+    float shl[NB];                                 // s_h * log2(e) of this lane's position
+    i32x8 hq[NCH][NB];
+    auto put_codes = [&](int c, int nb, int j, u32x2 q) {
+        hq[c][nb][2 * j] = static_cast<int32_t>(q.x);
+        hq[c][nb][2 * j + 1] = static_cast<int32_t>(q.y);
+    };
+    float m[NB];
+    if constexpr (NCH * NB <= 4) {
+        u32x4 raw[NCH][NB][4];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) raw[c][nb][j] = h_piece(nb, c, j);
+        issue_first_tiles();
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            m[nb] = 0.f;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) m[nb] = fmaxf(m[nb], absmax8(raw[c][nb][j]));
+        }
+        row_amax(m);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const RowQuant rq = row_quant(m[nb]);
             shl[nb] = rq.s * kLog2e;
 #pragma unroll
             for (int c = 0; c < NCH; ++c)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const u32x2 q = quant8(h_piece(nb, c, j), rq.r);
-                    hq[c][nb][2 * j] = static_cast<int32_t>(q.x);
-                    hq[c][nb][2 * j + 1] = static_cast<int32_t>(q.y);
-                }
+                for (int j = 0; j < 4; ++j) put_codes(c, nb, j, quant8(raw[c][nb][j], rq.r));
         }
+    } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            m[nb] = 0.f;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) m[nb] = fmaxf(m[nb], absmax8(h_piece(nb, c, j)));
+        }
+        row_amax(m);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const RowQuant rq = row_quant(m[nb]);
+            shl[nb] = rq.s * kLog2e;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) put_codes(c, nb, j, quant8(h_piece(nb, c, j), rq.r));
+        }
+        issue_first_tiles();
     }
 
     ArgSoft st[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) st[nb] = ArgSoft{-INFINITY, 0.f, 0x7fffffff};
 
+    // One tile: stage it, refill its register buffer with the tile two
+    // ahead, multiply, reduce across the waves, fold.
     int it = 0;
-    for (int tile = t_beg; tile < t_end; ++tile, ++it) {
+    auto step = [&](u32x4 (&buf)[NL], f32x4 (&scb)[RT], int tile) {
         // The previous tile's operand reads precede these writes in this
         // wave's program order, so the wave-private buffer can be refilled.
 #pragma unroll
-        for (int i = 0; i < NL; ++i) stage[wave][64 * i + lane] = nxt[i];
+        for (int i = 0; i < NL; ++i) stage[wave][64 * i + lane] = buf[i];
         f32x4 sc[RT];
 #pragma unroll
-        for (int s = 0; s < RT; ++s) sc[s] = nsc[s];
-        if (tile + 1 < t_end) {
-            load_tile(nxt, tile + 1);
-            load_scales(nsc, tile + 1);
+        for (int s = 0; s < RT; ++s) sc[s] = scb[s];
+        if (tile + 2 < t_end) {
+            load_tile(buf, tile + 2);
+            load_scales(scb, tile + 2);
         }
 
         f32x4 acc[RT][NB];
@@ -289,6 +340,11 @@ __global__ __launch_bounds__(256) void lmhead_fp8_kernel(const uint16_t* __restr
                 }
             }
         }
+        ++it;
+    };
+    for (int tile = t_beg; tile < t_end; tile += 2) {
+        step(bufA, scA, tile);
+        if (tile + 1 < t_end) step(bufB, scB, tile + 1);
     }
 
     store_workgroup_partials<NB>(st, fin, ws, B);

@@ -4,11 +4,12 @@
         per-kernel dispatch count and average / min / max duration (us)
     python -m block_diffusion_vlm_amd.rocprof_summary pmc <results.db> <COUNTER>
         per-kernel dispatch count and average counter value per dispatch
-    python -m block_diffusion_vlm_amd.rocprof_summary traffic <fetch.db> <write.db> <out.json>
-        HBM bytes of one bd_lmhead_conf call (the contraction kernel plus its
-        merge kernel), from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
-        scaled by the ratio of known bytes to the counter value of a plain
-        256 MiB device copy recorded in the same run.
+    python -m block_diffusion_vlm_amd.rocprof_summary traffic <fetch.db> <write.db> <out.json> [bf16|fp8]
+        HBM bytes of one bd_lmhead_conf (bf16, default) or bd_lmhead_conf_fp8
+        call (the streaming kernel plus its merge kernel), from FETCH_SIZE and
+        WRITE_SIZE (KiB per dispatch), each scaled by the ratio of known bytes
+        to the counter value of a plain 256 MiB device copy recorded in the
+        same run.
 """
 from __future__ import annotations
 
@@ -72,7 +73,23 @@ def _avg(rows, pred):
     return (sum(vals) / len(vals)) if vals else None
 
 
-def traffic(fetch_db: str, write_db: str, out_json: str, sources) -> dict:
+# Streaming kernel of each LM-head flavour and the sources its hash covers.
+LMHEAD_KINDS = {
+    "bf16": ("void bd::lmhead_bf16_kernel", ("k_lmhead.hip", "lmhead_common.h")),
+    "fp8": ("void bd::lmhead_fp8_kernel", ("k_lmhead_fp8.hip", "lmhead_common.h")),
+}
+
+
+def source_sha(names) -> str:
+    csrc = Path(__file__).resolve().parent / "csrc"
+    h = hashlib.sha256()
+    for n in names:
+        h.update((csrc / n).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def traffic(fetch_db: str, write_db: str, out_json: str, kind: str = "bf16") -> dict:
+    prefix, sources = LMHEAD_KINDS[kind]
     res = {}
     for kind, db, cname in (("fetch", fetch_db, "FETCH_SIZE"), ("write", write_db, "WRITE_SIZE")):
         rows = pmc_per_dispatch(db, cname)
@@ -84,7 +101,7 @@ def traffic(fetch_db: str, write_db: str, out_json: str, sources) -> dict:
         kib = COPY_BYTES / 1024.0
         vals = [v for n, g, v in rows if "copy" in n.lower() and 0.25 * kib <= v <= 1.5 * kib]
         copy = sum(vals) / len(vals) if vals else None
-        lm = _avg(rows, lambda n, g: n.startswith("void bd::lmhead_bf16_kernel"))
+        lm = _avg(rows, lambda n, g: n.startswith(prefix))
         merge = _avg(rows, lambda n, g: "lmhead_combine" in n)
         if copy is None or lm is None:
             raise SystemExit(f"{cname}: calibration copy or LM-head dispatches not found")
@@ -93,10 +110,7 @@ def traffic(fetch_db: str, write_db: str, out_json: str, sources) -> dict:
                      "merge_kib": merge or 0.0,
                      "bytes_per_call": (lm + (merge or 0.0)) * 1024.0 * scale}
     res["hbm_bytes_per_call"] = res["fetch"]["bytes_per_call"] + res["write"]["bytes_per_call"]
-    h = hashlib.sha256()
-    for f in sources:
-        h.update(Path(f).read_bytes())
-    res["kernel_source_sha"] = h.hexdigest()[:16]
+    res["kernel_source_sha"] = source_sha(sources)
     Path(out_json).write_text(json.dumps(res, indent=1) + "\n")
     return res
 
@@ -107,9 +121,8 @@ def main(argv):
     elif len(argv) >= 3 and argv[0] == "pmc":
         print(pmc(argv[1], argv[2]))
     elif len(argv) >= 4 and argv[0] == "traffic":
-        csrc = Path(__file__).resolve().parent / "csrc"
-        srcs = [csrc / "k_lmhead.hip", csrc / "lmhead_common.h"]
-        print(json.dumps(traffic(argv[1], argv[2], argv[3], srcs), indent=1))
+        kind = argv[4] if len(argv) >= 5 else "bf16"
+        print(json.dumps(traffic(argv[1], argv[2], argv[3], kind), indent=1))
     else:
         print(__doc__)
         return 2

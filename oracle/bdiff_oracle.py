@@ -51,16 +51,16 @@ design notes of the repository):
       see all of the draft half.  Both halves see the whole prefix.
   R11 Certificate order: stable sort by anchor confidence, descending, lower
       index first on ties.
-  R12 FP8 means OCP E4M3 for weights and activations (W8A8), float32
+  R15 FP8 means OCP E4M3 for weights and activations (W8A8), float32
       accumulation, one float32 scale per vocabulary row of W.
-  R13 Activations are quantized per position with the scale amax/448 (the
+  R16 Activations are quantized per position with the scale amax/448 (the
       row maximum maps onto the largest E4M3 value), in float32, rounding to
       nearest with ties to even.
 
 Every function below takes float64 (or integer) arrays and returns new arrays;
 bfloat16 inputs are passed as raw uint16 bit patterns and widened exactly.
 The FP8 functions follow the OCP 8-bit floating point specification (OFP8)
-for the E4M3 format; their quantization step is taken in float32 (R13).
+for the E4M3 format; their quantization step is taken in float32 (R16).
 """
 
 from __future__ import annotations
@@ -267,7 +267,7 @@ def lmhead_conf(h, W):
 # NaN; every other code is (1 + m/8) 2^(e-7).  No infinities; the largest
 # finite magnitude is 448.
 #
-# W8A8 (R12, R13): every vocabulary row of W is stored as E4M3 codes with one
+# W8A8 (R15, R16): every vocabulary row of W is stored as E4M3 codes with one
 # float32 scale (per-output-channel weight quantization, done offline); the
 # hidden states are quantized per position at run time (per-token dynamic
 # activation quantization).  SmoothQuant's smoothing factors are folded into
@@ -318,7 +318,7 @@ def e4m3_encode(y) -> np.ndarray:
 
 
 def quant_fp8_rows(x):
-    """Per-row dynamic quantization to E4M3 (R13).  The steps are taken in
+    """Per-row dynamic quantization to E4M3 (R16).  The steps are taken in
     float32, the precision in which the kernels take the same rounding
     decisions:  amax = max_k |x_k|;  r = 448 / amax and s = amax / 448, each
     rounded to float32 (r = s = 1 for an all-zero row);  code_k = the E4M3
