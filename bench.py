@@ -247,6 +247,7 @@ def dualstream_pairs(n_vis, n_txt, block):
 
 def secondary(args, stream):
     """The other workloads, each timed on its own (not part of `value`)."""
+    import numpy as np
     import torch
     from block_diffusion_vlm_amd import runner, synth
     res = {}
@@ -276,6 +277,41 @@ def secondary(args, stream):
     del st8, r6
     if args.fp8_only:
         return res
+
+    # Whole blocks: the device-resident loop (up to 16 steps enqueued, the
+    # steps that run decided on the device), bf16 and FP8 LM heads.
+    for fp8 in (False, True):
+        rl = synth.qwen_block_loop(fp8=fp8)
+        loop = runner.BlockLoop(rl)
+        loop.reset()
+        loop.run()
+        torch.cuda.synchronize()
+        n_steps = int(loop.n_steps.item())
+        tok_ref = loop.tokens.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            loop.reset()
+            loop.run()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            loop.reset()
+            loop.run()
+        torch.cuda.synchronize()
+        ms = timed(g.replay, max(5, iters // 8), 2, stream)
+        torch.cuda.synchronize()
+        assert torch.equal(loop.tokens, tok_ref) and int(loop.n_steps.item()) == n_steps
+        committed = int(np.asarray(rl["masked"]).sum())
+        res["block_loop_fp8" if fp8 else "block_loop"] = {
+            "us_per_block": round(ms * 1e3, 2), "steps": n_steps, "max_steps": loop.S,
+            "committed_per_block": committed,
+            "committed_tok_per_s": round(committed / (ms * 1e-3), 1),
+            "us_per_step": round(ms * 1e3 / n_steps, 2),
+            "shape": "one 16-position block of the Qwen-shaped decode, planted to finish in "
+                     "8 steps"}
+        del loop, rl, g
 
     r5 = synth.dualstream()
     ds = runner.DualStream(r5)

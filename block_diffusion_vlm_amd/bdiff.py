@@ -26,7 +26,7 @@ EXPORTS = (
     "bd_block_attn_ws_bytes", "bd_block_attn",
     "bd_lmhead_conf_ws_bytes", "bd_lmhead_conf", "bd_lmhead_conf_commit",
     "bd_lmhead_conf_fp8_ws_bytes", "bd_lmhead_conf_fp8", "bd_lmhead_conf_commit_fp8",
-    "bd_quant_fp8_rows", "bd_commit", "bd_spec_accept", "bd_cert_scan", "bd_dualstream_attn",
+    "bd_quant_fp8_rows", "bd_block_loop_ws_bytes", "bd_block_loop", "bd_commit", "bd_spec_accept", "bd_cert_scan", "bd_dualstream_attn",
 )
 
 
@@ -57,6 +57,9 @@ _SIGS = {
     "bd_lmhead_conf_commit_fp8": ([_P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _SZ,
                                    _P], _I),
     "bd_quant_fp8_rows": ([_P, _I, _I, _P, _P, _P], _I),
+    "bd_block_loop_ws_bytes": ([_I, _I, _I, _I, _I, _I, _I, _I], _SZ),
+    "bd_block_loop": ([_I, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _F, _P, _P, _P, _I, _I, _F,
+                       _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "bd_commit": ([_P, _P, _I, _F, _P, _P, _P, _P], _I),
     "bd_spec_accept": ([_P, _P, _I, _I, _P, _P, _P, _P], _I),
     "bd_cert_scan": ([_P, _P, _P, _I, _I, _P, _P, _P, _P], _I),
@@ -172,6 +175,21 @@ def bd_lmhead_conf_commit_fp8(h, Wq, w_scale, B, d, V, tau, conf, argmax, masked
 def bd_quant_fp8_rows(x, R, d, q, scale, stream=None, check=True) -> int:
     st = lib().bd_quant_fp8_rows(_ptr(x), R, d, _ptr(q), _ptr(scale), _stream(stream))
     return _ret("bd_quant_fp8_rows", st, check)
+
+
+def bd_block_loop_ws_bytes(P, B, Hq, Hkv, dh, d, V, w_fp8) -> int:
+    return int(lib().bd_block_loop_ws_bytes(P, B, Hq, Hkv, dh, d, V, int(bool(w_fp8))))
+
+
+def bd_block_loop(dt, q_steps, k_cache, v_cache, P, cap, intra_mask, B, Hq, Hkv, dh, scale,
+                  h_steps, W, w_scale, d, V, tau, max_steps, masked, tokens, attn_out, conf,
+                  argmax, n_committed, n_steps, ws, ws_bytes, stream=None, check=True) -> int:
+    st = lib().bd_block_loop(dt, _ptr(q_steps), _ptr(k_cache), _ptr(v_cache), P, cap,
+                             _ptr(intra_mask), B, Hq, Hkv, dh, scale, _ptr(h_steps), _ptr(W),
+                             _ptr(w_scale), d, V, tau, max_steps, _ptr(masked), _ptr(tokens),
+                             _ptr(attn_out), _ptr(conf), _ptr(argmax), _ptr(n_committed),
+                             _ptr(n_steps), _ptr(ws), ws_bytes, _stream(stream))
+    return _ret("bd_block_loop", st, check)
 
 
 def bd_commit(conf, argmax, B, tau, masked, tokens, n_committed, stream=None, check=True) -> int:

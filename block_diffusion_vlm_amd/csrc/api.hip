@@ -197,6 +197,106 @@ bd_status bd_quant_fp8_rows(const void* x, int32_t R, int32_t d, uint8_t* q, flo
     return launch_status(bd::launch_quant_fp8_rows(x, R, d, q, scale, stream));
 }
 
+namespace {
+
+inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct LoopWs {
+    size_t attn_off, lm_off, total;
+};
+
+LoopWs loop_ws(int32_t P, int32_t B, int32_t Hq, int32_t Hkv, int32_t dh, int32_t d, int32_t V,
+               bool fp8) {
+    LoopWs L;
+    L.attn_off = 256;                                       // the gate word
+    L.lm_off = L.attn_off + al256(bd::block_attn_ws_bytes(P, B, Hq, Hkv, dh));
+    L.total = L.lm_off + al256(fp8 ? bd::lmhead_fp8_ws_bytes(B, d, V)
+                                   : bd::lmhead_ws_bytes(B, d, V));
+    return L;
+}
+
+}  // namespace
+
+size_t bd_block_loop_ws_bytes(int32_t P, int32_t B, int32_t Hq, int32_t Hkv, int32_t dh,
+                              int32_t d, int32_t V, int32_t w_fp8) {
+    if (P < 0 || B < 1 || B > 64 || Hq < 1 || Hkv < 1 || dh < 1 || d < 1 || V < 1) return 0;
+    if (w_fp8 && (d < 128 || d > 16384 || d % 128 != 0)) return 0;
+    return loop_ws(P, B, Hq, Hkv, dh, d, V, w_fp8 != 0).total;
+}
+
+bd_status bd_block_loop(bd_dtype dt, const void* q_steps, const void* k_cache,
+                        const void* v_cache, int32_t P, int32_t cap, const uint64_t* intra_mask,
+                        int32_t B, int32_t Hq, int32_t Hkv, int32_t dh, float scale,
+                        const void* h_steps, const void* W, const float* w_scale, int32_t d,
+                        int32_t V, float tau, int32_t max_steps, uint8_t* masked,
+                        int32_t* tokens, void* attn_out, float* conf, int32_t* argmax,
+                        int32_t* n_committed, int32_t* n_steps, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+    if (!q_steps || !k_cache || !v_cache || !intra_mask || !h_steps || !W || !masked ||
+        !tokens || !attn_out || !conf || !argmax || !n_committed || !n_steps)
+        return BD_E_NULL;
+    if (dt != BD_F32 && dt != BD_BF16) return BD_E_DTYPE;
+    const bool fp8 = w_scale != nullptr;
+    if (fp8 && dt != BD_BF16) return BD_E_DTYPE;
+    // attention limits (bd_block_attn)
+    if (B < 1 || B > 64 || P < 0 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0) return BD_E_SHAPE;
+    if ((int64_t)P + B > cap) return BD_E_SHAPE;
+    if (!dh_ok(dt, dh)) return BD_E_SHAPE;
+    if (dt == BD_BF16 && (int64_t)P + B > 65536) return BD_E_SHAPE;
+    if (!(scale >= 0.f) || isinf(scale)) return BD_E_SHAPE;
+    // LM-head limits (bd_lmhead_conf / bd_lmhead_conf_fp8)
+    if (d < 1 || V < 1) return BD_E_SHAPE;
+    if ((dt == BD_BF16 || fp8) && (d % 128 != 0 || d > 16384)) return BD_E_SHAPE;
+    if (!(tau == tau)) return BD_E_SHAPE;
+    if (max_steps < 1 || max_steps > 1024) return BD_E_SHAPE;
+    if (!aligned16(q_steps) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        !aligned16(attn_out) || !aligned16(h_steps) || !aligned16(W) ||
+        (fp8 && !aligned16(w_scale)))
+        return BD_E_ALIGN;
+    const LoopWs L = loop_ws(P, B, Hq, Hkv, dh, d, V, fp8);
+    if (!ws || ws_bytes < L.total) return BD_E_WORKSPACE;
+    if (!aligned16(ws)) return BD_E_ALIGN;
+
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    int32_t* gate = reinterpret_cast<int32_t*>(base);
+    void* attn_ws = base + L.attn_off;
+    void* lm_ws = base + L.lm_off;
+    const float sc = default_scale(scale, dh);
+    const size_t es = dt == BD_BF16 ? 2 : 4;
+    const size_t q_step = size_t(B) * Hq * dh * es;
+    const size_t h_step = size_t(B) * d * es;
+    hipError_t e = bd::launch_loop_init(masked, B, gate, n_steps, n_committed, max_steps, stream);
+    for (int s = 0; s < max_steps && e == hipSuccess; ++s) {
+        const uint8_t* qs = static_cast<const uint8_t*>(q_steps) + s * q_step;
+        uint8_t* os = static_cast<uint8_t*>(attn_out) + s * q_step;
+        const uint8_t* hs = static_cast<const uint8_t*>(h_steps) + s * h_step;
+        if (dt == BD_BF16)
+            e = bd::launch_block_attn_bf16(qs, k_cache, v_cache, P, cap, intra_mask, B, Hq, Hkv,
+                                           sc, os, attn_ws, stream, gate);
+        else
+            e = bd::launch_block_attn_f32(reinterpret_cast<const float*>(qs),
+                                          static_cast<const float*>(k_cache),
+                                          static_cast<const float*>(v_cache), P, cap, intra_mask,
+                                          B, Hq, Hkv, dh, sc, reinterpret_cast<float*>(os),
+                                          stream, gate);
+        if (e != hipSuccess) break;
+        bd::Finish f{conf + size_t(s) * B, argmax + size_t(s) * B, true, tau, masked, tokens,
+                     n_committed + s};
+        f.gate = gate;
+        f.gate_out = gate;
+        f.steps = n_steps;
+        if (fp8)
+            e = bd::launch_lmhead_fp8(hs, static_cast<const uint8_t*>(W), w_scale, B, d, V, f,
+                                      lm_ws, stream);
+        else if (dt == BD_BF16)
+            e = bd::launch_lmhead_bf16(hs, W, B, d, V, f, lm_ws, stream);
+        else
+            e = bd::launch_lmhead_f32(reinterpret_cast<const float*>(hs),
+                                      static_cast<const float*>(W), B, d, V, f, lm_ws, stream);
+    }
+    return launch_status(e);
+}
+
 bd_status bd_commit(const float* conf, const int32_t* argmax, int32_t B, float tau,
                     uint8_t* masked, int32_t* tokens, int32_t* n_committed, hipStream_t stream) {
     if (!conf || !argmax || !masked || !tokens || !n_committed) return BD_E_NULL;

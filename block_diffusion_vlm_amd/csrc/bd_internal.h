@@ -37,6 +37,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
 }
 
+// Gate of a step of the device-resident block loop: the number of block
+// positions still masked, written by the previous step's commit.  A kernel
+// given a gate that reads 0 returns at once (the block is complete); a null
+// gate always runs.
+__device__ __forceinline__ bool gated_off(const int32_t* gate) {
+    return gate != nullptr && *gate == 0;
+}
+
 // Softmax partial state (max in log2 units, sum of 2^(x - max), index).
 struct ArgSoft {
     float m;
@@ -67,6 +75,10 @@ hipError_t launch_spec_accept(const int32_t* draft, const int32_t* verify, int B
 hipError_t launch_cert_scan(const float* conf, const int32_t* atok, const int32_t* ttok, int n,
                             int k, int32_t* order, int32_t* accepted, int32_t* skip,
                             hipStream_t st);
+// Start of the device-resident block loop: gate = masked positions, the step
+// counter and the per-step commit counts zeroed.
+hipError_t launch_loop_init(const uint8_t* masked, int B, int32_t* gate, int32_t* steps,
+                            int32_t* n_committed, int S, hipStream_t st);
 
 // LM head.  The merge of the per-workgroup partials writes conf/argmax and,
 // when `commit` is set, also applies the threshold commit to the block.
@@ -78,6 +90,12 @@ struct Finish {
     uint8_t* masked;
     int32_t* tokens;
     int32_t* n_committed;
+    // Device-resident block loop only (null otherwise): the step's gate (see
+    // gated_off), where the commit leaves the next gate (the same word), and
+    // the executed-step counter it increments.
+    const int32_t* gate = nullptr;
+    int32_t* gate_out = nullptr;
+    int32_t* steps = nullptr;
 };
 int lmhead_grid(int B, int d, int V);           // workgroups used for a shape
 size_t lmhead_ws_bytes(int B, int d, int V);
@@ -98,10 +116,12 @@ hipError_t launch_quant_fp8_rows(const void* x, int R, int d, uint8_t* q, float*
 size_t block_attn_ws_bytes(int P, int Bq, int Hq, int Hkv, int dh);
 hipError_t launch_block_attn_bf16(const void* q, const void* kc, const void* vc, int P, int cap,
                                   const uint64_t* mask, int Bq, int Hq, int Hkv, float scale,
-                                  void* out, void* ws, hipStream_t st);
+                                  void* out, void* ws, hipStream_t st,
+                                  const int32_t* gate = nullptr);
 hipError_t launch_block_attn_f32(const float* q, const float* kc, const float* vc, int P, int cap,
                                  const uint64_t* mask, int Bq, int Hq, int Hkv, int dh,
-                                 float scale, float* out, hipStream_t st);
+                                 float scale, float* out, hipStream_t st,
+                                 const int32_t* gate = nullptr);
 
 // Dual-stream attention
 hipError_t launch_dualstream_bf16(const void* q, const void* k, const void* v, int n_vis,

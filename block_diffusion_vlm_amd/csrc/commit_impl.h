@@ -11,11 +11,15 @@ namespace bd {
 // some position is masked, the most confident masked position (lowest index
 // on ties) is committed alone.  Committing sets tokens[i] = argmax and
 // masked[i] = 0.  Must be called by all 64 lanes of a wave; c/a are lane i's
-// confidence and token (ignored for i >= B).
+// confidence and token (ignored for i >= B).  Inside the device-resident
+// block loop (else both null), `gate_out` receives the number of positions
+// still masked afterwards (the next step's gate) and `steps` counts the step.
 __device__ __forceinline__ void commit_wave(float c, int32_t a, int B, float tau,
                                             uint8_t* __restrict__ masked,
                                             int32_t* __restrict__ tokens,
-                                            int32_t* __restrict__ n_committed) {
+                                            int32_t* __restrict__ n_committed,
+                                            int32_t* gate_out = nullptr,
+                                            int32_t* steps = nullptr) {
     const int i = threadIdx.x & 63;
     const bool in = i < B;
     const bool m = in && masked[i] != 0;
@@ -44,7 +48,11 @@ __device__ __forceinline__ void commit_wave(float c, int32_t a, int B, float tau
         tokens[i] = a;
         masked[i] = 0;
     }
-    if (i == 0) *n_committed = n;
+    if (i == 0) {
+        *n_committed = n;
+        if (gate_out != nullptr) *gate_out = __popcll(masked_bits) - n;
+        if (steps != nullptr) *steps += 1;
+    }
 }
 
 }  // namespace bd

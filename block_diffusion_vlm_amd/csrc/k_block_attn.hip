@@ -45,7 +45,9 @@ inline size_t partials_bytes(int rows, int nsplit) {
 __global__ __launch_bounds__(256) void block_attn_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int P, int cap, const uint64_t* __restrict__ mask, int Bq,
-    int Hq, int Hkv, float scale_log2, void* __restrict__ ws, int nsplit, int kt) {
+    int Hq, int Hkv, float scale_log2, void* __restrict__ ws, int nsplit, int kt,
+    const int32_t* __restrict__ gate) {
+    if (gated_off(gate)) return;
     __shared__ __align__(16) uint16_t kbuf[2][kTile];
     __shared__ __align__(16) uint16_t vbuf[2][kTile];
     const int split = blockIdx.x;
@@ -165,7 +167,9 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
 constexpr int kCombineThreads = 128;
 
 __global__ __launch_bounds__(kCombineThreads) void block_attn_combine_kernel(
-    const void* __restrict__ ws, int Bq, int Hq, int Hkv, int nsplit, uint16_t* __restrict__ out) {
+    const void* __restrict__ ws, int Bq, int Hq, int Hkv, int nsplit, uint16_t* __restrict__ out,
+    const int32_t* __restrict__ gate) {
+    if (gated_off(gate)) return;
     __shared__ float wsh[1024];
     __shared__ float red[kCombineThreads / 64];
     const int rg = blockIdx.x;                      // global row = g * R + r
@@ -228,7 +232,8 @@ __global__ __launch_bounds__(kCombineThreads) void block_attn_combine_kernel(
 __global__ __launch_bounds__(64) void block_attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
     int P, int cap, const uint64_t* __restrict__ mask, int Bq, int Hq, int Hkv, int dh,
-    float scale_log2, float* __restrict__ out) {
+    float scale_log2, float* __restrict__ out, const int32_t* __restrict__ gate) {
+    if (gated_off(gate)) return;
     __shared__ float qs[128];
     const int qi = blockIdx.x / Hq;
     const int h = blockIdx.x % Hq;
@@ -306,7 +311,7 @@ size_t block_attn_ws_bytes(int P, int Bq, int Hq, int Hkv, int dh) {
 
 hipError_t launch_block_attn_bf16(const void* q, const void* kc, const void* vc, int P, int cap,
                                   const uint64_t* mask, int Bq, int Hq, int Hkv, float scale,
-                                  void* out, void* ws, hipStream_t st) {
+                                  void* out, void* ws, hipStream_t st, const int32_t* gate) {
     const int kt = tiles_per_split(P, Bq, Hq, Hkv);
     const int nsplit = num_splits(P, Bq, Hq, Hkv);
     const int R = Bq * (Hq / Hkv);
@@ -314,19 +319,19 @@ hipError_t launch_block_attn_bf16(const void* q, const void* kc, const void* vc,
     hipLaunchKernelGGL(block_attn_split_kernel, grid, dim3(256), 0, st,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                        static_cast<const uint16_t*>(vc), P, cap, mask, Bq, Hq, Hkv,
-                       scale * kLog2e, ws, nsplit, kt);
+                       scale * kLog2e, ws, nsplit, kt, gate);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(block_attn_combine_kernel, dim3(Bq * Hq), dim3(kCombineThreads), 0, st, ws,
-                       Bq, Hq, Hkv, nsplit, static_cast<uint16_t*>(out));
+                       Bq, Hq, Hkv, nsplit, static_cast<uint16_t*>(out), gate);
     return hipGetLastError();
 }
 
 hipError_t launch_block_attn_f32(const float* q, const float* kc, const float* vc, int P, int cap,
                                  const uint64_t* mask, int Bq, int Hq, int Hkv, int dh,
-                                 float scale, float* out, hipStream_t st) {
+                                 float scale, float* out, hipStream_t st, const int32_t* gate) {
     hipLaunchKernelGGL(block_attn_f32_kernel, dim3(Bq * Hq), dim3(64), 0, st, q, kc, vc, P, cap,
-                       mask, Bq, Hq, Hkv, dh, scale * kLog2e, out);
+                       mask, Bq, Hq, Hkv, dh, scale * kLog2e, out, gate);
     return hipGetLastError();
 }
 

@@ -62,7 +62,9 @@ __device__ ArgSoft reduce_column(const WsView& w, int G, int col) {
 // One wave per position: merged confidence and argmax.
 __global__ __launch_bounds__(64) void lmhead_combine_kernel(const void* __restrict__ ws, int G,
                                                             int B, float* __restrict__ conf,
-                                                            int32_t* __restrict__ argmax) {
+                                                            int32_t* __restrict__ argmax,
+                                                            const int32_t* __restrict__ gate) {
+    if (gated_off(gate)) return;
     const WsView w = ws_view(const_cast<void*>(ws), G, B);
     const int col = blockIdx.x;
     const ArgSoft r = reduce_column(w, G, col);
@@ -77,7 +79,11 @@ __global__ __launch_bounds__(64) void lmhead_combine_kernel(const void* __restri
 __global__ __launch_bounds__(1024) void lmhead_combine_commit_kernel(
     const void* __restrict__ ws, int G, int B, float* __restrict__ conf,
     int32_t* __restrict__ argmax, float tau, uint8_t* __restrict__ masked,
-    int32_t* __restrict__ tokens, int32_t* __restrict__ n_committed) {
+    int32_t* __restrict__ tokens, int32_t* __restrict__ n_committed, const int32_t* gate,
+    int32_t* gate_out, int32_t* steps) {
+    // gate and gate_out are the same word inside the block loop: the gate is
+    // read here, before the commit below replaces it.
+    if (gated_off(gate)) return;
     __shared__ float sconf[64];
     __shared__ int sarg[64];
     const WsView w = ws_view(const_cast<void*>(ws), G, B);
@@ -96,7 +102,7 @@ __global__ __launch_bounds__(1024) void lmhead_combine_commit_kernel(
     __syncthreads();
     if (wave == 0)
         commit_wave(lane < B ? sconf[lane] : 0.f, lane < B ? sarg[lane] : 0, B, tau, masked,
-                    tokens, n_committed);
+                    tokens, n_committed, gate_out, steps);
 }
 
 }  // namespace
@@ -104,10 +110,11 @@ __global__ __launch_bounds__(1024) void lmhead_combine_commit_kernel(
 hipError_t launch_combine(void* ws, int G, int B, const Finish& f, hipStream_t st) {
     if (f.commit)
         hipLaunchKernelGGL(lmhead_combine_commit_kernel, dim3(1), dim3(1024), 0, st, ws, G, B,
-                           f.conf, f.argmax, f.tau, f.masked, f.tokens, f.n_committed);
+                           f.conf, f.argmax, f.tau, f.masked, f.tokens, f.n_committed, f.gate,
+                           f.gate_out, f.steps);
     else
         hipLaunchKernelGGL(lmhead_combine_kernel, dim3(B), dim3(64), 0, st, ws, G, B, f.conf,
-                           f.argmax);
+                           f.argmax, f.gate);
     return hipGetLastError();
 }
 
@@ -133,7 +140,9 @@ template <int NB, int NCH>
 __global__ __launch_bounds__(256) void lmhead_bf16_kernel(const uint16_t* __restrict__ h,
                                                           const uint16_t* __restrict__ W,
                                                           int B, int d, int V, int ntiles,
-                                                          void* __restrict__ ws) {
+                                                          void* __restrict__ ws,
+                                                          const int32_t* __restrict__ gate) {
+    if (gated_off(gate)) return;
     constexpr int NL = NCH * 4;                       // 16-byte loads per lane per tile
     constexpr int PIECES = NCH * 16;                  // 16-byte pieces per row segment
     __shared__ f32x4 red[2][4][NB][64];               // per-wave partial logits, 2 buffers
@@ -249,7 +258,8 @@ __global__ __launch_bounds__(256) void lmhead_bf16_kernel(const uint16_t* __rest
 template <int NB>
 __global__ __launch_bounds__(256) void lmhead_bf16_generic_kernel(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int B, int d, int V,
-    int ntiles, void* __restrict__ ws) {
+    int ntiles, void* __restrict__ ws, const int32_t* __restrict__ gate) {
+    if (gated_off(gate)) return;
     __shared__ ArgSoft fin[4][NB][16];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -303,7 +313,9 @@ constexpr int kF32Rows = 256;
 
 __global__ __launch_bounds__(256) void lmhead_f32_kernel(const float* __restrict__ h,
                                                          const float* __restrict__ W, int B,
-                                                         int d, int V, void* __restrict__ ws) {
+                                                         int d, int V, void* __restrict__ ws,
+                                                         const int32_t* __restrict__ gate) {
+    if (gated_off(gate)) return;
     extern __shared__ float hs[];
     __shared__ ArgSoft wst[4];
     const int b = blockIdx.y;
@@ -356,7 +368,7 @@ hipError_t launch_nb(const void* h, const void* W, int B, int d, int V, const Fi
     int ks = 0, nch = 0;
     if (!plan_bf16(B, d, &ks, &nch)) {
         hipLaunchKernelGGL(lmhead_bf16_generic_kernel<NB>, dim3(G), dim3(256), 0, st, hh, ww, B,
-                           d, V, ntiles, ws);
+                           d, V, ntiles, ws, f.gate);
         const hipError_t e = hipGetLastError();
         return e != hipSuccess ? e : launch_combine(ws, G, B, f, st);
     }
@@ -364,7 +376,7 @@ hipError_t launch_nb(const void* h, const void* W, int B, int d, int V, const Fi
     case N:                                                                                \
         if constexpr (N * NB <= 8) {                                                       \
             hipLaunchKernelGGL((lmhead_bf16_kernel<NB, N>), dim3(G), dim3(64 * ks), 0, st, \
-                               hh, ww, B, d, V, ntiles, ws);                               \
+                               hh, ww, B, d, V, ntiles, ws, f.gate);                       \
         } else {                                                                           \
             return hipErrorInvalidValue;                                                   \
         }                                                                                  \
@@ -418,7 +430,7 @@ hipError_t launch_lmhead_f32(const float* h, const float* W, int B, int d, int V
                              const Finish& f, void* ws, hipStream_t st) {
     const dim3 grid((V + kF32Rows - 1) / kF32Rows, B);
     hipLaunchKernelGGL(lmhead_f32_kernel, grid, dim3(kF32Rows), size_t(d) * sizeof(float), st, h,
-                       W, B, d, V, ws);
+                       W, B, d, V, ws, f.gate);
     const hipError_t e = hipGetLastError();
     return e != hipSuccess ? e : launch_combine(ws, grid.x, B, f, st);
 }

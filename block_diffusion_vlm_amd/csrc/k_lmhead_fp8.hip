@@ -90,7 +90,9 @@ __device__ __forceinline__ f32x4 load_scales4(const float* __restrict__ ws, int 
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, int d,
                                                          uint8_t* __restrict__ q,
-                                                         float* __restrict__ scale) {
+                                                         float* __restrict__ scale,
+                                                         const int32_t* __restrict__ gate) {
+    if (gated_off(gate)) return;
     __shared__ float wmax[4];
     const size_t row = blockIdx.x;
     const u32x4* xr = reinterpret_cast<const u32x4*>(x + row * d);
@@ -131,7 +133,9 @@ __global__ __launch_bounds__(256) void lmhead_fp8_kernel(const uint16_t* __restr
                                                          const uint8_t* __restrict__ W,
                                                          const float* __restrict__ wscale, int B,
                                                          int d, int V, int ntiles,
-                                                         void* __restrict__ ws) {
+                                                         void* __restrict__ ws,
+                                                         const int32_t* __restrict__ gate) {
+    if (gated_off(gate)) return;
     constexpr int RT = kFp8Rows / 16;              // MFMA row blocks per tile
     constexpr int PIECES = NCH * 8;                // 16-byte pieces per row segment
     constexpr int NL = kFp8Rows * PIECES / 64;     // 16-byte loads per lane per tile
@@ -357,7 +361,9 @@ __global__ __launch_bounds__(256) void lmhead_fp8_kernel(const uint16_t* __restr
 template <int NB>
 __global__ __launch_bounds__(256) void lmhead_fp8_generic_kernel(
     const uint8_t* __restrict__ hq, const float* __restrict__ hs, const uint8_t* __restrict__ W,
-    const float* __restrict__ wscale, int B, int d, int V, int ntiles, void* __restrict__ ws) {
+    const float* __restrict__ wscale, int B, int d, int V, int ntiles, void* __restrict__ ws,
+    const int32_t* __restrict__ gate) {
+    if (gated_off(gate)) return;
     __shared__ ArgSoft fin[4][NB][16];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -461,9 +467,10 @@ Fp8Ws fp8_ws_layout(int B, int d, int V) {
 
 template <int NB, int NCH>
 void launch_fp8_stream(int G, int ks, const uint16_t* h, const uint8_t* W, const float* wsc,
-                       int B, int d, int V, int ntiles, void* ws, hipStream_t st) {
+                       int B, int d, int V, int ntiles, void* ws, hipStream_t st,
+                       const int32_t* gate) {
     hipLaunchKernelGGL((lmhead_fp8_kernel<NB, NCH>), dim3(G), dim3(64 * ks), 0, st, h, W, wsc, B,
-                       d, V, ntiles, ws);
+                       d, V, ntiles, ws, gate);
 }
 
 template <int NB>
@@ -478,11 +485,11 @@ hipError_t launch_fp8_nb(const void* h, const uint8_t* W, const float* wsc, int 
         uint8_t* base = static_cast<uint8_t*>(ws);
         uint8_t* hq = base + L.codes_off;
         float* hs = reinterpret_cast<float*>(base + L.scales_off);
-        hipLaunchKernelGGL(quant_rows_kernel, dim3(B), dim3(256), 0, st, hh, d, hq, hs);
+        hipLaunchKernelGGL(quant_rows_kernel, dim3(B), dim3(256), 0, st, hh, d, hq, hs, f.gate);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(lmhead_fp8_generic_kernel<NB>, dim3(G), dim3(256), 0, st, hq, hs, W,
-                           wsc, B, d, V, ntiles, ws);
+                           wsc, B, d, V, ntiles, ws, f.gate);
         e = hipGetLastError();
         return e != hipSuccess ? e : launch_combine(ws, G, B, f, st);
     }
@@ -490,7 +497,7 @@ hipError_t launch_fp8_nb(const void* h, const uint8_t* W, const float* wsc, int 
 #define BD_FP8_CASE(N)                                                               \
     case N:                                                                          \
         if constexpr (N * (2 + NB) <= 24 && NB + N <= 9) {                           \
-            launch_fp8_stream<NB, N>(G, ks, hh, W, wsc, B, d, V, ntiles, ws, st);   \
+            launch_fp8_stream<NB, N>(G, ks, hh, W, wsc, B, d, V, ntiles, ws, st, f.gate); \
         } else {                                                                     \
             return hipErrorInvalidValue;                                             \
         }                                                                            \
@@ -537,7 +544,7 @@ hipError_t launch_quant_fp8_rows(const void* x, int R, int d, uint8_t* q, float*
                                  hipStream_t st) {
     if (R == 0) return hipSuccess;
     hipLaunchKernelGGL(quant_rows_kernel, dim3(R), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(x), d, q, scale);
+                       static_cast<const uint16_t*>(x), d, q, scale, nullptr);
     return hipGetLastError();
 }
 

@@ -76,6 +76,29 @@ __global__ __launch_bounds__(1024) void cert_scan_kernel(const float* __restrict
     }
 }
 
+// Start of the device-resident block loop (one wave): the gate is the number
+// of masked positions, the step counter and the per-step commit counts start
+// at zero.
+__global__ __launch_bounds__(64) void loop_init_kernel(const uint8_t* __restrict__ masked, int B,
+                                                       int32_t* __restrict__ gate,
+                                                       int32_t* __restrict__ steps,
+                                                       int32_t* __restrict__ n_committed, int S) {
+    const int i = threadIdx.x;
+    const uint64_t bits = __ballot(i < B && masked[i] != 0);
+    for (int s = i; s < S; s += 64) n_committed[s] = 0;
+    if (i == 0) {
+        *gate = __popcll(bits);
+        *steps = 0;
+    }
+}
+
+hipError_t launch_loop_init(const uint8_t* masked, int B, int32_t* gate, int32_t* steps,
+                            int32_t* n_committed, int S, hipStream_t st) {
+    hipLaunchKernelGGL(loop_init_kernel, dim3(1), dim3(64), 0, st, masked, B, gate, steps,
+                       n_committed, S);
+    return hipGetLastError();
+}
+
 hipError_t launch_commit(const float* conf, const int32_t* argmax, int B, float tau,
                          uint8_t* masked, int32_t* tokens, int32_t* n_committed, hipStream_t st) {
     hipLaunchKernelGGL(commit_kernel, dim3(1), dim3(64), 0, st, conf, argmax, B, tau, masked,

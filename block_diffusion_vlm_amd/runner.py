@@ -170,6 +170,56 @@ class DecodeStep:
                          self.n_committed, stream)
 
 
+class BlockLoop:
+    """bd_block_loop over device buffers: every decode step of one block, on
+    the device, until the block is committed.  Inputs from
+    synth.qwen_block_loop (bf16, or the FP8 LM head), or any dict with the
+    same keys (q_steps, h_steps, ...).  ``reset()`` restores the block state
+    with two device copies."""
+
+    def __init__(self, inp: dict, device="cuda", max_steps=None):
+        fp8 = inp["dtype"] == "fp8"
+        self.dt = bd.BD_BF16 if fp8 else dtype_code(inp["dtype"])
+        B, P = inp["B"], inp["P"]
+        S = inp["q_steps"].shape[0] if max_steps is None else max_steps
+        Hq, Hkv, dh, d, V = (inp[k] for k in ("Hq", "Hkv", "dh", "d", "V"))
+        self.inp = inp
+        self.B, self.P, self.S, self.Hq, self.Hkv, self.dh, self.d, self.V = (
+            B, P, S, Hq, Hkv, dh, d, V)
+        self.cap = inp["cap"]
+        self.tau = float(inp["tau"])
+        self.q = to_dev(inp["q_steps"], device)
+        self.h = to_dev(inp["h_steps"], device)
+        self.k_cache = to_dev(inp["k_cache"], device)
+        self.v_cache = to_dev(inp["v_cache"], device)
+        self.W = to_dev(inp["W"], device)
+        self.w_scale = to_dev(inp["w_scale"], device) if fp8 else None
+        self.mask = mask_dev(bd.BD_MASK_BIDIR, B, device)
+        self.masked0 = to_dev(np.asarray(inp["masked"], np.uint8), device)
+        self.tokens0 = to_dev(np.asarray(inp["tokens"], np.int32), device)
+        self.masked = self.masked0.clone()
+        self.tokens = self.tokens0.clone()
+        tdt = torch.float32 if self.dt == bd.BD_F32 else torch.bfloat16
+        self.attn_out = torch.zeros((S, B, Hq, dh), dtype=tdt, device=device)
+        self.conf = torch.full((S, B), -1.0, dtype=torch.float32, device=device)
+        self.argmax = torch.full((S, B), -1, dtype=torch.int32, device=device)
+        self.n_committed = torch.full((S,), -1, dtype=torch.int32, device=device)
+        self.n_steps = torch.full((1,), -1, dtype=torch.int32, device=device)
+        self.ws_bytes = bd.bd_block_loop_ws_bytes(P, B, Hq, Hkv, dh, d, V, fp8)
+        self.ws = workspace(self.ws_bytes, device)
+
+    def reset(self):
+        self.masked.copy_(self.masked0)
+        self.tokens.copy_(self.tokens0)
+
+    def run(self, stream=None):
+        bd.bd_block_loop(self.dt, self.q, self.k_cache, self.v_cache, self.P, self.cap, self.mask,
+                         self.B, self.Hq, self.Hkv, self.dh, 0.0, self.h, self.W, self.w_scale,
+                         self.d, self.V, self.tau, self.S, self.masked, self.tokens,
+                         self.attn_out, self.conf, self.argmax, self.n_committed, self.n_steps,
+                         self.ws, self.ws_bytes, stream)
+
+
 class LinearSpecStep:
     """Linear self-speculative step: draft (bidirectional) and verify (causal)
     passes, each block attention + LM head, then bd_spec_accept."""

@@ -23,7 +23,7 @@ from __future__ import annotations
 import numpy as np
 
 BASE_SEED = 20261203
-N_CONFIGS = 6
+N_CONFIGS = 8
 
 
 # ---------------------------------------------------------------------------
@@ -31,7 +31,7 @@ N_CONFIGS = 6
 # ---------------------------------------------------------------------------
 
 def config_rng(cfg: int, seed: int | None = None) -> np.random.Generator:
-    """PCG64 stream for workload ``cfg`` (1..6): child ``cfg-1`` of
+    """PCG64 stream for workload ``cfg`` (1..8): child ``cfg-1`` of
     SeedSequence(seed or BASE_SEED)."""
     ss = np.random.SeedSequence(BASE_SEED if seed is None else seed)
     return np.random.Generator(np.random.PCG64(ss.spawn(N_CONFIGS)[cfg - 1]))
@@ -264,6 +264,60 @@ def qwen_decode_fp8(seed: int | None = None, B=16, n_vis=1024, n_prompt=256, Hq=
         "targets": t.astype(np.int32), "target_conf": c, "planted_commit": z,
         "masked": masked, "tokens": tokens,
     }
+
+
+def qwen_block_loop(seed: int | None = None, B=16, S=16, T=8, n_vis=1024, n_prompt=256,
+                    Hq=16, Hkv=2, dh=128, d=2048, V=151936, sigma_w=0.02, fp8=False) -> dict:
+    """All steps of one block of the Qwen-shaped decode, bf16 (or with the
+    FP8 LM head): a denoising trajectory.  Position 0 is the AR seed; each
+    masked position i gets a commit step c_i in [0, T), the masked positions
+    being split in random order into T non-empty groups, so that every step
+    before T commits at least one position by threshold (about two per step
+    at B = 16, T = 8, in line with MDM's 1.95 tokens per forward on the
+    overview's benchmarks).  Hidden rows per step: from step c_i on, row i is
+    planted on its final token with top probability in [0.92, 0.999]; before
+    it, on a fresh uniform token with top probability in [0.02, 0.88].
+    Block queries are drawn afresh for every step; the KV cache is fixed.
+    S >= T steps are provided (the loop must stop at T on its own)."""
+    rng = config_rng(7 if fp8 else 8, seed)
+    P = n_vis + n_prompt
+    cap = P + B
+    if fp8:
+        W = normal_e4m3(rng, (V, d))
+        w_scale = (np.float32(sigma_w / E4M3_CODE_STD)
+                   * rng.uniform(0.9, 1.1, V).astype(np.float32))
+        row = lambda v: e4m3_row_values(W[v]) * float(w_scale[v])  # noqa: E731
+    else:
+        W = normal_bf16(rng, (V, d), std=sigma_w)
+        w_scale, row = None, None
+    final = rng.integers(0, V, B)
+    order = rng.permutation(np.arange(1, B))
+    cuts = np.sort(rng.choice(np.arange(1, B - 1), T - 1, replace=False))
+    c = np.zeros(B, np.int64)
+    for g, part in enumerate(np.split(order, cuts)):
+        c[part] = g
+    h = np.empty((S, B, d), np.uint16)
+    for s in range(S):
+        late = c <= s
+        tgt = np.where(late, final, rng.integers(0, V, B))
+        conf = np.where(late, rng.uniform(0.92, 0.999, B), rng.uniform(0.02, 0.88, B))
+        h[s] = bf16_bits(plant_hidden(rng, W, tgt, conf, sigma_w, row=row))
+    masked = np.ones(B, np.uint8)
+    masked[0] = 0
+    tokens = np.zeros(B, np.int32)
+    tokens[0] = int(rng.integers(0, V))
+    r = {
+        "dtype": "fp8" if fp8 else "bf16", "B": B, "S": S, "T": T, "P": P, "n_vis": n_vis,
+        "n_prompt": n_prompt, "cap": cap, "Hq": Hq, "Hkv": Hkv, "dh": dh, "d": d, "V": V,
+        "tau": 0.9, "q_steps": normal_bf16(rng, (S * B, Hq, dh)).reshape(S, B, Hq, dh),
+        "k_cache": normal_bf16(rng, (Hkv * cap, dh)).reshape(Hkv, cap, dh),
+        "v_cache": normal_bf16(rng, (Hkv * cap, dh), trunc=4.0).reshape(Hkv, cap, dh),
+        "W": W, "h_steps": h, "final_tokens": final.astype(np.int32), "commit_step": c,
+        "masked": masked, "tokens": tokens,
+    }
+    if fp8:
+        r["w_scale"] = w_scale
+    return r
 
 
 def linear_spec(seed: int | None = None, B=32, n_vis=1024, n_prompt=256, Hq=16, Hkv=2,

@@ -205,6 +205,52 @@ bd_status bd_quant_fp8_rows(const void* x, int32_t R, int32_t d, uint8_t* q, flo
                             hipStream_t stream);
 
 /*
+ * bd_block_loop - the device-resident block loop: decode steps on one block
+ * until every position is committed, with no host round trip.  [OV §1.2:
+ * each block is denoised in parallel over several steps before the next
+ * block starts; OV §2.2.2: the block's first position is the AR seed; OV
+ * §4.1: threshold 0.9]
+ * Step s (s < max_steps) runs only while some position is still masked:
+ *   bd_block_attn(q_steps[s]) -> attn_out[s];
+ *   the LM head on h_steps[s] (bd_lmhead_conf, or bd_lmhead_conf_fp8 when
+ *   w_scale is given) -> conf[s], argmax[s]; then bd_commit on the block.
+ * A step that finds the block complete is skipped entirely on the device:
+ * its outputs are left untouched and n_committed[s] stays 0.  Every kernel
+ * of every step is enqueued up front, so the call can be captured in a HIP
+ * graph; the steps that run are decided on the device.  The per-step inputs
+ * stand for the hidden states and queries that the model's other layers
+ * produce at each step.
+ *   q_steps    [max_steps][B][Hq][dh] dtype dt (block queries per step)
+ *   k_cache, v_cache, P, cap, intra_mask, Hq, Hkv, dh, scale: as in
+ *              bd_block_attn with Bq = B (the block's K/V rows stay fixed)
+ *   h_steps    [max_steps][B][d] dtype dt (bf16 when w_scale is given)
+ *   W          [V][d] dtype dt, or E4M3 codes when w_scale ([V] float32) is
+ *              given (then dt must be BD_BF16)
+ *   tau        threshold (not NaN);  max_steps in [1, 1024]
+ *   masked [B] uint8, tokens [B] int32: block state, in/out
+ *   attn_out   [max_steps][B][Hq][dh] dtype dt out
+ *   conf, argmax [max_steps][B] out
+ *   n_committed [max_steps] int32 out (commits per step, 0 for skipped steps)
+ *   n_steps    [1] int32 out (steps executed)
+ *   ws         workspace of at least bd_block_loop_ws_bytes(P, B, Hq, Hkv, dh,
+ *              d, V, w_scale != NULL) bytes (holds the gate word between
+ *              steps; no initial contents required)
+ * Limits: those of bd_block_attn and of the LM-head call used.
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_ALIGN, BD_E_WORKSPACE,
+ *   BD_E_LAUNCH.
+ */
+size_t bd_block_loop_ws_bytes(int32_t P, int32_t B, int32_t Hq, int32_t Hkv, int32_t dh,
+                              int32_t d, int32_t V, int32_t w_fp8);
+bd_status bd_block_loop(bd_dtype dt, const void* q_steps, const void* k_cache,
+                        const void* v_cache, int32_t P, int32_t cap, const uint64_t* intra_mask,
+                        int32_t B, int32_t Hq, int32_t Hkv, int32_t dh, float scale,
+                        const void* h_steps, const void* W, const float* w_scale, int32_t d,
+                        int32_t V, float tau, int32_t max_steps, uint8_t* masked,
+                        int32_t* tokens, void* attn_out, float* conf, int32_t* argmax,
+                        int32_t* n_committed, int32_t* n_steps, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/*
  * bd_commit - threshold unmasking with the always-one rule.
  * [OV §4.1: denoising confidence threshold 0.9; OV §1.2 parallel unmasking]
  * Every position i with masked[i] != 0 and conf[i] > tau is committed.  If

@@ -72,7 +72,7 @@ __all__ = [
     "intra_block_mask", "masked_attention", "block_attn", "dualstream_attn",
     "lm_logits", "conf_argmax", "lmhead_conf", "E4M3_MAX", "e4m3_decode", "e4m3_encode",
     "quant_fp8_rows", "lm_logits_fp8", "lmhead_conf_fp8", "commit", "spec_accept", "cert_scan",
-    "decode_step", "linear_spec_step", "fused_spec_step",
+    "decode_step", "block_loop", "linear_spec_step", "fused_spec_step",
 ]
 
 
@@ -429,6 +429,35 @@ def decode_step(q, k_cache, v_cache, P, h, W, masked, tokens, tau, kind="bidir",
     conf, a = lmhead_conf(h, W) if w_scale is None else lmhead_conf_fp8(h, W, w_scale)
     m2, t2, n = commit(conf, a, masked, tokens, tau)
     return {"attn": o, "conf": conf, "argmax": a, "masked": m2, "tokens": t2, "n_committed": n}
+
+
+def block_loop(q_steps, k_cache, v_cache, P, h_steps, W, masked, tokens, tau, kind="bidir",
+               w_scale=None):
+    """The block loop: decode steps on one block while any position is still
+    masked, at most S = len(h_steps) steps; step s takes the block queries
+    q_steps[s] and hidden rows h_steps[s] (the inputs the model's other
+    layers would produce at that step).  [OV §1.2: a block is denoised in
+    parallel over several steps before the next one starts; OV §4.1:
+    threshold 0.9]  Returns the final block state, the number of steps run,
+    the commits of every step (0 for steps not run) and the outputs of the
+    steps that ran."""
+    masked = np.asarray(masked).astype(np.uint8).copy()
+    tokens = np.asarray(tokens).astype(np.int64).copy()
+    S = len(h_steps)
+    n_comm = np.zeros(S, dtype=np.int64)
+    attn, conf, argmax = [], [], []
+    for s in range(S):
+        if not masked.any():
+            break
+        o = decode_step(q_steps[s], k_cache, v_cache, P, h_steps[s], W, masked, tokens, tau,
+                        kind, w_scale)
+        masked, tokens = o["masked"], o["tokens"]
+        n_comm[s] = o["n_committed"]
+        attn.append(o["attn"])
+        conf.append(o["conf"])
+        argmax.append(o["argmax"])
+    return {"masked": masked, "tokens": tokens, "n_steps": len(conf), "n_committed": n_comm,
+            "attn": attn, "conf": conf, "argmax": argmax}
 
 
 def linear_spec_step(q_draft, kc_draft, vc_draft, q_verify, kc_verify, vc_verify, P,

@@ -201,6 +201,46 @@ def test_quant_fp8_rows_validation():
     assert q(q=MISALIGNED) == bd.BD_E_ALIGN
 
 
+def _loop(**kw):
+    a = dict(dt=bd.BD_BF16, q_steps=FAKE, k_cache=FAKE, v_cache=FAKE, P=32, cap=64,
+             intra_mask=FAKE, B=16, Hq=16, Hkv=2, dh=128, scale=0.0, h_steps=FAKE, W=FAKE,
+             w_scale=None, d=2048, V=151936, tau=0.9, max_steps=16, masked=FAKE, tokens=FAKE,
+             attn_out=FAKE, conf=FAKE, argmax=FAKE, n_committed=FAKE, n_steps=FAKE, ws=FAKE,
+             ws_bytes=1 << 30, stream=0, check=False)
+    a.update(kw)
+    return bd.bd_block_loop(**a)
+
+
+def test_block_loop_validation():
+    for name in ("q_steps", "k_cache", "intra_mask", "h_steps", "W", "masked", "tokens",
+                 "attn_out", "conf", "argmax", "n_committed", "n_steps"):
+        assert _loop(**{name: None}) == bd.BD_E_NULL, name
+    assert _loop(dt=4) == bd.BD_E_DTYPE
+    assert _loop(dt=bd.BD_F32, w_scale=FAKE, dh=16, d=16) == bd.BD_E_DTYPE   # FP8 head needs bf16
+    assert _loop(B=0) == bd.BD_E_SHAPE
+    assert _loop(B=65, cap=200) == bd.BD_E_SHAPE
+    assert _loop(P=49) == bd.BD_E_SHAPE                 # P + B > cap
+    assert _loop(Hq=15) == bd.BD_E_SHAPE
+    assert _loop(dh=64) == bd.BD_E_SHAPE
+    assert _loop(d=2000) == bd.BD_E_SHAPE
+    assert _loop(V=0) == bd.BD_E_SHAPE
+    assert _loop(tau=float("nan")) == bd.BD_E_SHAPE
+    assert _loop(max_steps=0) == bd.BD_E_SHAPE
+    assert _loop(max_steps=1025) == bd.BD_E_SHAPE
+    assert _loop(scale=-1.0) == bd.BD_E_SHAPE
+    assert _loop(q_steps=MISALIGNED) == bd.BD_E_ALIGN
+    assert _loop(w_scale=MISALIGNED) == bd.BD_E_ALIGN
+    assert _loop(attn_out=MISALIGNED) == bd.BD_E_ALIGN
+    assert _loop(ws=None) == bd.BD_E_WORKSPACE
+    need = bd.bd_block_loop_ws_bytes(32, 16, 16, 2, 128, 2048, 151936, 0)
+    assert _loop(ws_bytes=need - 1) == bd.BD_E_WORKSPACE
+    need8 = bd.bd_block_loop_ws_bytes(32, 16, 16, 2, 128, 2048, 151936, 1)
+    assert _loop(w_scale=FAKE, ws_bytes=need8 - 1) == bd.BD_E_WORKSPACE
+    assert _loop(ws=MISALIGNED) == bd.BD_E_ALIGN
+    assert bd.bd_block_loop_ws_bytes(32, 0, 16, 2, 128, 2048, 1000, 0) == 0
+    assert bd.bd_block_loop_ws_bytes(32, 16, 16, 2, 128, 2000, 1000, 1) == 0
+
+
 def test_small_calls_validation():
     c = lambda **kw: bd.bd_commit(**{**dict(conf=FAKE, argmax=FAKE, B=16, tau=0.9, masked=FAKE,
                                             tokens=FAKE, n_committed=FAKE, stream=0,
