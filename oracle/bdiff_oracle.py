@@ -56,6 +56,9 @@ design notes of the repository):
   R16 Activations are quantized per position with the scale amax/448 (the
       row maximum maps onto the largest E4M3 value), in float32, rounding to
       nearest with ties to even.
+  R17 Auto-truncation: segments (prompts, responses) start at given text
+      positions; N2N blocks tile each segment from its start and end at the
+      segment's end.  One segment reduces to R2.
 
 Every function below takes float64 (or integer) arrays and returns new arrays;
 bfloat16 inputs are passed as raw uint16 bit patterns and widened exactly.
@@ -94,12 +97,25 @@ def widen(x) -> np.ndarray:
 # Masks  [OV §2.2.1, §2.2.2; TH §4.1]
 # ---------------------------------------------------------------------------
 
-def mask_n2n(n_txt: int, block: int) -> np.ndarray:
+def mask_n2n(n_txt: int, block: int, seg_starts=None) -> np.ndarray:
     """Noisy -> noisy: bidirectional inside a block of ``block`` tokens, blocks
-    tiling the noisy stream from its first token (R2).  [OV §2.2.1 'N2N']"""
-    i = np.arange(n_txt)[:, None]
-    j = np.arange(n_txt)[None, :]
-    return (i // block) == (j // block)
+    tiling the noisy stream from its first token (R2).  [OV §2.2.1 'N2N']
+
+    With ``seg_starts`` (the auto-truncation mask, R17): the text is split
+    into segments (the turns' prompts and responses) starting at the given
+    text positions; blocks tile every segment from its own start, and a block
+    ends at its segment's end, so no block crosses into the next segment.
+    [OV §2.2.2 auto-truncation mask; TH §4.3]"""
+    starts = [0] if seg_starts is None else [int(x) for x in seg_starts]
+    label = []
+    for r in range(n_txt):
+        s = max(k for k in range(len(starts)) if starts[k] <= r)
+        label.append((s, (r - starts[s]) // block))
+    m = np.zeros((n_txt, n_txt), dtype=bool)
+    for i in range(n_txt):
+        for j in range(n_txt):
+            m[i, j] = label[i] == label[j]
+    return m
 
 
 def mask_n2c(n_txt: int) -> np.ndarray:
@@ -118,17 +134,18 @@ def mask_c2c(n: int) -> np.ndarray:
     return j <= i
 
 
-def dualstream_mask(n_vis: int, n_txt: int, block: int) -> np.ndarray:
+def dualstream_mask(n_vis: int, n_txt: int, block: int, seg_starts=None) -> np.ndarray:
     """Full boolean mask over the token order [visual | clean text | noisy
     text] (vision-efficient concatenation: one copy of the visual tokens,
-    in the clean stream).  Row = query, column = key.  [OV §2.2.1, §2.2.2]"""
+    in the clean stream).  Row = query, column = key.  ``seg_starts`` selects
+    the auto-truncated N2N blocks (see mask_n2n).  [OV §2.2.1, §2.2.2]"""
     ctx = n_vis + n_txt
     n = ctx + n_txt
     m = np.zeros((n, n), dtype=bool)
     m[:ctx, :ctx] = mask_c2c(ctx)                 # C2C over [vis | clean] (R3)
     m[ctx:, :n_vis] = True                        # noisy -> every visual key (R1)
     m[ctx:, n_vis:ctx] = mask_n2c(n_txt)          # N2C
-    m[ctx:, ctx:] = mask_n2n(n_txt, block)        # N2N
+    m[ctx:, ctx:] = mask_n2n(n_txt, block, seg_starts)   # N2N
     # clean -> noisy stays False (R4)
     return m
 
@@ -205,11 +222,12 @@ def block_attn(q, k_cache, v_cache, P: int, intra, scale: float | None = None) -
 
 
 def dualstream_attn(q, k, v, n_vis: int, n_txt: int, block: int,
-                    scale: float | None = None, rows=None) -> np.ndarray:
+                    scale: float | None = None, rows=None, seg_starts=None) -> np.ndarray:
     """Training-time attention over [visual | clean text | noisy text] with the
     N2N / N2C / C2C masks.  q/k/v [N][H][dh].  If ``rows`` is given, only those
     query rows are computed (returned in that order), for spot checks at large
-    N.  [OV §2.2.1, §2.2.2; TH §4.1]"""
+    N.  ``seg_starts`` applies the auto-truncation mask.  [OV §2.2.1, §2.2.2;
+    TH §4.1]"""
     q = widen(q)
     k = widen(k)
     v = widen(v)
@@ -218,7 +236,7 @@ def dualstream_attn(q, k, v, n_vis: int, n_txt: int, block: int,
         raise ValueError("N must equal n_vis + 2 * n_txt")
     if scale is None:
         scale = 1.0 / np.sqrt(dh)
-    allowed = dualstream_mask(n_vis, n_txt, block)
+    allowed = dualstream_mask(n_vis, n_txt, block, seg_starts)
     rows = np.arange(n) if rows is None else np.asarray(rows)
     out = np.zeros((rows.size, nh, dh))
     for h in range(nh):

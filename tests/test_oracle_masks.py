@@ -77,3 +77,58 @@ def test_spec_fused_b1_by_hand():
     # verify row sees itself; draft row sees verify row 0 (j <= i - B = 0) and itself
     assert np.array_equal(oracle.intra_block_mask("spec_fused", 2),
                           np.array([[1, 0], [1, 1]], dtype=bool))
+
+
+# ---------------------------------------------------------------------------
+# Auto-truncation (segment-clamped N2N blocks)  [OV §2.2.2; TH §4.3]
+# ---------------------------------------------------------------------------
+
+def test_one_segment_is_the_plain_n2n_mask():
+    for n, b in ((12, 2), (37, 5), (64, 64), (9, 1)):
+        assert np.array_equal(oracle.mask_n2n(n, b, [0]), oracle.mask_n2n(n, b))
+
+
+def test_segment_clamp_worked_example():
+    # 7 text tokens, block 2, a prompt of 3 tokens then a response of 4:
+    # blocks {0,1} {2} | {3,4} {5,6} -- token 2 ends its segment, so its
+    # block is cut to one token instead of spilling into the response.
+    want = np.array([
+        [1, 1, 0, 0, 0, 0, 0],
+        [1, 1, 0, 0, 0, 0, 0],
+        [0, 0, 1, 0, 0, 0, 0],
+        [0, 0, 0, 1, 1, 0, 0],
+        [0, 0, 0, 1, 1, 0, 0],
+        [0, 0, 0, 0, 0, 1, 1],
+        [0, 0, 0, 0, 0, 1, 1],
+    ], dtype=bool)
+    assert np.array_equal(oracle.mask_n2n(7, 2, [0, 3]), want)
+
+
+def test_segment_clamped_blocks_tile_each_segment():
+    rng = np.random.default_rng(5)
+    for _ in range(30):
+        n = int(rng.integers(1, 80))
+        b = int(rng.integers(1, 9))
+        k = int(rng.integers(0, min(n, 10)))
+        starts = [0] + sorted(rng.choice(np.arange(1, n), k, replace=False).tolist()) if n > 1 else [0]
+        m = oracle.mask_n2n(n, b, starts)
+        assert np.array_equal(m, m.T) and m.diagonal().all()
+        bounds = starts + [n]
+        for s in range(len(starts)):
+            lo, hi = bounds[s], bounds[s + 1]
+            for r in range(lo, hi):
+                blk = np.nonzero(m[r])[0]
+                b0 = lo + ((r - lo) // b) * b
+                # the block is contiguous, starts on the segment's grid and is
+                # cut at the segment's end
+                assert blk[0] == b0 and np.array_equal(blk, np.arange(b0, min(b0 + b, hi)))
+
+
+def test_segments_change_only_the_n2n_quadrant():
+    n_vis, n_txt, b = 3, 10, 4
+    plain = oracle.dualstream_mask(n_vis, n_txt, b)
+    seg = oracle.dualstream_mask(n_vis, n_txt, b, [0, 6])
+    ctx = n_vis + n_txt
+    diff = plain != seg
+    assert not diff[:, :ctx].any() and not diff[:ctx].any()
+    assert np.array_equal(seg[ctx:, ctx:], oracle.mask_n2n(n_txt, b, [0, 6]))
