@@ -26,7 +26,9 @@ EXPORTS = (
     "bd_block_attn_ws_bytes", "bd_block_attn",
     "bd_lmhead_conf_ws_bytes", "bd_lmhead_conf", "bd_lmhead_conf_commit",
     "bd_lmhead_conf_fp8_ws_bytes", "bd_lmhead_conf_fp8", "bd_lmhead_conf_commit_fp8",
-    "bd_quant_fp8_rows", "bd_block_loop_ws_bytes", "bd_block_loop", "bd_commit", "bd_spec_accept", "bd_cert_scan", "bd_dualstream_attn",
+    "bd_quant_fp8_rows", "bd_block_loop_ws_bytes", "bd_block_loop",
+    "bd_commit", "bd_spec_accept", "bd_cert_scan",
+    "bd_dualstream_attn", "bd_dualstream_attn_seg",
 )
 
 
@@ -64,6 +66,7 @@ _SIGS = {
     "bd_spec_accept": ([_P, _P, _I, _I, _P, _P, _P, _P], _I),
     "bd_cert_scan": ([_P, _P, _P, _I, _I, _P, _P, _P, _P], _I),
     "bd_dualstream_attn": ([_I, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P], _I),
+    "bd_dualstream_attn_seg": ([_I, _P, _P, _P, _I, _I, _I, _P, _I, _I, _I, _F, _P, _P], _I),
 }
 
 
@@ -217,3 +220,13 @@ def bd_dualstream_attn(dt, q, k, v, n_vis, n_txt, block, H, dh, scale, out, stre
     st = lib().bd_dualstream_attn(dt, _ptr(q), _ptr(k), _ptr(v), n_vis, n_txt, block, H, dh,
                                   scale, _ptr(out), _stream(stream))
     return _ret("bd_dualstream_attn", st, check)
+
+
+def bd_dualstream_attn_seg(dt, q, k, v, n_vis, n_txt, block, seg_starts, H, dh, scale, out,
+                           stream=None, check=True) -> int:
+    """``seg_starts``: a host sequence of int32 segment starts (copied)."""
+    seg = np.ascontiguousarray(np.asarray(seg_starts, dtype=np.int32))
+    st = lib().bd_dualstream_attn_seg(dt, _ptr(q), _ptr(k), _ptr(v), n_vis, n_txt, block,
+                                      seg.ctypes.data if seg.size else None, int(seg.size), H,
+                                      dh, scale, _ptr(out), _stream(stream))
+    return _ret("bd_dualstream_attn_seg", st, check)

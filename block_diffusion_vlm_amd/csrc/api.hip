@@ -325,9 +325,12 @@ bd_status bd_cert_scan(const float* anchor_conf, const int32_t* anchor_tok,
                                               accepted, skip_full, stream));
 }
 
-bd_status bd_dualstream_attn(bd_dtype dt, const void* q, const void* k, const void* v,
-                             int32_t n_vis, int32_t n_txt, int32_t block, int32_t H, int32_t dh,
-                             float scale, void* out, hipStream_t stream) {
+namespace {
+
+bd_status dualstream_common(bd_dtype dt, const void* q, const void* k, const void* v,
+                            int32_t n_vis, int32_t n_txt, int32_t block, const int32_t* seg,
+                            int32_t n_seg, int32_t H, int32_t dh, float scale, void* out,
+                            hipStream_t stream) {
     if (!q || !k || !v || !out) return BD_E_NULL;
     if (dt != BD_F32 && dt != BD_BF16) return BD_E_DTYPE;
     if (n_vis < 0 || n_txt < 0 || block < 1 || H < 1) return BD_E_SHAPE;
@@ -341,9 +344,30 @@ bd_status bd_dualstream_attn(bd_dtype dt, const void* q, const void* k, const vo
         return launch_status(bd::launch_dualstream_f32(
             static_cast<const float*>(q), static_cast<const float*>(k),
             static_cast<const float*>(v), n_vis, n_txt, block, H, dh, sc,
-            static_cast<float*>(out), stream));
-    return launch_status(
-        bd::launch_dualstream_bf16(q, k, v, n_vis, n_txt, block, H, sc, out, stream));
+            static_cast<float*>(out), stream, seg, n_seg));
+    return launch_status(bd::launch_dualstream_bf16(q, k, v, n_vis, n_txt, block, H, sc, out,
+                                                    stream, seg, n_seg));
+}
+
+}  // namespace
+
+bd_status bd_dualstream_attn(bd_dtype dt, const void* q, const void* k, const void* v,
+                             int32_t n_vis, int32_t n_txt, int32_t block, int32_t H, int32_t dh,
+                             float scale, void* out, hipStream_t stream) {
+    return dualstream_common(dt, q, k, v, n_vis, n_txt, block, nullptr, 1, H, dh, scale, out,
+                             stream);
+}
+
+bd_status bd_dualstream_attn_seg(bd_dtype dt, const void* q, const void* k, const void* v,
+                                 int32_t n_vis, int32_t n_txt, int32_t block,
+                                 const int32_t* seg_starts, int32_t n_seg, int32_t H,
+                                 int32_t dh, float scale, void* out, hipStream_t stream) {
+    if (!seg_starts) return BD_E_NULL;
+    if (n_seg < 1 || n_seg > bd::kMaxSegments || seg_starts[0] != 0) return BD_E_SHAPE;
+    for (int s = 1; s < n_seg; ++s)
+        if (seg_starts[s] <= seg_starts[s - 1] || seg_starts[s] >= n_txt) return BD_E_SHAPE;
+    return dualstream_common(dt, q, k, v, n_vis, n_txt, block, seg_starts, n_seg, H, dh, scale,
+                             out, stream);
 }
 
 }  // extern "C"

@@ -123,12 +123,14 @@ hipError_t launch_block_attn_f32(const float* q, const float* kc, const float* v
                                  float scale, float* out, hipStream_t st,
                                  const int32_t* gate = nullptr);
 
-// Dual-stream attention
+// Dual-stream attention.  seg (host, n_seg entries) holds the text segment
+// starts of the auto-truncation mask; null means one segment.
+constexpr int kMaxSegments = 64;
 hipError_t launch_dualstream_bf16(const void* q, const void* k, const void* v, int n_vis,
                                   int n_txt, int block, int H, float scale, void* out,
-                                  hipStream_t st);
+                                  hipStream_t st, const int32_t* seg = nullptr, int n_seg = 1);
 hipError_t launch_dualstream_f32(const float* q, const float* k, const float* v, int n_vis,
                                  int n_txt, int block, int H, int dh, float scale, float* out,
-                                 hipStream_t st);
+                                 hipStream_t st, const int32_t* seg = nullptr, int n_seg = 1);
 
 }  // namespace bd

@@ -6,6 +6,11 @@
 //        own position (the printed N2C matrix includes the diagonal);
 //   N2N  noisy tokens attend bidirectionally inside their block;
 //   no clean token sees a noisy one.
+// With the auto-truncation mask (overview §2.2.2; Thai article §4.3) the text
+// is split into segments (the turns' prompts and responses): N2N blocks tile
+// every segment from its own start and end at the segment's end, so the last
+// block of a response never reaches into the next prompt.  One segment is
+// the plain mask.
 //
 // bf16 path: flash attention forward on v_mfma_f32_32x32x16_bf16.  A
 // workgroup owns 128 query rows of one head (4 waves x 32 rows), two
@@ -32,19 +37,39 @@ constexpr float kLazy = 8.0f;
 
 struct Geometry {
     int n_vis, n_txt, ctx, N, block;
+    int n_seg;                          // text segments, 1 .. kMaxSegments
+    int seg[kMaxSegments];              // their starts (text positions), seg[0] = 0
 };
 
-// Visibility of key j for query i (both < N).
-__device__ __forceinline__ bool visible(const Geometry& G, int i, int j) {
-    if (i < G.ctx) return j <= i;                      // C2C (j <= i < ctx)
-    const int r = i - G.ctx;
-    if (j < G.n_vis) return true;                      // N2C, visual keys
-    if (j < G.ctx) return (j - G.n_vis) <= r;          // N2C, clean text
-    return (j - G.ctx) / G.block == r / G.block;       // N2N
+// The N2N block [lo, hi) (text positions) of noisy text position r: blocks
+// tile r's segment from its start and are cut at its end.  SEG = false is
+// the one-segment case.  The scan has static indices only, so the segment
+// starts stay in kernel-argument (scalar) memory.
+template <bool SEG = true>
+__host__ __device__ inline void noisy_block(const Geometry& G, int r, int* lo, int* hi) {
+    if constexpr (!SEG) {
+        *lo = (r / G.block) * G.block;
+        *hi = *lo + G.block < G.n_txt ? *lo + G.block : G.n_txt;
+        return;
+    }
+    int s0 = 0, s1 = G.n_txt;
+#pragma unroll
+    for (int s = 1; s < kMaxSegments; ++s) {
+        if (s < G.n_seg) {
+            const int b = G.seg[s];
+            if (b <= r)
+                s0 = b;
+            else if (b < s1)
+                s1 = b;
+        }
+    }
+    *lo = s0 + ((r - s0) / G.block) * G.block;
+    *hi = *lo + G.block < s1 ? *lo + G.block : s1;
 }
 
 // Key ranges a query tile [i0, i1) must visit: range A = [0, a_end) (visual +
 // clean keys), range B = [b_beg, b_end) (noisy keys, possibly empty).
+template <bool SEG>
 __host__ __device__ inline void key_ranges(const Geometry& G, int i0, int i1, int* a_end,
                                            int* b_beg, int* b_end) {
     int ae = 0;
@@ -54,9 +79,11 @@ __host__ __device__ inline void key_ranges(const Geometry& G, int i0, int i1, in
         const int noisy_reach = G.n_vis + r_last + 1;                // visual + clean <= r
         ae = ae > noisy_reach ? ae : noisy_reach;
         const int r_first = (i0 > G.ctx ? i0 : G.ctx) - G.ctx;
-        *b_beg = G.ctx + (r_first / G.block) * G.block;
-        int be = G.ctx + (r_last / G.block + 1) * G.block;
-        *b_end = be < G.N ? be : G.N;
+        int lo, hi;
+        noisy_block<SEG>(G, r_first, &lo, &hi);
+        *b_beg = G.ctx + lo;
+        noisy_block<SEG>(G, r_last, &lo, &hi);
+        *b_end = G.ctx + hi;
     } else {
         *b_beg = *b_end = 0;
     }
@@ -71,6 +98,7 @@ struct RowVis {
     int lim, lo, hi;
 };
 
+template <bool SEG>
 __device__ __forceinline__ RowVis row_vis(const Geometry& G, int i) {
     RowVis v;
     if (i < G.ctx) {
@@ -79,8 +107,10 @@ __device__ __forceinline__ RowVis row_vis(const Geometry& G, int i) {
     } else {
         const int r = i - G.ctx;
         v.lim = G.n_vis + r;
-        v.lo = G.ctx + (r / G.block) * G.block;
-        v.hi = v.lo + G.block < G.N ? v.lo + G.block : G.N;
+        int lo, hi;
+        noisy_block<SEG>(G, r, &lo, &hi);
+        v.lo = G.ctx + lo;
+        v.hi = G.ctx + hi;
     }
     return v;
 }
@@ -96,7 +126,7 @@ __device__ __forceinline__ RowVis row_vis(const Geometry& G, int i) {
 // V(t) and loads K(t+2) and V(t+1) into the other halves of two double
 // buffers (complete tiles with per-lane offsets computed once); one barrier
 // per iteration separates the loads from their readers.
-template <int WAVES>
+template <int WAVES, bool SEG>
 __global__ __launch_bounds__(WAVES * 64, 2) void dualstream_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, Geometry G, int H, float scale_log2,
@@ -116,7 +146,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void dualstream_bf16_kernel(
     const int rs = H * kDh;                          // element stride between tokens
 
     int a_end, b_beg, b_end;
-    key_ranges(G, i0, i1, &a_end, &b_beg, &b_end);
+    key_ranges<SEG>(G, i0, i1, &a_end, &b_beg, &b_end);
     const int na = (a_end + kBN - 1) / kBN;
     const int nb = b_end > b_beg ? (b_end - b_beg + kBN - 1) / kBN : 0;
     const int ntile = na + nb;
@@ -126,7 +156,13 @@ __global__ __launch_bounds__(WAVES * 64, 2) void dualstream_bf16_kernel(
     // A complete tile of range B is when all rows lie in one noisy block
     // (range B is then exactly that block's keys).
     const int full_a = i1 <= G.ctx ? i0 : (i0 >= G.ctx ? G.n_vis + (i0 - G.ctx) : -1);
-    const bool full_b = i0 >= G.ctx && (i0 - G.ctx) / G.block == (i1 - 1 - G.ctx) / G.block;
+    bool full_b = false;
+    if (i0 >= G.ctx) {
+        int lo0, hi0, lo1, hi1;
+        noisy_block<SEG>(G, i0 - G.ctx, &lo0, &hi0);
+        noisy_block<SEG>(G, i1 - 1 - G.ctx, &lo1, &hi1);
+        full_b = lo0 == lo1;
+    }
     const uint16_t* kh = k + size_t(h) * kDh;
     const uint16_t* vh = v + size_t(h) * kDh;
     auto tile_j0 = [&](int t) { return t < na ? t * kBN : b_beg + (t - na) * kBN; };
@@ -165,7 +201,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void dualstream_bf16_kernel(
     const bool row_ok = row < G.N;
     bf16x8 qf[8];
     load_q(qf, row_ok ? q + size_t(row) * rs + size_t(h) * kDh : nullptr, lane);
-    const RowVis rv = row_ok ? row_vis(G, row) : RowVis{-1, 0, 0};
+    const RowVis rv = row_ok ? row_vis<SEG>(G, row) : RowVis{-1, 0, 0};
     float m = -INFINITY, l = 0.f;
     f32x16 oacc[4];
 #pragma unroll
@@ -341,11 +377,12 @@ __global__ __launch_bounds__(64) void dualstream_f32_kernel(const float* __restr
     const size_t rs = size_t(H) * dh;
     for (int d = lane; d < dh; d += 64) qs[d] = q[size_t(i) * rs + size_t(h) * dh + d];
     __syncthreads();
+    const RowVis rv = row_vis<true>(G, i);
     float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
     for (int j0 = 0; j0 < G.N; j0 += 64) {
         const int j = j0 + lane;
         float x = -INFINITY;
-        if (j < G.N && visible(G, i, j)) {
+        if (j < G.N && (j <= rv.lim || (j >= rv.lo && j < rv.hi))) {
             const float* kr = k + size_t(j) * rs + size_t(h) * dh;
             float acc = 0.f;
             for (int d = 0; d < dh; ++d) acc = fmaf(qs[d], kr[d], acc);
@@ -377,27 +414,45 @@ __global__ __launch_bounds__(64) void dualstream_f32_kernel(const float* __restr
     if (lane + 64 < dh) orow[lane + 64] = o1 * inv;
 }
 
+Geometry make_geometry(int n_vis, int n_txt, int block, const int32_t* seg, int n_seg) {
+    Geometry G{};
+    G.n_vis = n_vis;
+    G.n_txt = n_txt;
+    G.ctx = n_vis + n_txt;
+    G.N = n_vis + 2 * n_txt;
+    G.block = block;
+    G.n_seg = seg != nullptr ? n_seg : 1;
+    for (int s = 0; s < G.n_seg; ++s) G.seg[s] = seg != nullptr ? seg[s] : 0;
+    return G;
+}
+
 }  // namespace
 
 hipError_t launch_dualstream_bf16(const void* q, const void* k, const void* v, int n_vis,
                                   int n_txt, int block, int H, float scale, void* out,
-                                  hipStream_t st) {
+                                  hipStream_t st, const int32_t* seg, int n_seg) {
     constexpr int kWaves = 4;
     constexpr int BM = kWaves * 32;
-    Geometry G{n_vis, n_txt, n_vis + n_txt, n_vis + 2 * n_txt, block};
+    const Geometry G = make_geometry(n_vis, n_txt, block, seg, n_seg);
     const int nqt = (G.N + BM - 1) / BM;
     const dim3 grid(H, nqt);
-    hipLaunchKernelGGL(dualstream_bf16_kernel<kWaves>, grid, dim3(kWaves * 64), 0, st,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), G, H, scale * kLog2e,
-                       static_cast<uint16_t*>(out), nqt);
+    if (G.n_seg > 1)
+        hipLaunchKernelGGL((dualstream_bf16_kernel<kWaves, true>), grid, dim3(kWaves * 64), 0,
+                           st, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), G, H, scale * kLog2e,
+                           static_cast<uint16_t*>(out), nqt);
+    else
+        hipLaunchKernelGGL((dualstream_bf16_kernel<kWaves, false>), grid, dim3(kWaves * 64), 0,
+                           st, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), G, H, scale * kLog2e,
+                           static_cast<uint16_t*>(out), nqt);
     return hipGetLastError();
 }
 
 hipError_t launch_dualstream_f32(const float* q, const float* k, const float* v, int n_vis,
                                  int n_txt, int block, int H, int dh, float scale, float* out,
-                                 hipStream_t st) {
-    Geometry G{n_vis, n_txt, n_vis + n_txt, n_vis + 2 * n_txt, block};
+                                 hipStream_t st, const int32_t* seg, int n_seg) {
+    const Geometry G = make_geometry(n_vis, n_txt, block, seg, n_seg);
     hipLaunchKernelGGL(dualstream_f32_kernel, dim3(G.N * H), dim3(64), 0, st, q, k, v, G, H, dh,
                        scale * kLog2e, out);
     return hipGetLastError();

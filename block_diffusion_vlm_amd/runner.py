@@ -287,7 +287,8 @@ class FusedSpecStep:
 
 
 class DualStream:
-    """bd_dualstream_attn over device buffers from synth.dualstream."""
+    """bd_dualstream_attn over device buffers from synth.dualstream; with a
+    ``seg_starts`` entry (text segment starts), bd_dualstream_attn_seg."""
 
     def __init__(self, inp: dict, device="cuda"):
         self.inp = inp
@@ -297,8 +298,13 @@ class DualStream:
 
     def run(self, stream=None):
         i = self.inp
-        bd.bd_dualstream_attn(self.dt, self.q, self.k, self.v, i["n_vis"], i["n_txt"], i["block"],
-                              i["H"], i["dh"], 0.0, self.out, stream)
+        if i.get("seg_starts") is not None:
+            bd.bd_dualstream_attn_seg(self.dt, self.q, self.k, self.v, i["n_vis"], i["n_txt"],
+                                      i["block"], i["seg_starts"], i["H"], i["dh"], 0.0,
+                                      self.out, stream)
+        else:
+            bd.bd_dualstream_attn(self.dt, self.q, self.k, self.v, i["n_vis"], i["n_txt"],
+                                  i["block"], i["H"], i["dh"], 0.0, self.out, stream)
 
 
 def default_scale(dh: int) -> float:

@@ -321,6 +321,29 @@ bd_status bd_dualstream_attn(bd_dtype dt, const void* q, const void* k, const vo
                              int32_t n_vis, int32_t n_txt, int32_t block, int32_t H,
                              int32_t dh, float scale, void* out, hipStream_t stream);
 
+/*
+ * bd_dualstream_attn_seg - bd_dualstream_attn with the auto-truncation mask
+ * for multi-turn text [OV §2.2.2: the mask keeps the last block of a
+ * response from spilling into the next turn's prompt; TH §4.3].  The text
+ * positions 0..n_txt-1 are split into n_seg segments (the turns' prompts and
+ * responses) starting at seg_starts[s].  N2N blocks tile every segment from
+ * its own start and end at the segment's end:
+ *   N2N: noisy r, r' (text positions) see each other iff they lie in the
+ *        same segment S = [s0, s1) and floor((r - s0) / block) ==
+ *        floor((r' - s0) / block).
+ * C2C and N2C are those of bd_dualstream_attn.  n_seg = 1 gives exactly
+ * bd_dualstream_attn.
+ *   seg_starts  HOST array of n_seg int32: seg_starts[0] = 0, strictly
+ *               increasing, every entry < n_txt (copied at the call)
+ * Limits: those of bd_dualstream_attn; 1 <= n_seg <= 64.
+ * Errors: those of bd_dualstream_attn, plus BD_E_NULL for seg_starts and
+ *   BD_E_SHAPE for an invalid segmentation.
+ */
+bd_status bd_dualstream_attn_seg(bd_dtype dt, const void* q, const void* k, const void* v,
+                                 int32_t n_vis, int32_t n_txt, int32_t block,
+                                 const int32_t* seg_starts, int32_t n_seg, int32_t H,
+                                 int32_t dh, float scale, void* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

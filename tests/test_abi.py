@@ -282,6 +282,21 @@ def test_dualstream_validation():
     assert d(scale=-1.0) == bd.BD_E_SHAPE
 
 
+def test_dualstream_seg_validation():
+    d = lambda seg, **kw: bd.bd_dualstream_attn_seg(**{**dict(  # noqa: E731
+        dt=bd.BD_BF16, q=FAKE, k=FAKE, v=FAKE, n_vis=16, n_txt=16, block=4, seg_starts=seg,
+        H=2, dh=128, scale=0.0, out=FAKE, stream=0, check=False), **kw})
+    assert d([]) == bd.BD_E_NULL                        # no segment at all
+    assert d([1]) == bd.BD_E_SHAPE                      # must start at 0
+    assert d([0, 5, 5]) == bd.BD_E_SHAPE                # strictly increasing
+    assert d([0, 9, 4]) == bd.BD_E_SHAPE
+    assert d([0, 16]) == bd.BD_E_SHAPE                  # inside the text
+    assert d(list(range(65)), n_txt=100) == bd.BD_E_SHAPE   # at most 64 segments
+    assert d([0, 3], v=None) == bd.BD_E_NULL
+    assert d([0, 3], block=0) == bd.BD_E_SHAPE
+    assert d([0, 3], k=MISALIGNED) == bd.BD_E_ALIGN
+
+
 def test_python_binding_raises_on_error():
     with pytest.raises(bd.BdError) as e:
         bd.bd_commit(FAKE, FAKE, 99, 0.9, FAKE, FAKE, FAKE, stream=0)

@@ -281,6 +281,60 @@ def test_dualstream_bf16_full_size_sampled_rows():
     assert np.abs(got - ref).max() <= 2e-2
 
 
+SEGMENTED = [
+    # n_vis, n_txt, block, H, segment starts
+    (64, 300, 32, 2, [0, 37, 150, 151, 299]),
+    (0, 256, 16, 1, [0, 100]),
+    (128, 130, 7, 1, list(range(0, 130, 13))),
+    (32, 512, 32, 1, [0] + sorted(np.random.default_rng(9).choice(
+        np.arange(1, 512), 63, replace=False).tolist())),
+    (1024, 2048, 32, 1, [0, 300, 301, 1000, 1500, 2047]),
+]
+
+
+@pytest.mark.parametrize("n_vis,n_txt,block,H,seg", SEGMENTED)
+def test_dualstream_auto_truncation_bf16_matches_oracle(n_vis, n_txt, block, H, seg):
+    r = synth.dualstream(seed=n_vis + 3 * n_txt, n_vis=n_vis, n_txt=n_txt, block=block, H=H)
+    r["seg_starts"] = seg
+    ds = runner.DualStream(r)
+    ds.run()
+    torch.cuda.synchronize()
+    N = n_vis + 2 * n_txt
+    rows = None
+    if N > 2000:                      # spot rows: clean, first noisy, every segment edge
+        ctx = n_vis + n_txt
+        edges = [ctx + s for s in seg] + [ctx + s - 1 for s in seg[1:]]
+        rows = np.unique(np.concatenate([[0, ctx - 1, N - 1], edges,
+                                         np.random.default_rng(1).integers(ctx, N, 40)]))
+    ref = oracle.dualstream_attn(r["q"], r["k"], r["v"], n_vis, n_txt, block, rows=rows,
+                                 seg_starts=seg)
+    got = bf16_host(ds.out)
+    got = got if rows is None else got[rows]
+    assert np.abs(got - ref).max() <= 2e-2
+
+
+def test_dualstream_one_segment_equals_plain_call():
+    r = synth.dualstream(seed=4, n_vis=64, n_txt=200, block=32, H=2)
+    a = runner.DualStream(r)
+    a.run()
+    r2 = dict(r, seg_starts=[0])
+    b = runner.DualStream(r2)
+    b.run()
+    torch.cuda.synchronize()
+    assert torch.equal(a.out, b.out)
+
+
+def test_dualstream_auto_truncation_f32_tiny():
+    r = synth.tiny()
+    d = {"dtype": "f32", "n_vis": 4, "n_txt": 4, "block": 2, "H": 1, "dh": 16,
+         "q": r["ds_q"], "k": r["ds_k"], "v": r["ds_v"], "seg_starts": [0, 1]}
+    ds = runner.DualStream(d)
+    ds.run()
+    torch.cuda.synchronize()
+    ref = oracle.dualstream_attn(r["ds_q"], r["ds_k"], r["ds_v"], 4, 4, 2, seg_starts=[0, 1])
+    assert rel_err(ds.out.cpu().numpy(), ref) <= 1e-5
+
+
 def test_dualstream_f32_tiny():
     r = synth.tiny()
     d = {"dtype": "f32", "n_vis": 4, "n_txt": 4, "block": 2, "H": 1, "dh": 16,
