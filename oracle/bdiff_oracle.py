@@ -73,6 +73,7 @@ import numpy as np
 __all__ = [
     "widen", "mask_n2n", "mask_n2c", "mask_c2c", "dualstream_mask",
     "intra_block_mask", "masked_attention", "block_attn", "dualstream_attn",
+    "dualstream_lse", "dualstream_attn_bwd",
     "lm_logits", "conf_argmax", "lmhead_conf", "E4M3_MAX", "e4m3_decode", "e4m3_encode",
     "quant_fp8_rows", "lm_logits_fp8", "lmhead_conf_fp8", "commit", "spec_accept", "cert_scan",
     "decode_step", "block_loop", "linear_spec_step", "fused_spec_step",
@@ -243,6 +244,61 @@ def dualstream_attn(q, k, v, n_vis: int, n_txt: int, block: int,
         out[:, h, :] = masked_attention(q[rows, h, :], k[:, h, :], v[:, h, :],
                                         allowed[rows], scale)
     return out
+
+
+def dualstream_lse(q, k, n_vis: int, n_txt: int, block: int, scale: float | None = None,
+                   seg_starts=None) -> np.ndarray:
+    """Row log-sum-exp of the masked, scaled scores, natural log, [N][H]:
+    lse[i, h] = log sum_{j visible from i} exp(scale q_i . k_j).  It is what a
+    training forward keeps for the backward (P = exp(scale S - lse)).
+    [OV §2.2.1, §2.2.2]"""
+    q = widen(q)
+    k = widen(k)
+    n, nh, dh = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(dh)
+    allowed = dualstream_mask(n_vis, n_txt, block, seg_starts)
+    out = np.empty((n, nh))
+    for h in range(nh):
+        s = scale * (q[:, h, :] @ k[:, h, :].T)
+        s = np.where(allowed, s, -np.inf)
+        m = s.max(axis=1)
+        out[:, h] = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+    return out
+
+
+def dualstream_attn_bwd(q, k, v, d_out, n_vis: int, n_txt: int, block: int,
+                        scale: float | None = None, seg_starts=None):
+    """Gradients of the dual-stream attention with respect to q, k and v for
+    the output gradient d_out, per head, from the definition of masked
+    softmax attention O = P V, P = softmax_row(scale Q K^T + mask):
+        dV = P^T dO,   dP = dO V^T,   dS = P * (dP - rowsum(P * dP)),
+        dQ = scale dS K,   dK = scale dS^T Q.
+    All [N][H][dh], float64.  Training the dual-stream model needs this pass
+    [OV §2.2.1; TH §4.1]."""
+    q = widen(q)
+    k = widen(k)
+    v = widen(v)
+    g = widen(d_out)
+    n, nh, dh = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(dh)
+    allowed = dualstream_mask(n_vis, n_txt, block, seg_starts)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for h in range(nh):
+        s = scale * (q[:, h, :] @ k[:, h, :].T)
+        s = np.where(allowed, s, -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        e = np.where(allowed, np.exp(s - m), 0.0)
+        p = e / e.sum(axis=1, keepdims=True)
+        dv[:, h, :] = p.T @ g[:, h, :]
+        dp = g[:, h, :] @ v[:, h, :].T
+        ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        dq[:, h, :] = scale * (ds @ k[:, h, :])
+        dk[:, h, :] = scale * (ds.T @ q[:, h, :])
+    return dq, dk, dv
 
 
 # ---------------------------------------------------------------------------
