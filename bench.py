@@ -323,6 +323,20 @@ def secondary(args, stream):
                              "shape": "1024 vis + 2048 clean + 2048 noisy, block 32, 16 heads x 128"}
     del ds
 
+    # Training backward on the same input: dQ, dK, dV from the forward's
+    # output and row log-sum-exp.  Algorithmic work = 2.5x the forward's
+    # (dV, dP, dQ, dK products and one recomputation of S).
+    tr = runner.DualStreamTrain(r5)
+    tr.forward()
+    ms_b = timed(tr.backward, iters, warm, stream)
+    bflops = 2.5 * flops
+    res["dualstream_bwd"] = {"us": round(ms_b * 1e3, 2),
+                             "tflops": round(bflops / (ms_b * 1e-3) / 1e12, 1),
+                             "mfma_frac": round(bflops / (ms_b * 1e-3) / 1e12
+                                                / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "shape": "the dual-stream forward's input, output gradient N(0,1)"}
+    del tr
+
     r3 = synth.linear_spec()
     lin = runner.LinearSpecStep(r3)
     ms = timed(lin.run, iters, warm, stream)

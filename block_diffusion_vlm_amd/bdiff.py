@@ -28,7 +28,8 @@ EXPORTS = (
     "bd_lmhead_conf_fp8_ws_bytes", "bd_lmhead_conf_fp8", "bd_lmhead_conf_commit_fp8",
     "bd_quant_fp8_rows", "bd_block_loop_ws_bytes", "bd_block_loop",
     "bd_commit", "bd_spec_accept", "bd_cert_scan",
-    "bd_dualstream_attn", "bd_dualstream_attn_seg",
+    "bd_dualstream_attn", "bd_dualstream_attn_seg", "bd_dualstream_attn_fwd",
+    "bd_dualstream_attn_bwd_ws_bytes", "bd_dualstream_attn_bwd",
 )
 
 
@@ -67,6 +68,10 @@ _SIGS = {
     "bd_cert_scan": ([_P, _P, _P, _I, _I, _P, _P, _P, _P], _I),
     "bd_dualstream_attn": ([_I, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P], _I),
     "bd_dualstream_attn_seg": ([_I, _P, _P, _P, _I, _I, _I, _P, _I, _I, _I, _F, _P, _P], _I),
+    "bd_dualstream_attn_fwd": ([_I, _P, _P, _P, _I, _I, _I, _P, _I, _I, _I, _F, _P, _P, _P], _I),
+    "bd_dualstream_attn_bwd_ws_bytes": ([_I, _I, _I], _SZ),
+    "bd_dualstream_attn_bwd": ([_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _I, _I, _F,
+                                _P, _P, _P, _P, _SZ, _P], _I),
 }
 
 
@@ -230,3 +235,33 @@ def bd_dualstream_attn_seg(dt, q, k, v, n_vis, n_txt, block, seg_starts, H, dh, 
                                       seg.ctypes.data if seg.size else None, int(seg.size), H,
                                       dh, scale, _ptr(out), _stream(stream))
     return _ret("bd_dualstream_attn_seg", st, check)
+
+
+def _segments(seg_starts):
+    """(pointer, count, keep-alive array) of a host segment list, or (None, 1, None)."""
+    if seg_starts is None:
+        return None, 1, None
+    seg = np.ascontiguousarray(np.asarray(seg_starts, dtype=np.int32))
+    return (seg.ctypes.data if seg.size else None), int(seg.size), seg
+
+
+def bd_dualstream_attn_fwd(dt, q, k, v, n_vis, n_txt, block, seg_starts, H, dh, scale, out, lse,
+                           stream=None, check=True) -> int:
+    p, n, _keep = _segments(seg_starts)
+    st = lib().bd_dualstream_attn_fwd(dt, _ptr(q), _ptr(k), _ptr(v), n_vis, n_txt, block, p, n,
+                                      H, dh, scale, _ptr(out), _ptr(lse), _stream(stream))
+    return _ret("bd_dualstream_attn_fwd", st, check)
+
+
+def bd_dualstream_attn_bwd_ws_bytes(n_vis, n_txt, H) -> int:
+    return int(lib().bd_dualstream_attn_bwd_ws_bytes(n_vis, n_txt, H))
+
+
+def bd_dualstream_attn_bwd(dt, q, k, v, out, d_out, lse, n_vis, n_txt, block, seg_starts, H, dh,
+                           scale, dq, dk, dv, ws, ws_bytes, stream=None, check=True) -> int:
+    p, n, _keep = _segments(seg_starts)
+    st = lib().bd_dualstream_attn_bwd(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(d_out),
+                                      _ptr(lse), n_vis, n_txt, block, p, n, H, dh, scale,
+                                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws_bytes,
+                                      _stream(stream))
+    return _ret("bd_dualstream_attn_bwd", st, check)

@@ -327,26 +327,43 @@ bd_status bd_cert_scan(const float* anchor_conf, const int32_t* anchor_tok,
 
 namespace {
 
-bd_status dualstream_common(bd_dtype dt, const void* q, const void* k, const void* v,
-                            int32_t n_vis, int32_t n_txt, int32_t block, const int32_t* seg,
-                            int32_t n_seg, int32_t H, int32_t dh, float scale, void* out,
-                            hipStream_t stream) {
-    if (!q || !k || !v || !out) return BD_E_NULL;
+// Checks of a segmentation given as a host array (null = one segment).
+bd_status check_segments(const int32_t* seg, int32_t n_seg, int32_t n_txt) {
+    if (!seg) return BD_OK;
+    if (n_seg < 1 || n_seg > bd::kMaxSegments || seg[0] != 0) return BD_E_SHAPE;
+    for (int s = 1; s < n_seg; ++s)
+        if (seg[s] <= seg[s - 1] || seg[s] >= n_txt) return BD_E_SHAPE;
+    return BD_OK;
+}
+
+// Shape, dtype and alignment checks shared by the dual-stream calls.
+bd_status dualstream_check(bd_dtype dt, int32_t n_vis, int32_t n_txt, int32_t block, int32_t H,
+                           int32_t dh, float scale) {
     if (dt != BD_F32 && dt != BD_BF16) return BD_E_DTYPE;
     if (n_vis < 0 || n_txt < 0 || block < 1 || H < 1) return BD_E_SHAPE;
     const int64_t N = (int64_t)n_vis + 2 * (int64_t)n_txt;
     if (N < 1 || N > (1 << 24)) return BD_E_SHAPE;
     if (!dh_ok(dt, dh)) return BD_E_SHAPE;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return BD_E_ALIGN;
     if (!(scale >= 0.f) || isinf(scale)) return BD_E_SHAPE;
+    return BD_OK;
+}
+
+bd_status dualstream_common(bd_dtype dt, const void* q, const void* k, const void* v,
+                            int32_t n_vis, int32_t n_txt, int32_t block, const int32_t* seg,
+                            int32_t n_seg, int32_t H, int32_t dh, float scale, void* out,
+                            hipStream_t stream, float* lse = nullptr) {
+    if (!q || !k || !v || !out) return BD_E_NULL;
+    const bd_status s = dualstream_check(dt, n_vis, n_txt, block, H, dh, scale);
+    if (s != BD_OK) return s;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return BD_E_ALIGN;
     const float sc = default_scale(scale, dh);
     if (dt == BD_F32)
         return launch_status(bd::launch_dualstream_f32(
             static_cast<const float*>(q), static_cast<const float*>(k),
             static_cast<const float*>(v), n_vis, n_txt, block, H, dh, sc,
-            static_cast<float*>(out), stream, seg, n_seg));
+            static_cast<float*>(out), stream, seg, n_seg, lse));
     return launch_status(bd::launch_dualstream_bf16(q, k, v, n_vis, n_txt, block, H, sc, out,
-                                                    stream, seg, n_seg));
+                                                    stream, seg, n_seg, lse));
 }
 
 }  // namespace
@@ -363,11 +380,60 @@ bd_status bd_dualstream_attn_seg(bd_dtype dt, const void* q, const void* k, cons
                                  const int32_t* seg_starts, int32_t n_seg, int32_t H,
                                  int32_t dh, float scale, void* out, hipStream_t stream) {
     if (!seg_starts) return BD_E_NULL;
-    if (n_seg < 1 || n_seg > bd::kMaxSegments || seg_starts[0] != 0) return BD_E_SHAPE;
-    for (int s = 1; s < n_seg; ++s)
-        if (seg_starts[s] <= seg_starts[s - 1] || seg_starts[s] >= n_txt) return BD_E_SHAPE;
+    const bd_status s = check_segments(seg_starts, n_seg, n_txt);
+    if (s != BD_OK) return s;
     return dualstream_common(dt, q, k, v, n_vis, n_txt, block, seg_starts, n_seg, H, dh, scale,
                              out, stream);
+}
+
+bd_status bd_dualstream_attn_fwd(bd_dtype dt, const void* q, const void* k, const void* v,
+                                 int32_t n_vis, int32_t n_txt, int32_t block,
+                                 const int32_t* seg_starts, int32_t n_seg, int32_t H,
+                                 int32_t dh, float scale, void* out, float* lse,
+                                 hipStream_t stream) {
+    const bd_status s = check_segments(seg_starts, n_seg, n_txt);
+    if (s != BD_OK) return s;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return BD_E_ALIGN;
+    return dualstream_common(dt, q, k, v, n_vis, n_txt, block, seg_starts,
+                             seg_starts ? n_seg : 1, H, dh, scale, out, stream, lse);
+}
+
+size_t bd_dualstream_attn_bwd_ws_bytes(int32_t n_vis, int32_t n_txt, int32_t H) {
+    const int64_t N = (int64_t)n_vis + 2 * (int64_t)n_txt;
+    if (n_vis < 0 || n_txt < 0 || H < 1 || N < 1 || N > (1 << 24)) return 0;
+    return bd::dualstream_bwd_ws_bytes(int(N), H);
+}
+
+bd_status bd_dualstream_attn_bwd(bd_dtype dt, const void* q, const void* k, const void* v,
+                                 const void* out, const void* d_out, const float* lse,
+                                 int32_t n_vis, int32_t n_txt, int32_t block,
+                                 const int32_t* seg_starts, int32_t n_seg, int32_t H, int32_t dh,
+                                 float scale, void* dq, void* dk, void* dv, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+    if (!q || !k || !v || !out || !d_out || !lse || !dq || !dk || !dv) return BD_E_NULL;
+    bd_status s = dualstream_check(dt, n_vis, n_txt, block, H, dh, scale);
+    if (s != BD_OK) return s;
+    s = check_segments(seg_starts, n_seg, n_txt);
+    if (s != BD_OK) return s;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(d_out) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+        (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return BD_E_ALIGN;
+    const int N = n_vis + 2 * n_txt;
+    if (!ws || ws_bytes < bd::dualstream_bwd_ws_bytes(N, H)) return BD_E_WORKSPACE;
+    if (!aligned16(ws)) return BD_E_ALIGN;
+    const float sc = default_scale(scale, dh);
+    const int ns = seg_starts ? n_seg : 1;
+    if (dt == BD_F32)
+        return launch_status(bd::launch_dualstream_bwd_f32(
+            static_cast<const float*>(q), static_cast<const float*>(k),
+            static_cast<const float*>(v), static_cast<const float*>(out),
+            static_cast<const float*>(d_out), lse, n_vis, n_txt, block, seg_starts, ns, H, dh, sc,
+            static_cast<float*>(dq), static_cast<float*>(dk), static_cast<float*>(dv), ws,
+            stream));
+    return launch_status(bd::launch_dualstream_bwd_bf16(q, k, v, out, d_out, lse, n_vis, n_txt,
+                                                        block, seg_starts, ns, H, sc, dq, dk, dv,
+                                                        ws, stream));
 }
 
 }  // extern "C"

@@ -18,6 +18,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kWave = 64;
 
 // bfloat16 bits -> float32 (exact).
@@ -126,11 +127,27 @@ hipError_t launch_block_attn_f32(const float* q, const float* kc, const float* v
 // Dual-stream attention.  seg (host, n_seg entries) holds the text segment
 // starts of the auto-truncation mask; null means one segment.
 constexpr int kMaxSegments = 64;
+// lse (nullable): the row log-sum-exp [N][H] (natural log) for the backward.
 hipError_t launch_dualstream_bf16(const void* q, const void* k, const void* v, int n_vis,
                                   int n_txt, int block, int H, float scale, void* out,
-                                  hipStream_t st, const int32_t* seg = nullptr, int n_seg = 1);
+                                  hipStream_t st, const int32_t* seg = nullptr, int n_seg = 1,
+                                  float* lse = nullptr);
 hipError_t launch_dualstream_f32(const float* q, const float* k, const float* v, int n_vis,
                                  int n_txt, int block, int H, int dh, float scale, float* out,
-                                 hipStream_t st, const int32_t* seg = nullptr, int n_seg = 1);
+                                 hipStream_t st, const int32_t* seg = nullptr, int n_seg = 1,
+                                 float* lse = nullptr);
+// Backward: dq, dk, dv from q, k, v, out, d_out and the forward's lse; ws
+// holds D = rowsum(d_out * out) [N][H] float.
+size_t dualstream_bwd_ws_bytes(int N, int H);
+hipError_t launch_dualstream_bwd_bf16(const void* q, const void* k, const void* v,
+                                      const void* out, const void* dout, const float* lse,
+                                      int n_vis, int n_txt, int block, const int32_t* seg,
+                                      int n_seg, int H, float scale, void* dq, void* dk, void* dv,
+                                      void* ws, hipStream_t st);
+hipError_t launch_dualstream_bwd_f32(const float* q, const float* k, const float* v,
+                                     const float* out, const float* dout, const float* lse,
+                                     int n_vis, int n_txt, int block, const int32_t* seg,
+                                     int n_seg, int H, int dh, float scale, float* dq, float* dk,
+                                     float* dv, void* ws, hipStream_t st);
 
 }  // namespace bd

@@ -24,96 +24,18 @@
 #include <type_traits>
 
 #include "attn_common.h"
+#include "dualstream_common.h"
 
 namespace bd {
 
 namespace {
 
 using namespace attn;
+using namespace ds;
 
 
 // Headroom (log2 units) before the running maximum of a row is moved.
 constexpr float kLazy = 8.0f;
-
-struct Geometry {
-    int n_vis, n_txt, ctx, N, block;
-    int n_seg;                          // text segments, 1 .. kMaxSegments
-    int seg[kMaxSegments];              // their starts (text positions), seg[0] = 0
-};
-
-// The N2N block [lo, hi) (text positions) of noisy text position r: blocks
-// tile r's segment from its start and are cut at its end.  SEG = false is
-// the one-segment case.  The scan has static indices only, so the segment
-// starts stay in kernel-argument (scalar) memory.
-template <bool SEG = true>
-__host__ __device__ inline void noisy_block(const Geometry& G, int r, int* lo, int* hi) {
-    if constexpr (!SEG) {
-        *lo = (r / G.block) * G.block;
-        *hi = *lo + G.block < G.n_txt ? *lo + G.block : G.n_txt;
-        return;
-    }
-    int s0 = 0, s1 = G.n_txt;
-#pragma unroll
-    for (int s = 1; s < kMaxSegments; ++s) {
-        if (s < G.n_seg) {
-            const int b = G.seg[s];
-            if (b <= r)
-                s0 = b;
-            else if (b < s1)
-                s1 = b;
-        }
-    }
-    *lo = s0 + ((r - s0) / G.block) * G.block;
-    *hi = *lo + G.block < s1 ? *lo + G.block : s1;
-}
-
-// Key ranges a query tile [i0, i1) must visit: range A = [0, a_end) (visual +
-// clean keys), range B = [b_beg, b_end) (noisy keys, possibly empty).
-template <bool SEG>
-__host__ __device__ inline void key_ranges(const Geometry& G, int i0, int i1, int* a_end,
-                                           int* b_beg, int* b_end) {
-    int ae = 0;
-    if (i0 < G.ctx) ae = (i1 < G.ctx ? i1 : G.ctx);                 // clean rows: j <= i
-    if (i1 > G.ctx) {
-        const int r_last = i1 - 1 - G.ctx;
-        const int noisy_reach = G.n_vis + r_last + 1;                // visual + clean <= r
-        ae = ae > noisy_reach ? ae : noisy_reach;
-        const int r_first = (i0 > G.ctx ? i0 : G.ctx) - G.ctx;
-        int lo, hi;
-        noisy_block<SEG>(G, r_first, &lo, &hi);
-        *b_beg = G.ctx + lo;
-        noisy_block<SEG>(G, r_last, &lo, &hi);
-        *b_end = G.ctx + hi;
-    } else {
-        *b_beg = *b_end = 0;
-    }
-    *a_end = ae;
-}
-
-// Visibility of keys for one query row as two intervals: key j is visible
-// iff j <= lim or lo <= j < hi.  Clean row i: lim = i (C2C), no interval.
-// Noisy row r: lim = n_vis + r (every visual key, clean text up to r: N2C),
-// interval = the keys of its N2N block.
-struct RowVis {
-    int lim, lo, hi;
-};
-
-template <bool SEG>
-__device__ __forceinline__ RowVis row_vis(const Geometry& G, int i) {
-    RowVis v;
-    if (i < G.ctx) {
-        v.lim = i;
-        v.lo = v.hi = 0;
-    } else {
-        const int r = i - G.ctx;
-        v.lim = G.n_vis + r;
-        int lo, hi;
-        noisy_block<SEG>(G, r, &lo, &hi);
-        v.lo = G.ctx + lo;
-        v.hi = G.ctx + hi;
-    }
-    return v;
-}
 
 // One wave per 32 query rows, WAVES waves per workgroup sharing the K/V
 // tiles, two waves per SIMD.  The scores of tile t+1 are computed while the
@@ -126,11 +48,11 @@ __device__ __forceinline__ RowVis row_vis(const Geometry& G, int i) {
 // V(t) and loads K(t+2) and V(t+1) into the other halves of two double
 // buffers (complete tiles with per-lane offsets computed once); one barrier
 // per iteration separates the loads from their readers.
-template <int WAVES, bool SEG>
+template <int WAVES, bool SEG, bool LSE>
 __global__ __launch_bounds__(WAVES * 64, 2) void dualstream_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, Geometry G, int H, float scale_log2,
-    uint16_t* __restrict__ out, int nqt) {
+    uint16_t* __restrict__ out, int nqt, float* __restrict__ lse) {
     constexpr int BM = WAVES * 32;
     constexpr int kAhead = 2;                        // fragment reads issued ahead
     __shared__ __align__(16) uint16_t kbuf[2][kTile];
@@ -348,6 +270,10 @@ __global__ __launch_bounds__(WAVES * 64, 2) void dualstream_bf16_kernel(
     }
 
     if (!row_ok) return;
+    // Row log-sum-exp (natural log) for the backward: the sum of
+    // 2^(x scale_log2) over the visible keys is 2^m l.
+    if (LSE && lane < 32)
+        lse[size_t(row) * H + h] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     uint16_t* orow = out + size_t(row) * rs + size_t(h) * kDh;
 #pragma unroll
@@ -369,7 +295,8 @@ __global__ __launch_bounds__(64) void dualstream_f32_kernel(const float* __restr
                                                             const float* __restrict__ v,
                                                             Geometry G, int H, int dh,
                                                             float scale_log2,
-                                                            float* __restrict__ out) {
+                                                            float* __restrict__ out,
+                                                            float* __restrict__ lse) {
     __shared__ float qs[128];
     const int i = blockIdx.x / H;
     const int h = blockIdx.x % H;
@@ -408,53 +335,54 @@ __global__ __launch_bounds__(64) void dualstream_f32_kernel(const float* __restr
         }
         m = mn;
     }
+    if (lse != nullptr && lane == 0)
+        lse[size_t(i) * H + h] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     float* orow = out + size_t(i) * rs + size_t(h) * dh;
     if (lane < dh) orow[lane] = o0 * inv;
     if (lane + 64 < dh) orow[lane + 64] = o1 * inv;
 }
 
-Geometry make_geometry(int n_vis, int n_txt, int block, const int32_t* seg, int n_seg) {
-    Geometry G{};
-    G.n_vis = n_vis;
-    G.n_txt = n_txt;
-    G.ctx = n_vis + n_txt;
-    G.N = n_vis + 2 * n_txt;
-    G.block = block;
-    G.n_seg = seg != nullptr ? n_seg : 1;
-    for (int s = 0; s < G.n_seg; ++s) G.seg[s] = seg != nullptr ? seg[s] : 0;
-    return G;
-}
-
 }  // namespace
 
 hipError_t launch_dualstream_bf16(const void* q, const void* k, const void* v, int n_vis,
                                   int n_txt, int block, int H, float scale, void* out,
-                                  hipStream_t st, const int32_t* seg, int n_seg) {
+                                  hipStream_t st, const int32_t* seg, int n_seg, float* lse) {
     constexpr int kWaves = 4;
     constexpr int BM = kWaves * 32;
     const Geometry G = make_geometry(n_vis, n_txt, block, seg, n_seg);
     const int nqt = (G.N + BM - 1) / BM;
     const dim3 grid(H, nqt);
-    if (G.n_seg > 1)
-        hipLaunchKernelGGL((dualstream_bf16_kernel<kWaves, true>), grid, dim3(kWaves * 64), 0,
-                           st, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                           static_cast<const uint16_t*>(v), G, H, scale * kLog2e,
-                           static_cast<uint16_t*>(out), nqt);
-    else
-        hipLaunchKernelGGL((dualstream_bf16_kernel<kWaves, false>), grid, dim3(kWaves * 64), 0,
-                           st, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                           static_cast<const uint16_t*>(v), G, H, scale * kLog2e,
-                           static_cast<uint16_t*>(out), nqt);
+    const auto* qq = static_cast<const uint16_t*>(q);
+    const auto* kk = static_cast<const uint16_t*>(k);
+    const auto* vv = static_cast<const uint16_t*>(v);
+    auto* oo = static_cast<uint16_t*>(out);
+    const float sl = scale * kLog2e;
+    const dim3 blk(kWaves * 64);
+    if (G.n_seg > 1) {
+        if (lse)
+            hipLaunchKernelGGL((dualstream_bf16_kernel<kWaves, true, true>), grid, blk, 0, st, qq,
+                               kk, vv, G, H, sl, oo, nqt, lse);
+        else
+            hipLaunchKernelGGL((dualstream_bf16_kernel<kWaves, true, false>), grid, blk, 0, st,
+                               qq, kk, vv, G, H, sl, oo, nqt, lse);
+    } else {
+        if (lse)
+            hipLaunchKernelGGL((dualstream_bf16_kernel<kWaves, false, true>), grid, blk, 0, st,
+                               qq, kk, vv, G, H, sl, oo, nqt, lse);
+        else
+            hipLaunchKernelGGL((dualstream_bf16_kernel<kWaves, false, false>), grid, blk, 0, st,
+                               qq, kk, vv, G, H, sl, oo, nqt, lse);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_dualstream_f32(const float* q, const float* k, const float* v, int n_vis,
                                  int n_txt, int block, int H, int dh, float scale, float* out,
-                                 hipStream_t st, const int32_t* seg, int n_seg) {
+                                 hipStream_t st, const int32_t* seg, int n_seg, float* lse) {
     const Geometry G = make_geometry(n_vis, n_txt, block, seg, n_seg);
     hipLaunchKernelGGL(dualstream_f32_kernel, dim3(G.N * H), dim3(64), 0, st, q, k, v, G, H, dh,
-                       scale * kLog2e, out);
+                       scale * kLog2e, out, lse);
     return hipGetLastError();
 }
 

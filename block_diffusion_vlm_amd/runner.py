@@ -307,5 +307,40 @@ class DualStream:
                                   i["block"], i["H"], i["dh"], 0.0, self.out, stream)
 
 
+class DualStreamTrain:
+    """Training forward (output + row log-sum-exp) and backward of the
+    dual-stream attention over device buffers from synth.dualstream (which
+    also draws the output gradient d_out); an optional ``seg_starts`` entry
+    applies the auto-truncation mask."""
+
+    def __init__(self, inp: dict, device="cuda"):
+        self.inp = inp
+        self.dt = dtype_code(inp["dtype"])
+        self.q, self.k, self.v, self.d_out = (to_dev(inp[x], device)
+                                              for x in ("q", "k", "v", "d_out"))
+        N, H = self.q.shape[0], self.q.shape[1]
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty((N, H), dtype=torch.float32, device=device)
+        self.dq = torch.empty_like(self.q)
+        self.dk = torch.empty_like(self.q)
+        self.dv = torch.empty_like(self.q)
+        self.ws_bytes = bd.bd_dualstream_attn_bwd_ws_bytes(inp["n_vis"], inp["n_txt"], H)
+        self.ws = workspace(self.ws_bytes, device)
+        self.seg = inp.get("seg_starts")
+
+    def forward(self, stream=None):
+        i = self.inp
+        bd.bd_dualstream_attn_fwd(self.dt, self.q, self.k, self.v, i["n_vis"], i["n_txt"],
+                                  i["block"], self.seg, i["H"], i["dh"], 0.0, self.out, self.lse,
+                                  stream)
+
+    def backward(self, stream=None):
+        i = self.inp
+        bd.bd_dualstream_attn_bwd(self.dt, self.q, self.k, self.v, self.out, self.d_out,
+                                  self.lse, i["n_vis"], i["n_txt"], i["block"], self.seg, i["H"],
+                                  i["dh"], 0.0, self.dq, self.dk, self.dv, self.ws,
+                                  self.ws_bytes, stream)
+
+
 def default_scale(dh: int) -> float:
     return 1.0 / math.sqrt(dh)

@@ -415,7 +415,9 @@ def dualstream(seed: int | None = None, n_vis=1024, n_txt=2048, block=32, H=16, 
     [visual | clean text | noisy text].  Q, K ~ N(0,1), V ~ N(0,1) truncated
     to |v| <= 4.  A mask probability t ~ U(0,1) is drawn once; each noisy
     position is replaced by [MASK] with probability t, and every [MASK]
-    position carries the same Q/K/V row (one shared embedding)."""
+    position carries the same Q/K/V row (one shared embedding).  d_out, the
+    output gradient for the training backward, is N(0, 1) (drawn last, so the
+    other tensors do not depend on it)."""
     rng = config_rng(5, seed)
     n = n_vis + 2 * n_txt
     q = normal(rng, (n, H, dh))
@@ -426,6 +428,8 @@ def dualstream(seed: int | None = None, n_vis=1024, n_txt=2048, block=32, H=16, 
     mq, mk, mv = normal(rng, (H, dh)), normal(rng, (H, dh)), normal(rng, (H, dh), trunc=4.0)
     rows = n_vis + n_txt + np.nonzero(is_mask)[0]
     q[rows], k[rows], v[rows] = mq, mk, mv
+    d_out = normal(rng, (n, H, dh))
     conv = bf16_bits if dtype == "bf16" else (lambda x: x)
     return {"dtype": dtype, "n_vis": n_vis, "n_txt": n_txt, "block": block, "H": H, "dh": dh,
-            "N": n, "t": t, "is_mask": is_mask, "q": conv(q), "k": conv(k), "v": conv(v)}
+            "N": n, "t": t, "is_mask": is_mask, "q": conv(q), "k": conv(k), "v": conv(v),
+            "d_out": conv(d_out)}

@@ -344,6 +344,49 @@ bd_status bd_dualstream_attn_seg(bd_dtype dt, const void* q, const void* k, cons
                                  const int32_t* seg_starts, int32_t n_seg, int32_t H,
                                  int32_t dh, float scale, void* out, hipStream_t stream);
 
+/*
+ * bd_dualstream_attn_fwd - the training forward: bd_dualstream_attn (or, with
+ * seg_starts, bd_dualstream_attn_seg) that also keeps the row log-sum-exp
+ * the backward needs.  [OV §2.2.1-§2.2.2; TH §4.1]
+ *   lse[i][h] = log sum_{j visible from i} exp(scale q_i . k_j)  (natural log)
+ *   seg_starts  HOST array of n_seg segment starts, or NULL for one segment
+ *   lse         [N][H] float32 out, or NULL (then this is the plain forward)
+ * For bf16, lse is formed from the same rounded probabilities that the output
+ * uses (about 1e-3 from the exact value).
+ * Errors: those of bd_dualstream_attn_seg; BD_E_ALIGN for a misaligned lse.
+ */
+bd_status bd_dualstream_attn_fwd(bd_dtype dt, const void* q, const void* k, const void* v,
+                                 int32_t n_vis, int32_t n_txt, int32_t block,
+                                 const int32_t* seg_starts, int32_t n_seg, int32_t H,
+                                 int32_t dh, float scale, void* out, float* lse,
+                                 hipStream_t stream);
+
+/*
+ * bd_dualstream_attn_bwd - the training backward of the dual-stream
+ * attention: given the forward's q, k, v, out and lse and the output
+ * gradient d_out, the gradients
+ *   dV = P^T dO,  dS = P * (dO V^T - D),  D = rowsum(dO * O),
+ *   dQ = scale dS K,  dK = scale dS^T Q,   P = exp(scale Q K^T - lse),
+ * per head under the same masks (and segments) as the forward.  Nothing is
+ * accumulated with atomics; the result is deterministic.
+ * [OV §2.2.1: the dual-stream training objective; TH §4.1]
+ *   q, k, v, out, d_out  [N][H][dh] dtype dt (out from bd_dualstream_attn_fwd)
+ *   lse          [N][H] float32 from bd_dualstream_attn_fwd
+ *   dq, dk, dv   [N][H][dh] dtype dt out (float32 accumulation inside)
+ *   ws           workspace of at least bd_dualstream_attn_bwd_ws_bytes(n_vis,
+ *                n_txt, H) bytes (holds D; no initial contents required)
+ * Limits: those of bd_dualstream_attn; seg_starts as in bd_dualstream_attn_fwd.
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_ALIGN, BD_E_WORKSPACE,
+ *   BD_E_LAUNCH.
+ */
+size_t bd_dualstream_attn_bwd_ws_bytes(int32_t n_vis, int32_t n_txt, int32_t H);
+bd_status bd_dualstream_attn_bwd(bd_dtype dt, const void* q, const void* k, const void* v,
+                                 const void* out, const void* d_out, const float* lse,
+                                 int32_t n_vis, int32_t n_txt, int32_t block,
+                                 const int32_t* seg_starts, int32_t n_seg, int32_t H, int32_t dh,
+                                 float scale, void* dq, void* dk, void* dv, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

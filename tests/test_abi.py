@@ -297,6 +297,32 @@ def test_dualstream_seg_validation():
     assert d([0, 3], k=MISALIGNED) == bd.BD_E_ALIGN
 
 
+def test_dualstream_training_validation():
+    f = lambda **kw: bd.bd_dualstream_attn_fwd(**{**dict(  # noqa: E731
+        dt=bd.BD_BF16, q=FAKE, k=FAKE, v=FAKE, n_vis=16, n_txt=16, block=4, seg_starts=None,
+        H=2, dh=128, scale=0.0, out=FAKE, lse=FAKE, stream=0, check=False), **kw})
+    assert f(out=None) == bd.BD_E_NULL
+    assert f(seg_starts=[1]) == bd.BD_E_SHAPE
+    assert f(lse=FAKE + 2) == bd.BD_E_ALIGN
+    assert f(dh=64) == bd.BD_E_SHAPE
+    b = lambda **kw: bd.bd_dualstream_attn_bwd(**{**dict(  # noqa: E731
+        dt=bd.BD_BF16, q=FAKE, k=FAKE, v=FAKE, out=FAKE, d_out=FAKE, lse=FAKE, n_vis=16,
+        n_txt=16, block=4, seg_starts=None, H=2, dh=128, scale=0.0, dq=FAKE, dk=FAKE,
+        dv=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=0, check=False), **kw})
+    for name in ("q", "k", "v", "out", "d_out", "lse", "dq", "dk", "dv"):
+        assert b(**{name: None}) == bd.BD_E_NULL, name
+    assert b(dt=7) == bd.BD_E_DTYPE
+    assert b(block=0) == bd.BD_E_SHAPE
+    assert b(seg_starts=[0, 20]) == bd.BD_E_SHAPE
+    assert b(dk=MISALIGNED) == bd.BD_E_ALIGN
+    assert b(lse=FAKE + 2) == bd.BD_E_ALIGN
+    assert b(ws=None) == bd.BD_E_WORKSPACE
+    need = bd.bd_dualstream_attn_bwd_ws_bytes(16, 16, 2)
+    assert need >= 48 * 2 * 4
+    assert b(ws_bytes=need - 1) == bd.BD_E_WORKSPACE
+    assert bd.bd_dualstream_attn_bwd_ws_bytes(0, 0, 2) == 0
+
+
 def test_python_binding_raises_on_error():
     with pytest.raises(bd.BdError) as e:
         bd.bd_commit(FAKE, FAKE, 99, 0.9, FAKE, FAKE, FAKE, stream=0)
