@@ -59,6 +59,9 @@ design notes of the repository):
   R17 Auto-truncation: segments (prompts, responses) start at given text
       positions; N2N blocks tile each segment from its start and end at the
       segment's end.  One segment reduces to R2.
+  R18 Paged KV: the pool holds pages of page_size token rows per KV head,
+      [n_pages][Hkv][page_size][dh]; a page table maps logical pages to
+      physical ones.  A TEXT-ONLY forward attends the prefix from key_lo on.
 
 Every function below takes float64 (or integer) arrays and returns new arrays;
 bfloat16 inputs are passed as raw uint16 bit patterns and widened exactly.
@@ -72,7 +75,8 @@ import numpy as np
 
 __all__ = [
     "widen", "mask_n2n", "mask_n2c", "mask_c2c", "dualstream_mask",
-    "intra_block_mask", "masked_attention", "block_attn", "dualstream_attn",
+    "intra_block_mask", "masked_attention", "block_attn", "paged_rows", "block_attn_paged",
+    "dualstream_attn",
     "dualstream_lse", "dualstream_attn_bwd",
     "lm_logits", "conf_argmax", "lmhead_conf", "E4M3_MAX", "e4m3_decode", "e4m3_encode",
     "quant_fp8_rows", "lm_logits_fp8", "lmhead_conf_fp8", "commit", "spec_accept", "cert_scan",
@@ -220,6 +224,33 @@ def block_attn(q, k_cache, v_cache, P: int, intra, scale: float | None = None) -
         out[:, h, :] = masked_attention(q[:, h, :], k_cache[g, :P + bq], v_cache[g, :P + bq],
                                         allowed, scale)
     return out
+
+
+def paged_rows(pool, page_table, page_size: int, n: int) -> np.ndarray:
+    """Logical K or V rows 0..n-1 of a paged cache, [Hkv][n][dh]: logical
+    position j of KV head g lives at pool[page_table[j // page_size]][g]
+    [j % page_size] (pool [n_pages][Hkv][page_size][dh]).  [OV §2.3.2: the
+    serving system manages the KV cache in pages]"""
+    pool = np.asarray(pool)
+    table = np.asarray(page_table)
+    hkv = pool.shape[1]
+    out = np.empty((hkv, n, pool.shape[3]), dtype=pool.dtype)
+    for j in range(n):
+        out[:, j, :] = pool[int(table[j // page_size]), :, j % page_size, :]
+    return out
+
+
+def block_attn_paged(q, k_pool, v_pool, page_table, page_size: int, P: int, intra,
+                     key_lo: int = 0, scale: float | None = None) -> np.ndarray:
+    """bd_block_attn over a paged KV cache, with the prefix keys below key_lo
+    left out (key_lo = the number of visual tokens gives LOWN's TEXT-ONLY
+    forward, which skips the visual keys [LOWN 'method step details'; R18]):
+    the logical rows [key_lo, P + Bq) gathered from the pages, attended as
+    block_attn attends a contiguous cache."""
+    bq = q.shape[0]
+    kl = paged_rows(k_pool, page_table, page_size, P + bq)[:, key_lo:]
+    vl = paged_rows(v_pool, page_table, page_size, P + bq)[:, key_lo:]
+    return block_attn(q, kl, vl, P - key_lo, intra, scale)
 
 
 def dualstream_attn(q, k, v, n_vis: int, n_txt: int, block: int,

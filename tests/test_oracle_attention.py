@@ -162,3 +162,63 @@ def test_widen_bf16_is_exact():
     assert vals[2] == 3.140625                      # 0x4049 = 0 10000000 1001001
     assert vals[3] == 2.0 ** -133                   # smallest bf16 subnormal
     assert vals[4] == (2 - 2 ** -7) * 2.0 ** 127    # largest finite bf16
+
+
+# ---------------------------------------------------------------------------
+# Paged KV cache and the key-range start  [OV §2.3.2 paged KV; LOWN TEXT-ONLY]
+# ---------------------------------------------------------------------------
+
+def _paged_case(seed, P=37, bq=5, hq=4, hkv=2, dh=8, ps=4, extra_pages=3):
+    rng = np.random.default_rng(seed)
+    n = P + bq
+    n_log = -(-n // ps)
+    n_phys = n_log + extra_pages
+    table = rng.permutation(n_phys)[:n_log]
+    k_pool = rng.standard_normal((n_phys, hkv, ps, dh))
+    v_pool = rng.standard_normal((n_phys, hkv, ps, dh))
+    q = rng.standard_normal((bq, hq, dh))
+    intra = rng.random((bq, bq)) < 0.6
+    np.fill_diagonal(intra, True)
+    return q, k_pool, v_pool, table, ps, P, intra
+
+
+def test_paged_rows_follow_the_page_table():
+    q, kp, vp, table, ps, P, intra = _paged_case(0)
+    rows = oracle.paged_rows(kp, table, ps, P + q.shape[0])
+    for j in (0, 3, 4, 17, P + 2):
+        assert np.array_equal(rows[:, j], kp[table[j // ps], :, j % ps])
+
+
+def test_paged_attention_equals_attention_on_the_gathered_cache():
+    q, kp, vp, table, ps, P, intra = _paged_case(1)
+    n = P + q.shape[0]
+    # an independent gather: physical row of every logical position by loops
+    kc = np.stack([np.stack([kp[table[j // ps], g, j % ps] for j in range(n)])
+                   for g in range(kp.shape[1])])
+    vc = np.stack([np.stack([vp[table[j // ps], g, j % ps] for j in range(n)])
+                   for g in range(vp.shape[1])])
+    a = oracle.block_attn_paged(q, kp, vp, table, ps, P, intra)
+    b = oracle.block_attn(q, kc, vc, P, intra)
+    assert np.abs(a - b).max() <= 1e-14
+    # relabelling physical pages leaves the result unchanged
+    perm = np.random.default_rng(2).permutation(kp.shape[0])
+    inv = np.argsort(perm)
+    c = oracle.block_attn_paged(q, kp[perm], vp[perm], inv[table], ps, P, intra)
+    assert np.abs(a - c).max() <= 1e-14
+
+
+def test_key_lo_leaves_out_the_prefix_below_it():
+    q, kp, vp, table, ps, P, intra = _paged_case(3)
+    for key_lo in (0, 1, 16, P):
+        got = oracle.block_attn_paged(q, kp, vp, table, ps, P, intra, key_lo=key_lo)
+        n = P + q.shape[0]
+        kc = oracle.paged_rows(kp, table, ps, n)
+        vc = oracle.paged_rows(vp, table, ps, n)
+        allowed = np.zeros((q.shape[0], n), dtype=bool)
+        allowed[:, key_lo:P] = True
+        allowed[:, P:] = intra
+        scale = 1 / np.sqrt(q.shape[2])
+        group = q.shape[1] // kp.shape[1]
+        for h in range(q.shape[1]):
+            ref = oracle.masked_attention(q[:, h], kc[h // group], vc[h // group], allowed, scale)
+            assert np.abs(got[:, h] - ref).max() <= 1e-14
