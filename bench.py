@@ -249,6 +249,7 @@ def secondary(args, stream):
     """The other workloads, each timed on its own (not part of `value`)."""
     import numpy as np
     import torch
+    from block_diffusion_vlm_amd import bdiff as bd
     from block_diffusion_vlm_amd import runner, synth
     res = {}
     iters = max(20, args.steps // 5)
@@ -336,6 +337,42 @@ def secondary(args, stream):
                                                 / MFMA_BF16_PEAK_TFLOPS, 4),
                              "shape": "the dual-stream forward's input, output gradient N(0,1)"}
     del tr
+
+    # Block attention of the decode step over a paged KV cache (16-token
+    # pages in shuffled order), full prefix and TEXT-ONLY (visual keys left
+    # out), beside the contiguous cache.
+    rq = synth.qwen_decode(V=64, d=128)
+    B, P, Hq, Hkv = rq["B"], rq["P"], rq["Hq"], rq["Hkv"]
+    n = P + B
+    ps = 16
+    n_pages = -(-n // ps) + 8
+    rng = np.random.default_rng(0)
+    table = rng.permutation(n_pages)[:-(-n // ps)].astype(np.int32)
+    pools = []
+    for cache in (rq["k_cache"], rq["v_cache"]):
+        pool = np.zeros((n_pages, Hkv, ps, 128), np.uint16)
+        for j in range(n):
+            pool[table[j // ps], :, j % ps] = cache[:, j]
+        pools.append(runner.to_dev(pool))
+    tab = runner.to_dev(table)
+    qd = runner.to_dev(rq["q"])
+    mask = runner.mask_dev(bd.BD_MASK_BIDIR, B)
+    out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device="cuda")
+    pa = {}
+    for key_lo in (0, rq["n_vis"]):
+        wsb = bd.bd_block_attn_ws_bytes(P - key_lo, B, Hq, Hkv, 128)
+        ws = runner.workspace(wsb)
+        ms = timed(lambda: bd.bd_block_attn_paged(qd, pools[0], pools[1], tab, ps, n_pages, P,
+                                                  key_lo, mask, B, Hq, Hkv, 128, 0.0, out, ws,
+                                                  wsb), iters, warm, stream)
+        pa["us_full_prefix" if key_lo == 0 else "us_text_only"] = round(ms * 1e3, 2)
+    ba = runner.BlockAttn(bd.BD_BF16, bd.BD_MASK_BIDIR, B, P, rq["cap"], Hq, Hkv, 128)
+    kc, vc = runner.to_dev(rq["k_cache"]), runner.to_dev(rq["v_cache"])
+    ms = timed(lambda: ba(qd, kc, vc), iters, warm, stream)
+    pa["us_contiguous"] = round(ms * 1e3, 2)
+    pa["shape"] = "the decode step's block attention, 16-token pages in shuffled order"
+    res["block_attn_paged"] = pa
+    del pools, ba, kc, vc
 
     r3 = synth.linear_spec()
     lin = runner.LinearSpecStep(r3)

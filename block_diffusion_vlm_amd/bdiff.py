@@ -23,7 +23,7 @@ BD_MASK_BIDIR, BD_MASK_CAUSAL, BD_MASK_SPEC_FUSED = 0, 1, 2
 # Every symbol include/bdiff.h declares.
 EXPORTS = (
     "bd_status_str", "bd_device_check", "bd_make_intra_mask",
-    "bd_block_attn_ws_bytes", "bd_block_attn",
+    "bd_block_attn_ws_bytes", "bd_block_attn", "bd_block_attn_paged",
     "bd_lmhead_conf_ws_bytes", "bd_lmhead_conf", "bd_lmhead_conf_commit",
     "bd_lmhead_conf_fp8_ws_bytes", "bd_lmhead_conf_fp8", "bd_lmhead_conf_commit_fp8",
     "bd_quant_fp8_rows", "bd_block_loop_ws_bytes", "bd_block_loop",
@@ -52,6 +52,8 @@ _SIGS = {
     "bd_make_intra_mask": ([_I, _I, _P], _I),
     "bd_block_attn_ws_bytes": ([_I, _I, _I, _I, _I], _SZ),
     "bd_block_attn": ([_I, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _F, _P, _P, _SZ, _P], _I),
+    "bd_block_attn_paged": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _I, _I, _I, _F, _P, _P,
+                             _SZ, _P], _I),
     "bd_lmhead_conf_ws_bytes": ([_I, _I, _I], _SZ),
     "bd_lmhead_conf": ([_I, _P, _P, _I, _I, _I, _P, _P, _P, _SZ, _P], _I),
     "bd_lmhead_conf_commit": ([_I, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
@@ -141,6 +143,15 @@ def bd_block_attn(dt, q, k_cache, v_cache, P, cap, intra_mask, Bq, Hq, Hkv, dh, 
                              Bq, Hq, Hkv, dh, scale, _ptr(out), _ptr(ws), ws_bytes,
                              _stream(stream))
     return _ret("bd_block_attn", st, check)
+
+
+def bd_block_attn_paged(q, k_pool, v_pool, page_table, page_size, n_pages, P, key_lo, intra_mask,
+                        Bq, Hq, Hkv, dh, scale, out, ws, ws_bytes, stream=None,
+                        check=True) -> int:
+    st = lib().bd_block_attn_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+                                   page_size, n_pages, P, key_lo, _ptr(intra_mask), Bq, Hq, Hkv,
+                                   dh, scale, _ptr(out), _ptr(ws), ws_bytes, _stream(stream))
+    return _ret("bd_block_attn_paged", st, check)
 
 
 def bd_lmhead_conf_ws_bytes(B, d, V) -> int:

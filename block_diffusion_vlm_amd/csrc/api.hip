@@ -108,6 +108,29 @@ bd_status bd_block_attn(bd_dtype dt, const void* q, const void* k_cache, const v
                                                     Hq, Hkv, sc, out, ws, stream));
 }
 
+bd_status bd_block_attn_paged(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* page_table, int32_t page_size, int32_t n_pages,
+                              int32_t P, int32_t key_lo, const uint64_t* intra_mask, int32_t Bq,
+                              int32_t Hq, int32_t Hkv, int32_t dh, float scale, void* out,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!q || !k_pool || !v_pool || !page_table || !intra_mask || !out) return BD_E_NULL;
+    if (Bq < 1 || Bq > 64 || P < 0 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0) return BD_E_SHAPE;
+    if (dh != 128 || page_size < 1 || n_pages < 1 || key_lo < 0 || key_lo > P) return BD_E_SHAPE;
+    const int64_t n_keys = (int64_t)P + Bq;
+    if (n_keys - key_lo > 65536) return BD_E_SHAPE;              // at most 1024 key tiles
+    if ((n_keys + page_size - 1) / page_size > n_pages) return BD_E_SHAPE;
+    if ((int64_t)n_pages * Hkv * page_size * dh * 2 >= ((int64_t)1 << 32)) return BD_E_SHAPE;
+    if (!(scale >= 0.f) || isinf(scale)) return BD_E_SHAPE;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+        return BD_E_ALIGN;
+    const size_t need = bd::block_attn_ws_bytes(P - key_lo, Bq, Hq, Hkv, dh);
+    if (!ws || ws_bytes < need) return BD_E_WORKSPACE;
+    if (!aligned16(ws)) return BD_E_ALIGN;
+    return launch_status(bd::launch_block_attn_paged(q, k_pool, v_pool, page_table, page_size,
+                                                     n_pages, P, key_lo, intra_mask, Bq, Hq, Hkv,
+                                                     default_scale(scale, dh), out, ws, stream));
+}
+
 size_t bd_lmhead_conf_ws_bytes(int32_t B, int32_t d, int32_t V) {
     if (B < 1 || B > 64 || d < 1 || V < 1) return 0;
     return bd::lmhead_ws_bytes(B, d, V);

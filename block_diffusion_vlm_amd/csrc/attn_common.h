@@ -110,6 +110,44 @@ __device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* g, int r
     }
 }
 
+// Loads of one 64-key tile of a paged KV cache (see dma_tile): tile key
+// `key` (clamped to nkeys - 1) is logical position j = j0 + key, which lives
+// in row (page_table[j / page_size] * hkv + g) * page_size + j % page_size of
+// the pool ([n_pages][hkv][page_size][128] elements).  Page indices are
+// clamped to [0, n_pages), so a bad table entry reads a wrong page but never
+// outside the pool; the pool must be smaller than 4 GiB (32-bit offsets).
+template <int WAVES, bool IS_V>
+__device__ __forceinline__ void dma_tile_paged(uint16_t* lds, const uint16_t* pool,
+                                               const int32_t* __restrict__ page_table,
+                                               int page_size, int n_pages, int hkv, int g,
+                                               int j0, int nkeys) {
+    constexpr int PER_WAVE = 16 / WAVES;
+    const int lane = threadIdx.x & 63;
+    const unsigned wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int s = lane & 15;
+    const unsigned lofs =
+        static_cast<unsigned>(reinterpret_cast<uintptr_t>((BD_LDS void*)lds));
+    unsigned off[PER_WAVE];
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) {
+        const int key = 4 * int(wave * PER_WAVE + u) + (lane >> 4);
+        const int j = j0 + (key < nkeys ? key : nkeys - 1);
+        int page = page_table[j / page_size];
+        page = page < 0 ? 0 : (page < n_pages ? page : n_pages - 1);
+        const unsigned row = unsigned((page * hkv + g) * page_size + j % page_size);
+        const int slot = IS_V ? v_slot(key, s) : k_slot(key, s);
+        off[u] = row * unsigned(2 * kDh) + 16u * unsigned(slot);
+    }
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) {
+        const unsigned m0 = __builtin_amdgcn_readfirstlane(lofs + 1024u * (wave * PER_WAVE + u));
+        __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                         :
+                         : "{m0}"(m0), "v"(off[u]), "s"(pool)
+                         : "memory");
+    }
+}
+
 // Per-lane global byte offsets of the loads of a complete tile (all 64 keys
 // present), the same for every tile: off[u] for load u of this wave.
 template <int WAVES, bool IS_V>

@@ -119,6 +119,11 @@ hipError_t launch_block_attn_bf16(const void* q, const void* kc, const void* vc,
                                   const uint64_t* mask, int Bq, int Hq, int Hkv, float scale,
                                   void* out, void* ws, hipStream_t st,
                                   const int32_t* gate = nullptr);
+// Paged cache: pools [n_pages][Hkv][page_size][128], logical keys from key_lo.
+hipError_t launch_block_attn_paged(const void* q, const void* k_pool, const void* v_pool,
+                                   const int32_t* page_table, int page_size, int n_pages, int P,
+                                   int key_lo, const uint64_t* mask, int Bq, int Hq, int Hkv,
+                                   float scale, void* out, void* ws, hipStream_t st);
 hipError_t launch_block_attn_f32(const float* q, const float* kc, const float* vc, int P, int cap,
                                  const uint64_t* mask, int Bq, int Hq, int Hkv, int dh,
                                  float scale, float* out, hipStream_t st,

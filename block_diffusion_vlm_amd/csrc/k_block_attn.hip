@@ -42,11 +42,21 @@ inline size_t partials_bytes(int rows, int nsplit) {
     return 2 * al256(size_t(rows) * nsplit * 4) + al256(size_t(rows) * nsplit * kDh * 4);
 }
 
+// Paged cache: kc/vc are the page pools ([n_pages][Hkv][page_size][128]),
+// key positions are logical, and the visited keys start at key_lo (prefix
+// keys below it are left out); otherwise kc/vc are [Hkv][cap][128] and
+// key_lo = 0.
+struct Paging {
+    const int32_t* table;
+    int page_size, n_pages, key_lo;
+};
+
+template <bool PAGED>
 __global__ __launch_bounds__(256) void block_attn_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int P, int cap, const uint64_t* __restrict__ mask, int Bq,
     int Hq, int Hkv, float scale_log2, void* __restrict__ ws, int nsplit, int kt,
-    const int32_t* __restrict__ gate) {
+    const int32_t* __restrict__ gate, Paging pg) {
     if (gated_off(gate)) return;
     __shared__ __align__(16) uint16_t kbuf[2][kTile];
     __shared__ __align__(16) uint16_t vbuf[2][kTile];
@@ -59,16 +69,20 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
     const int Nk = P + Bq;
     const uint16_t* kb = kc + size_t(g) * cap * kDh;
     const uint16_t* vb = vc + size_t(g) * cap * kDh;
+    const int key_lo = PAGED ? pg.key_lo : 0;
     const int t_beg = split * kt;
-    const int ntiles = (Nk + kBN - 1) / kBN;
+    const int ntiles = (Nk - key_lo + kBN - 1) / kBN;
     const int t_end = t_beg + kt < ntiles ? t_beg + kt : ntiles;
     unsigned koff[4], voff[4];
     dma_offsets<4, false>(koff, kDh);
     dma_offsets<4, true>(voff, kDh);
     auto load = [&](int t, uint16_t* kd, uint16_t* vd) {
-        const int j0 = t * kBN;
+        const int j0 = key_lo + t * kBN;
         const int n = Nk - j0 < kBN ? Nk - j0 : kBN;
-        if (n == kBN) {
+        if constexpr (PAGED) {
+            dma_tile_paged<4, false>(kd, kc, pg.table, pg.page_size, pg.n_pages, Hkv, g, j0, n);
+            dma_tile_paged<4, true>(vd, vc, pg.table, pg.page_size, pg.n_pages, Hkv, g, j0, n);
+        } else if (n == kBN) {
             dma_tile_full<4>(kd, kb + size_t(j0) * kDh, koff);
             dma_tile_full<4>(vd, vb + size_t(j0) * kDh, voff);
         } else {
@@ -96,7 +110,7 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
     // One tile: the next tile's loads go into the other buffers.
     auto step = [&](int t, const uint16_t* kcur, const uint16_t* vcur, uint16_t* knxt,
                     uint16_t* vnxt) {
-        const int j0 = t * kBN;
+        const int j0 = key_lo + t * kBN;
         if (t + 1 < t_end) load(t + 1, knxt, vnxt);
 
         f32x16 sacc[2];
@@ -302,6 +316,32 @@ int num_splits(int P, int Bq, int Hq, int Hkv) {
     return (ntiles + kt - 1) / kt;
 }
 
+hipError_t launch_block_attn_any(const void* q, const void* kc, const void* vc, int P, int cap,
+                                 const uint64_t* mask, int Bq, int Hq, int Hkv, float scale,
+                                 void* out, void* ws, hipStream_t st, const int32_t* gate,
+                                 Paging pg) {
+    // Splits over the visited keys [key_lo, P + Bq).
+    const int kt = tiles_per_split(P - pg.key_lo, Bq, Hq, Hkv);
+    const int nsplit = num_splits(P - pg.key_lo, Bq, Hq, Hkv);
+    const int R = Bq * (Hq / Hkv);
+    const dim3 grid(nsplit, Hkv, (R + kRowsPerWg - 1) / kRowsPerWg);
+    if (pg.table != nullptr)
+        hipLaunchKernelGGL(block_attn_split_kernel<true>, grid, dim3(256), 0, st,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
+                           static_cast<const uint16_t*>(vc), P, cap, mask, Bq, Hq, Hkv,
+                           scale * kLog2e, ws, nsplit, kt, gate, pg);
+    else
+        hipLaunchKernelGGL(block_attn_split_kernel<false>, grid, dim3(256), 0, st,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
+                           static_cast<const uint16_t*>(vc), P, cap, mask, Bq, Hq, Hkv,
+                           scale * kLog2e, ws, nsplit, kt, gate, pg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(block_attn_combine_kernel, dim3(Bq * Hq), dim3(kCombineThreads), 0, st, ws,
+                       Bq, Hq, Hkv, nsplit, static_cast<uint16_t*>(out), gate);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 size_t block_attn_ws_bytes(int P, int Bq, int Hq, int Hkv, int dh) {
@@ -312,20 +352,18 @@ size_t block_attn_ws_bytes(int P, int Bq, int Hq, int Hkv, int dh) {
 hipError_t launch_block_attn_bf16(const void* q, const void* kc, const void* vc, int P, int cap,
                                   const uint64_t* mask, int Bq, int Hq, int Hkv, float scale,
                                   void* out, void* ws, hipStream_t st, const int32_t* gate) {
-    const int kt = tiles_per_split(P, Bq, Hq, Hkv);
-    const int nsplit = num_splits(P, Bq, Hq, Hkv);
-    const int R = Bq * (Hq / Hkv);
-    const dim3 grid(nsplit, Hkv, (R + kRowsPerWg - 1) / kRowsPerWg);
-    hipLaunchKernelGGL(block_attn_split_kernel, grid, dim3(256), 0, st,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
-                       static_cast<const uint16_t*>(vc), P, cap, mask, Bq, Hq, Hkv,
-                       scale * kLog2e, ws, nsplit, kt, gate);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(block_attn_combine_kernel, dim3(Bq * Hq), dim3(kCombineThreads), 0, st, ws,
-                       Bq, Hq, Hkv, nsplit, static_cast<uint16_t*>(out), gate);
-    return hipGetLastError();
+    return launch_block_attn_any(q, kc, vc, P, cap, mask, Bq, Hq, Hkv, scale, out, ws, st, gate,
+                                 Paging{nullptr, 1, 1, 0});
 }
+
+hipError_t launch_block_attn_paged(const void* q, const void* k_pool, const void* v_pool,
+                                   const int32_t* page_table, int page_size, int n_pages, int P,
+                                   int key_lo, const uint64_t* mask, int Bq, int Hq, int Hkv,
+                                   float scale, void* out, void* ws, hipStream_t st) {
+    return launch_block_attn_any(q, k_pool, v_pool, P, 0, mask, Bq, Hq, Hkv, scale, out, ws, st,
+                                 nullptr, Paging{page_table, page_size, n_pages, key_lo});
+}
+
 
 hipError_t launch_block_attn_f32(const float* q, const float* kc, const float* vc, int P, int cap,
                                  const uint64_t* mask, int Bq, int Hq, int Hkv, int dh,

@@ -102,6 +102,32 @@ bd_status bd_block_attn(bd_dtype dt, const void* q, const void* k_cache, const v
                         void* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * bd_block_attn_paged - bd_block_attn (bf16) over a paged KV cache, visiting
+ * the keys from key_lo on.  [OV §2.3.2: the serving system keeps the KV
+ * cache in pages; LOWN 'method step details': the TEXT-ONLY forward leaves
+ * the visual tokens out - key_lo = the number of visual tokens]
+ *   Logical key position j (prefix 0..P-1, then the block's own keys
+ *   P..P+Bq-1) of KV head g is row j % page_size of page
+ *   page_table[j / page_size]:  k_pool[page][g][j % page_size][dh].
+ *   Query i sees prefix keys key_lo <= j < P and block key P + jb iff bit jb
+ *   of intra_mask[i] is set; otherwise as bd_block_attn.
+ *   k_pool, v_pool [n_pages][Hkv][page_size][dh] bf16
+ *   page_table     [ceil((P + Bq) / page_size)] int32 (device); entries are
+ *                  physical page indices in [0, n_pages) (the kernel clamps
+ *                  others into that range)
+ *   ws             at least bd_block_attn_ws_bytes(P - key_lo, Bq, Hq, Hkv, dh)
+ * Limits: dh == 128, page_size >= 1, 0 <= key_lo <= P,
+ *   P + Bq - key_lo <= 65536, n_pages * page_size >= P + Bq, the pools
+ *   smaller than 4 GiB each; otherwise those of bd_block_attn.
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_ALIGN, BD_E_WORKSPACE, BD_E_LAUNCH.
+ */
+bd_status bd_block_attn_paged(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* page_table, int32_t page_size, int32_t n_pages,
+                              int32_t P, int32_t key_lo, const uint64_t* intra_mask, int32_t Bq,
+                              int32_t Hq, int32_t Hkv, int32_t dh, float scale, void* out,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * bd_lmhead_conf - LM-head contraction fused with the softmax maximum:
  * per position b, logits l[v] = h[b] . W[v] (never written to memory),
  *   argmax[b] = smallest v with l[v] = max l,

@@ -109,6 +109,26 @@ def test_block_attn_validation():
     assert _attn(ws=MISALIGNED) == bd.BD_E_ALIGN
 
 
+def test_block_attn_paged_validation():
+    f = lambda **kw: bd.bd_block_attn_paged(**{**dict(  # noqa: E731
+        q=FAKE, k_pool=FAKE, v_pool=FAKE, page_table=FAKE, page_size=16, n_pages=100, P=1280,
+        key_lo=0, intra_mask=FAKE, Bq=16, Hq=16, Hkv=2, dh=128, scale=0.0, out=FAKE, ws=FAKE,
+        ws_bytes=1 << 30, stream=0, check=False), **kw})
+    assert f(page_table=None) == bd.BD_E_NULL
+    assert f(v_pool=None) == bd.BD_E_NULL
+    assert f(page_size=0) == bd.BD_E_SHAPE
+    assert f(n_pages=80) == bd.BD_E_SHAPE          # 1296 keys need 81 pages of 16
+    assert f(key_lo=-1) == bd.BD_E_SHAPE
+    assert f(key_lo=1281) == bd.BD_E_SHAPE
+    assert f(dh=64) == bd.BD_E_SHAPE
+    assert f(n_pages=1 << 20) == bd.BD_E_SHAPE     # pool of 4 GiB or more
+    assert f(Hq=15) == bd.BD_E_SHAPE
+    assert f(k_pool=MISALIGNED) == bd.BD_E_ALIGN
+    assert f(ws=None) == bd.BD_E_WORKSPACE
+    need = bd.bd_block_attn_ws_bytes(1280 - 1024, 16, 16, 2, 128)
+    assert f(key_lo=1024, ws_bytes=need - 1) == bd.BD_E_WORKSPACE
+
+
 def _lm(**kw):
     a = dict(dt=bd.BD_BF16, h=FAKE, W=FAKE, B=16, d=2048, V=151936, conf=FAKE, argmax=FAKE,
              ws=FAKE, ws_bytes=1 << 30, stream=0, check=False)
