@@ -36,15 +36,20 @@ def kernel_rows(db: str):
 
 
 def trace(db: str) -> str:
+    """Per kernel: calls, average, median, min and max duration, share of the
+    total.  The median is the figure to compare with event timings when some
+    dispatches of a kernel return at once (the skipped steps of the block
+    loop)."""
     agg = collections.OrderedDict()
     for _, n, s, e, *_ in kernel_rows(db):
         agg.setdefault(_short(n), []).append((e - s) / 1000.0)
     tot = sum(sum(v) for v in agg.values())
-    out = [f"{'kernel':64s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} "
-           f"{'time%':>6s}"]
+    out = [f"{'kernel':58s} {'calls':>6s} {'avg_us':>8s} {'med_us':>8s} {'min_us':>8s} "
+           f"{'max_us':>8s} {'time%':>6s}"]
     for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
-        out.append(f"{k[:64]:64s} {len(v):6d} {sum(v) / len(v):9.2f} {min(v):9.2f} "
-                   f"{max(v):9.2f} {100 * sum(v) / tot:6.2f}")
+        med = sorted(v)[len(v) // 2]
+        out.append(f"{k[:58]:58s} {len(v):6d} {sum(v) / len(v):8.2f} {med:8.2f} {min(v):8.2f} "
+                   f"{max(v):8.2f} {100 * sum(v) / tot:6.2f}")
     return "\n".join(out)
 
 
