@@ -148,6 +148,22 @@ __device__ __forceinline__ void dma_tile_paged(uint16_t* lds, const uint16_t* po
     }
 }
 
+// One direct-to-LDS load of 64 floats, one per lane: lane l fetches
+// g[min(first + l, last) * stride] into lds[l] (issued by a single wave;
+// ordered like dma_tile).
+__device__ __forceinline__ void dma_floats64(float* lds, const float* g, int stride, int first,
+                                             int last) {
+    const int lane = threadIdx.x & 63;
+    const int row = first + lane < last ? first + lane : last;
+    const unsigned off = unsigned(row) * unsigned(stride) * 4u;
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(
+        static_cast<unsigned>(reinterpret_cast<uintptr_t>((BD_LDS void*)lds)));
+    __asm__ volatile("s_nop 0\n\tglobal_load_lds_dword %1, %2"
+                     :
+                     : "{m0}"(m0), "v"(off), "s"(g)
+                     : "memory");
+}
+
 // Per-lane global byte offsets of the loads of a complete tile (all 64 keys
 // present), the same for every tile: off[u] for load u of this wave.
 template <int WAVES, bool IS_V>

@@ -20,6 +20,8 @@
 // Each kernel writes every output element once; nothing is accumulated with
 // atomics, so the result is deterministic.  Row and key tiles come from the
 // closed-form visibility rules; the per-element test runs on every tile.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "dualstream_common.h"
 
@@ -147,7 +149,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: 128 keys per workgroup, query-row tiles of 64.
+// dK, dV: 128 keys per workgroup, query-row tiles of 64, two tiles in LDS:
+// the loads of tile t+1 (Q and dO in both layouts, and the rows' lse and D)
+// run while tile t is multiplied.
 // ---------------------------------------------------------------------------
 template <bool SEG>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
@@ -155,12 +159,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ D, Geometry G, int H,
     float scale_log2, float scale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
-    __shared__ __align__(16) uint16_t qK[kTile];     // Q row tile, A-operand layout
-    __shared__ __align__(16) uint16_t qV[kTile];     // Q row tile, transposed-read layout
-    __shared__ __align__(16) uint16_t gK[kTile];     // dO row tile, A-operand layout
-    __shared__ __align__(16) uint16_t gV[kTile];     // dO row tile, transposed-read layout
-    __shared__ __align__(16) float lse2s[kBN];
-    __shared__ __align__(16) float Ds[kBN];
+    // [buffer][Q A-operand, Q transposed-read, dO A-operand, dO transposed-read]
+    __shared__ __align__(16) uint16_t tiles[2][4][kTile];
+    __shared__ __align__(16) float lse_s[2][kBN];
+    __shared__ __align__(16) float D_s[2][kBN];
     const int h = blockIdx.x;
     const int j0w = blockIdx.y * kRowsPerWg;         // keys seen by the most rows first
     const int j1w = (j0w + kRowsPerWg < G.N) ? j0w + kRowsPerWg : G.N;
@@ -184,11 +186,43 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     bf16x8 kf[8], vf[8];
     load_q(kf, key_ok ? k + size_t(key) * rs + size_t(h) * kDh : nullptr, lane);
     load_q(vf, key_ok ? v + size_t(key) * rs + size_t(h) * kDh : nullptr, lane);
+    // The fragments are consumed here, so that the compiler completes their
+    // loads before the tile loop: a wait for them inside the loop would also
+    // wait for the next tile's loads, which it does not track.
+#pragma unroll
+    for (int s = 0; s < 8; ++s) __asm__ volatile("" ::"v"(kf[s]), "v"(vf[s]));
     // An absent key (past N) is seen by no row.
     const KeyVis kv = key_ok ? key_vis<SEG>(G, key) : KeyVis{G.N, G.n_txt, 0, 0};
     const ReadOffsets ro = read_offsets(lane);
     const uint16_t* qh = q + size_t(h) * kDh;
     const uint16_t* gh = dout + size_t(h) * kDh;
+
+    // Loads of row tile t into buffer b: 16 per wave, plus the 64 rows' lse
+    // and D (wave 0, two more).
+    auto issue = [&](int t, int b) {
+        const int i0 = tile_i0(t);
+        const int n = tile_n(t);
+        dma_tile<4, false>(tiles[b][0], qh + size_t(i0) * rs, rs, n);
+        dma_tile<4, true>(tiles[b][1], qh + size_t(i0) * rs, rs, n);
+        dma_tile<4, false>(tiles[b][2], gh + size_t(i0) * rs, rs, n);
+        dma_tile<4, true>(tiles[b][3], gh + size_t(i0) * rs, rs, n);
+        if (wave == 0) {
+            dma_floats64(lse_s[b], lse + h, H, i0, i0 + n - 1);
+            dma_floats64(D_s[b], D + h, H, i0, i0 + n - 1);
+        }
+    };
+
+    // A row tile is visible from every key of a complete key range when its
+    // rows are clean and all at or after the last key, or noisy and the keys
+    // all visual or clean text at or before the first row's position; such
+    // tiles skip the per-element test.
+    const bool keys_full = j1w - j0w == kRowsPerWg;
+    auto tile_full = [&](int i0, int n) {
+        if (!keys_full || n != kBN) return false;
+        if (i0 + n <= G.ctx) return j1w - 1 <= i0;
+        if (i0 >= G.ctx) return j1w <= G.ctx && (i0 - G.ctx) >= (j1w - 1 - G.n_vis);
+        return false;
+    };
 
     f32x16 dkacc[4], dvacc[4];
 #pragma unroll
@@ -196,47 +230,57 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         dkacc[db] = f32x16{};
         dvacc[db] = f32x16{};
     }
+    if (ntile > 0) issue(0, 0);
     for (int t = 0; t < ntile; ++t) {
+        const int b = t & 1;
+        if (t + 1 < ntile) {
+            issue(t + 1, b ^ 1);
+            // this tile's loads have landed; the next tile's stay in flight
+            if (wave == 0)
+                dma_wait<18>();
+            else
+                dma_wait<16>();
+        } else {
+            dma_wait<0>();
+        }
+        tile_barrier();
         const int i0 = tile_i0(t);
         const int n = tile_n(t);
-        dma_tile<4, false>(qK, qh + size_t(i0) * rs, rs, n);
-        dma_tile<4, true>(qV, qh + size_t(i0) * rs, rs, n);
-        dma_tile<4, false>(gK, gh + size_t(i0) * rs, rs, n);
-        dma_tile<4, true>(gV, gh + size_t(i0) * rs, rs, n);
-        if (threadIdx.x < kBN) {
-            const bool ok = int(threadIdx.x) < n;
-            const size_t r = size_t(i0 + threadIdx.x) * H + h;
-            lse2s[threadIdx.x] = ok ? lse[r] * kLog2e : INFINITY;
-            Ds[threadIdx.x] = ok ? D[r] : 0.f;
-        }
-        dma_wait<0>();
-        __syncthreads();
         f32x16 sacc[2], dpacc[2];
-        scores(sacc, qK, kf, ro);                    // S[row][key]
-        scores(dpacc, gK, vf, ro);                   // dP[row][key] = dO[row] . V[key]
+        scores(sacc, tiles[b][0], kf, ro);           // S[row][key]
+        scores(dpacc, tiles[b][2], vf, ro);          // dP[row][key] = dO[row] . V[key]
         bf16x8 pf[2][2], dsf[2][2];
         const int il = 4 * (lane >> 5);
+        auto grad = [&](auto masked_tag) {
+            constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                const int ir0 = 32 * kb + il + 8 * e4;   // rows ir0 .. ir0 + 3 of the tile
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[ir0]);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[ir0]);
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int ir0 = 32 * kb + il + 8 * e4;   // rows ir0 .. ir0 + 3 of the tile
+                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[b][ir0]);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(&D_s[b][ir0]);
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int e = 4 * e4 + x;
-                    const int ir = ir0 + x;
-                    const bool vis = (ir < n) & seen_by(G, kv, i0 + ir);
-                    const float p =
-                        vis ? __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], scale_log2, -l4[x])) : 0.f;
-                    pf[kb][e >> 3][e & 7] = static_cast<__bf16>(p);
-                    dsf[kb][e >> 3][e & 7] = static_cast<__bf16>(p * (dpacc[kb][e] - d4[x]));
+                    for (int x = 0; x < 4; ++x) {
+                        const int e = 4 * e4 + x;
+                        bool vis = true;
+                        if constexpr (MASKED) vis = (ir0 + x < n) & seen_by(G, kv, i0 + ir0 + x);
+                        const float p = vis ? __builtin_amdgcn_exp2f(fmaf(
+                                                  sacc[kb][e], scale_log2, -l4[x] * kLog2e))
+                                            : 0.f;
+                        pf[kb][e >> 3][e & 7] = static_cast<__bf16>(p);
+                        dsf[kb][e >> 3][e & 7] =
+                            static_cast<__bf16>(p * (dpacc[kb][e] - d4[x]));
+                    }
                 }
-            }
-        accumulate_pv(dvacc, gV, pf, ro);            // dV^T += dO^T P
-        accumulate_pv(dkacc, qV, dsf, ro);           // dK^T += Q^T dS
-        __syncthreads();                             // the tile is read before it is replaced
+        };
+        if (tile_full(i0, n))
+            grad(std::false_type{});
+        else
+            grad(std::true_type{});
+        accumulate_pv(dvacc, tiles[b][3], pf, ro);   // dV^T += dO^T P
+        accumulate_pv(dkacc, tiles[b][1], dsf, ro);  // dK^T += Q^T dS
+        tile_barrier();                              // buffer b is read before it is refilled
     }
     if (!key_ok) return;
     store_rowT(dk + size_t(key) * rs + size_t(h) * kDh, dkacc, scale, lane);
