@@ -85,15 +85,19 @@ __device__ __forceinline__ float other_half(float x) {
 // no register; the callers order them with dma_wait<N>() (vmcnt counts them,
 // and they complete in issue order) followed by tile_barrier().  M0 holds the
 // wave-uniform LDS address; one wait state separates its write from the load.
+// The LDS destination is given as an LDS byte address (lds_addr); the
+// overloads below take a pointer into a __shared__ array instead.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return static_cast<unsigned>(reinterpret_cast<uintptr_t>((BD_LDS const void*)p));
+}
+
 template <int WAVES, bool IS_V>
-__device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* g, int row_stride,
+__device__ __forceinline__ void dma_tile(unsigned lofs, const uint16_t* g, int row_stride,
                                          int nkeys) {
     constexpr int PER_WAVE = 16 / WAVES;
     const int lane = threadIdx.x & 63;
     const unsigned wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int s = lane & 15;
-    const unsigned lofs =
-        static_cast<unsigned>(reinterpret_cast<uintptr_t>((BD_LDS void*)lds));
     const unsigned rb = 2u * unsigned(row_stride);
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u) {
@@ -108,6 +112,12 @@ __device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* g, int r
                          : "{m0}"(m0), "v"(off), "s"(g)
                          : "memory");
     }
+}
+
+template <int WAVES, bool IS_V>
+__device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* g, int row_stride,
+                                         int nkeys) {
+    dma_tile<WAVES, IS_V>(lds_addr(lds), g, row_stride, nkeys);
 }
 
 // Loads of one 64-key tile of a paged KV cache (see dma_tile): tile key
@@ -194,6 +204,39 @@ __device__ __forceinline__ void dma_tile_full(uint16_t* lds, const uint16_t* g,
         __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                          :
                          : "{m0}"(m0), "v"(off[u]), "s"(g)
+                         : "memory");
+    }
+}
+
+// Loads of a complete tile from one per-lane offset (see dma_tile).  Load
+// instruction I brings keys 4I .. 4I+3: the row of key 4I goes into the
+// scalar base address, so the lane's byte offset is that of key (lane >> 4)
+// of the group plus 16 bytes per slot.  The V slot is the same for every
+// group; the K slot of group I is that of group 0 with bits 2-3 flipped by
+// I & 3.  Requires a row stride that is a multiple of 128 elements (the row
+// part of the offset then leaves the low 8 bits to the slot).
+template <bool IS_V>
+__device__ __forceinline__ unsigned dma_lane_offset(int row_stride) {
+    const int lane = threadIdx.x & 63;
+    const int kq = lane >> 4;
+    const int slot = IS_V ? v_slot(kq, lane & 15) : k_slot(kq, lane & 15);
+    return unsigned(kq) * 2u * unsigned(row_stride) + 16u * unsigned(slot);
+}
+
+template <int WAVES, bool IS_V>
+__device__ __forceinline__ void dma_tile_full1(unsigned lofs, const uint16_t* g, int row_stride,
+                                               unsigned off0) {
+    constexpr int PER_WAVE = 16 / WAVES;
+    const unsigned wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) {
+        const unsigned I = wave * PER_WAVE + u;
+        const uint16_t* gi = g + size_t(4u * I) * unsigned(row_stride);
+        const unsigned off = IS_V ? off0 : off0 ^ (64u * (I & 3u));
+        const unsigned m0 = __builtin_amdgcn_readfirstlane(lofs + 1024u * I);
+        __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                         :
+                         : "{m0}"(m0), "v"(off), "s"(gi)
                          : "memory");
     }
 }
@@ -349,6 +392,45 @@ __device__ __forceinline__ void accumulate_pv(f32x16 (&oacc)[4], const uint16_t*
                 const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][s2], oacc[db], 0, 0, 0);
             }
+}
+
+// scores() with each K fragment read issued AHEAD MFMAs before its use, in
+// fixed issue slots (the key blocks alternate, so consecutive MFMAs are
+// independent): the read latency is covered by MFMAs already in flight,
+// which matters when a wave has no other wave on its SIMD to switch to.
+template <int AHEAD>
+__device__ __forceinline__ void scores_ahead(f32x16 (&sacc)[2], const uint16_t* kt,
+                                             const bf16x8 (&qf)[8], const ReadOffsets& ro) {
+    auto rk = [&](int i) { return read_k(kt, ro, i & 1, i >> 1); };
+    bf16x8 ka[16];
+    static_for<0, AHEAD>([&](auto I) { ka[I] = rk(I); });
+    static_for<0, 16>([&](auto Ic) {
+        constexpr int i = Ic;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (i + AHEAD < 16) ka[i + AHEAD] = rk(i + AHEAD);
+        sacc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            ka[i], qf[i >> 1], i < 2 ? f32x16{} : sacc[i & 1], 0, 0, 0);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// accumulate_pv() with each V^T fragment read issued AHEAD MFMAs before its
+// use (the dh blocks alternate).
+template <int AHEAD>
+__device__ __forceinline__ void accumulate_pv_ahead(f32x16 (&oacc)[4], const uint16_t* vt,
+                                                    const bf16x8 (&pf)[2][2],
+                                                    const ReadOffsets& ro) {
+    auto rv = [&](int j) { return read_v(vt, ro, j & 3, j >> 3, (j >> 2) & 1); };
+    bf16x8 va[16];
+    static_for<0, AHEAD>([&](auto J) { va[J] = rv(J); });
+    static_for<0, 16>([&](auto Jc) {
+        constexpr int j = Jc;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (j + AHEAD < 16) va[j + AHEAD] = rv(j + AHEAD);
+        oacc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], pf[j >> 3][(j >> 2) & 1],
+                                                              oacc[j & 3], 0, 0, 0);
+    });
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 }  // namespace attn

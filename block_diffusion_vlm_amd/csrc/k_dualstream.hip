@@ -92,32 +92,35 @@ __global__ __launch_bounds__(WAVES * 64, 2) void dualstream_bf16_kernel(
         const int n = (t < na ? a_end : b_end) - tile_j0(t);
         return n < kBN ? n : kBN;
     };
-    unsigned koff[16 / WAVES], voff[16 / WAVES];
-    dma_offsets<WAVES, false>(koff, rs);
-    dma_offsets<WAVES, true>(voff, rs);
+    const unsigned koff = dma_lane_offset<false>(rs);
+    const unsigned voff = dma_lane_offset<true>(rs);
     // Tiles past the last one are replaced by the last one (their buffers are
-    // not read).
-    auto load_k = [&](int t, uint16_t* dst) {
+    // not read).  Destinations are LDS byte addresses of buffer halves.
+    const unsigned kbuf_lds = lds_addr(&kbuf[0][0]);
+    const unsigned vbuf_lds = lds_addr(&vbuf[0][0]);
+    auto load_k = [&](int t, int half) {
+        const unsigned dst = kbuf_lds + unsigned(half) * (2u * kTile);
         t = t < ntile ? t : ntile - 1;
         const int n = tile_n(t);
         if (n == kBN)
-            dma_tile_full<WAVES>(dst, kh + size_t(tile_j0(t)) * rs, koff);
+            dma_tile_full1<WAVES, false>(dst, kh + size_t(tile_j0(t)) * rs, rs, koff);
         else
             dma_tile<WAVES, false>(dst, kh + size_t(tile_j0(t)) * rs, rs, n);
     };
-    auto load_v = [&](int t, uint16_t* dst) {
+    auto load_v = [&](int t, int half) {
+        const unsigned dst = vbuf_lds + unsigned(half) * (2u * kTile);
         t = t < ntile ? t : ntile - 1;
         const int n = tile_n(t);
         if (n == kBN)
-            dma_tile_full<WAVES>(dst, vh + size_t(tile_j0(t)) * rs, voff);
+            dma_tile_full1<WAVES, true>(dst, vh + size_t(tile_j0(t)) * rs, rs, voff);
         else
             dma_tile<WAVES, true>(dst, vh + size_t(tile_j0(t)) * rs, rs, n);
     };
     if (ntile <= 0) return;                          // every row sees at least key 0
 
-    load_k(0, kbuf[0]);
-    load_k(1, kbuf[1]);
-    load_v(0, vbuf[0]);
+    load_k(0, 0);
+    load_k(1, 1);
+    load_v(0, 0);
     const ReadOffsets ro = read_offsets(lane);
     const int row = i0 + wave * 32 + (lane & 31);
     const bool row_ok = row < G.N;
@@ -231,8 +234,8 @@ __global__ __launch_bounds__(WAVES * 64, 2) void dualstream_bf16_kernel(
     // Iteration t: reads K(t+1) and V(t); loads K(t+2) where K(t) was and
     // V(t+1) where V(t-1) was.
     auto step = [&](int t, const f32x16 (&s)[2], f32x16 (&snext)[2]) {
-        load_k(t + 2, kbuf[t & 1]);
-        load_v(t + 1, vbuf[(t + 1) & 1]);
+        load_k(t + 2, t & 1);
+        load_v(t + 1, (t + 1) & 1);
         const int j0 = tile_j0(t);
         const int n = tile_n(t);
         const bool full = n == kBN && (t < na ? j0 + kBN - 1 <= full_a : full_b);

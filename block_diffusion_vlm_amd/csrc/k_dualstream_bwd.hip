@@ -33,6 +33,10 @@ using namespace attn;
 using namespace ds;
 
 constexpr int kRowsPerWg = 128;      // 4 waves x 32 rows (dQ) or keys (dK, dV)
+// Operand reads issued this many MFMAs ahead of their use: the dK/dV kernel
+// runs one wave per SIMD, so its reads cannot hide behind another wave.
+constexpr int kAheadDq = 2;
+constexpr int kAheadDkdv = 4;
 
 __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
 __device__ __forceinline__ float to_f32(float x) { return x; }
@@ -126,8 +130,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         dma_wait<0>();
         tile_barrier();
         f32x16 sacc[2], dpacc[2];
-        scores(sacc, kK, qf, ro);                    // S^T[key][row]
-        scores(dpacc, vK, gf, ro);                   // dP^T[key][row] = V[key] . dO[row]
+        scores_ahead<kAheadDq>(sacc, kK, qf, ro);    // S^T[key][row]
+        scores_ahead<kAheadDq>(dpacc, vK, gf, ro);   // dP^T[key][row] = V[key] . dO[row]
         bf16x8 dsf[2][2];
         const int jl = j0 + 4 * (lane >> 5);
         const int jn = j0 + n;
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
                     vis ? __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], scale_log2, -lse2)) : 0.f;
                 dsf[kb][e >> 3][e & 7] = static_cast<__bf16>(p * (dpacc[kb][e] - Dr));
             }
-        accumulate_pv(dqacc, kV, dsf, ro);           // dQ^T += K^T dS^T
+        accumulate_pv_ahead<kAheadDq>(dqacc, kV, dsf, ro);   // dQ^T += K^T dS^T
         tile_barrier();                              // the tile is read before it is replaced
     }
     if (!row_ok) return;
@@ -247,8 +251,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         const int i0 = tile_i0(t);
         const int n = tile_n(t);
         f32x16 sacc[2], dpacc[2];
-        scores(sacc, tiles[b][0], kf, ro);           // S[row][key]
-        scores(dpacc, tiles[b][2], vf, ro);          // dP[row][key] = dO[row] . V[key]
+        scores_ahead<kAheadDkdv>(sacc, tiles[b][0], kf, ro);    // S[row][key]
+        scores_ahead<kAheadDkdv>(dpacc, tiles[b][2], vf, ro);   // dP[row][key] = dO[row] . V[key]
         bf16x8 pf[2][2], dsf[2][2];
         const int il = 4 * (lane >> 5);
         auto grad = [&](auto masked_tag) {
@@ -278,8 +282,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
             grad(std::false_type{});
         else
             grad(std::true_type{});
-        accumulate_pv(dvacc, tiles[b][3], pf, ro);   // dV^T += dO^T P
-        accumulate_pv(dkacc, tiles[b][1], dsf, ro);  // dK^T += Q^T dS
+        accumulate_pv_ahead<kAheadDkdv>(dvacc, tiles[b][3], pf, ro);    // dV^T += dO^T P
+        accumulate_pv_ahead<kAheadDkdv>(dkacc, tiles[b][1], dsf, ro);   // dK^T += Q^T dS
         tile_barrier();                              // buffer b is read before it is refilled
     }
     if (!key_ok) return;
