@@ -62,6 +62,11 @@ design notes of the repository):
   R18 Paged KV: the pool holds pages of page_size token rows per KV head,
       [n_pages][Hkv][page_size][dh]; a page table maps logical pages to
       physical ones.  A TEXT-ONLY forward attends the prefix from key_lo on.
+  R19 FP8 KV cache: K and V are cached as E4M3 codes with one float32 scale
+      per KV head for K and one for V; a cached entry stands for
+      decode(code) * scale.  New rows are quantized as code = E4M3 rounding of
+      fl32(x * fl32(1 / scale)), clamped to [-448, 448] first (float32 steps,
+      as in R16).
 
 Every function below takes float64 (or integer) arrays and returns new arrays;
 bfloat16 inputs are passed as raw uint16 bit patterns and widened exactly.
@@ -76,6 +81,7 @@ import numpy as np
 __all__ = [
     "widen", "mask_n2n", "mask_n2c", "mask_c2c", "dualstream_mask",
     "intra_block_mask", "masked_attention", "block_attn", "paged_rows", "block_attn_paged",
+    "kv_quant_fp8", "kv_dequant_fp8", "block_attn_fp8kv",
     "dualstream_attn",
     "dualstream_lse", "dualstream_attn_bwd",
     "lm_logits", "conf_argmax", "lmhead_conf", "E4M3_MAX", "e4m3_decode", "e4m3_encode",
@@ -251,6 +257,36 @@ def block_attn_paged(q, k_pool, v_pool, page_table, page_size: int, P: int, intr
     kl = paged_rows(k_pool, page_table, page_size, P + bq)[:, key_lo:]
     vl = paged_rows(v_pool, page_table, page_size, P + bq)[:, key_lo:]
     return block_attn(q, kl, vl, P - key_lo, intra, scale)
+
+
+def kv_dequant_fp8(codes, scale) -> np.ndarray:
+    """Values of an FP8 KV cache (R19): codes [Hkv][rows][dh] uint8, scale
+    [Hkv] float32; entry = decode(code) * scale[head], in float64."""
+    sc = np.asarray(scale, dtype=np.float32).astype(np.float64)
+    return e4m3_decode(codes) * sc[:, None, None]
+
+
+def kv_quant_fp8(x, scale) -> np.ndarray:
+    """E4M3 codes of new K or V rows for an FP8 cache (R19), in float32 steps:
+    inv = fl32(1 / scale[g]); y = fl32(x * inv), clamped to [-448, 448];
+    code = the E4M3 rounding of y (ties to even).
+    x: [n][Hkv][dh] bfloat16 bits (uint16) or float32; scale [Hkv] float32.
+    Returns codes [n][Hkv][dh] uint8 (the caller places them in the cache)."""
+    x = np.asarray(x)
+    x32 = widen(x).astype(np.float32) if x.dtype == np.uint16 else x.astype(np.float32)
+    inv = (np.float32(1) / np.asarray(scale, dtype=np.float32)).astype(np.float32)
+    y = (x32 * inv[None, :, None]).astype(np.float32)
+    y = np.clip(y, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    return e4m3_encode(y.astype(np.float64))
+
+
+def block_attn_fp8kv(q, k_codes, v_codes, k_scale, v_scale, P: int, intra,
+                     scale: float | None = None) -> np.ndarray:
+    """bd_block_attn over an FP8 KV cache (R19): the cache's values are
+    decode(code) * scale of their KV head, attended as block_attn attends a
+    bfloat16 cache.  [OV §2.3.2: the fastest configuration runs FP8]"""
+    return block_attn(q, kv_dequant_fp8(k_codes, k_scale), kv_dequant_fp8(v_codes, v_scale),
+                      P, intra, scale)
 
 
 def dualstream_attn(q, k, v, n_vis: int, n_txt: int, block: int,
