@@ -374,6 +374,26 @@ def secondary(args, stream):
     res["block_attn_paged"] = pa
     del pools, ba, kc, vc
 
+    # Block attention of the decode step over an FP8 (E4M3) KV cache with
+    # per-head scales, and the quantizer writing the block's own K/V rows.
+    rf = synth.qwen_decode_fp8kv()
+    B, P, cap, Hq, Hkv = rf["B"], rf["P"], rf["cap"], rf["Hq"], rf["Hkv"]
+    att8 = runner.BlockAttnFP8KV(bd.BD_MASK_BIDIR, B, P, cap, Hq, Hkv)
+    q8 = runner.to_dev(rf["q"])
+    kc8, vc8 = runner.to_dev(rf["k_codes"]), runner.to_dev(rf["v_codes"])
+    ks8, vs8 = runner.to_dev(rf["k_scale"]), runner.to_dev(rf["v_scale"])
+    kn8 = runner.to_dev(rf["k_new"])
+    ms = timed(lambda: att8(q8, kc8, vc8, ks8, vs8), iters, warm, stream)
+    ms_q = timed(lambda: bd.bd_kv_quant_fp8(kn8, B, Hkv, 128, ks8, kc8, cap, P), iters, warm,
+                 stream)
+    kv_bytes = 2 * Hkv * (P + B) * 128
+    res["block_attn_fp8kv"] = {
+        "us": round(ms * 1e3, 2), "kv_bytes": kv_bytes,
+        "us_bf16_cache": pa["us_contiguous"], "us_quant_block_rows": round(ms_q * 1e3, 2),
+        "shape": "the decode step's block attention, E4M3 K/V (one byte per entry) "
+                 "with per-head scales"}
+    del att8, kc8, vc8
+
     r3 = synth.linear_spec()
     lin = runner.LinearSpecStep(r3)
     ms = timed(lin.run, iters, warm, stream)

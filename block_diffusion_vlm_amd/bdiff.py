@@ -23,7 +23,8 @@ BD_MASK_BIDIR, BD_MASK_CAUSAL, BD_MASK_SPEC_FUSED = 0, 1, 2
 # Every symbol include/bdiff.h declares.
 EXPORTS = (
     "bd_status_str", "bd_device_check", "bd_make_intra_mask",
-    "bd_block_attn_ws_bytes", "bd_block_attn", "bd_block_attn_paged",
+    "bd_block_attn_ws_bytes", "bd_block_attn", "bd_block_attn_paged", "bd_block_attn_fp8kv",
+    "bd_kv_quant_fp8",
     "bd_lmhead_conf_ws_bytes", "bd_lmhead_conf", "bd_lmhead_conf_commit",
     "bd_lmhead_conf_fp8_ws_bytes", "bd_lmhead_conf_fp8", "bd_lmhead_conf_commit_fp8",
     "bd_quant_fp8_rows", "bd_block_loop_ws_bytes", "bd_block_loop",
@@ -65,6 +66,9 @@ _SIGS = {
     "bd_block_loop_ws_bytes": ([_I, _I, _I, _I, _I, _I, _I, _I], _SZ),
     "bd_block_loop": ([_I, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _F, _P, _P, _P, _I, _I, _F,
                        _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
+    "bd_block_attn_fp8kv": ([_P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _F, _P, _P, _SZ,
+                             _P], _I),
+    "bd_kv_quant_fp8": ([_P, _I, _I, _I, _P, _P, _I, _I, _P], _I),
     "bd_commit": ([_P, _P, _I, _F, _P, _P, _P, _P], _I),
     "bd_spec_accept": ([_P, _P, _I, _I, _P, _P, _P, _P], _I),
     "bd_cert_scan": ([_P, _P, _P, _I, _I, _P, _P, _P, _P], _I),
@@ -222,6 +226,20 @@ def bd_spec_accept(draft, verify, B, P, accepted, kv_len, out_tokens, stream=Non
     st = lib().bd_spec_accept(_ptr(draft), _ptr(verify), B, P, _ptr(accepted), _ptr(kv_len),
                               _ptr(out_tokens), _stream(stream))
     return _ret("bd_spec_accept", st, check)
+
+
+def bd_block_attn_fp8kv(q, k_cache, v_cache, k_scale, v_scale, P, cap, intra_mask, Bq, Hq, Hkv,
+                        dh, scale, out, ws, ws_bytes, stream=None, check=True) -> int:
+    st = lib().bd_block_attn_fp8kv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                   _ptr(v_scale), P, cap, _ptr(intra_mask), Bq, Hq, Hkv, dh,
+                                   scale, _ptr(out), _ptr(ws), ws_bytes, _stream(stream))
+    return _ret("bd_block_attn_fp8kv", st, check)
+
+
+def bd_kv_quant_fp8(x, n, Hkv, dh, scale, cache, cap, pos, stream=None, check=True) -> int:
+    st = lib().bd_kv_quant_fp8(_ptr(x), n, Hkv, dh, _ptr(scale), _ptr(cache), cap, pos,
+                               _stream(stream))
+    return _ret("bd_kv_quant_fp8", st, check)
 
 
 def bd_cert_scan(anchor_conf, anchor_tok, text_tok, n, k, order, accepted, skip_full,

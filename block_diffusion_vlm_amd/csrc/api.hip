@@ -131,6 +131,39 @@ bd_status bd_block_attn_paged(const void* q, const void* k_pool, const void* v_p
                                                      default_scale(scale, dh), out, ws, stream));
 }
 
+bd_status bd_block_attn_fp8kv(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                              const float* k_scale, const float* v_scale, int32_t P, int32_t cap,
+                              const uint64_t* intra_mask, int32_t Bq, int32_t Hq, int32_t Hkv,
+                              int32_t dh, float scale, void* out, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+    if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !intra_mask || !out)
+        return BD_E_NULL;
+    if (Bq < 1 || Bq > 64 || P < 0 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0) return BD_E_SHAPE;
+    if ((int64_t)P + Bq > cap || (int64_t)P + Bq > 65536 || dh != 128) return BD_E_SHAPE;
+    if (!(scale >= 0.f) || isinf(scale)) return BD_E_SHAPE;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return BD_E_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3u)
+        return BD_E_ALIGN;
+    const size_t need = bd::block_attn_ws_bytes(P, Bq, Hq, Hkv, dh);
+    if (!ws || ws_bytes < need) return BD_E_WORKSPACE;
+    if (!aligned16(ws)) return BD_E_ALIGN;
+    return launch_status(bd::launch_block_attn_fp8kv(q, k_cache, v_cache, k_scale, v_scale, P,
+                                                     cap, intra_mask, Bq, Hq, Hkv,
+                                                     default_scale(scale, dh), out, ws, stream));
+}
+
+bd_status bd_kv_quant_fp8(const void* x, int32_t n, int32_t Hkv, int32_t dh, const float* scale,
+                          uint8_t* cache, int32_t cap, int32_t pos, hipStream_t stream) {
+    if (!x || !scale || !cache) return BD_E_NULL;
+    if (n < 0 || Hkv < 1 || dh < 4 || dh % 4 != 0 || pos < 0 || cap < 1) return BD_E_SHAPE;
+    if ((int64_t)pos + n > cap) return BD_E_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(x) & 7u) || (reinterpret_cast<uintptr_t>(cache) & 3u) ||
+        (reinterpret_cast<uintptr_t>(scale) & 3u))
+        return BD_E_ALIGN;
+    return launch_status(bd::launch_kv_quant_fp8(x, n, Hkv, dh, scale, cache, cap, pos, stream));
+}
+
 size_t bd_lmhead_conf_ws_bytes(int32_t B, int32_t d, int32_t V) {
     if (B < 1 || B > 64 || d < 1 || V < 1) return 0;
     return bd::lmhead_ws_bytes(B, d, V);

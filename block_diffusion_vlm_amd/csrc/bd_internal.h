@@ -124,6 +124,14 @@ hipError_t launch_block_attn_paged(const void* q, const void* k_pool, const void
                                    const int32_t* page_table, int page_size, int n_pages, int P,
                                    int key_lo, const uint64_t* mask, int Bq, int Hq, int Hkv,
                                    float scale, void* out, void* ws, hipStream_t st);
+// FP8 (E4M3) KV cache: codes [Hkv][cap][128], per-KV-head float32 scales.
+hipError_t launch_block_attn_fp8kv(const void* q, const uint8_t* kc, const uint8_t* vc,
+                                   const float* k_scale, const float* v_scale, int P, int cap,
+                                   const uint64_t* mask, int Bq, int Hq, int Hkv, float scale,
+                                   void* out, void* ws, hipStream_t st);
+// New rows x [n][Hkv][dh] (bf16) into cache rows pos .. pos+n-1 of an FP8 cache.
+hipError_t launch_kv_quant_fp8(const void* x, int n, int Hkv, int dh, const float* scale,
+                               uint8_t* cache, int cap, int pos, hipStream_t st);
 hipError_t launch_block_attn_f32(const float* q, const float* kc, const float* vc, int P, int cap,
                                  const uint64_t* mask, int Bq, int Hq, int Hkv, int dh,
                                  float scale, float* out, hipStream_t st,

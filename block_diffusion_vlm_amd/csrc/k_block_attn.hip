@@ -9,6 +9,15 @@
 // one tile; workgroup (split, kv head, row block) handles 64 keys for up to
 // 128 rows (4 waves x 32 rows) and writes an unnormalised partial
 // (max, sum, O) per row; a second kernel merges the splits in a fixed order.
+//
+// FP8 KV cache (the fastest configuration of the overview runs FP8, §2.3.2):
+// K and V hold OCP E4M3 codes with one float32 scale per KV head for each.
+// Every E4M3 value is exact in bfloat16, so tiles are converted while they
+// are staged into LDS and the bf16 MFMA path runs unchanged on the exact code
+// values; the K scale joins the score scale and the V scale multiplies the
+// partial outputs.
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace bd {
@@ -51,12 +60,37 @@ struct Paging {
     int page_size, n_pages, key_lo;
 };
 
-template <bool PAGED>
+// Per-KV-head scales of an FP8 cache (unused otherwise).
+struct Fp8Kv {
+    const float* k_scale;
+    const float* v_scale;
+};
+
+// Eight E4M3 codes (two little-endian words) as bfloat16 values; exact.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(int(lo), false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(int(lo), true);
+    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(int(hi), false);
+    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(int(hi), true);
+    return bf16x8{static_cast<__bf16>(a[0]), static_cast<__bf16>(a[1]),
+                  static_cast<__bf16>(b[0]), static_cast<__bf16>(b[1]),
+                  static_cast<__bf16>(c[0]), static_cast<__bf16>(c[1]),
+                  static_cast<__bf16>(d[0]), static_cast<__bf16>(d[1])};
+}
+
+// One 64-key tile of an FP8 cache in flight: thread t holds 32 codes (dh
+// 32 (t % 4) .. +31) of key t / 4 of the tile, for K and for V.
+struct Fp8Stage {
+    u32x4 k[2], v[2];
+};
+
+template <bool PAGED, bool FP8 = false>
 __global__ __launch_bounds__(256) void block_attn_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int P, int cap, const uint64_t* __restrict__ mask, int Bq,
     int Hq, int Hkv, float scale_log2, void* __restrict__ ws, int nsplit, int kt,
-    const int32_t* __restrict__ gate, Paging pg) {
+    const int32_t* __restrict__ gate, Paging pg, Fp8Kv f8) {
+    static_assert(!(PAGED && FP8), "the FP8 cache is contiguous");
     if (gated_off(gate)) return;
     __shared__ __align__(16) uint16_t kbuf[2][kTile];
     __shared__ __align__(16) uint16_t vbuf[2][kTile];
@@ -74,8 +108,37 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
     const int ntiles = (Nk - key_lo + kBN - 1) / kBN;
     const int t_end = t_beg + kt < ntiles ? t_beg + kt : ntiles;
     unsigned koff[4], voff[4];
-    dma_offsets<4, false>(koff, kDh);
-    dma_offsets<4, true>(voff, kDh);
+    if constexpr (!FP8) {
+        dma_offsets<4, false>(koff, kDh);
+        dma_offsets<4, true>(voff, kDh);
+    }
+    // FP8 cache: codes of tile t into registers (keys past the last one read
+    // the last one), then converted into the swizzled bf16 LDS layouts.
+    const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(kc) + size_t(g) * cap * kDh;
+    const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(vc) + size_t(g) * cap * kDh;
+    auto fetch8 = [&](int t, Fp8Stage& st) {
+        const int j0 = t * kBN;
+        const int n = Nk - j0 < kBN ? Nk - j0 : kBN;
+        const int key = threadIdx.x >> 2;
+        const size_t off = size_t(j0 + (key < n ? key : n - 1)) * kDh + 32 * (threadIdx.x & 3);
+        st.k[0] = *reinterpret_cast<const u32x4*>(kb8 + off);
+        st.k[1] = *reinterpret_cast<const u32x4*>(kb8 + off + 16);
+        st.v[0] = *reinterpret_cast<const u32x4*>(vb8 + off);
+        st.v[1] = *reinterpret_cast<const u32x4*>(vb8 + off + 16);
+    };
+    auto stage8 = [&](const Fp8Stage& st, uint16_t* kd, uint16_t* vd) {
+        const int key = threadIdx.x >> 2;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                const int piece = 4 * (threadIdx.x & 3) + 2 * h2 + pp;   // 8 dh values
+                *reinterpret_cast<bf16x8*>(kd + key * kDh + 8 * k_slot(key, piece)) =
+                    e4m3x8_to_bf16(st.k[h2][2 * pp], st.k[h2][2 * pp + 1]);
+                *reinterpret_cast<bf16x8*>(vd + key * kDh + 8 * v_slot(key, piece)) =
+                    e4m3x8_to_bf16(st.v[h2][2 * pp], st.v[h2][2 * pp + 1]);
+            }
+    };
     auto load = [&](int t, uint16_t* kd, uint16_t* vd) {
         const int j0 = key_lo + t * kBN;
         const int n = Nk - j0 < kBN ? Nk - j0 : kBN;
@@ -90,7 +153,13 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
             dma_tile<4, true>(vd, vb + size_t(j0) * kDh, kDh, n);
         }
     };
-    load(t_beg, kbuf[0], vbuf[0]);
+    Fp8Stage st8;
+    if constexpr (FP8) {
+        fetch8(t_beg, st8);
+        stage8(st8, kbuf[0], vbuf[0]);
+    } else {
+        load(t_beg, kbuf[0], vbuf[0]);
+    }
 
     // Query row of this lane: r -> (block query i, head g*group + r % group).
     const int r = blockIdx.z * kRowsPerWg + wave * 32 + (lane & 31);
@@ -102,16 +171,26 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
     const uint64_t mbits = row_ok ? mask[qi] : 0;
     const ReadOffsets ro = read_offsets(lane);
 
-    dma_wait<0>();
-    tile_barrier();
+    if constexpr (FP8) {
+        __syncthreads();
+        scale_log2 *= f8.k_scale[g];
+    } else {
+        dma_wait<0>();
+        tile_barrier();
+    }
 
     float m = -INFINITY, l = 0.f;
     f32x16 oacc[4] = {};
-    // One tile: the next tile's loads go into the other buffers.
+    // One tile: the next tile's loads go into the other buffers (for an FP8
+    // cache its codes are fetched here and staged after this tile).
     auto step = [&](int t, const uint16_t* kcur, const uint16_t* vcur, uint16_t* knxt,
                     uint16_t* vnxt) {
         const int j0 = key_lo + t * kBN;
-        if (t + 1 < t_end) load(t + 1, knxt, vnxt);
+        if constexpr (FP8) {
+            if (t + 1 < t_end) fetch8(t + 1, st8);
+        } else {
+            if (t + 1 < t_end) load(t + 1, knxt, vnxt);
+        }
 
         f32x16 sacc[2];
         scores(sacc, kcur, qf, ro);
@@ -143,15 +222,31 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
             for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
         }
         accumulate_pv(oacc, vcur, pf, ro);
+        if constexpr (FP8) {
+            if (t + 1 < t_end) stage8(st8, knxt, vnxt);
+        }
+    };
+    // Loads (DMA) or staged stores (FP8) of the next tile complete before the
+    // barrier; every wave has read the current tile after it.
+    auto sync = [&] {
+        if constexpr (FP8) {
+            __syncthreads();
+        } else {
+            dma_wait<0>();
+            tile_barrier();
+        }
     };
     for (int t = t_beg; t < t_end; t += 2) {
         step(t, kbuf[0], vbuf[0], kbuf[1], vbuf[1]);
-        dma_wait<0>();
-        tile_barrier();
+        sync();
         if (t + 1 == t_end) break;
         step(t + 1, kbuf[1], vbuf[1], kbuf[0], vbuf[0]);
-        dma_wait<0>();
-        tile_barrier();
+        sync();
+    }
+    if constexpr (FP8) {
+        const float vs = f8.v_scale[g];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[db] *= vs;
     }
 
     if (row_ok) {
@@ -319,22 +414,27 @@ int num_splits(int P, int Bq, int Hq, int Hkv) {
 hipError_t launch_block_attn_any(const void* q, const void* kc, const void* vc, int P, int cap,
                                  const uint64_t* mask, int Bq, int Hq, int Hkv, float scale,
                                  void* out, void* ws, hipStream_t st, const int32_t* gate,
-                                 Paging pg) {
+                                 Paging pg, const Fp8Kv* f8 = nullptr) {
     // Splits over the visited keys [key_lo, P + Bq).
     const int kt = tiles_per_split(P - pg.key_lo, Bq, Hq, Hkv);
     const int nsplit = num_splits(P - pg.key_lo, Bq, Hq, Hkv);
     const int R = Bq * (Hq / Hkv);
     const dim3 grid(nsplit, Hkv, (R + kRowsPerWg - 1) / kRowsPerWg);
-    if (pg.table != nullptr)
+    if (f8 != nullptr)
+        hipLaunchKernelGGL((block_attn_split_kernel<false, true>), grid, dim3(256), 0, st,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
+                           static_cast<const uint16_t*>(vc), P, cap, mask, Bq, Hq, Hkv,
+                           scale * kLog2e, ws, nsplit, kt, gate, pg, *f8);
+    else if (pg.table != nullptr)
         hipLaunchKernelGGL(block_attn_split_kernel<true>, grid, dim3(256), 0, st,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                            static_cast<const uint16_t*>(vc), P, cap, mask, Bq, Hq, Hkv,
-                           scale * kLog2e, ws, nsplit, kt, gate, pg);
+                           scale * kLog2e, ws, nsplit, kt, gate, pg, Fp8Kv{});
     else
         hipLaunchKernelGGL(block_attn_split_kernel<false>, grid, dim3(256), 0, st,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                            static_cast<const uint16_t*>(vc), P, cap, mask, Bq, Hq, Hkv,
-                           scale * kLog2e, ws, nsplit, kt, gate, pg);
+                           scale * kLog2e, ws, nsplit, kt, gate, pg, Fp8Kv{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(block_attn_combine_kernel, dim3(Bq * Hq), dim3(kCombineThreads), 0, st, ws,
@@ -354,6 +454,50 @@ hipError_t launch_block_attn_bf16(const void* q, const void* kc, const void* vc,
                                   void* out, void* ws, hipStream_t st, const int32_t* gate) {
     return launch_block_attn_any(q, kc, vc, P, cap, mask, Bq, Hq, Hkv, scale, out, ws, st, gate,
                                  Paging{nullptr, 1, 1, 0});
+}
+
+hipError_t launch_block_attn_fp8kv(const void* q, const uint8_t* kc, const uint8_t* vc,
+                                   const float* k_scale, const float* v_scale, int P, int cap,
+                                   const uint64_t* mask, int Bq, int Hq, int Hkv, float scale,
+                                   void* out, void* ws, hipStream_t st) {
+    const Fp8Kv f8{k_scale, v_scale};
+    return launch_block_attn_any(q, kc, vc, P, cap, mask, Bq, Hq, Hkv, scale, out, ws, st, nullptr,
+                                 Paging{nullptr, 1, 1, 0}, &f8);
+}
+
+// New K or V rows into an FP8 cache: row i of head g goes to cache row pos + i.
+// Four elements per thread: fl32(x * fl32(1 / scale)), clamped to +-448,
+// rounded to E4M3 (nearest, ties to even).
+__global__ __launch_bounds__(256) void kv_quant_fp8_kernel(const uint16_t* __restrict__ x, int n,
+                                                           int Hkv, int dh,
+                                                           const float* __restrict__ scale,
+                                                           uint8_t* __restrict__ cache, int cap,
+                                                           int pos) {
+    const size_t i4 = (size_t(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+    const size_t total = size_t(n) * Hkv * dh;
+    if (i4 >= total) return;
+    const int d = int(i4 % dh);
+    const size_t rh = i4 / dh;                       // row * Hkv + head
+    const int g = int(rh % Hkv);
+    const int row = int(rh / Hkv);
+    const float inv = 1.0f / scale[g];
+    const uint2 w = *reinterpret_cast<const uint2*>(x + i4);
+    float f[4] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                  __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = fminf(fmaxf(f[e] * inv, -448.f), 448.f);
+    int packed = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+    packed = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], packed, true);
+    *reinterpret_cast<int*>(cache + (size_t(g) * cap + pos + row) * dh + d) = packed;
+}
+
+hipError_t launch_kv_quant_fp8(const void* x, int n, int Hkv, int dh, const float* scale,
+                               uint8_t* cache, int cap, int pos, hipStream_t st) {
+    const size_t quads = size_t(n) * Hkv * dh / 4;
+    if (quads == 0) return hipSuccess;
+    hipLaunchKernelGGL(kv_quant_fp8_kernel, dim3(unsigned((quads + 255) / 256)), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(x), n, Hkv, dh, scale, cache, cap, pos);
+    return hipGetLastError();
 }
 
 hipError_t launch_block_attn_paged(const void* q, const void* k_pool, const void* v_pool,

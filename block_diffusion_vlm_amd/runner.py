@@ -106,6 +106,24 @@ class BlockAttn:
                          stream)
 
 
+class BlockAttnFP8KV:
+    """bd_block_attn_fp8kv (bf16 queries, FP8 E4M3 KV cache with per-head
+    scales) over fixed device buffers."""
+
+    def __init__(self, kind: int, Bq: int, P: int, cap: int, Hq: int, Hkv: int, dh: int = 128,
+                 device="cuda"):
+        self.Bq, self.P, self.cap, self.Hq, self.Hkv, self.dh = Bq, P, cap, Hq, Hkv, dh
+        self.mask = mask_dev(kind, Bq, device)
+        self.out = torch.empty((Bq, Hq, dh), dtype=torch.bfloat16, device=device)
+        self.ws_bytes = bd.bd_block_attn_ws_bytes(P, Bq, Hq, Hkv, dh)
+        self.ws = workspace(self.ws_bytes, device)
+
+    def __call__(self, q, k_codes, v_codes, k_scale, v_scale, stream=None, scale=0.0):
+        bd.bd_block_attn_fp8kv(q, k_codes, v_codes, k_scale, v_scale, self.P, self.cap,
+                               self.mask, self.Bq, self.Hq, self.Hkv, self.dh, scale, self.out,
+                               self.ws, self.ws_bytes, stream)
+
+
 class DecodeStep:
     """One threshold (MDM) block-decode step: bd_block_attn (bidirectional
     block) -> bd_lmhead_conf_commit (LM head, then commit).  With

@@ -23,7 +23,7 @@ from __future__ import annotations
 import numpy as np
 
 BASE_SEED = 20261203
-N_CONFIGS = 8
+N_CONFIGS = 9
 
 
 # ---------------------------------------------------------------------------
@@ -31,7 +31,7 @@ N_CONFIGS = 8
 # ---------------------------------------------------------------------------
 
 def config_rng(cfg: int, seed: int | None = None) -> np.random.Generator:
-    """PCG64 stream for workload ``cfg`` (1..8): child ``cfg-1`` of
+    """PCG64 stream for workload ``cfg`` (1..9): child ``cfg-1`` of
     SeedSequence(seed or BASE_SEED)."""
     ss = np.random.SeedSequence(BASE_SEED if seed is None else seed)
     return np.random.Generator(np.random.PCG64(ss.spawn(N_CONFIGS)[cfg - 1]))
@@ -227,6 +227,33 @@ def qwen_decode(seed: int | None = None, B=16, n_vis=1024, n_prompt=256, Hq=16, 
         "v_cache": normal_bf16(rng, (Hkv * cap, dh), trunc=4.0).reshape(Hkv, cap, dh),
         "W": W, "h": h, "targets": t.astype(np.int32), "target_conf": c, "planted_commit": z,
         "masked": masked, "tokens": tokens,
+    }
+
+
+def qwen_decode_fp8kv(seed: int | None = None, B=16, n_vis=1024, n_prompt=256, Hq=16, Hkv=2,
+                      dh=128, scale_spread=0.1) -> dict:
+    """The block attention of ``qwen_decode`` over an FP8 (E4M3) KV cache.
+    K and V are stored as E4M3 codes of 112 x N(0,1) truncated at 4 std, with
+    one float32 scale per KV head, k_scale[g], v_scale[g] = U(1 - spread,
+    1 + spread) / 112, so that the stored entries stand for ~N(0,1) values
+    (V within +-4, as in the bf16 workload).  Queries bf16 N(0,1);
+    bidirectional block.  ``k_new``/``v_new`` [B][Hkv][dh] bf16 are fresh
+    block rows for the quantizer (K ~ N(0,1), V truncated at 4)."""
+    rng = config_rng(9, seed)
+    P = n_vis + n_prompt
+    cap = P + B
+    return {
+        "dtype": "bf16", "B": B, "P": P, "n_vis": n_vis, "n_prompt": n_prompt, "cap": cap,
+        "Hq": Hq, "Hkv": Hkv, "dh": dh,
+        "q": normal_bf16(rng, (B, Hq, dh)),
+        "k_codes": normal_e4m3(rng, (Hkv * cap, dh)).reshape(Hkv, cap, dh),
+        "v_codes": normal_e4m3(rng, (Hkv * cap, dh)).reshape(Hkv, cap, dh),
+        "k_scale": (rng.uniform(1 - scale_spread, 1 + scale_spread, Hkv)
+                    / E4M3_CODE_STD).astype(np.float32),
+        "v_scale": (rng.uniform(1 - scale_spread, 1 + scale_spread, Hkv)
+                    / E4M3_CODE_STD).astype(np.float32),
+        "k_new": normal_bf16(rng, (B, Hkv, dh)),
+        "v_new": normal_bf16(rng, (B, Hkv, dh), trunc=4.0),
     }
 
 

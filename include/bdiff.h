@@ -329,6 +329,43 @@ bd_status bd_cert_scan(const float* anchor_conf, const int32_t* anchor_tok,
                        hipStream_t stream);
 
 /*
+ * bd_block_attn_fp8kv - bd_block_attn (bf16 queries and output) over an FP8
+ * KV cache.  [OV §2.3.2: the fastest configuration runs FP8; OCP OFP8 E4M3]
+ * The cache holds OCP E4M3 codes, and a cached entry stands for
+ *   decode(code) * k_scale[g]   (K of KV head g),  decode(code) * v_scale[g]
+ * (V), so scores are scale * k_scale[g] * (q . decode(k)) and the output is
+ * v_scale[g] * (softmax-weighted decoded V).  Masks, heads, prefix and the
+ * block's own rows as in bd_block_attn.
+ *   q            [Bq][Hq][dh] bfloat16;  out the same
+ *   k_cache, v_cache  [Hkv][cap][dh] uint8 E4M3 codes (NaN codes not allowed)
+ *   k_scale, v_scale  [Hkv] float32 (device)
+ *   ws           at least bd_block_attn_ws_bytes(P, Bq, Hq, dh) bytes
+ * Limits: dh == 128, Bq <= 64, P + Bq <= min(cap, 65536), Hq % Hkv == 0.
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_ALIGN (16 bytes; scales 4),
+ *   BD_E_WORKSPACE, BD_E_LAUNCH.
+ */
+bd_status bd_block_attn_fp8kv(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                              const float* k_scale, const float* v_scale, int32_t P, int32_t cap,
+                              const uint64_t* intra_mask, int32_t Bq, int32_t Hq, int32_t Hkv,
+                              int32_t dh, float scale, void* out, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/*
+ * bd_kv_quant_fp8 - writes n new K (or V) rows into an FP8 cache, e.g. the
+ * block's own rows at pos = P.  [OV §2.3.2; OCP OFP8 E4M3]
+ *   cache[g][pos + i][d] = E4M3 rounding (nearest, ties to even) of
+ *                          clamp(fl32(x[i][g][d] * fl32(1 / scale[g])), -448, 448)
+ *   x      [n][Hkv][dh] bfloat16 (finite), 8-byte aligned
+ *   scale  [Hkv] float32 (device), > 0
+ *   cache  [Hkv][cap][dh] uint8, 4-byte aligned; rows outside pos .. pos+n-1
+ *          are left untouched
+ * Limits: dh % 4 == 0, 0 <= pos, pos + n <= cap; n = 0 is a no-op.
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_ALIGN, BD_E_LAUNCH.
+ */
+bd_status bd_kv_quant_fp8(const void* x, int32_t n, int32_t Hkv, int32_t dh, const float* scale,
+                          uint8_t* cache, int32_t cap, int32_t pos, hipStream_t stream);
+
+/*
  * bd_dualstream_attn - training-time attention over the vision-efficient
  * dual-stream sequence [visual (n_vis) | clean text (n_txt) | noisy text
  * (n_txt)], N = n_vis + 2 n_txt.  [OV §2.2.1-§2.2.2; TH §4.1, §4.4]

@@ -129,6 +129,42 @@ def test_block_attn_paged_validation():
     assert f(key_lo=1024, ws_bytes=need - 1) == bd.BD_E_WORKSPACE
 
 
+def test_block_attn_fp8kv_validation():
+    f = lambda **kw: bd.bd_block_attn_fp8kv(**{**dict(  # noqa: E731
+        q=FAKE, k_cache=FAKE, v_cache=FAKE, k_scale=FAKE, v_scale=FAKE, P=1280, cap=1296,
+        intra_mask=FAKE, Bq=16, Hq=16, Hkv=2, dh=128, scale=0.0, out=FAKE, ws=FAKE,
+        ws_bytes=1 << 30, stream=0, check=False), **kw})
+    for name in ("q", "k_cache", "v_cache", "k_scale", "v_scale", "intra_mask", "out"):
+        assert f(**{name: None}) == bd.BD_E_NULL, name
+    assert f(cap=1295) == bd.BD_E_SHAPE            # P + Bq rows must fit the cache
+    assert f(dh=64) == bd.BD_E_SHAPE
+    assert f(Bq=65) == bd.BD_E_SHAPE
+    assert f(Hq=15) == bd.BD_E_SHAPE
+    assert f(scale=-1.0) == bd.BD_E_SHAPE
+    assert f(v_cache=MISALIGNED) == bd.BD_E_ALIGN
+    assert f(k_scale=FAKE + 2) == bd.BD_E_ALIGN
+    assert f(ws=None) == bd.BD_E_WORKSPACE
+    need = bd.bd_block_attn_ws_bytes(1280, 16, 16, 2, 128)
+    assert f(ws_bytes=need - 1) == bd.BD_E_WORKSPACE
+    assert f(ws=MISALIGNED) == bd.BD_E_ALIGN
+
+
+def test_kv_quant_fp8_validation():
+    f = lambda **kw: bd.bd_kv_quant_fp8(**{**dict(  # noqa: E731
+        x=FAKE, n=16, Hkv=2, dh=128, scale=FAKE, cache=FAKE, cap=1296, pos=1280, stream=0,
+        check=False), **kw})
+    for name in ("x", "scale", "cache"):
+        assert f(**{name: None}) == bd.BD_E_NULL, name
+    assert f(pos=1281) == bd.BD_E_SHAPE            # rows past the cache
+    assert f(pos=-1) == bd.BD_E_SHAPE
+    assert f(n=-1) == bd.BD_E_SHAPE
+    assert f(dh=126) == bd.BD_E_SHAPE              # whole groups of four
+    assert f(Hkv=0) == bd.BD_E_SHAPE
+    assert f(x=FAKE + 4) == bd.BD_E_ALIGN
+    assert f(cache=FAKE + 2) == bd.BD_E_ALIGN
+    assert f(scale=FAKE + 1) == bd.BD_E_ALIGN
+
+
 def _lm(**kw):
     a = dict(dt=bd.BD_BF16, h=FAKE, W=FAKE, B=16, d=2048, V=151936, conf=FAKE, argmax=FAKE,
              ws=FAKE, ws_bytes=1 << 30, stream=0, check=False)
