@@ -37,6 +37,17 @@ using namespace ds;
 // Headroom (log2 units) before the running maximum of a row is moved.
 constexpr float kLazy = 8.0f;
 
+// Score register e (0..31) of a lane holds the key at offset
+// 32 (e / 16) + 8 (e % 16 / 4) + e % 4 from the lane's first key, offsets
+// that increase with e; the registers whose keys lie below offset D
+// therefore form a prefix, of length 4 (D / 8) + min(4, D % 8).  Returns
+// that prefix as a bit mask.
+__device__ __forceinline__ unsigned key_prefix(int D) {
+    D = D < 0 ? 0 : (D > 64 ? 64 : D);
+    const int c = 4 * (D >> 3) + ((D & 7) < 4 ? (D & 7) : 4);
+    return c >= 32 ? 0xffffffffu : (1u << c) - 1u;
+}
+
 // One wave per 32 query rows, WAVES waves per workgroup sharing the K/V
 // tiles, two waves per SIMD.  The scores of tile t+1 are computed while the
 // softmax of tile t runs: the score block of an iteration is laid out as 16
@@ -157,15 +168,22 @@ __global__ __launch_bounds__(WAVES * 64, 2) void dualstream_bf16_kernel(
         auto rk = [&](int i) { return read_k(kread, ro, i & 1, i >> 1); };
         bf16x8 ka[16];
         static_for<0, kAhead>([&](auto I) { ka[I] = rk(I); });
-        // Key of accumulator register e of this lane: jl + 8 (e / 4) + e % 4.
-        const int jl = j0 + 4 * (lane >> 5);
-        const int lim = rv.lim < j1 - 1 ? rv.lim : j1 - 1;
-        const int hi = rv.hi < j1 ? rv.hi : j1;
+        // Visible registers of a partly visible tile, one bit each: keys up
+        // to lim, and keys in [lo, hi), both cut at the tile's end j1.
+        unsigned vis_bits = 0xffffffffu;
+        if constexpr (MASKED) {
+            const int jl = j0 + 4 * (lane >> 5);        // this lane's first key
+            const int lim = rv.lim < j1 - 1 ? rv.lim : j1 - 1;
+            const int hi = rv.hi < j1 ? rv.hi : j1;
+            vis_bits = key_prefix(lim - jl + 1) |
+                       (key_prefix(hi - jl) & ~key_prefix(rv.lo - jl));
+        }
         auto val = [&](int e) -> float {
             if constexpr (MASKED) {
-                const int jj = jl + 32 * (e >> 4) + 8 * ((e & 15) >> 2) + (e & 3);
-                const bool vis = (jj <= lim) | ((jj >= rv.lo) & (jj < hi));
-                return vis ? s[e >> 4][e & 15] : -INFINITY;
+                // bit e, sign-extended to a full-word select mask
+                const unsigned sel = unsigned(int(vis_bits << (31 - e)) >> 31);
+                return __uint_as_float((__float_as_uint(s[e >> 4][e & 15]) & sel) |
+                                       (0xff800000u & ~sel));
             } else {
                 return s[e >> 4][e & 15];
             }
