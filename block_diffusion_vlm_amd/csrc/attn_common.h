@@ -57,6 +57,23 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ int k_slot(int key, int piece) { return piece ^ (key & 15); }
 __device__ __forceinline__ int v_slot(int key, int piece) { return piece ^ (4 * (key & 3)); }
 
+// Accumulator register e (0..31) over two 32-key (or 32-row) blocks holds,
+// for a lane, the key at offset 32 (e / 16) + 8 (e % 16 / 4) + e % 4 from
+// the lane's first key (acc_row below); these offsets increase with e, so
+// the registers whose keys lie below offset D form a prefix, of length
+// 4 (D / 8) + min(4, D % 8).  Returns that prefix as a bit mask: visibility
+// rules that are unions of key intervals become a few such masks per tile.
+__device__ __forceinline__ unsigned key_prefix(int D) {
+    D = D < 0 ? 0 : (D > 64 ? 64 : D);
+    const int c = 4 * (D >> 3) + ((D & 7) < 4 ? (D & 7) : 4);
+    return c >= 32 ? 0xffffffffu : (1u << c) - 1u;
+}
+
+// Full-word select mask from bit e of a register bit mask (0 or all ones).
+__device__ __forceinline__ unsigned bit_select(unsigned bits, int e) {
+    return unsigned(int(bits << (31 - e)) >> 31);
+}
+
 // Key held by accumulator register r of lane l inside a 32-key block.
 __device__ __forceinline__ int acc_row(int r, int lane) {
     return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);

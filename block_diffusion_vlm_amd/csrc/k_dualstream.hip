@@ -37,17 +37,6 @@ using namespace ds;
 // Headroom (log2 units) before the running maximum of a row is moved.
 constexpr float kLazy = 8.0f;
 
-// Score register e (0..31) of a lane holds the key at offset
-// 32 (e / 16) + 8 (e % 16 / 4) + e % 4 from the lane's first key, offsets
-// that increase with e; the registers whose keys lie below offset D
-// therefore form a prefix, of length 4 (D / 8) + min(4, D % 8).  Returns
-// that prefix as a bit mask.
-__device__ __forceinline__ unsigned key_prefix(int D) {
-    D = D < 0 ? 0 : (D > 64 ? 64 : D);
-    const int c = 4 * (D >> 3) + ((D & 7) < 4 ? (D & 7) : 4);
-    return c >= 32 ? 0xffffffffu : (1u << c) - 1u;
-}
-
 // One wave per 32 query rows, WAVES waves per workgroup sharing the K/V
 // tiles, two waves per SIMD.  The scores of tile t+1 are computed while the
 // softmax of tile t runs: the score block of an iteration is laid out as 16
@@ -180,8 +169,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void dualstream_bf16_kernel(
         }
         auto val = [&](int e) -> float {
             if constexpr (MASKED) {
-                // bit e, sign-extended to a full-word select mask
-                const unsigned sel = unsigned(int(vis_bits << (31 - e)) >> 31);
+                const unsigned sel = bit_select(vis_bits, e);
                 return __uint_as_float((__float_as_uint(s[e >> 4][e & 15]) & sel) |
                                        (0xff800000u & ~sel));
             } else {

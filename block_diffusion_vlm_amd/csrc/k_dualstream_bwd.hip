@@ -133,16 +133,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         scores_ahead<kAheadDq>(sacc, kK, qf, ro);    // S^T[key][row]
         scores_ahead<kAheadDq>(dpacc, vK, gf, ro);   // dP^T[key][row] = V[key] . dO[row]
         bf16x8 dsf[2][2];
+        // Visible keys of this lane's registers (bit e for register e): keys
+        // up to lim or in [lo, hi), and inside the tile.
         const int jl = j0 + 4 * (lane >> 5);
-        const int jn = j0 + n;
+        const unsigned vis_bits =
+            key_prefix(n - 4 * (lane >> 5)) &
+            (key_prefix(rv.lim - jl + 1) | (key_prefix(rv.hi - jl) & ~key_prefix(rv.lo - jl)));
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int jj = jl + 32 * kb + 8 * (e >> 2) + (e & 3);
-                const bool vis = (jj < jn) & ((jj <= rv.lim) | ((jj >= rv.lo) & (jj < rv.hi)));
-                const float p =
-                    vis ? __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], scale_log2, -lse2)) : 0.f;
+                const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], scale_log2, -lse2));
+                const float p = __uint_as_float(__float_as_uint(pe) & bit_select(vis_bits, 16 * kb + e));
                 dsf[kb][e >> 3][e & 7] = static_cast<__bf16>(p * (dpacc[kb][e] - Dr));
             }
         accumulate_pv_ahead<kAheadDq>(dqacc, kV, dsf, ro);   // dQ^T += K^T dS^T
@@ -257,6 +259,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         const int il = 4 * (lane >> 5);
         auto grad = [&](auto masked_tag) {
             constexpr bool MASKED = decltype(masked_tag)::value;
+            // Rows of this lane's registers that see the key (bit e for
+            // register e; rows at offsets from i0 + il): clean rows at or
+            // after the key; noisy rows from rmin on or inside [lo, hi);
+            // all inside the tile.  A tile is all clean or all noisy.
+            unsigned vis_bits = 0xffffffffu;
+            if constexpr (MASKED) {
+                const int base = i0 + il;
+                if (i0 < G.ctx) {
+                    vis_bits = ~key_prefix(kv.j - base);
+                } else {
+                    const int rb = base - G.ctx;
+                    vis_bits = ~key_prefix(kv.rmin - rb) |
+                               (key_prefix(kv.hi - rb) & ~key_prefix(kv.lo - rb));
+                }
+                vis_bits &= key_prefix(n - il);
+            }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -267,11 +285,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
                         const int e = 4 * e4 + x;
-                        bool vis = true;
-                        if constexpr (MASKED) vis = (ir0 + x < n) & seen_by(G, kv, i0 + ir0 + x);
-                        const float p = vis ? __builtin_amdgcn_exp2f(fmaf(
-                                                  sacc[kb][e], scale_log2, -l4[x] * kLog2e))
-                                            : 0.f;
+                        float p = __builtin_amdgcn_exp2f(
+                            fmaf(sacc[kb][e], scale_log2, -l4[x] * kLog2e));
+                        if constexpr (MASKED)
+                            p = __uint_as_float(__float_as_uint(p) &
+                                                bit_select(vis_bits, 16 * kb + e));
                         pf[kb][e >> 3][e & 7] = static_cast<__bf16>(p);
                         dsf[kb][e >> 3][e & 7] =
                             static_cast<__bf16>(p * (dpacc[kb][e] - d4[x]));
