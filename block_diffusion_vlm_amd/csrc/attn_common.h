@@ -191,40 +191,6 @@ __device__ __forceinline__ void dma_floats64(float* lds, const float* g, int str
                      : "memory");
 }
 
-// Per-lane global byte offsets of the loads of a complete tile (all 64 keys
-// present), the same for every tile: off[u] for load u of this wave.
-template <int WAVES, bool IS_V>
-__device__ __forceinline__ void dma_offsets(unsigned (&off)[16 / WAVES], int row_stride) {
-    constexpr int PER_WAVE = 16 / WAVES;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int s = lane & 15;
-#pragma unroll
-    for (int u = 0; u < PER_WAVE; ++u) {
-        const int key = 4 * (wave * PER_WAVE + u) + (lane >> 4);
-        const int slot = IS_V ? v_slot(key, s) : k_slot(key, s);
-        off[u] = unsigned(key) * 2u * unsigned(row_stride) + 16u * unsigned(slot);
-    }
-}
-
-// Loads of a complete tile with precomputed offsets (see dma_tile).
-template <int WAVES>
-__device__ __forceinline__ void dma_tile_full(uint16_t* lds, const uint16_t* g,
-                                              const unsigned (&off)[16 / WAVES]) {
-    constexpr int PER_WAVE = 16 / WAVES;
-    const unsigned wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const unsigned lofs =
-        static_cast<unsigned>(reinterpret_cast<uintptr_t>((BD_LDS void*)lds));
-#pragma unroll
-    for (int u = 0; u < PER_WAVE; ++u) {
-        const unsigned m0 = __builtin_amdgcn_readfirstlane(lofs + 1024u * (wave * PER_WAVE + u));
-        __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                         :
-                         : "{m0}"(m0), "v"(off[u]), "s"(g)
-                         : "memory");
-    }
-}
-
 // Loads of a complete tile from one per-lane offset (see dma_tile).  Load
 // instruction I brings keys 4I .. 4I+3: the row of key 4I goes into the
 // scalar base address, so the lane's byte offset is that of key (lane >> 4)

@@ -107,11 +107,8 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
     const int t_beg = split * kt;
     const int ntiles = (Nk - key_lo + kBN - 1) / kBN;
     const int t_end = t_beg + kt < ntiles ? t_beg + kt : ntiles;
-    unsigned koff[4], voff[4];
-    if constexpr (!FP8) {
-        dma_offsets<4, false>(koff, kDh);
-        dma_offsets<4, true>(voff, kDh);
-    }
+    const unsigned koff = dma_lane_offset<false>(kDh);
+    const unsigned voff = dma_lane_offset<true>(kDh);
     // FP8 cache: codes of tile t into registers (keys past the last one read
     // the last one), then converted into the swizzled bf16 LDS layouts.
     const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(kc) + size_t(g) * cap * kDh;
@@ -146,8 +143,8 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
             dma_tile_paged<4, false>(kd, kc, pg.table, pg.page_size, pg.n_pages, Hkv, g, j0, n);
             dma_tile_paged<4, true>(vd, vc, pg.table, pg.page_size, pg.n_pages, Hkv, g, j0, n);
         } else if (n == kBN) {
-            dma_tile_full<4>(kd, kb + size_t(j0) * kDh, koff);
-            dma_tile_full<4>(vd, vb + size_t(j0) * kDh, voff);
+            dma_tile_full1<4, false>(lds_addr(kd), kb + size_t(j0) * kDh, kDh, koff);
+            dma_tile_full1<4, true>(lds_addr(vd), vb + size_t(j0) * kDh, kDh, voff);
         } else {
             dma_tile<4, false>(kd, kb + size_t(j0) * kDh, kDh, n);
             dma_tile<4, true>(vd, vb + size_t(j0) * kDh, kDh, n);
