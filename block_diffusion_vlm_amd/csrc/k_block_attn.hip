@@ -266,18 +266,20 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
     }
 }
 
-// One workgroup of 128 threads per query row: the split weights
-// 2^(m_s - M) are formed once (thread s owns split s), then thread t
-// accumulates output dim t over the splits in a fixed order, with the loads
-// of consecutive splits independent of each other.
+// One workgroup of 128 threads per query row; thread t owns output dim t.
+// The splits are taken kCombineBatch at a time and every load of a batch is
+// issued before any is used, so a batch costs one memory round trip: lane u
+// of each wave reads split s0 + u's maximum and sum (vector loads), every
+// thread reads its output dim of each split, and the weights 2^(m_s - M) are
+// broadcast from their lanes with readlane.  Splits are accumulated in a
+// fixed order; the running maximum moves once per batch.
 constexpr int kCombineThreads = 128;
+constexpr int kCombineBatch = 32;
 
 __global__ __launch_bounds__(kCombineThreads) void block_attn_combine_kernel(
     const void* __restrict__ ws, int Bq, int Hq, int Hkv, int nsplit, uint16_t* __restrict__ out,
     const int32_t* __restrict__ gate) {
     if (gated_off(gate)) return;
-    __shared__ float wsh[1024];
-    __shared__ float red[kCombineThreads / 64];
     const int rg = blockIdx.x;                      // global row = g * R + r
     const int group = Hq / Hkv;
     const int R = Bq * group;
@@ -286,43 +288,39 @@ __global__ __launch_bounds__(kCombineThreads) void block_attn_combine_kernel(
     const int qi = r / group;
     const int qh = g * group + r % group;
     const int t = threadIdx.x;
+    const int u_lane = t & (kCombineBatch - 1);
     const Partials pt = partials(const_cast<void*>(ws), Hkv * R, nsplit);
     const float* m = pt.m + size_t(rg) * nsplit;
     const float* l = pt.l + size_t(rg) * nsplit;
-
-    // Row maximum over the splits.
-    float M = -INFINITY;
-    for (int s = t; s < nsplit; s += kCombineThreads) M = fmaxf(M, m[s]);
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    if ((t & 63) == 0) red[t >> 6] = M;
-    __syncthreads();
-    M = fmaxf(red[0], red[1]);
-    __syncthreads();
-
-    // Split weights (0 for splits without a visible key) and their sum.
-    float L = 0.f;
-    for (int s = t; s < nsplit; s += kCombineThreads) {
-        const float ms = m[s];
-        const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-        wsh[s] = w;
-        L += w * l[s];
-    }
-    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
-    if ((t & 63) == 0) red[t >> 6] = L;
-    __syncthreads();
-    L = red[0] + red[1];
-
-    float acc = 0.f;
     const float* o = pt.o + size_t(rg) * nsplit * kDh + t;
-    int s = 0;
-    for (; s + 8 <= nsplit; s += 8) {
-        float v[8];
+
+    float M = -INFINITY, L = 0.f, acc = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += kCombineBatch) {
+        // Past the last split the last one is read again and dropped.
+        const int su = min(s0 + u_lane, nsplit - 1);
+        float mu = m[su];
+        const float lu = l[su];
+        float ov[kCombineBatch];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = o[size_t(s + u) * kDh];
+        for (int u = 0; u < kCombineBatch; ++u) ov[u] = o[size_t(min(s0 + u, nsplit - 1)) * kDh];
+        if (s0 + u_lane >= nsplit) mu = -INFINITY;
+        float mb = mu;                              // batch maximum (lanes 32..63 mirror 0..31)
+        for (int off = kCombineBatch / 2; off > 0; off >>= 1) mb = fmaxf(mb, __shfl_xor(mb, off));
+        // No branch here, so that the output loads stay next to the others.
+        const float Mn = fmaxf(M, mb);
+        const float a = (Mn == -INFINITY) ? 1.f : exp2f(M - Mn);  // 0 while M is -inf
+        const float wu = (mu == -INFINITY) ? 0.f : exp2f(mu - Mn);
+        L *= a;
+        acc *= a;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc += wsh[s + u] * v[u];
+        for (int u = 0; u < kCombineBatch; ++u) {
+            const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wu), u));
+            const float lw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lu), u));
+            L += w * lw;
+            acc += w * ov[u];
+        }
+        M = Mn;
     }
-    for (; s < nsplit; ++s) acc += wsh[s] * o[size_t(s) * kDh];
     const float res = (M == -INFINITY) ? 0.f : acc / L;
     const float nb = __shfl_down(res, 1);
     if ((t & 1) == 0) {
