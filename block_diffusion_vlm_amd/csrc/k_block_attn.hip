@@ -246,23 +246,45 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
         for (int db = 0; db < 4; ++db) oacc[db] *= vs;
     }
 
-    if (row_ok) {
+    const Partials pt = partials(ws, Hkv * R, nsplit);
+    if (row_ok && lane < 32) {
         const size_t rg = size_t(g) * R + r;        // global row
-        const Partials pt = partials(ws, Hkv * R, nsplit);
-        if (lane < 32) {
-            pt.m[rg * nsplit + split] = m;
-            pt.l[rg * nsplit + split] = l;
+        pt.m[rg * nsplit + split] = m;
+        pt.l[rg * nsplit + split] = l;
+    }
+    // The partial output leaves through LDS.  A lane holds 16-byte pieces of
+    // its own row only, so stores straight from the accumulators would write
+    // 32 rows x 32 bytes per instruction.  Each wave instead writes its
+    // 32 x 128 block into one of the four tile buffers (free after the last
+    // barrier of the loop), row-major with 16-byte piece c of row rr at slot
+    // c ^ rr, and reads it back so that each store instruction writes two
+    // whole 512-byte rows.
+    uint16_t* const region = wave < 2 ? kbuf[wave] : vbuf[wave - 2];
+    f32x4* const sl = reinterpret_cast<f32x4*>(region);
+    const int rr = lane & 31;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const int c = (32 * db + acc_row(4 * e4, lane)) >> 2;
+            sl[rr * 32 + (c ^ rr)] = f32x4{oacc[db][4 * e4], oacc[db][4 * e4 + 1],
+                                           oacc[db][4 * e4 + 2], oacc[db][4 * e4 + 3]};
         }
-        float* o = pt.o + (rg * nsplit + split) * kDh;
+    const int r0 = blockIdx.z * kRowsPerWg + wave * 32;  // first query row of this wave
+    const int c = lane & 31;
+    f32x4 val[16];
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+    for (int it = 0; it < 16; ++it) {
+        const int row = 2 * it + (lane >> 5);
+        val[it] = sl[row * 32 + (c ^ row)];
+    }
 #pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                const int dh = 32 * db + acc_row(4 * e4, lane);
-                *reinterpret_cast<f32x4*>(o + dh) =
-                    f32x4{oacc[db][4 * e4], oacc[db][4 * e4 + 1], oacc[db][4 * e4 + 2],
-                          oacc[db][4 * e4 + 3]};
-            }
+    for (int it = 0; it < 16; ++it) {
+        const int row = 2 * it + (lane >> 5);
+        if (r0 + row < R) {
+            const size_t rg = size_t(g) * R + r0 + row;
+            *reinterpret_cast<f32x4*>(pt.o + (rg * nsplit + split) * kDh + 4 * c) = val[it];
+        }
     }
 }
 
