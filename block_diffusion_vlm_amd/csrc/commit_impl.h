@@ -14,15 +14,15 @@ namespace bd {
 // confidence and token (ignored for i >= B).  Inside the device-resident
 // block loop (else both null), `gate_out` receives the number of positions
 // still masked afterwards (the next step's gate) and `steps` counts the step.
-__device__ __forceinline__ void commit_wave(float c, int32_t a, int B, float tau,
-                                            uint8_t* __restrict__ masked,
-                                            int32_t* __restrict__ tokens,
-                                            int32_t* __restrict__ n_committed,
-                                            int32_t* gate_out = nullptr,
-                                            int32_t* steps = nullptr) {
+// `was_masked` is lane i's masked[i] != 0 (false for i >= B), read by the
+// caller, which can then issue that read early.
+__device__ __forceinline__ void commit_wave_flag(bool was_masked, float c, int32_t a, int B,
+                                                 float tau, uint8_t* __restrict__ masked,
+                                                 int32_t* __restrict__ tokens,
+                                                 int32_t* __restrict__ n_committed,
+                                                 int32_t* gate_out, int32_t* steps) {
     const int i = threadIdx.x & 63;
-    const bool in = i < B;
-    const bool m = in && masked[i] != 0;
+    const bool m = was_masked;
     const bool above = m && (c > tau);
     const uint64_t above_bits = __ballot(above);
     const uint64_t masked_bits = __ballot(m);
@@ -53,6 +53,17 @@ __device__ __forceinline__ void commit_wave(float c, int32_t a, int B, float tau
         if (gate_out != nullptr) *gate_out = __popcll(masked_bits) - n;
         if (steps != nullptr) *steps += 1;
     }
+}
+
+__device__ __forceinline__ void commit_wave(float c, int32_t a, int B, float tau,
+                                            uint8_t* __restrict__ masked,
+                                            int32_t* __restrict__ tokens,
+                                            int32_t* __restrict__ n_committed,
+                                            int32_t* gate_out = nullptr,
+                                            int32_t* steps = nullptr) {
+    const int i = threadIdx.x & 63;
+    commit_wave_flag(i < B && masked[i] != 0, c, a, B, tau, masked, tokens, n_committed,
+                     gate_out, steps);
 }
 
 }  // namespace bd

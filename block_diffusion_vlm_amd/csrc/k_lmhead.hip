@@ -32,29 +32,33 @@ namespace bd {
 namespace {
 
 // Merge of the G partial states of one position by one wave, in a fixed
-// order: lane l folds partials l, l + 64, ... (loads issued eight at a time,
-// independent of each other), then a fixed xor-shuffle tree.  The result is
-// valid in every lane.
+// order: lane l folds partials l, l + 64, ... .  They are read 512 at a time
+// (eight per lane, every load of a batch issued before the first fold, so a
+// batch costs one memory round trip), then a fixed xor-shuffle tree merges
+// the lanes.  The result is valid in every lane.
 __device__ ArgSoft reduce_column(const WsView& w, int G, int col) {
     const int lane = threadIdx.x & 63;
     const float* m = w.m + size_t(col) * G;
     const float* s = w.s + size_t(col) * G;
     const int* a = w.a + size_t(col) * G;
     ArgSoft st{-INFINITY, 0.f, 0x7fffffff};
-    int p = lane;
-    for (; p + 7 * 64 < G; p += 8 * 64) {
+    for (int p0 = 0; p0 < G; p0 += 8 * 64) {
         float mm[8], ss[8];
         int aa[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            mm[u] = m[p + 64 * u];
-            ss[u] = s[p + 64 * u];
-            aa[u] = a[p + 64 * u];
+            // Past the last partial: reload the last one and drop it below.
+            const int p = min(p0 + 64 * u + lane, G - 1);
+            mm[u] = m[p];
+            ss[u] = s[p];
+            aa[u] = a[p];
         }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (p0 + 64 * u + lane >= G) mm[u] = -INFINITY, ss[u] = 0.f, aa[u] = 0x7fffffff;
 #pragma unroll
         for (int u = 0; u < 8; ++u) st = merge(st, ArgSoft{mm[u], ss[u], aa[u]});
     }
-    for (; p < G; p += 64) st = merge(st, ArgSoft{m[p], s[p], a[p]});
     for (int off = 1; off < 64; off <<= 1) st = merge(st, shfl_xor_state(st, off));
     return st;
 }
@@ -89,6 +93,9 @@ __global__ __launch_bounds__(1024) void lmhead_combine_commit_kernel(
     const WsView w = ws_view(const_cast<void*>(ws), G, B);
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
+    // The masked flags are read now, with the partials, not after the merge
+    // (every wave reads them, unconditionally, so no branch waits on them).
+    const int mk = masked[min(lane, B - 1)];
     for (int col = wave; col < B; col += 16) {
         const ArgSoft r = reduce_column(w, G, col);
         if (lane == 0) {
@@ -101,8 +108,8 @@ __global__ __launch_bounds__(1024) void lmhead_combine_commit_kernel(
     }
     __syncthreads();
     if (wave == 0)
-        commit_wave(lane < B ? sconf[lane] : 0.f, lane < B ? sarg[lane] : 0, B, tau, masked,
-                    tokens, n_committed, gate_out, steps);
+        commit_wave_flag(lane < B && mk != 0, lane < B ? sconf[lane] : 0.f, lane < B ? sarg[lane] : 0, B,
+                         tau, masked, tokens, n_committed, gate_out, steps);
 }
 
 }  // namespace
