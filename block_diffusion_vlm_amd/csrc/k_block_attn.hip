@@ -165,7 +165,9 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
     const int qh = g * group + (row_ok ? r % group : 0);
     bf16x8 qf[8];
     load_q(qf, row_ok ? q + (size_t(qi) * Hq + qh) * kDh : nullptr, lane);
-    const uint64_t mbits = row_ok ? mask[qi] : 0;
+    // The row's intra-block mask; bits at or beyond Bq (keys past the block) are
+    // never visible.
+    const uint64_t mbits = row_ok ? mask[qi] & (Bq < 64 ? (1ull << Bq) - 1 : ~0ull) : 0;
     const ReadOffsets ro = read_offsets(lane);
 
     if constexpr (FP8) {
@@ -191,18 +193,35 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
 
         f32x16 sacc[2];
         scores(sacc, kcur, qf, ro);
+        // Visibility of the lane's 32 score registers, one bit each.  Register
+        // i (i / 16 = key block, i % 16 = e) holds the key at offset
+        // 8 (i / 4) + i % 4 from the lane's first key jl.  Keys below P (the
+        // prefix) form a prefix of the registers; a block key b = j - P is
+        // visible by bit b of the row's mask, so the row's mask shifted to jl
+        // has register i's bit at 8 (i / 4) + i % 4, and packing its low
+        // nibbles gives the block part.
+        const int jl = j0 + 4 * (lane >> 5);
+        const int bb = jl - P;                      // block index of key jl
+        uint64_t w = 0;
+        if (bb >= 0) {
+            if (bb < 64) w = mbits >> bb;
+        } else if (bb > -64) {
+            w = mbits << -bb;
+        }
+        w &= 0x0F0F0F0F0F0F0F0Full;
+        w = (w | (w >> 4)) & 0x00FF00FF00FF00FFull;
+        w = (w | (w >> 8)) & 0x0000FFFF0000FFFFull;
+        w = (w | (w >> 16)) & 0x00000000FFFFFFFFull;
+        const unsigned vis_bits = key_prefix(P - jl) | unsigned(w);
         float x[2][16];
         float mx = -INFINITY;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int j = j0 + 32 * kb2 + acc_row(e, lane);
-                const int jb = j - P;            // block key index (negative in the prefix)
-                const bool in_block = (jb >= 0) & (j < Nk);
-                const bool bit = ((mbits >> (jb & 63)) & 1ull) != 0;
-                const bool vis = (j < P) | (in_block & bit);
-                x[kb2][e] = vis ? sacc[kb2][e] : -INFINITY;
+                const unsigned sel = bit_select(vis_bits, 16 * kb2 + e);
+                x[kb2][e] = __uint_as_float((__float_as_uint(sacc[kb2][e]) & sel) |
+                                            (0xff800000u & ~sel));
                 mx = fmaxf(mx, x[kb2][e]);
             }
         mx = fmaxf(mx, other_half(mx)) * scale_log2;
@@ -214,7 +233,8 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
         const float alpha = __builtin_amdgcn_exp2f(m - mref);
         l = l * alpha + ls;
         m = mnew;
-        if (__ballot(alpha != 1.f)) {
+        // The first tile of a split finds oacc still zero: nothing to rescale.
+        if (t != t_beg && __ballot(alpha != 1.f)) {
 #pragma unroll
             for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
         }
