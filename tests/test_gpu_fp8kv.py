@@ -97,6 +97,7 @@ def _attn_case(Bq, P, Hq, Hkv, kind, seed):
 @pytest.mark.parametrize("Bq,P,Hq,Hkv,kind", [
     (16, 1280, 16, 2, "bidir"), (5, 100, 4, 2, "causal"), (32, 4608, 16, 2, "spec_fused"),
     (1, 0, 2, 1, "bidir"), (7, 63, 8, 8, "causal"), (64, 700, 2, 1, "bidir"),
+    (16, 65520, 2, 1, "bidir"),                     # P + Bq = 65536, the largest
 ])
 def test_block_attn_fp8kv_matches_oracle(Bq, P, Hq, Hkv, kind):
     print(f"fp8kv attention Bq={Bq} P={P} Hq={Hq} Hkv={Hkv} {kind}", flush=True)

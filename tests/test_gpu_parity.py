@@ -215,8 +215,11 @@ def _block_attn_case(Bq, P, Hq, Hkv, kind, seed, dt="bf16", dh=128, extra_cap=3)
     (32, 4608, 16, 2, "spec_fused"), (5, 70, 4, 1, "causal"), (1, 0, 2, 2, "bidir"),
     (64, 100, 8, 2, "bidir"), (3, 63, 6, 3, "causal"), (2, 1, 1, 1, "spec_fused"),
     (64, 0, 4, 4, "causal"),
+    # the largest key count the bf16 path takes: P + Bq = 65536 (1024 splits)
+    (16, 65520, 2, 1, "causal"),
 ])
 def test_block_attn_bf16_matches_oracle(Bq, P, Hq, Hkv, kind):
+    print(f"block attention Bq={Bq} P={P} Hq={Hq} Hkv={Hkv} {kind}", flush=True)
     got, ref = _block_attn_case(Bq, P, Hq, Hkv, kind, seed=Bq * 1000 + P)
     assert np.abs(got - ref).max() <= 2e-2
 
