@@ -104,3 +104,38 @@ def test_block_attention_random(case):
     assert np.abs(bf16_host(a.out) - oracle.block_attn(q, kc, vc, P, intra)).max() <= 2e-2
     ref8 = oracle.block_attn_fp8kv(q, k8, v8, ks, vs, P, intra)
     assert np.abs(bf16_host(a8.out) - ref8).max() <= 2e-2
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_block_attention_random_masks(case):
+    """Arbitrary intra-block masks: every row a random 64-bit word, of which
+    bit j < Bq says whether the row's query sees block key j (the higher bits
+    are ignored).  Bq up to 64, ragged prefixes, GQA; bf16 and FP8 caches."""
+    rng = np.random.default_rng(9500 + case)
+    Hkv = int(rng.choice([1, 2]))
+    Hq = Hkv * int(rng.choice([1, 4, 8]))
+    Bq = int(rng.integers(1, 65))
+    P = int(rng.integers(0, 2000))
+    cap = P + Bq + int(rng.integers(0, 10))
+    print(f"block attention, random masks: Bq={Bq} P={P} Hq={Hq} Hkv={Hkv}", flush=True)
+    rows = rng.integers(0, 2**63, size=Bq, dtype=np.int64).astype(np.uint64) * np.uint64(2) \
+        + rng.integers(0, 2, size=Bq).astype(np.uint64)
+    intra = ((rows[:, None] >> np.arange(Bq, dtype=np.uint64)[None]) & np.uint64(1)).astype(bool)
+    q = synth.bf16_bits(synth.normal(rng, (Bq, Hq, 128)))
+    kc = synth.bf16_bits(synth.normal(rng, (Hkv, cap, 128)))
+    vc = synth.bf16_bits(synth.normal(rng, (Hkv, cap, 128), trunc=4.0))
+    a = runner.BlockAttn(bd.BD_BF16, bd.BD_MASK_BIDIR, Bq, P, cap, Hq, Hkv, 128)
+    a.mask.copy_(runner.to_dev(rows))
+    a(runner.to_dev(q), runner.to_dev(kc), runner.to_dev(vc))
+    k8 = synth.normal_e4m3(rng, (Hkv * cap, 128)).reshape(Hkv, cap, 128)
+    v8 = synth.normal_e4m3(rng, (Hkv * cap, 128)).reshape(Hkv, cap, 128)
+    ks = (rng.uniform(0.5, 2.0, Hkv) / 112).astype(np.float32)
+    vs = (rng.uniform(0.5, 2.0, Hkv) / 112).astype(np.float32)
+    a8 = runner.BlockAttnFP8KV(bd.BD_MASK_BIDIR, Bq, P, cap, Hq, Hkv)
+    a8.mask.copy_(runner.to_dev(rows))
+    a8(runner.to_dev(q), runner.to_dev(k8), runner.to_dev(v8), runner.to_dev(ks),
+       runner.to_dev(vs))
+    torch.cuda.synchronize()
+    assert np.abs(bf16_host(a.out) - oracle.block_attn(q, kc, vc, P, intra)).max() <= 2e-2
+    ref8 = oracle.block_attn_fp8kv(q, k8, v8, ks, vs, P, intra)
+    assert np.abs(bf16_host(a8.out) - ref8).max() <= 2e-2
