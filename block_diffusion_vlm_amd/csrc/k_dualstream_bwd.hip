@@ -46,7 +46,9 @@ __device__ __forceinline__ float to_f32(float x) { return x; }
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const T* __restrict__ out,
                                                          const T* __restrict__ dout, int rows,
-                                                         int dh, float* __restrict__ D) {
+                                                         int dh, float* __restrict__ D,
+                                                         const float* __restrict__ lse,
+                                                         float* __restrict__ lse2) {
     const int r = blockIdx.x * 16 + (threadIdx.x >> 4);
     const int l = threadIdx.x & 15;
     float acc = 0.f;
@@ -56,7 +58,12 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const T* __restrict__ o
         for (int d = l; d < dh; d += 16) acc = fmaf(to_f32(o[d]), to_f32(g[d]), acc);
     }
     for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
-    if (l == 0 && r < rows) D[r] = acc;
+    if (l == 0 && r < rows) {
+        D[r] = acc;
+        // The row log-sum-exp in log2 units for the dK/dV kernel, which
+        // stages it straight into LDS (no multiply per score there).
+        if (lse2 != nullptr) lse2[r] = lse[r] * kLog2e;
+    }
 }
 
 // Stores a wave's transposed 32 x 128 result (accumulator layout, lane =
@@ -163,7 +170,7 @@ template <bool SEG>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ D, Geometry G, int H,
+    const float* __restrict__ lse2, const float* __restrict__ D, Geometry G, int H,
     float scale_log2, float scale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
     // [buffer][Q A-operand, Q transposed-read, dO A-operand, dO transposed-read]
     __shared__ __align__(16) uint16_t tiles[2][4][kTile];
@@ -213,7 +220,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         dma_tile<4, false>(tiles[b][2], gh + size_t(i0) * rs, rs, n);
         dma_tile<4, true>(tiles[b][3], gh + size_t(i0) * rs, rs, n);
         if (wave == 0) {
-            dma_floats64(lse_s[b], lse + h, H, i0, i0 + n - 1);
+            dma_floats64(lse_s[b], lse2 + h, H, i0, i0 + n - 1);
             dma_floats64(D_s[b], D + h, H, i0, i0 + n - 1);
         }
     };
@@ -285,8 +292,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
                         const int e = 4 * e4 + x;
-                        float p = __builtin_amdgcn_exp2f(
-                            fmaf(sacc[kb][e], scale_log2, -l4[x] * kLog2e));
+                        float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], scale_log2, -l4[x]));
                         if constexpr (MASKED)
                             p = __uint_as_float(__float_as_uint(p) &
                                                 bit_select(vis_bits, 16 * kb + e));
@@ -419,16 +425,17 @@ __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(
 
 template <typename T>
 hipError_t launch_rowdot(const T* out, const T* dout, int rows, int dh, float* D,
-                         hipStream_t st) {
+                         const float* lse, float* lse2, hipStream_t st) {
     hipLaunchKernelGGL(bwd_rowdot_kernel<T>, dim3((rows + 15) / 16), dim3(256), 0, st, out, dout,
-                       rows, dh, D);
+                       rows, dh, D, lse, lse2);
     return hipGetLastError();
 }
 
 }  // namespace
 
+// D, then (bf16 path) the row log-sum-exp in log2 units, [N][H] float32 each.
 size_t dualstream_bwd_ws_bytes(int N, int H) {
-    return ((size_t(N) * H * sizeof(float)) + 255) & ~size_t(255);
+    return 2 * (((size_t(N) * H * sizeof(float)) + 255) & ~size_t(255));
 }
 
 hipError_t launch_dualstream_bwd_bf16(const void* q, const void* k, const void* v,
@@ -438,11 +445,13 @@ hipError_t launch_dualstream_bwd_bf16(const void* q, const void* k, const void* 
                                       void* ws, hipStream_t st) {
     const Geometry G = make_geometry(n_vis, n_txt, block, seg, n_seg);
     float* D = static_cast<float*>(ws);
+    float* lse2 = D + dualstream_bwd_ws_bytes(G.N, H) / 2 / sizeof(float);
     const auto* qq = static_cast<const uint16_t*>(q);
     const auto* kk = static_cast<const uint16_t*>(k);
     const auto* vv = static_cast<const uint16_t*>(v);
     const auto* gg = static_cast<const uint16_t*>(dout);
-    hipError_t e = launch_rowdot(static_cast<const uint16_t*>(out), gg, G.N * H, kDh, D, st);
+    hipError_t e = launch_rowdot(static_cast<const uint16_t*>(out), gg, G.N * H, kDh, D, lse,
+                                 lse2, st);
     if (e != hipSuccess) return e;
     const int nt = (G.N + kRowsPerWg - 1) / kRowsPerWg;
     const dim3 grid(H, nt), blk(256);
@@ -450,12 +459,12 @@ hipError_t launch_dualstream_bwd_bf16(const void* q, const void* k, const void* 
     if (G.n_seg > 1) {
         hipLaunchKernelGGL(bwd_dq_kernel<true>, grid, blk, 0, st, qq, kk, vv, gg, lse, D, G, H, sl,
                            scale, static_cast<uint16_t*>(dq), nt);
-        hipLaunchKernelGGL(bwd_dkdv_kernel<true>, grid, blk, 0, st, qq, kk, vv, gg, lse, D, G, H,
+        hipLaunchKernelGGL(bwd_dkdv_kernel<true>, grid, blk, 0, st, qq, kk, vv, gg, lse2, D, G, H,
                            sl, scale, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
     } else {
         hipLaunchKernelGGL(bwd_dq_kernel<false>, grid, blk, 0, st, qq, kk, vv, gg, lse, D, G, H,
                            sl, scale, static_cast<uint16_t*>(dq), nt);
-        hipLaunchKernelGGL(bwd_dkdv_kernel<false>, grid, blk, 0, st, qq, kk, vv, gg, lse, D, G, H,
+        hipLaunchKernelGGL(bwd_dkdv_kernel<false>, grid, blk, 0, st, qq, kk, vv, gg, lse2, D, G, H,
                            sl, scale, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
     }
     return hipGetLastError();
@@ -468,7 +477,7 @@ hipError_t launch_dualstream_bwd_f32(const float* q, const float* k, const float
                                      float* dv, void* ws, hipStream_t st) {
     const Geometry G = make_geometry(n_vis, n_txt, block, seg, n_seg);
     float* D = static_cast<float*>(ws);
-    hipError_t e = launch_rowdot(out, dout, G.N * H, dh, D, st);
+    hipError_t e = launch_rowdot(out, dout, G.N * H, dh, D, nullptr, nullptr, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_dq_f32_kernel, dim3(G.N * H), dim3(64), 0, st, q, k, v, dout, lse, D,
                        G, H, dh, scale, dq);

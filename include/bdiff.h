@@ -437,7 +437,8 @@ bd_status bd_dualstream_attn_fwd(bd_dtype dt, const void* q, const void* k, cons
  *   lse          [N][H] float32 from bd_dualstream_attn_fwd
  *   dq, dk, dv   [N][H][dh] dtype dt out (float32 accumulation inside)
  *   ws           workspace of at least bd_dualstream_attn_bwd_ws_bytes(n_vis,
- *                n_txt, H) bytes (holds D; no initial contents required)
+ *                n_txt, H) bytes (holds D and lse in log2 units; no initial
+ *                contents required)
  * Limits: those of bd_dualstream_attn; seg_starts as in bd_dualstream_attn_fwd.
  * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_ALIGN, BD_E_WORKSPACE,
  *   BD_E_LAUNCH.
