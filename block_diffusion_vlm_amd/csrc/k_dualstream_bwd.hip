@@ -140,20 +140,37 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         scores_ahead<kAheadDq>(sacc, kK, qf, ro);    // S^T[key][row]
         scores_ahead<kAheadDq>(dpacc, vK, gf, ro);   // dP^T[key][row] = V[key] . dO[row]
         bf16x8 dsf[2][2];
-        // Visible keys of this lane's registers (bit e for register e): keys
-        // up to lim or in [lo, hi), and inside the tile.
-        const int jl = j0 + 4 * (lane >> 5);
-        const unsigned vis_bits =
-            key_prefix(n - 4 * (lane >> 5)) &
-            (key_prefix(rv.lim - jl + 1) | (key_prefix(rv.hi - jl) & ~key_prefix(rv.lo - jl)));
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], scale_log2, -lse2));
-                const float p = __uint_as_float(__float_as_uint(pe) & bit_select(vis_bits, 16 * kb + e));
-                dsf[kb][e >> 3][e & 7] = static_cast<__bf16>(p * (dpacc[kb][e] - Dr));
+        auto grad = [&](auto masked_tag) {
+            constexpr bool MASKED = decltype(masked_tag)::value;
+            // Visible keys of this lane's registers (bit e for register e):
+            // keys up to lim or in [lo, hi), and inside the tile.
+            unsigned vis_bits = 0xffffffffu;
+            if constexpr (MASKED) {
+                const int jl = j0 + 4 * (lane >> 5);
+                vis_bits = key_prefix(n - 4 * (lane >> 5)) &
+                           (key_prefix(rv.lim - jl + 1) |
+                            (key_prefix(rv.hi - jl) & ~key_prefix(rv.lo - jl)));
             }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], scale_log2, -lse2));
+                    if constexpr (MASKED)
+                        p = __uint_as_float(__float_as_uint(p) & bit_select(vis_bits, 16 * kb + e));
+                    dsf[kb][e >> 3][e & 7] = static_cast<__bf16>(p * (dpacc[kb][e] - Dr));
+                }
+        };
+        // A tile that every row of the wave sees whole skips the selection
+        // (rows past the end take no part: their results are dropped).  The
+        // segmented instance always selects: a second copy of the step would
+        // not fit its registers.
+        const bool whole = n == kBN && (!row_ok || rv.lim >= j0 + kBN - 1 ||
+                                        (rv.lo <= j0 && rv.hi >= j0 + kBN));
+        if (!SEG && __all(whole))
+            grad(std::false_type{});
+        else
+            grad(std::true_type{});
         accumulate_pv_ahead<kAheadDq>(dqacc, kV, dsf, ro);   // dQ^T += K^T dS^T
         tile_barrier();                              // the tile is read before it is replaced
     }
