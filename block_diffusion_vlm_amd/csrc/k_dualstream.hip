@@ -72,12 +72,15 @@ __global__ __launch_bounds__(WAVES * 64, 2) void dualstream_bf16_kernel(
     const int na = (a_end + kBN - 1) / kBN;
     const int nb = b_end > b_beg ? (b_end - b_beg + kBN - 1) / kBN : 0;
     const int ntile = na + nb;
-    // A complete tile of range A is visible for every (query, key) pair when
-    // its last key is at most full_a: below the causal diagonal for clean
-    // rows, inside visual + clean text up to the first row for noisy rows.
+    // A complete tile of range A is visible for every (query, key) pair of a
+    // wave when its last key is at most full_a: below the causal diagonal
+    // for clean rows, inside visual + clean text up to the first row for
+    // noisy rows, taken from the wave's first row (the choice is per wave:
+    // nothing inside a tile step synchronises the waves).
     // A complete tile of range B is when all rows lie in one noisy block
     // (range B is then exactly that block's keys).
-    const int full_a = i1 <= G.ctx ? i0 : (i0 >= G.ctx ? G.n_vis + (i0 - G.ctx) : -1);
+    const int iw0 = i0 + 32 * (threadIdx.x >> 6);    // the wave's first row
+    const int full_a = i1 <= G.ctx ? iw0 : (i0 >= G.ctx ? G.n_vis + (iw0 - G.ctx) : -1);
     bool full_b = false;
     if (i0 >= G.ctx) {
         int lo0, hi0, lo1, hi1;
