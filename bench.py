@@ -36,7 +36,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=400,
+                    help="untimed steps first (~43 ms of work: the clocks settle)")
     ap.add_argument("--graph-steps", type=int, default=8,
                     help="decode steps captured per HIP graph (replays = steps / graph-steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
