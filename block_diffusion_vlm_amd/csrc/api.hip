@@ -17,6 +17,9 @@ inline float default_scale(float scale, int dh) {
     return scale != 0.f ? scale : 1.0f / sqrtf(static_cast<float>(dh));
 }
 
+// Vocabulary sizes up to 2^30 (tile counts stay far inside int32).
+inline bool vocab_ok(int32_t V) { return V >= 1 && V <= (1 << 30); }
+
 bool dh_ok(bd_dtype dt, int dh) {
     if (dt == BD_BF16) return dh == 128;
     return dh >= 4 && dh <= 128 && dh % 4 == 0;
@@ -165,29 +168,48 @@ bd_status bd_kv_quant_fp8(const void* x, int32_t n, int32_t Hkv, int32_t dh, con
 }
 
 size_t bd_lmhead_conf_ws_bytes(int32_t B, int32_t d, int32_t V) {
-    if (B < 1 || B > 64 || d < 1 || V < 1) return 0;
+    if (B < 1 || B > 64 || d < 1 || !vocab_ok(V)) return 0;
     return bd::lmhead_ws_bytes(B, d, V);
 }
+
+}  // extern "C"
+
+namespace bd {
+
+bd_status lmhead_args_status(bd_dtype dt, const void* h, const void* W, int32_t B, int32_t d,
+                             int32_t V, const Finish& f) {
+    if (!h || !W || !f.conf || !f.argmax) return BD_E_NULL;
+    if (f.commit && (!f.masked || !f.tokens || !f.n_committed)) return BD_E_NULL;
+    if (dt != BD_F32 && dt != BD_BF16) return BD_E_DTYPE;
+    if (B < 1 || B > 64 || d < 1 || !vocab_ok(V)) return BD_E_SHAPE;
+    if (dt == BD_BF16 && (d % 128 != 0 || d > 16384)) return BD_E_SHAPE;
+    if (f.commit && !(f.tau == f.tau)) return BD_E_SHAPE;
+    if (!aligned16(h) || !aligned16(W)) return BD_E_ALIGN;
+    return BD_OK;
+}
+
+hipError_t launch_lmhead(bd_dtype dt, const void* h, const void* W, int B, int d, int V,
+                         const Finish& f, void* ws, hipStream_t st) {
+    if (dt == BD_F32)
+        return launch_lmhead_f32(static_cast<const float*>(h), static_cast<const float*>(W), B, d,
+                                 V, f, ws, st);
+    return launch_lmhead_bf16(h, W, B, d, V, f, ws, st);
+}
+
+}  // namespace bd
+
+extern "C" {
 
 namespace {
 
 bd_status lmhead_common(bd_dtype dt, const void* h, const void* W, int32_t B, int32_t d,
                         int32_t V, const bd::Finish& f, void* ws, size_t ws_bytes,
                         hipStream_t stream) {
-    if (!h || !W || !f.conf || !f.argmax) return BD_E_NULL;
-    if (f.commit && (!f.masked || !f.tokens || !f.n_committed)) return BD_E_NULL;
-    if (dt != BD_F32 && dt != BD_BF16) return BD_E_DTYPE;
-    if (B < 1 || B > 64 || d < 1 || V < 1) return BD_E_SHAPE;
-    if (dt == BD_BF16 && (d % 128 != 0 || d > 16384)) return BD_E_SHAPE;
-    if (f.commit && !(f.tau == f.tau)) return BD_E_SHAPE;
-    if (!aligned16(h) || !aligned16(W)) return BD_E_ALIGN;
+    const bd_status s = bd::lmhead_args_status(dt, h, W, B, d, V, f);
+    if (s != BD_OK) return s;
     if (!ws || ws_bytes < bd::lmhead_ws_bytes(B, d, V)) return BD_E_WORKSPACE;
     if (!aligned16(ws)) return BD_E_ALIGN;
-    if (dt == BD_F32)
-        return launch_status(bd::launch_lmhead_f32(static_cast<const float*>(h),
-                                                   static_cast<const float*>(W), B, d, V, f, ws,
-                                                   stream));
-    return launch_status(bd::launch_lmhead_bf16(h, W, B, d, V, f, ws, stream));
+    return launch_status(bd::launch_lmhead(dt, h, W, B, d, V, f, ws, stream));
 }
 
 }  // namespace
@@ -208,7 +230,7 @@ bd_status bd_lmhead_conf_commit(bd_dtype dt, const void* h, const void* W, int32
 }
 
 size_t bd_lmhead_conf_fp8_ws_bytes(int32_t B, int32_t d, int32_t V) {
-    if (B < 1 || B > 64 || d < 128 || d > 16384 || d % 128 != 0 || V < 1) return 0;
+    if (B < 1 || B > 64 || d < 128 || d > 16384 || d % 128 != 0 || !vocab_ok(V)) return 0;
     return bd::lmhead_fp8_ws_bytes(B, d, V);
 }
 
@@ -219,7 +241,7 @@ bd_status lmhead_fp8_common(const void* h, const uint8_t* Wq, const float* w_sca
                             size_t ws_bytes, hipStream_t stream) {
     if (!h || !Wq || !w_scale || !f.conf || !f.argmax) return BD_E_NULL;
     if (f.commit && (!f.masked || !f.tokens || !f.n_committed)) return BD_E_NULL;
-    if (B < 1 || B > 64 || V < 1 || d < 128 || d > 16384 || d % 128 != 0) return BD_E_SHAPE;
+    if (B < 1 || B > 64 || !vocab_ok(V) || d < 128 || d > 16384 || d % 128 != 0) return BD_E_SHAPE;
     if (f.commit && !(f.tau == f.tau)) return BD_E_SHAPE;
     if (!aligned16(h) || !aligned16(Wq) || !aligned16(w_scale)) return BD_E_ALIGN;
     if (!ws || ws_bytes < bd::lmhead_fp8_ws_bytes(B, d, V)) return BD_E_WORKSPACE;
@@ -275,7 +297,7 @@ LoopWs loop_ws(int32_t P, int32_t B, int32_t Hq, int32_t Hkv, int32_t dh, int32_
 
 size_t bd_block_loop_ws_bytes(int32_t P, int32_t B, int32_t Hq, int32_t Hkv, int32_t dh,
                               int32_t d, int32_t V, int32_t w_fp8) {
-    if (P < 0 || B < 1 || B > 64 || Hq < 1 || Hkv < 1 || dh < 1 || d < 1 || V < 1) return 0;
+    if (P < 0 || B < 1 || B > 64 || Hq < 1 || Hkv < 1 || dh < 1 || d < 1 || !vocab_ok(V)) return 0;
     if (w_fp8 && (d < 128 || d > 16384 || d % 128 != 0)) return 0;
     return loop_ws(P, B, Hq, Hkv, dh, d, V, w_fp8 != 0).total;
 }
@@ -301,7 +323,7 @@ bd_status bd_block_loop(bd_dtype dt, const void* q_steps, const void* k_cache,
     if (dt == BD_BF16 && (int64_t)P + B > 65536) return BD_E_SHAPE;
     if (!(scale >= 0.f) || isinf(scale)) return BD_E_SHAPE;
     // LM-head limits (bd_lmhead_conf / bd_lmhead_conf_fp8)
-    if (d < 1 || V < 1) return BD_E_SHAPE;
+    if (d < 1 || !vocab_ok(V)) return BD_E_SHAPE;
     if ((dt == BD_BF16 || fp8) && (d % 128 != 0 || d > 16384)) return BD_E_SHAPE;
     if (!(tau == tau)) return BD_E_SHAPE;
     if (max_steps < 1 || max_steps > 1024) return BD_E_SHAPE;

@@ -99,11 +99,18 @@ struct Finish {
     int32_t* steps = nullptr;
 };
 int lmhead_grid(int B, int d, int V);           // workgroups used for a shape
-size_t lmhead_ws_bytes(int B, int d, int V);
+size_t lmhead_ws_bytes(int B, int d, int V);              // either dtype
+size_t lmhead_ws_bytes_dt(bd_dtype dt, int B, int d, int V);
 hipError_t launch_lmhead_bf16(const void* h, const void* W, int B, int d, int V, const Finish& f,
                               void* ws, hipStream_t st);
 hipError_t launch_lmhead_f32(const float* h, const float* W, int B, int d, int V,
                              const Finish& f, void* ws, hipStream_t st);
+// Host checks of an LM-head call's arguments (everything but the workspace),
+// and the launch of the dt path on a validated workspace.
+bd_status lmhead_args_status(bd_dtype dt, const void* h, const void* W, int32_t B, int32_t d,
+                             int32_t V, const Finish& f);
+hipError_t launch_lmhead(bd_dtype dt, const void* h, const void* W, int B, int d, int V,
+                         const Finish& f, void* ws, hipStream_t st);
 
 // FP8 (E4M3, W8A8) LM head and the per-row quantizer it applies to h.
 int lmhead_fp8_grid(int B, int d, int V);

@@ -413,13 +413,17 @@ int lmhead_grid(int B, int d, int V) {
     return persistent_grid((V + 15) / 16);
 }
 
-size_t lmhead_ws_bytes(int B, int d, int V) {
+size_t lmhead_ws_bytes_dt(bd_dtype dt, int B, int d, int V) {
     // bf16: one partial per workgroup and position; f32: one per 256-row
     // vocabulary slice and position.
-    const int g_bf16 = lmhead_grid(B, d, V);
-    const int g_f32 = (V + kF32Rows - 1) / kF32Rows;
-    const int G = g_bf16 > g_f32 ? g_bf16 : g_f32;
+    const int G = dt == BD_F32 ? (V + kF32Rows - 1) / kF32Rows : lmhead_grid(B, d, V);
     return ws_size(G, B);
+}
+
+size_t lmhead_ws_bytes(int B, int d, int V) {
+    const size_t a = lmhead_ws_bytes_dt(BD_BF16, B, d, V);
+    const size_t b = lmhead_ws_bytes_dt(BD_F32, B, d, V);
+    return a > b ? a : b;
 }
 
 hipError_t launch_lmhead_bf16(const void* h, const void* W, int B, int d, int V, const Finish& f,

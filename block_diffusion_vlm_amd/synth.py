@@ -159,10 +159,61 @@ def _commit_band_conf(rng, n, p_commit=0.4, hi=(0.92, 0.999), lo=(0.02, 0.88)):
     return c, z
 
 
+def _band_redraw(z, hi=(0.92, 0.999), lo=(0.02, 0.88)):
+    """Re-draw of target probabilities that keeps each row in its band
+    (``z`` true: above the threshold)."""
+    z = np.asarray(z, dtype=bool)
+
+    def draw(rng, rows):
+        n = len(rows)
+        return np.where(z[rows], rng.uniform(hi[0], hi[1], n), rng.uniform(lo[0], lo[1], n))
+    return draw
+
+
+def _uniform_redraw(lo, hi):
+    return lambda rng, rows: rng.uniform(lo, hi, len(rows))
+
+
 def _different_token(rng, tok, V):
     """A uniform token id different from ``tok``."""
     x = int(rng.integers(0, V - 1))
     return x + (x >= tok)
+
+
+def _redraw_stream(rng) -> np.random.Generator:
+    """A fresh PCG64 stream spawned from ``rng``'s seed sequence: re-draws
+    take their numbers from it, so the main stream (and every tensor drawn
+    after the hidden rows) is the same whether or not a row was re-drawn."""
+    return np.random.Generator(np.random.PCG64(rng.bit_generator.seed_seq.spawn(1)[0]))
+
+
+def planted_bits(rng, W, targets, target_conf, sigma_w, row=None, guard=None, w_scale=None,
+                 redraw_conf=None):
+    """bf16 bits of hidden rows planted as in ``plant_hidden``.
+
+    ``guard``, when given, is a callable ``guard(h_bits, W, w_scale) -> bool
+    per row`` (the tests build it from the oracle's top-2-gap and
+    distance-from-threshold checks; this module computes no logits).  Every
+    row it rejects is planted again, with fresh noise and a fresh target
+    probability ``redraw_conf(rng, rows)`` taken from a spawned stream, until
+    it passes (at most 64 rounds).  Returns (bits, target probabilities)."""
+    targets = np.asarray(targets)
+    conf = np.array(target_conf, dtype=np.float64)
+    h = bf16_bits(plant_hidden(rng, W, targets, conf, sigma_w, row=row))
+    if guard is None:
+        return h, conf
+    ok = np.asarray(guard(h, W, w_scale), dtype=bool)
+    rr = None
+    for _ in range(64):
+        bad = np.nonzero(~ok)[0]
+        if bad.size == 0:
+            return h, conf
+        rr = _redraw_stream(rng) if rr is None else rr
+        if redraw_conf is not None:
+            conf[bad] = redraw_conf(rr, bad)
+        h[bad] = bf16_bits(plant_hidden(rr, W, targets[bad], conf[bad], sigma_w, row=row))
+        ok[bad] = np.asarray(guard(h[bad], W, w_scale), dtype=bool)
+    raise RuntimeError("planted rows still fail the guard after 64 re-draws")
 
 
 # ---------------------------------------------------------------------------
@@ -201,20 +252,22 @@ def tiny(seed: int | None = None) -> dict:
 
 
 def qwen_decode(seed: int | None = None, B=16, n_vis=1024, n_prompt=256, Hq=16, Hkv=2,
-                dh=128, d=2048, V=151936, p_commit=0.4, sigma_w=0.02) -> dict:
+                dh=128, d=2048, V=151936, p_commit=0.4, sigma_w=0.02, guard=None) -> dict:
     """One MDM block-decode step shaped like Qwen2.5-VL-3B, bf16.  Prefix KV of
     n_vis visual + n_prompt prompt tokens, then the block's B rows; bidirectional
     intra-block mask.  q, K ~ N(0,1); V ~ N(0,1) truncated to |v| <= 4.  W ~
     N(0, sigma_w^2).  Hidden rows planted so that about p_commit of them have top
     probability in [0.92, 0.999] and the rest in [0.02, 0.88].  Position 0 holds
-    the block's AR seed token (already unmasked); 1..B-1 are masked."""
+    the block's AR seed token (already unmasked); 1..B-1 are masked.
+    ``guard`` (see ``planted_bits``) re-draws rows that fail it, keeping each
+    row's target token and its side of the threshold."""
     rng = config_rng(2, seed)
     P = n_vis + n_prompt
     cap = P + B
     W = normal_bf16(rng, (V, d), std=sigma_w)
     t = rng.integers(0, V, B)
     c, z = _commit_band_conf(rng, B, p_commit)
-    h = bf16_bits(plant_hidden(rng, W, t, c, sigma_w))
+    h, c = planted_bits(rng, W, t, c, sigma_w, guard=guard, redraw_conf=_band_redraw(z))
     masked = np.ones(B, np.uint8)
     masked[0] = 0
     tokens = np.zeros(B, np.int32)
@@ -259,14 +312,15 @@ def qwen_decode_fp8kv(seed: int | None = None, B=16, n_vis=1024, n_prompt=256, H
 
 def qwen_decode_fp8(seed: int | None = None, B=16, n_vis=1024, n_prompt=256, Hq=16, Hkv=2,
                     dh=128, d=2048, V=151936, p_commit=0.4, sigma_w=0.02,
-                    scale_spread=0.1) -> dict:
+                    scale_spread=0.1, guard=None) -> dict:
     """The decode step of ``qwen_decode`` with an FP8 (E4M3, W8A8) LM head.
     W is stored as E4M3 codes of 112 x N(0,1) (truncated at 4 std) with one
     float32 scale per vocabulary row, w_scale[v] = sigma_w / 112 x U(1 -
     spread, 1 + spread), so that the stored weights stand for N(0, sigma_w^2)
     entries with a per-channel spread.  Hidden rows (bf16) are planted
     against the stored (decoded and scaled) weight rows as in qwen_decode;
-    the attention inputs and the block state are drawn the same way."""
+    the attention inputs and the block state are drawn the same way.
+    ``guard`` as in qwen_decode (it receives the codes and w_scale)."""
     rng = config_rng(6, seed)
     P = n_vis + n_prompt
     cap = P + B
@@ -275,8 +329,9 @@ def qwen_decode_fp8(seed: int | None = None, B=16, n_vis=1024, n_prompt=256, Hq=
                * rng.uniform(1 - scale_spread, 1 + scale_spread, V).astype(np.float32))
     t = rng.integers(0, V, B)
     c, z = _commit_band_conf(rng, B, p_commit)
-    h = bf16_bits(plant_hidden(rng, Wq, t, c, sigma_w,
-                               row=lambda v: e4m3_row_values(Wq[v]) * float(w_scale[v])))
+    h, c = planted_bits(rng, Wq, t, c, sigma_w,
+                        row=lambda v: e4m3_row_values(Wq[v]) * float(w_scale[v]),
+                        guard=guard, w_scale=w_scale, redraw_conf=_band_redraw(z))
     masked = np.ones(B, np.uint8)
     masked[0] = 0
     tokens = np.zeros(B, np.int32)
@@ -294,7 +349,8 @@ def qwen_decode_fp8(seed: int | None = None, B=16, n_vis=1024, n_prompt=256, Hq=
 
 
 def qwen_block_loop(seed: int | None = None, B=16, S=16, T=8, n_vis=1024, n_prompt=256,
-                    Hq=16, Hkv=2, dh=128, d=2048, V=151936, sigma_w=0.02, fp8=False) -> dict:
+                    Hq=16, Hkv=2, dh=128, d=2048, V=151936, sigma_w=0.02, fp8=False,
+                    guard=None) -> dict:
     """All steps of one block of the Qwen-shaped decode, bf16 (or with the
     FP8 LM head): a denoising trajectory.  Position 0 is the AR seed; each
     masked position i gets a commit step c_i in [0, T), the masked positions
@@ -305,7 +361,8 @@ def qwen_block_loop(seed: int | None = None, B=16, S=16, T=8, n_vis=1024, n_prom
     planted on its final token with top probability in [0.92, 0.999]; before
     it, on a fresh uniform token with top probability in [0.02, 0.88].
     Block queries are drawn afresh for every step; the KV cache is fixed.
-    S >= T steps are provided (the loop must stop at T on its own)."""
+    S >= T steps are provided (the loop must stop at T on its own).
+    ``guard`` as in qwen_decode, applied to every step's rows."""
     rng = config_rng(7 if fp8 else 8, seed)
     P = n_vis + n_prompt
     cap = P + B
@@ -328,7 +385,8 @@ def qwen_block_loop(seed: int | None = None, B=16, S=16, T=8, n_vis=1024, n_prom
         late = c <= s
         tgt = np.where(late, final, rng.integers(0, V, B))
         conf = np.where(late, rng.uniform(0.92, 0.999, B), rng.uniform(0.02, 0.88, B))
-        h[s] = bf16_bits(plant_hidden(rng, W, tgt, conf, sigma_w, row=row))
+        h[s], _ = planted_bits(rng, W, tgt, conf, sigma_w, row=row, guard=guard,
+                               w_scale=w_scale, redraw_conf=_band_redraw(late))
     masked = np.ones(B, np.uint8)
     masked[0] = 0
     tokens = np.zeros(B, np.int32)
@@ -348,13 +406,14 @@ def qwen_block_loop(seed: int | None = None, B=16, S=16, T=8, n_vis=1024, n_prom
 
 
 def linear_spec(seed: int | None = None, B=32, n_vis=1024, n_prompt=256, Hq=16, Hkv=2,
-                dh=128, d=2048, V=151936, p_geo=0.15, sigma_w=0.02) -> dict:
+                dh=128, d=2048, V=151936, p_geo=0.15, sigma_w=0.02, guard=None) -> dict:
     """Linear self-speculative step, bf16: a bidirectional draft pass and a
     causal verify pass of the same B queries over the prefix.  Draft targets
     d_i ~ U{V}; verify targets equal d_i for i < L_true, differ at L_true, and
     are uniform after it; L_true = min(Geometric(p_geo), B) (support >= 1, the
     first token being the AR seed).  Each pass has its own q and its own block
-    K/V rows (rows P..P+B-1 of its cache)."""
+    K/V rows (rows P..P+B-1 of its cache).  ``guard`` as in qwen_decode
+    (target probabilities re-drawn in U(0.3, 0.999))."""
     rng = config_rng(3, seed)
     P = n_vis + n_prompt
     cap = P + B
@@ -367,8 +426,10 @@ def linear_spec(seed: int | None = None, B=32, n_vis=1024, n_prompt=256, Hq=16, 
         ver_t[L_true] = _different_token(rng, int(draft_t[L_true]), V)
     c_d = rng.uniform(0.3, 0.999, B)
     c_v = rng.uniform(0.3, 0.999, B)
-    h_d = bf16_bits(plant_hidden(rng, W, draft_t, c_d, sigma_w))
-    h_v = bf16_bits(plant_hidden(rng, W, ver_t, c_v, sigma_w))
+    h_d, _ = planted_bits(rng, W, draft_t, c_d, sigma_w, guard=guard,
+                          redraw_conf=_uniform_redraw(0.3, 0.999))
+    h_v, _ = planted_bits(rng, W, ver_t, c_v, sigma_w, guard=guard,
+                          redraw_conf=_uniform_redraw(0.3, 0.999))
     kp = normal_bf16(rng, (Hkv * P, dh)).reshape(Hkv, P, dh)
     vp = normal_bf16(rng, (Hkv * P, dh), trunc=4.0).reshape(Hkv, P, dh)
 
@@ -393,7 +454,7 @@ def linear_spec(seed: int | None = None, B=32, n_vis=1024, n_prompt=256, Hq=16, 
 
 def fused_spec(seed: int | None = None, B=16, n_vis=4096, n_prompt=512, Hq=16, Hkv=2,
                dh=128, d=2048, V=151936, p_geo=0.15, sigma_w=0.02, n_cert=64,
-               k_cert=4, p_agree=0.83) -> dict:
+               k_cert=4, p_agree=0.83, guard=None) -> dict:
     """Fused (quadratic) speculative step, bf16: 2B query rows under the
     SPEC_FUSED mask over a 4096-visual + 512-text prefix, one LM-head pass over
     the 2B rows.  The draft tokens fed to the verify half are uniform; verify
@@ -402,7 +463,8 @@ def fused_spec(seed: int | None = None, B=16, n_vis=4096, n_prompt=512, Hq=16, H
     Certificate inputs: n_cert anchor confidences ~ U(0,1) (float32), anchor
     tokens ~ U{V}, text-only tokens equal to the anchor with probability
     p_agree (83.4 % agreement in the LOWN article), else a different uniform
-    token; k_cert is the per-step unmask quota k."""
+    token; k_cert is the per-step unmask quota k.  ``guard`` as in
+    linear_spec."""
     rng = config_rng(4, seed)
     P = n_vis + n_prompt
     bq = 2 * B
@@ -417,7 +479,8 @@ def fused_spec(seed: int | None = None, B=16, n_vis=4096, n_prompt=512, Hq=16, H
     next_t = rng.integers(0, V, B)
     tgt = np.concatenate([ver_t, next_t])
     c = rng.uniform(0.3, 0.999, bq)
-    h = bf16_bits(plant_hidden(rng, W, tgt, c, sigma_w))
+    h, _ = planted_bits(rng, W, tgt, c, sigma_w, guard=guard,
+                        redraw_conf=_uniform_redraw(0.3, 0.999))
     anchor_conf = rng.random(n_cert, dtype=np.float32)
     anchor_tok = rng.integers(0, V, n_cert)
     agree = rng.random(n_cert) < p_agree

@@ -142,7 +142,7 @@ bd_status bd_block_attn_paged(const void* q, const void* k_pool, const void* v_p
  *           (per-workgroup partial maxima, sums and indices; no initial
  *           contents required).  Two kernels run: the streaming contraction
  *           and a small merge of the partials.
- * Limits: 1 <= B <= 64, V >= 1, d >= 1;  BD_BF16 needs d % 128 == 0 and
+ * Limits: 1 <= B <= 64, 1 <= V <= 2^30, d >= 1;  BD_BF16 needs d % 128 == 0 and
  *   d <= 16384.  The result is deterministic (fixed reduction order).
  * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_ALIGN, BD_E_WORKSPACE,
  *   BD_E_LAUNCH.
@@ -190,7 +190,7 @@ bd_status bd_lmhead_conf_commit(bd_dtype dt, const void* h, const void* W,
  *   conf     [B] float32 out;  argmax [B] int32 out
  *   ws       workspace of at least bd_lmhead_conf_fp8_ws_bytes(B, d, V) bytes
  *            (no initial contents required)
- * Limits: 1 <= B <= 64, V >= 1, d % 128 == 0, 128 <= d <= 16384.  h, Wq,
+ * Limits: 1 <= B <= 64, 1 <= V <= 2^30, d % 128 == 0, 128 <= d <= 16384.  h, Wq,
  *   w_scale and ws must be 16-byte aligned.  Deterministic (fixed reduction
  *   order).  bd_lmhead_conf_fp8_ws_bytes returns 0 for shapes out of range.
  * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_ALIGN, BD_E_WORKSPACE, BD_E_LAUNCH.
@@ -339,7 +339,7 @@ bd_status bd_cert_scan(const float* anchor_conf, const int32_t* anchor_tok,
  *   q            [Bq][Hq][dh] bfloat16;  out the same
  *   k_cache, v_cache  [Hkv][cap][dh] uint8 E4M3 codes (NaN codes not allowed)
  *   k_scale, v_scale  [Hkv] float32 (device)
- *   ws           at least bd_block_attn_ws_bytes(P, Bq, Hq, dh) bytes
+ *   ws           at least bd_block_attn_ws_bytes(P, Bq, Hq, Hkv, dh) bytes
  * Limits: dh == 128, Bq <= 64, P + Bq <= min(cap, 65536), Hq % Hkv == 0.
  * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_ALIGN (16 bytes; scales 4),
  *   BD_E_WORKSPACE, BD_E_LAUNCH.

@@ -28,6 +28,22 @@ def lmhead_margins(h, W, tau=None, w_scale=None):
     return gap, np.abs(conf - tau)
 
 
+def rows_guarded(h, W, tau=None, w_scale=None) -> np.ndarray:
+    """Per row: True iff its top-2 gap exceeds GAP_MIN and (with tau) its
+    confidence is at least TAU_DIST_MIN away from tau."""
+    gap, dist = lmhead_margins(h, W, tau, w_scale)
+    ok = gap > GAP_MIN
+    if dist is not None:
+        ok &= dist >= TAU_DIST_MIN
+    return ok
+
+
+def row_guard(tau=None):
+    """The guard the input generators accept (``guard(h, W, w_scale)`` -> bool
+    per row): rows_guarded with the given threshold."""
+    return lambda h, W, w_scale=None: rows_guarded(h, W, tau, w_scale)
+
+
 def lmhead_guarded(h, W, tau=None, w_scale=None) -> bool:
     gap, dist = lmhead_margins(h, W, tau, w_scale)
     ok = bool((gap > GAP_MIN).all())

@@ -182,6 +182,8 @@ def test_lmhead_validation():
     assert _lm(d=2000) == bd.BD_E_SHAPE          # bf16 needs d % 128 == 0
     assert _lm(d=16512) == bd.BD_E_SHAPE
     assert _lm(h=MISALIGNED) == bd.BD_E_ALIGN
+    assert _lm(V=2 ** 30 + 1) == bd.BD_E_SHAPE    # vocabulary sizes up to 2^30
+    assert bd.bd_lmhead_conf_ws_bytes(16, 2048, 2 ** 30 + 1) == 0
     assert _lm(ws=None) == bd.BD_E_WORKSPACE
     assert _lm(ws_bytes=bd.bd_lmhead_conf_ws_bytes(16, 2048, 151936) - 1) == bd.BD_E_WORKSPACE
 
@@ -383,3 +385,4 @@ def test_python_binding_raises_on_error():
     with pytest.raises(bd.BdError) as e:
         bd.bd_commit(FAKE, FAKE, 99, 0.9, FAKE, FAKE, FAKE, stream=0)
     assert e.value.status == bd.BD_E_SHAPE
+

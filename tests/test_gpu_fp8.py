@@ -15,7 +15,7 @@ import torch
 import oracle
 from block_diffusion_vlm_amd import bdiff as bd
 from block_diffusion_vlm_amd import runner, synth
-from oracle.guards import lmhead_margins
+from oracle.guards import lmhead_margins, row_guard
 
 pytestmark = pytest.mark.gpu
 
@@ -101,16 +101,14 @@ def test_quant_rows_empty_is_a_no_op():
 # ---------------------------------------------------------------------------
 
 def _case(B, d, V, seed, tau=None):
-    """The first of a fixed sequence of seeds whose input keeps every decision
-    off the floating-point boundary (top-2 gap > 1e-2; with tau, confidences
-    at least 1e-3 from it)."""
-    for k in range(20):
-        r = synth.qwen_decode_fp8(seed=seed + 1000 * k, B=B, d=d, V=V, n_vis=4, n_prompt=4,
-                                  Hq=2, Hkv=1)
-        gap, dist = lmhead_margins(r["h"], r["W"], tau, w_scale=r["w_scale"])
-        if gap.min() > 1e-2 and (dist is None or dist.min() >= 1e-3):
-            return r
-    raise AssertionError("no guarded input among 20 seeds")
+    """An input whose every decision is off the floating-point boundary (top-2
+    gap > 1e-2; with tau, confidences at least 1e-3 from it): rows that fail
+    are re-drawn by the generator."""
+    r = synth.qwen_decode_fp8(seed=seed, B=B, d=d, V=V, n_vis=4, n_prompt=4, Hq=2, Hkv=1,
+                              guard=row_guard(tau))
+    gap, dist = lmhead_margins(r["h"], r["W"], tau, w_scale=r["w_scale"])
+    assert gap.min() > 1e-2 and (dist is None or dist.min() >= 1e-3)
+    return r
 
 
 SHAPES = [
@@ -170,7 +168,9 @@ def test_lmhead_fp8_conf_commit_equals_separate_calls(B, d, V):
 
 
 def test_decode_step_fp8_full_size():
-    r = synth.qwen_decode_fp8()
+    r = synth.qwen_decode_fp8(guard=row_guard(TAU32))
+    gap, dist = lmhead_margins(r["h"], r["W"], TAU32, w_scale=r["w_scale"])
+    assert gap.min() > 1e-2 and dist.min() >= 1e-3
     step = runner.DecodeStep(r)
     step.run()
     torch.cuda.synchronize()

@@ -16,7 +16,7 @@ import torch
 import oracle
 from block_diffusion_vlm_amd import bdiff as bd
 from block_diffusion_vlm_amd import runner, synth
-from oracle.guards import lmhead_margins
+from oracle.guards import lmhead_margins, row_guard
 
 pytestmark = pytest.mark.gpu
 
@@ -30,20 +30,19 @@ def gfx950():
 
 
 def _bf16_case(B, d, V, seed):
-    r = synth.qwen_decode(seed=seed, B=B, d=d, V=V, n_vis=4, n_prompt=4, Hq=2, Hkv=1)
+    r = synth.qwen_decode(seed=seed, B=B, d=d, V=V, n_vis=4, n_prompt=4, Hq=2, Hkv=1,
+                          guard=row_guard())
     gap, _ = lmhead_margins(r["h"], r["W"])
     assert gap.min() > 1e-2
     return r
 
 
 def _fp8_case(B, d, V, seed):
-    for k in range(20):
-        r = synth.qwen_decode_fp8(seed=seed + 1000 * k, B=B, d=d, V=V, n_vis=4, n_prompt=4,
-                                  Hq=2, Hkv=1)
-        gap, _ = lmhead_margins(r["h"], r["W"], w_scale=r["w_scale"])
-        if gap.min() > 1e-2:
-            return r
-    raise AssertionError("no guarded input among 20 seeds")
+    r = synth.qwen_decode_fp8(seed=seed, B=B, d=d, V=V, n_vis=4, n_prompt=4, Hq=2, Hkv=1,
+                              guard=row_guard())
+    gap, _ = lmhead_margins(r["h"], r["W"], w_scale=r["w_scale"])
+    assert gap.min() > 1e-2
+    return r
 
 
 def _check_calls(outs, refs):

@@ -92,3 +92,43 @@ def test_full_size_fp8_decode_guards_hold():
     conf, a = oracle.lmhead_conf_fp8(r["h"], r["W"], r["w_scale"])
     assert np.array_equal(a, r["targets"])
     assert 0 < (conf[1:] > r["tau"]).sum() < 15
+
+
+def test_guard_redraws_only_failing_rows_from_a_separate_stream():
+    """A row the guard rejects is planted again (same target, same side of
+    the threshold); every other row and every tensor drawn after the hidden
+    rows stay as the unguarded draw has them."""
+    from oracle.guards import rows_guarded
+    base = synth.qwen_decode(V=3000, d=256)
+    calls = [0]
+
+    def reject_row3_once(h, W, w_scale=None):
+        calls[0] += 1
+        ok = rows_guarded(h, W, 0.9, w_scale)
+        if calls[0] == 1:
+            ok[3] = False
+        return ok
+
+    r = synth.qwen_decode(V=3000, d=256, guard=reject_row3_once)
+    changed = np.nonzero((r["h"] != base["h"]).any(axis=1))[0]
+    assert changed.tolist() == [3] and calls[0] == 2
+    for k in ("q", "k_cache", "v_cache", "W", "targets", "tokens", "masked"):
+        assert np.array_equal(r[k], base[k]), k
+    conf, a = oracle.lmhead_conf(r["h"], r["W"])
+    assert a[3] == r["targets"][3]
+    assert (conf[3] > 0.9) == bool(r["planted_commit"][3])
+    # a guard that never passes is an error, not a silent pass
+    with pytest.raises(RuntimeError):
+        synth.qwen_decode(V=3000, d=256, guard=lambda h, W, w=None: np.zeros(len(h), bool))
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_full_size_block_loop_guards_hold(fp8):
+    """Every step's planted rows of the full-size block loop keep the top-2
+    gap above 1e-2 and every confidence at least 1e-3 from tau as drawn, so
+    the unguarded draw (the benchmark's) equals the guarded one."""
+    r = synth.qwen_block_loop(fp8=fp8)
+    d = r["h_steps"].shape[-1]
+    gap, dist = lmhead_margins(r["h_steps"].reshape(-1, d), r["W"], r["tau"],
+                               w_scale=r.get("w_scale"))
+    assert gap.min() > 1e-2 and dist.min() >= 1e-3
