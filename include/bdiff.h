@@ -14,7 +14,9 @@
  *     and returns as soon as its kernels are enqueued.
  *   - The caller owns every buffer.  The library allocates no device memory
  *     and keeps no global mutable state; scratch space comes in as a
- *     caller-provided workspace sized by the matching *_ws_bytes query.
+ *     caller-provided workspace sized by the matching *_ws_bytes query.  The
+ *     one exception is bd_lmhead_conf_noalloc, whose scratch is a static
+ *     device array of the library (one per GPU).
  *   - Arguments are checked on the host before anything is enqueued; on an
  *     error nothing is launched and the outputs are untouched.  A failed
  *     launch returns BD_E_LAUNCH.  No call aborts or throws.
@@ -171,6 +173,31 @@ bd_status bd_lmhead_conf_commit(bd_dtype dt, const void* h, const void* W,
                                 float* conf, int32_t* argmax,
                                 uint8_t* masked, int32_t* tokens, int32_t* n_committed,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * bd_lmhead_conf_noalloc - bd_lmhead_conf without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  The partial
+ * states live in a static device array of the library, 196608 bytes (3 x 256
+ * partials x 64 positions x 4 bytes), of which each GPU that the library runs
+ * on holds its own copy until the process ends.  Results are bit-identical to
+ * bd_lmhead_conf's for the same inputs.
+ *   Arguments, layouts and limits as in bd_lmhead_conf.  Every bf16 shape
+ *   within those limits fits; a float32 shape needs V <= 65536 (its partials
+ *   are one per 256 vocabulary rows).  A shape whose partials exceed the
+ *   array returns BD_E_WORKSPACE.
+ *   The array needs no initial contents and is not cleared between calls.
+ *   All calls on one GPU share it: calls that may overlap on the same GPU
+ *   (different streams, or several host threads, without ordering between
+ *   them) race and give undefined results.  The first call on a device looks
+ *   the array's device address up (hipGetSymbolAddress; BD_E_DEVICE if that
+ *   fails); no call allocates memory.
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_ALIGN, BD_E_WORKSPACE,
+ *   BD_E_DEVICE, BD_E_LAUNCH.
+ */
+bd_status bd_lmhead_conf_noalloc(bd_dtype dt, const void* h, const void* W,
+                                 int32_t B, int32_t d, int32_t V,
+                                 float* conf, int32_t* argmax, hipStream_t stream);
 
 /*
  * bd_lmhead_conf_fp8 - bd_lmhead_conf with FP8 weights and activations

@@ -386,3 +386,27 @@ def test_python_binding_raises_on_error():
         bd.bd_commit(FAKE, FAKE, 99, 0.9, FAKE, FAKE, FAKE, stream=0)
     assert e.value.status == bd.BD_E_SHAPE
 
+
+def test_lmhead_noalloc_validation():
+    """Argument errors come back before any device is touched, exactly as for
+    bd_lmhead_conf; shapes whose partials exceed the library's scratch array
+    return BD_E_WORKSPACE."""
+    f = lambda **kw: bd.bd_lmhead_conf_noalloc(**{**dict(  # noqa: E731
+        dt=bd.BD_BF16, h=FAKE, W=FAKE, B=16, d=2048, V=151936, conf=FAKE, argmax=FAKE,
+        stream=0, check=False), **kw})
+    assert f(h=None) == bd.BD_E_NULL
+    assert f(argmax=None) == bd.BD_E_NULL
+    assert f(dt=5) == bd.BD_E_DTYPE
+    assert f(B=0) == bd.BD_E_SHAPE
+    assert f(B=65) == bd.BD_E_SHAPE
+    assert f(d=1000) == bd.BD_E_SHAPE
+    assert f(W=MISALIGNED) == bd.BD_E_ALIGN
+    # float32 partials: one per 256 vocabulary rows -> V > 65536 does not fit
+    assert f(dt=bd.BD_F32, d=16, V=65537, B=64) == bd.BD_E_WORKSPACE
+    # every bf16 shape fits (the persistent grid has at most 256 workgroups);
+    # these fail only later, at the device lookup, as there is no GPU here
+    if not __import__("torch").cuda.is_available():
+        assert f(B=64, d=16384, V=2 ** 30) == bd.BD_E_DEVICE
+        assert f(dt=bd.BD_F32, d=16, V=65536, B=64) == bd.BD_E_DEVICE
+    assert bd.bd_lmhead_conf_ws_bytes(16, 2048, 2 ** 30 + 1) == 0
+    assert f(V=2 ** 30 + 1) == bd.BD_E_SHAPE
