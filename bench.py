@@ -1,6 +1,6 @@
 """Benchmark of the block-diffusion decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads LIST]
 
 A step is one threshold (MDM) block-decode step of the Qwen2.5-VL-3B-shaped
 workload: bd_block_attn (16 block queries, bidirectional block, over a
@@ -9,16 +9,20 @@ bd_lmhead_conf (hidden 2048 x vocabulary 151936, bf16) -> bd_commit
 (threshold 0.9), plus the restore of the block state so that every step does
 the same work.  Inputs are seeded synthetic tensors already resident in HBM;
 S consecutive steps (default 8) are captured as one HIP graph, which is
-replayed K/S times between HIP events.  Each of the S steps of a graph works
+replayed K/S times between HIP events (S is the largest divisor of K up to
+8, so that exactly K steps are timed).  Each of the S steps of a graph works
 on its own copy of the block state, and one device copy at the head of the
 graph restores all S copies, so that every step starts from the same state.
-One JSON line is printed.
+One JSON line is printed.  ``--workloads`` selects the secondary workloads
+(comma-separated among fp8, loop, train, attn, spec; "all" or "none"), so
+that a profiled run can be cut to the kernels it is about.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 from pathlib import Path
@@ -39,14 +43,35 @@ def parse():
     ap.add_argument("--warmup", type=int, default=400,
                     help="untimed steps first (~43 ms of work: the clocks settle)")
     ap.add_argument("--graph-steps", type=int, default=8,
-                    help="decode steps captured per HIP graph (replays = steps / graph-steps)")
+                    help="at most this many decode steps per HIP graph (a divisor of --steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--fp8-only", action="store_true",
-                    help="of the secondary workloads, run only the FP8 decode step")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="approximate CPU time budget of the oracle baseline sample")
-    return ap.parse_args()
+    ap.add_argument("--workloads", default="all",
+                    help="secondary workloads: all, none, or a comma list of " + ",".join(SECTIONS))
+    ap.add_argument("--no-secondary", action="store_true", help="same as --workloads none")
+    ap.add_argument("--cpu-seconds", type=float, default=16.0,
+                    help="approximate CPU time budget of the oracle baseline samples")
+    a = ap.parse_args()
+    if a.no_secondary or a.workloads == "none":
+        a.sections = set()
+    elif a.workloads == "all":
+        a.sections = set(SECTIONS)
+    else:
+        a.sections = {w.strip() for w in a.workloads.split(",") if w.strip()}
+        bad = a.sections - set(SECTIONS)
+        if bad:
+            ap.error(f"unknown workloads {sorted(bad)}")
+    return a
+
+
+SECTIONS = ("fp8", "loop", "train", "attn", "spec")
+
+
+def graph_divisor(K, cap):
+    """Largest divisor of K that is at most cap (steps per captured graph)."""
+    for s in range(min(cap, K), 0, -1):
+        if K % s == 0:
+            return s
+    return 1
 
 
 
@@ -131,27 +156,129 @@ def graph_ms_per_step(step, S, reps, warm, stream):
     return ms, n_commit
 
 
-def cpu_baseline(inp, budget_s):
-    """The oracle's decode step on the same inputs, timed on the host cores."""
-    import numpy as np
-    import oracle
+def _cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
-    tau = float(np.float32(0.9))
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def _time_reps(fn, budget_s, max_reps=50):
+    """(reps, seconds) of back-to-back fn() calls, at least one, until the
+    budget is spent."""
     n, t0 = 0, time.perf_counter()
     while True:
-        oracle.decode_step(inp["q"], inp["k_cache"], inp["v_cache"], inp["P"], inp["h"],
-                           inp["W"], inp["masked"], inp["tokens"], tau)
+        fn()
         n += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or n >= 50:
-            break
-    return {"value": n / el, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} full decode steps of the same workload (float64 NumPy oracle: "
-                      f"block attention, LM head over all 151936 rows, commit), {el:.1f} s"}
+        if el >= budget_s or n >= max_reps:
+            return n, el
+
+
+def cpu_baseline(inp, others, budget_s):
+    """The oracle (float64 NumPy) on the same inputs, timed on the host cores
+    of the machine that holds the GPU: the headline decode step with every
+    core and with one thread (BLAS threads limited through threadpoolctl;
+    the rest of the oracle is single-threaded NumPy), and one bounded sample
+    of each other workload with every core.  `others` holds the other
+    workloads' inputs where the secondary section already drew them."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_limits
+    from block_diffusion_vlm_amd import synth
+    cores = len(os.sched_getaffinity(0))
+    tau = float(np.float32(0.9))
+
+    def decode():
+        oracle.decode_step(inp["q"], inp["k_cache"], inp["v_cache"], inp["P"], inp["h"],
+                           inp["W"], inp["masked"], inp["tokens"], tau)
+
+    with threadpool_limits(limits=cores):
+        n_all, t_all = _time_reps(decode, 0.3 * budget_s)
+    with threadpool_limits(limits=1):
+        n_one, t_one = _time_reps(decode, 0.25 * budget_s)
+    res = {"value": n_all / t_all, "unit": "steps/s", "cores": cores, "kind": "oracle",
+           "sample": f"{n_all} full decode steps of the headline workload (block attention, "
+                     f"LM head over all 151936 rows, commit) in {t_all:.1f} s with "
+                     f"{cores} BLAS threads",
+           "cpu_model": _cpu_model(), "host_cores": cores,
+           "single_thread": {"value": n_one / t_one, "unit": "steps/s", "cores": 1,
+                             "sample": f"{n_one} decode steps in {t_one:.1f} s"}}
+    cfg = {}
+    with threadpool_limits(limits=cores):
+        t = synth.tiny()
+        n, el = _time_reps(lambda: (
+            oracle.decode_step(t["q"], t["k_cache"], t["v_cache"], t["P"], t["h"], t["W"],
+                               t["masked"], t["tokens"], tau),
+            oracle.dualstream_attn(t["ds_q"], t["ds_k"], t["ds_v"], 4, 4, 2)), 0.03 * budget_s,
+            max_reps=1000)
+        cfg["tiny_f32"] = {"value": round(el / n * 1e6, 1), "unit": "us per decode step + "
+                           "dual-stream attention", "sample": f"{n} reps"}
+        r3 = others.get("linear") or synth.linear_spec()
+        n, el = _time_reps(lambda: oracle.linear_spec_step(
+            r3["q_draft"], r3["k_draft"], r3["v_draft"], r3["q_verify"], r3["k_verify"],
+            r3["v_verify"], r3["P"], r3["h_draft"], r3["h_verify"], r3["W"]), 0.1 * budget_s)
+        cfg["linear_spec_step"] = {"value": n / el, "unit": "spec-steps/s",
+                                   "sample": f"{n} steps in {el:.1f} s"}
+        r4 = others.get("fused") or synth.fused_spec()
+
+        def fused():
+            oracle.fused_spec_step(r4["q"], r4["k_cache"], r4["v_cache"], r4["P"], r4["h"],
+                                   r4["W"], r4["draft_in"])
+            oracle.cert_scan(r4["anchor_conf"], r4["anchor_tok"], r4["text_tok"], r4["k_cert"])
+        n, el = _time_reps(fused, 0.1 * budget_s)
+        cfg["fused_spec_step"] = {"value": n / el, "unit": "steps/s (with certificate)",
+                                  "sample": f"{n} steps in {el:.1f} s"}
+        r5 = others.get("dualstream") or synth.dualstream()
+        nh = 2
+        t0 = time.perf_counter()
+        oracle.dualstream_attn(r5["q"][:, :nh], r5["k"][:, :nh], r5["v"][:, :nh],
+                               r5["n_vis"], r5["n_txt"], r5["block"])
+        el = time.perf_counter() - t0
+        flops = dualstream_pairs(r5["n_vis"], r5["n_txt"], r5["block"]) * nh * 4 * r5["dh"]
+        cfg["dualstream_fwd"] = {"value": flops / el / 1e12, "unit": "TFLOP/s (algorithmic)",
+                                 "ms_per_forward": round(el * 1e3 * r5["H"] / nh, 1),
+                                 "sample": f"{nh} of {r5['H']} heads in {el:.1f} s, the "
+                                           "forward's time scaled by heads"}
+    res["configs"] = cfg
+    return res
+
+
+def graph_ms(run, S, reps, warm, stream):
+    """ms per call of run() (a stateless composition of library calls),
+    captured S times in one HIP graph and replayed `reps` times between HIP
+    events after `warm` untimed replays."""
+    import torch
+    run()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        run()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(S):
+            run()
+    torch.cuda.synchronize()
+    return timed(g.replay, reps, warm, stream) / S
+
+
+def stream_read_gbs(stream, n_bytes=2 ** 31, grid=256, reps=20):
+    """Achievable-bandwidth reference: GB/s of a plain streaming read of
+    n_bytes (bd_probe_stream_read), HIP events around `reps` reads."""
+    import torch
+    from block_diffusion_vlm_amd import bdiff as bd
+    buf = torch.empty(n_bytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ms = timed(lambda: bd.bd_probe_stream_read(buf, n_bytes, grid, sink), reps, 3, stream)
+    del buf
+    return n_bytes / (ms * 1e-3) / 1e9
 
 
 def main():
@@ -173,18 +300,18 @@ def main():
     stream = torch.cuda.current_stream()
 
     inp = synth.qwen_decode()
-    S = max(1, args.graph_steps)
+    K = max(1, args.steps)
+    S = graph_divisor(K, max(1, args.graph_steps))
     step = runner.DecodeStep(inp, slots=S)
     B, P, Hq, Hkv, dh, d, V = (inp[k] for k in ("B", "P", "Hq", "Hkv", "dh", "d", "V"))
 
-    reps = max(1, (args.steps + S - 1) // S)
-    args.steps = reps * S
-    ms_step, n_commit = graph_ms_per_step(step, S, reps, max(1, args.warmup // S), stream)
+    ms_step, n_commit = graph_ms_per_step(step, S, K // S, -(-max(0, args.warmup) // S), stream)
+    print(f"headline: {ms_step * 1e3:.2f} us per decode step", file=sys.stderr, flush=True)
 
     # Dominant kernel: the LM head (its two dispatches), timed alone.
-    ms_lm = timed(lambda: step.lm(step.h), args.steps, args.warmup, stream)
-    ms_attn = timed(lambda: step.attn(step.q, step.k_cache, step.v_cache), args.steps,
-                    args.warmup, stream)
+    ms_lm = timed(lambda: step.lm(step.h), K, args.warmup, stream)
+    ms_attn = timed(lambda: step.attn(step.q, step.k_cache, step.v_cache), K, args.warmup,
+                    stream)
 
     b_lm, b_step = step_bytes(inp)
     steps_per_s = 1e3 / ms_step
@@ -206,18 +333,19 @@ def main():
     del kc_rot, vc_rot
 
     # Plain device copy of known size (calibrates the HBM byte counters in a
-    # profiled run of this same command).
+    # profiled run of this same command), and the streaming-read reference.
     cal = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda")
     cal2 = torch.empty_like(cal)
     ms_copy = timed(lambda: cal2.copy_(cal), 20, 3, stream)
     del cal, cal2
+    read_gbs = stream_read_gbs(stream)
 
     out = {
         "metric": METRIC,
         "value": round(steps_per_s, 1),
         "unit": "steps/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
@@ -233,22 +361,26 @@ def main():
         "committed_per_step": n_commit,
         "step_hbm_gbs": round(b_step / (ms_step * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(b_step / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "steps_per_graph": S,
         "roofline": {"bound": "hbm", "kernel": "bd_lmhead_conf (contraction + merge)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile("bf16"),
-                     "us_per_launch": round(ms_lm * 1e3, 2), "bytes_per_launch": b_lm},
+                     "us_per_launch": round(ms_lm * 1e3, 2), "bytes_per_launch": b_lm,
+                     "frac_of_stream_read": round(achieved / read_gbs, 4)},
+        "stream_read_2GiB_GBs": round(read_gbs, 1),
         "kernels_us": {"bd_block_attn": round(ms_attn * 1e3, 2),
                        "bd_block_attn_kv_from_hbm": round(ms_attn_cold * 1e3, 2),
                        "bd_lmhead_conf": round(ms_lm * 1e3, 2),
                        "copy_256MiB_GBs": round(2 * 256 * 2 ** 20 / (ms_copy * 1e-3) / 1e9, 1)},
     }
 
-    if not args.no_secondary:
-        out["secondary"] = secondary(args, stream)
+    others = {}
+    if args.sections:
+        out["secondary"] = secondary(args, stream, others)
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(inp, others, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
@@ -262,8 +394,10 @@ def dualstream_pairs(n_vis, n_txt, block):
     return ctx * (ctx + 1) // 2 + n_txt * n_vis + n_txt * (n_txt + 1) // 2 + n2n
 
 
-def secondary(args, stream):
-    """The other workloads, each timed on its own (not part of `value`)."""
+def secondary(args, stream, others):
+    """The other workloads, each timed on its own (not part of `value`), for
+    the sections in args.sections; the inputs the CPU baseline reuses are left
+    in `others`."""
     import numpy as np
     import torch
     from block_diffusion_vlm_amd import bdiff as bd
@@ -271,173 +405,200 @@ def secondary(args, stream):
     res = {}
     iters = max(20, args.steps // 5)
     warm = max(3, args.warmup // 5)
+    S = graph_divisor(8 * max(1, iters // 8), max(1, args.graph_steps))
 
-    # The same decode step with the FP8 (E4M3, W8A8) LM head, captured and
-    # replayed like the headline step.
-    r6 = synth.qwen_decode_fp8()
-    S = max(1, args.graph_steps)
-    st8 = runner.DecodeStep(r6, slots=S)
-    reps = max(1, iters // S)
-    ms8, n8 = graph_ms_per_step(st8, S, reps, max(1, warm // S), stream)
-    ms_lm8 = timed(lambda: st8.lm(st8.h), iters, warm, stream)
-    b_lm8, b_step8 = step_bytes(r6)
-    res["decode_step_fp8"] = {
-        "us": round(ms8 * 1e3, 2), "steps_per_s": round(1e3 / ms8, 1),
-        "committed_per_step": n8,
-        "hbm_frac": round(b_step8 / (ms8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "lmhead_us": round(ms_lm8 * 1e3, 2),
-        "lmhead_gbs": round(b_lm8 / (ms_lm8 * 1e-3) / 1e9, 1),
-        "lmhead_hbm_frac": round(b_lm8 / (ms_lm8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "lmhead_bytes": b_lm8,
-        "lmhead_traffic": traffic_from_profile("fp8"),
-        "shape": "the headline step with E4M3 weights (one float32 scale per row) and "
-                 "per-position E4M3 activations"}
-    del st8, r6
-    if args.fp8_only:
-        return res
+    def note(name):
+        print(f"secondary: {name}", file=sys.stderr, flush=True)
 
-    # Whole blocks: the device-resident loop (up to 16 steps enqueued, the
-    # steps that run decided on the device), bf16 and FP8 LM heads.
-    for fp8 in (False, True):
-        rl = synth.qwen_block_loop(fp8=fp8)
-        loop = runner.BlockLoop(rl)
-        loop.reset()
-        loop.run()
-        torch.cuda.synchronize()
-        n_steps = int(loop.n_steps.item())
-        tok_ref = loop.tokens.clone()
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
+    if "fp8" in args.sections:
+        # The same decode step with the FP8 (E4M3, W8A8) LM head, captured
+        # and replayed like the headline step.
+        note("decode_step_fp8")
+        r6 = synth.qwen_decode_fp8()
+        st8 = runner.DecodeStep(r6, slots=S)
+        ms8, n8 = graph_ms_per_step(st8, S, max(1, iters // S), max(1, warm // S), stream)
+        ms_lm8 = timed(lambda: st8.lm(st8.h), iters, warm, stream)
+        b_lm8, b_step8 = step_bytes(r6)
+        res["decode_step_fp8"] = {
+            "us": round(ms8 * 1e3, 2), "steps_per_s": round(1e3 / ms8, 1),
+            "committed_per_step": n8,
+            "hbm_frac": round(b_step8 / (ms8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "lmhead_us": round(ms_lm8 * 1e3, 2),
+            "lmhead_gbs": round(b_lm8 / (ms_lm8 * 1e-3) / 1e9, 1),
+            "lmhead_hbm_frac": round(b_lm8 / (ms_lm8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "lmhead_bytes": b_lm8,
+            "lmhead_traffic": traffic_from_profile("fp8"),
+            "shape": "the headline step with E4M3 weights (one float32 scale per row) and "
+                     "per-position E4M3 activations"}
+        del st8, r6
+
+    if "loop" in args.sections:
+        # Whole blocks: the device-resident loop (up to 16 steps enqueued, the
+        # steps that run decided on the device), bf16 and FP8 LM heads.
+        for fp8 in (False, True):
+            note("block_loop" + ("_fp8" if fp8 else ""))
+            rl = synth.qwen_block_loop(fp8=fp8)
+            loop = runner.BlockLoop(rl)
             loop.reset()
             loop.run()
-        stream.wait_stream(side)
+            torch.cuda.synchronize()
+            n_steps = int(loop.n_steps.item())
+            tok_ref = loop.tokens.clone()
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                loop.reset()
+                loop.run()
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                loop.reset()
+                loop.run()
+            torch.cuda.synchronize()
+            ms = timed(g.replay, max(5, iters // 8), 2, stream)
+            torch.cuda.synchronize()
+            assert torch.equal(loop.tokens, tok_ref) and int(loop.n_steps.item()) == n_steps
+            committed = int(np.asarray(rl["masked"]).sum())
+            res["block_loop_fp8" if fp8 else "block_loop"] = {
+                "us_per_block": round(ms * 1e3, 2), "steps": n_steps, "max_steps": loop.S,
+                "committed_per_block": committed,
+                "committed_tok_per_s": round(committed / (ms * 1e-3), 1),
+                "us_per_step": round(ms * 1e3 / n_steps, 2),
+                "shape": "one 16-position block of the Qwen-shaped decode, planted to finish "
+                         "in 8 steps"}
+            del loop, rl, g
+
+    if "train" in args.sections:
+        # The training attention is compute-bound: its clock settles only
+        # after some tens of milliseconds of back-to-back calls, so these two
+        # lines warm up for 300 calls and time the steady state.
+        warm_train = max(warm, 300)
+        note("dualstream_fwd")
+        r5 = synth.dualstream()
+        others["dualstream"] = r5
+        ds = runner.DualStream(r5)
+        ms = timed(ds.run, iters, warm_train, stream)
+        flops = dualstream_pairs(r5["n_vis"], r5["n_txt"], r5["block"]) * r5["H"] * 4 * r5["dh"]
+        res["dualstream_fwd"] = {
+            "us": round(ms * 1e3, 2), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "algorithmic_gflop": round(flops / 1e9, 2),
+            "shape": "1024 vis + 2048 clean + 2048 noisy, block 32, 16 heads x 128"}
+        del ds
+        # Training backward on the same input: dQ, dK, dV from the forward's
+        # output and row log-sum-exp.  Algorithmic work = 2.5x the forward's
+        # (dV, dP, dQ, dK products and one recomputation of S).
+        note("dualstream_bwd")
+        tr = runner.DualStreamTrain(r5)
+        tr.forward()
+        ms_b = timed(tr.backward, iters, warm_train, stream)
+        bflops = 2.5 * flops
+        res["dualstream_bwd"] = {
+            "us": round(ms_b * 1e3, 2), "tflops": round(bflops / (ms_b * 1e-3) / 1e12, 1),
+            "mfma_frac": round(bflops / (ms_b * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "shape": "the dual-stream forward's input, output gradient N(0,1)"}
+        del tr
+
+    if "attn" in args.sections:
+        # Block attention of the decode step over a paged KV cache (16-token
+        # pages in shuffled order), full prefix and TEXT-ONLY (visual keys
+        # left out), beside the contiguous cache.
+        note("block_attn_paged")
+        rq = synth.qwen_decode(V=64, d=128)
+        B, P, Hq, Hkv = rq["B"], rq["P"], rq["Hq"], rq["Hkv"]
+        n = P + B
+        ps = 16
+        n_pages = -(-n // ps) + 8
+        rng = np.random.default_rng(0)
+        table = rng.permutation(n_pages)[:-(-n // ps)].astype(np.int32)
+        pools = []
+        for cache in (rq["k_cache"], rq["v_cache"]):
+            pool = np.zeros((n_pages, Hkv, ps, 128), np.uint16)
+            for j in range(n):
+                pool[table[j // ps], :, j % ps] = cache[:, j]
+            pools.append(runner.to_dev(pool))
+        tab = runner.to_dev(table)
+        qd = runner.to_dev(rq["q"])
+        mask = runner.mask_dev(bd.BD_MASK_BIDIR, B)
+        out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device="cuda")
+        pa = {}
+        for key_lo in (0, rq["n_vis"]):
+            wsb = bd.bd_block_attn_ws_bytes(P - key_lo, B, Hq, Hkv, 128)
+            ws = runner.workspace(wsb)
+            ms = timed(lambda: bd.bd_block_attn_paged(qd, pools[0], pools[1], tab, ps, n_pages,
+                                                      P, key_lo, mask, B, Hq, Hkv, 128, 0.0,
+                                                      out, ws, wsb), iters, warm, stream)
+            pa["us_full_prefix" if key_lo == 0 else "us_text_only"] = round(ms * 1e3, 2)
+        ba = runner.BlockAttn(bd.BD_BF16, bd.BD_MASK_BIDIR, B, P, rq["cap"], Hq, Hkv, 128)
+        kc, vc = runner.to_dev(rq["k_cache"]), runner.to_dev(rq["v_cache"])
+        ms = timed(lambda: ba(qd, kc, vc), iters, warm, stream)
+        pa["us_contiguous"] = round(ms * 1e3, 2)
+        pa["shape"] = "the decode step's block attention, 16-token pages in shuffled order"
+        res["block_attn_paged"] = pa
+        del pools, ba, kc, vc
+
+        # Block attention of the decode step over an FP8 (E4M3) KV cache with
+        # per-head scales, and the quantizer writing the block's own K/V rows.
+        note("block_attn_fp8kv")
+        rf = synth.qwen_decode_fp8kv()
+        B, P, cap, Hq, Hkv = rf["B"], rf["P"], rf["cap"], rf["Hq"], rf["Hkv"]
+        att8 = runner.BlockAttnFP8KV(bd.BD_MASK_BIDIR, B, P, cap, Hq, Hkv)
+        q8 = runner.to_dev(rf["q"])
+        kc8, vc8 = runner.to_dev(rf["k_codes"]), runner.to_dev(rf["v_codes"])
+        ks8, vs8 = runner.to_dev(rf["k_scale"]), runner.to_dev(rf["v_scale"])
+        kn8 = runner.to_dev(rf["k_new"])
+        ms = timed(lambda: att8(q8, kc8, vc8, ks8, vs8), iters, warm, stream)
+        ms_q = timed(lambda: bd.bd_kv_quant_fp8(kn8, B, Hkv, 128, ks8, kc8, cap, P), iters,
+                     warm, stream)
+        kv_bytes = 2 * Hkv * (P + B) * 128
+        res["block_attn_fp8kv"] = {
+            "us": round(ms * 1e3, 2), "kv_bytes": kv_bytes,
+            "us_bf16_cache": pa["us_contiguous"], "us_quant_block_rows": round(ms_q * 1e3, 2),
+            "shape": "the decode step's block attention, E4M3 K/V (one byte per entry) "
+                     "with per-head scales"}
+        del att8, kc8, vc8
+
+    if "spec" in args.sections:
+        # Both speculation steps are captured S at a time in one HIP graph,
+        # as the headline step is.
+        note("linear_spec_step")
+        r3 = synth.linear_spec()
+        others["linear"] = r3
+        lin = runner.LinearSpecStep(r3)
+        lin.run()
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            loop.reset()
-            loop.run()
+        L = int(lin.accepted.item())
+        ms = graph_ms(lin.run, S, max(1, iters // S), max(1, warm // S), stream)
         torch.cuda.synchronize()
-        ms = timed(g.replay, max(5, iters // 8), 2, stream)
+        assert int(lin.accepted.item()) == L
+        b = 2 * (r3["V"] * r3["d"] * 2 + 2 * r3["Hkv"] * r3["cap"] * r3["dh"] * 2)
+        ms_attn = timed(lambda: lin.attn_d(lin.t["q_draft"], lin.t["k_draft"], lin.t["v_draft"]),
+                        iters, warm, stream)
+        res["linear_spec_step"] = {"us": round(ms * 1e3, 2), "accepted": L,
+                                   "accepted_tok_per_s": round(L / (ms * 1e-3), 1),
+                                   "hbm_frac": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                   "attn_us": round(ms_attn * 1e3, 2), "bytes": b}
+        del lin
+
+        note("fused_spec_step")
+        r4 = synth.fused_spec()
+        others["fused"] = r4
+        fu = runner.FusedSpecStep(r4)
+        fu.run()
         torch.cuda.synchronize()
-        assert torch.equal(loop.tokens, tok_ref) and int(loop.n_steps.item()) == n_steps
-        committed = int(np.asarray(rl["masked"]).sum())
-        res["block_loop_fp8" if fp8 else "block_loop"] = {
-            "us_per_block": round(ms * 1e3, 2), "steps": n_steps, "max_steps": loop.S,
-            "committed_per_block": committed,
-            "committed_tok_per_s": round(committed / (ms * 1e-3), 1),
-            "us_per_step": round(ms * 1e3 / n_steps, 2),
-            "shape": "one 16-position block of the Qwen-shaped decode, planted to finish in "
-                     "8 steps"}
-        del loop, rl, g
-
-    # The training attention is compute-bound: its clock settles only after
-    # some tens of milliseconds of back-to-back calls, so these two lines
-    # warm up for 300 calls and time the steady state.
-    warm_train = max(warm, 300)
-    r5 = synth.dualstream()
-    ds = runner.DualStream(r5)
-    ms = timed(ds.run, iters, warm_train, stream)
-    flops = dualstream_pairs(r5["n_vis"], r5["n_txt"], r5["block"]) * r5["H"] * 4 * r5["dh"]
-    res["dualstream_fwd"] = {"us": round(ms * 1e3, 2),
-                             "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
-                             "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                             "shape": "1024 vis + 2048 clean + 2048 noisy, block 32, 16 heads x 128"}
-    del ds
-
-    # Training backward on the same input: dQ, dK, dV from the forward's
-    # output and row log-sum-exp.  Algorithmic work = 2.5x the forward's
-    # (dV, dP, dQ, dK products and one recomputation of S).
-    tr = runner.DualStreamTrain(r5)
-    tr.forward()
-    ms_b = timed(tr.backward, iters, warm_train, stream)
-    bflops = 2.5 * flops
-    res["dualstream_bwd"] = {"us": round(ms_b * 1e3, 2),
-                             "tflops": round(bflops / (ms_b * 1e-3) / 1e12, 1),
-                             "mfma_frac": round(bflops / (ms_b * 1e-3) / 1e12
-                                                / MFMA_BF16_PEAK_TFLOPS, 4),
-                             "shape": "the dual-stream forward's input, output gradient N(0,1)"}
-    del tr
-
-    # Block attention of the decode step over a paged KV cache (16-token
-    # pages in shuffled order), full prefix and TEXT-ONLY (visual keys left
-    # out), beside the contiguous cache.
-    rq = synth.qwen_decode(V=64, d=128)
-    B, P, Hq, Hkv = rq["B"], rq["P"], rq["Hq"], rq["Hkv"]
-    n = P + B
-    ps = 16
-    n_pages = -(-n // ps) + 8
-    rng = np.random.default_rng(0)
-    table = rng.permutation(n_pages)[:-(-n // ps)].astype(np.int32)
-    pools = []
-    for cache in (rq["k_cache"], rq["v_cache"]):
-        pool = np.zeros((n_pages, Hkv, ps, 128), np.uint16)
-        for j in range(n):
-            pool[table[j // ps], :, j % ps] = cache[:, j]
-        pools.append(runner.to_dev(pool))
-    tab = runner.to_dev(table)
-    qd = runner.to_dev(rq["q"])
-    mask = runner.mask_dev(bd.BD_MASK_BIDIR, B)
-    out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device="cuda")
-    pa = {}
-    for key_lo in (0, rq["n_vis"]):
-        wsb = bd.bd_block_attn_ws_bytes(P - key_lo, B, Hq, Hkv, 128)
-        ws = runner.workspace(wsb)
-        ms = timed(lambda: bd.bd_block_attn_paged(qd, pools[0], pools[1], tab, ps, n_pages, P,
-                                                  key_lo, mask, B, Hq, Hkv, 128, 0.0, out, ws,
-                                                  wsb), iters, warm, stream)
-        pa["us_full_prefix" if key_lo == 0 else "us_text_only"] = round(ms * 1e3, 2)
-    ba = runner.BlockAttn(bd.BD_BF16, bd.BD_MASK_BIDIR, B, P, rq["cap"], Hq, Hkv, 128)
-    kc, vc = runner.to_dev(rq["k_cache"]), runner.to_dev(rq["v_cache"])
-    ms = timed(lambda: ba(qd, kc, vc), iters, warm, stream)
-    pa["us_contiguous"] = round(ms * 1e3, 2)
-    pa["shape"] = "the decode step's block attention, 16-token pages in shuffled order"
-    res["block_attn_paged"] = pa
-    del pools, ba, kc, vc
-
-    # Block attention of the decode step over an FP8 (E4M3) KV cache with
-    # per-head scales, and the quantizer writing the block's own K/V rows.
-    rf = synth.qwen_decode_fp8kv()
-    B, P, cap, Hq, Hkv = rf["B"], rf["P"], rf["cap"], rf["Hq"], rf["Hkv"]
-    att8 = runner.BlockAttnFP8KV(bd.BD_MASK_BIDIR, B, P, cap, Hq, Hkv)
-    q8 = runner.to_dev(rf["q"])
-    kc8, vc8 = runner.to_dev(rf["k_codes"]), runner.to_dev(rf["v_codes"])
-    ks8, vs8 = runner.to_dev(rf["k_scale"]), runner.to_dev(rf["v_scale"])
-    kn8 = runner.to_dev(rf["k_new"])
-    ms = timed(lambda: att8(q8, kc8, vc8, ks8, vs8), iters, warm, stream)
-    ms_q = timed(lambda: bd.bd_kv_quant_fp8(kn8, B, Hkv, 128, ks8, kc8, cap, P), iters, warm,
-                 stream)
-    kv_bytes = 2 * Hkv * (P + B) * 128
-    res["block_attn_fp8kv"] = {
-        "us": round(ms * 1e3, 2), "kv_bytes": kv_bytes,
-        "us_bf16_cache": pa["us_contiguous"], "us_quant_block_rows": round(ms_q * 1e3, 2),
-        "shape": "the decode step's block attention, E4M3 K/V (one byte per entry) "
-                 "with per-head scales"}
-    del att8, kc8, vc8
-
-    r3 = synth.linear_spec()
-    lin = runner.LinearSpecStep(r3)
-    ms = timed(lin.run, iters, warm, stream)
-    torch.cuda.synchronize()
-    L = int(lin.accepted.item())
-    b = 2 * (r3["V"] * r3["d"] * 2 + 2 * r3["Hkv"] * r3["cap"] * r3["dh"] * 2)
-    res["linear_spec_step"] = {"us": round(ms * 1e3, 2), "accepted": L,
-                               "accepted_tok_per_s": round(L / (ms * 1e-3), 1),
-                               "hbm_frac": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    del lin, r3
-
-    r4 = synth.fused_spec()
-    fu = runner.FusedSpecStep(r4)
-    ms = timed(fu.run, iters, warm, stream)
-    torch.cuda.synchronize()
-    b = r4["V"] * r4["d"] * 2 + 2 * r4["Hkv"] * r4["cap"] * r4["dh"] * 2
-    res["fused_spec_step"] = {"us": round(ms * 1e3, 2), "accepted": int(fu.accepted.item()),
-                              "cert_accepted": int(fu.cert_L.item()),
-                              "hbm_frac": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    ms_attn = timed(lambda: fu.attn(fu.t["q"], fu.t["k_cache"], fu.t["v_cache"]), iters, warm,
-                    stream)
-    res["fused_spec_step"]["attn_us"] = round(ms_attn * 1e3, 2)
-    del fu, r4
+        acc, cert = int(fu.accepted.item()), int(fu.cert_L.item())
+        ms = graph_ms(fu.run, S, max(1, iters // S), max(1, warm // S), stream)
+        torch.cuda.synchronize()
+        assert int(fu.accepted.item()) == acc and int(fu.cert_L.item()) == cert
+        b = r4["V"] * r4["d"] * 2 + 2 * r4["Hkv"] * r4["cap"] * r4["dh"] * 2
+        ms_attn = timed(lambda: fu.attn(fu.t["q"], fu.t["k_cache"], fu.t["v_cache"]), iters,
+                        warm, stream)
+        res["fused_spec_step"] = {"us": round(ms * 1e3, 2), "accepted": acc,
+                                  "cert_accepted": cert,
+                                  "hbm_frac": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "attn_us": round(ms_attn * 1e3, 2), "bytes": b}
+        del fu
     return res
 
 

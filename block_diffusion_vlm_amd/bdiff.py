@@ -20,7 +20,7 @@ BD_OK, BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_ALIGN, BD_E_WORKSPACE, BD_E_DEVIC
 BD_F32, BD_BF16 = 0, 1
 BD_MASK_BIDIR, BD_MASK_CAUSAL, BD_MASK_SPEC_FUSED = 0, 1, 2
 
-# Every symbol include/bdiff.h declares.
+# Every symbol include/bdiff.h and include/bdiff_probe.h declare.
 EXPORTS = (
     "bd_status_str", "bd_device_check", "bd_make_intra_mask",
     "bd_block_attn_ws_bytes", "bd_block_attn", "bd_block_attn_paged", "bd_block_attn_fp8kv",
@@ -32,6 +32,7 @@ EXPORTS = (
     "bd_commit", "bd_spec_accept", "bd_cert_scan",
     "bd_dualstream_attn", "bd_dualstream_attn_seg", "bd_dualstream_attn_fwd",
     "bd_dualstream_attn_bwd_ws_bytes", "bd_dualstream_attn_bwd",
+    "bd_probe_stream_read",
 )
 
 
@@ -80,6 +81,7 @@ _SIGS = {
     "bd_dualstream_attn_bwd_ws_bytes": ([_I, _I, _I], _SZ),
     "bd_dualstream_attn_bwd": ([_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _I, _I, _F,
                                 _P, _P, _P, _P, _SZ, _P], _I),
+    "bd_probe_stream_read": ([_P, _SZ, _I, _P, _P], _I),
 }
 
 
@@ -302,3 +304,10 @@ def bd_dualstream_attn_bwd(dt, q, k, v, out, d_out, lse, n_vis, n_txt, block, se
                                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws_bytes,
                                       _stream(stream))
     return _ret("bd_dualstream_attn_bwd", st, check)
+
+
+def bd_probe_stream_read(src, n_bytes, grid, sink, stream=None, check=True) -> int:
+    """Measurement reference (include/bdiff_probe.h): one streaming read of
+    n_bytes of src, XOR-folded into the uint32 at sink."""
+    st = lib().bd_probe_stream_read(_ptr(src), n_bytes, grid, _ptr(sink), _stream(stream))
+    return _ret("bd_probe_stream_read", st, check)

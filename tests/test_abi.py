@@ -11,13 +11,13 @@ import pytest
 import oracle
 from block_diffusion_vlm_amd import bdiff as bd
 
-HEADER = Path(__file__).resolve().parents[1] / "include" / "bdiff.h"
+HEADERS = sorted((Path(__file__).resolve().parents[1] / "include").glob("*.h"))
 FAKE = 0x10000          # a 16-byte-aligned non-null address; never dereferenced
 MISALIGNED = 0x10008
 
 
 def declared_functions():
-    text = HEADER.read_text()
+    text = "\n".join(h.read_text() for h in HEADERS)
     return sorted(set(re.findall(r"^\s*(?:const char\*|bd_status|size_t)\s+(bd_\w+)\s*\(",
                                  text, re.M)))
 
@@ -410,3 +410,15 @@ def test_lmhead_noalloc_validation():
         assert f(dt=bd.BD_F32, d=16, V=65536, B=64) == bd.BD_E_DEVICE
     assert bd.bd_lmhead_conf_ws_bytes(16, 2048, 2 ** 30 + 1) == 0
     assert f(V=2 ** 30 + 1) == bd.BD_E_SHAPE
+
+
+def test_probe_stream_read_validation():
+    f = lambda **kw: bd.bd_probe_stream_read(**{**dict(  # noqa: E731
+        src=FAKE, n_bytes=1 << 20, grid=1024, sink=FAKE, stream=0, check=False), **kw})
+    assert f(src=None) == bd.BD_E_NULL
+    assert f(sink=None) == bd.BD_E_NULL
+    assert f(n_bytes=0) == bd.BD_E_SHAPE
+    assert f(n_bytes=24) == bd.BD_E_SHAPE
+    assert f(grid=0) == bd.BD_E_SHAPE
+    assert f(grid=65537) == bd.BD_E_SHAPE
+    assert f(src=MISALIGNED) == bd.BD_E_ALIGN
