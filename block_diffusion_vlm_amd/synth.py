@@ -23,7 +23,7 @@ from __future__ import annotations
 import numpy as np
 
 BASE_SEED = 20261203
-N_CONFIGS = 9
+N_CONFIGS = 10
 
 
 # ---------------------------------------------------------------------------
@@ -31,8 +31,9 @@ N_CONFIGS = 9
 # ---------------------------------------------------------------------------
 
 def config_rng(cfg: int, seed: int | None = None) -> np.random.Generator:
-    """PCG64 stream for workload ``cfg`` (1..9): child ``cfg-1`` of
-    SeedSequence(seed or BASE_SEED)."""
+    """PCG64 stream for workload ``cfg`` (1..10): child ``cfg-1`` of
+    SeedSequence(seed or BASE_SEED) (a child's stream does not depend on how
+    many children are spawned)."""
     ss = np.random.SeedSequence(BASE_SEED if seed is None else seed)
     return np.random.Generator(np.random.PCG64(ss.spawn(N_CONFIGS)[cfg - 1]))
 
@@ -348,6 +349,30 @@ def qwen_decode_fp8(seed: int | None = None, B=16, n_vis=1024, n_prompt=256, Hq=
     }
 
 
+def _plant_trajectory(rng, W, row, w_scale, B, S, T, V, sigma_w, guard):
+    """Hidden rows of S denoising steps of one block (position 0 is the AR
+    seed): each masked position i gets a commit step c_i in [0, T), the
+    positions 1..B-1 being split in random order into T non-empty groups;
+    from step c_i on, row i is planted on its final token with top
+    probability in [0.92, 0.999], before it on a fresh uniform token with top
+    probability in [0.02, 0.88].  Returns (final tokens, c, h [S][B][d])."""
+    d = W.shape[1]
+    final = rng.integers(0, V, B)
+    order = rng.permutation(np.arange(1, B))
+    cuts = np.sort(rng.choice(np.arange(1, B - 1), T - 1, replace=False))
+    c = np.zeros(B, np.int64)
+    for g, part in enumerate(np.split(order, cuts)):
+        c[part] = g
+    h = np.empty((S, B, d), np.uint16)
+    for s in range(S):
+        late = c <= s
+        tgt = np.where(late, final, rng.integers(0, V, B))
+        conf = np.where(late, rng.uniform(0.92, 0.999, B), rng.uniform(0.02, 0.88, B))
+        h[s], _ = planted_bits(rng, W, tgt, conf, sigma_w, row=row, guard=guard,
+                               w_scale=w_scale, redraw_conf=_band_redraw(late))
+    return final, c, h
+
+
 def qwen_block_loop(seed: int | None = None, B=16, S=16, T=8, n_vis=1024, n_prompt=256,
                     Hq=16, Hkv=2, dh=128, d=2048, V=151936, sigma_w=0.02, fp8=False,
                     guard=None) -> dict:
@@ -374,19 +399,7 @@ def qwen_block_loop(seed: int | None = None, B=16, S=16, T=8, n_vis=1024, n_prom
     else:
         W = normal_bf16(rng, (V, d), std=sigma_w)
         w_scale, row = None, None
-    final = rng.integers(0, V, B)
-    order = rng.permutation(np.arange(1, B))
-    cuts = np.sort(rng.choice(np.arange(1, B - 1), T - 1, replace=False))
-    c = np.zeros(B, np.int64)
-    for g, part in enumerate(np.split(order, cuts)):
-        c[part] = g
-    h = np.empty((S, B, d), np.uint16)
-    for s in range(S):
-        late = c <= s
-        tgt = np.where(late, final, rng.integers(0, V, B))
-        conf = np.where(late, rng.uniform(0.92, 0.999, B), rng.uniform(0.02, 0.88, B))
-        h[s], _ = planted_bits(rng, W, tgt, conf, sigma_w, row=row, guard=guard,
-                               w_scale=w_scale, redraw_conf=_band_redraw(late))
+    final, c, h = _plant_trajectory(rng, W, row, w_scale, B, S, T, V, sigma_w, guard)
     masked = np.ones(B, np.uint8)
     masked[0] = 0
     tokens = np.zeros(B, np.int32)
@@ -403,6 +416,53 @@ def qwen_block_loop(seed: int | None = None, B=16, S=16, T=8, n_vis=1024, n_prom
     if fp8:
         r["w_scale"] = w_scale
     return r
+
+
+def qwen_decode_blocks(seed: int | None = None, n_blocks=4, B=16, S=15, T=8, n_vis=1024,
+                       n_prompt=256, Hq=16, Hkv=2, dh=128, d=2048, V=151936, sigma_w=0.02,
+                       guard=None) -> dict:
+    """Several consecutive blocks of the Qwen-shaped decode, bf16, each
+    started by an AR seed step and appended to the KV cache before the next
+    (causal-context decoding, Fast-dVLM overview §2.2.2; blocks in order,
+    §1.2).  The cache holds the n_vis visual + n_prompt prompt rows (P0);
+    rows from P0 on are zero and get each block's own K/V rows ([B][Hkv][dh],
+    K ~ N(0,1), V truncated at 4) in turn; cap = P0 + n_blocks B.  Per block:
+    a seed query [Hq][dh] and a seed hidden row planted on a uniform token
+    with top probability in [0.92, 0.999] (the AR prediction of the block's
+    first token), and S >= T denoising steps planted as in qwen_block_loop
+    (every masked position committed by threshold within T steps; S = B - 1
+    steps always suffice, as every step commits at least one position).
+    ``guard`` as in qwen_decode, applied to every planted row."""
+    rng = config_rng(10, seed)
+    P0 = n_vis + n_prompt
+    cap = P0 + n_blocks * B
+    W = normal_bf16(rng, (V, d), std=sigma_w)
+    k_cache = np.zeros((Hkv, cap, dh), np.uint16)
+    v_cache = np.zeros((Hkv, cap, dh), np.uint16)
+    k_cache[:, :P0] = normal_bf16(rng, (Hkv * P0, dh)).reshape(Hkv, P0, dh)
+    v_cache[:, :P0] = normal_bf16(rng, (Hkv * P0, dh), trunc=4.0).reshape(Hkv, P0, dh)
+    seed_t = rng.integers(0, V, n_blocks)
+    seed_c = rng.uniform(0.92, 0.999, n_blocks)
+    h_seed, _ = planted_bits(rng, W, seed_t, seed_c, sigma_w, guard=guard,
+                             redraw_conf=_uniform_redraw(0.92, 0.999))
+    h_steps = np.empty((n_blocks, S, B, d), np.uint16)
+    final = np.empty((n_blocks, B), np.int32)
+    commit_step = np.empty((n_blocks, B), np.int64)
+    for b in range(n_blocks):
+        f, c, h = _plant_trajectory(rng, W, None, None, B, S, T, V, sigma_w, guard)
+        final[b], commit_step[b], h_steps[b] = f, c, h
+    return {
+        "dtype": "bf16", "n_blocks": n_blocks, "B": B, "S": S, "T": T, "P0": P0, "cap": cap,
+        "n_vis": n_vis, "n_prompt": n_prompt, "Hq": Hq, "Hkv": Hkv, "dh": dh, "d": d, "V": V,
+        "tau": 0.9, "W": W, "k_cache": k_cache, "v_cache": v_cache,
+        "k_blk": normal_bf16(rng, (n_blocks * B * Hkv, dh)).reshape(n_blocks, B, Hkv, dh),
+        "v_blk": normal_bf16(rng, (n_blocks * B * Hkv, dh), trunc=4.0).reshape(
+            n_blocks, B, Hkv, dh),
+        "q_seed": normal_bf16(rng, (n_blocks * Hq, dh)).reshape(n_blocks, Hq, dh),
+        "h_seed": h_seed, "seed_targets": seed_t.astype(np.int32),
+        "q_steps": normal_bf16(rng, (n_blocks * S * B * Hq, dh)).reshape(n_blocks, S, B, Hq, dh),
+        "h_steps": h_steps, "final_tokens": final, "commit_step": commit_step,
+    }
 
 
 def linear_spec(seed: int | None = None, B=32, n_vis=1024, n_prompt=256, Hq=16, Hkv=2,

@@ -86,7 +86,7 @@ __all__ = [
     "dualstream_lse", "dualstream_attn_bwd",
     "lm_logits", "conf_argmax", "lmhead_conf", "E4M3_MAX", "e4m3_decode", "e4m3_encode",
     "quant_fp8_rows", "lm_logits_fp8", "lmhead_conf_fp8", "commit", "spec_accept", "cert_scan",
-    "decode_step", "block_loop", "linear_spec_step", "fused_spec_step",
+    "decode_step", "block_loop", "decode_blocks", "linear_spec_step", "fused_spec_step",
 ]
 
 
@@ -599,6 +599,53 @@ def block_loop(q_steps, k_cache, v_cache, P, h_steps, W, masked, tokens, tau, ki
         argmax.append(o["argmax"])
     return {"masked": masked, "tokens": tokens, "n_steps": len(conf), "n_committed": n_comm,
             "attn": attn, "conf": conf, "argmax": argmax}
+
+
+def decode_blocks(q_seed, h_seed, q_steps, h_steps, k_blk, v_blk, k_cache, v_cache, P0, W, tau,
+                  w_scale=None):
+    """Several blocks decoded in order, each after the ones before it has
+    joined the KV cache.  [OV §1.2: blocks are generated one after another,
+    each denoised in parallel over several steps, with the KV cache of the
+    earlier ones reused; OV §2.2.2: causal-context decoding, the first token
+    of a block comes from the AR (causal) prediction]
+
+    The KV length starts at P0 (the prompt prefix).  For block b:
+      1. its own K/V rows k_blk[b], v_blk[b] ([B][Hkv][dh], the rows the
+         model's projections give for the block) are written into the cache
+         rows kv_len .. kv_len + B - 1;
+      2. AR seed: the query q_seed[b] ([Hq][dh]) attends the cached prefix
+         [0, kv_len) (the block's own rows are not visible to it), and the
+         argmax of the LM head on h_seed[b] ([d]) becomes the block's first
+         token; positions 1 .. B-1 start masked;
+      3. the block loop (block_loop) over q_steps[b], h_steps[b] with the
+         prefix length kv_len and the block's rows as its keys;
+      4. kv_len += B: the block becomes part of the prefix.
+    Caches are bfloat16 bit patterns ([Hkv][cap][dh]); copies are updated
+    and returned.  Returns the final cache, kv_len, and per block the seed's
+    attention output, confidence and token and the block loop's results."""
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    nb = len(h_steps)
+    B = np.asarray(k_blk).shape[1]
+    kv = int(P0)
+    blocks = []
+    for b in range(nb):
+        kc[:, kv:kv + B, :] = np.transpose(np.asarray(k_blk[b]), (1, 0, 2))
+        vc[:, kv:kv + B, :] = np.transpose(np.asarray(v_blk[b]), (1, 0, 2))
+        seed_attn = block_attn(np.asarray(q_seed[b])[None], kc, vc, kv,
+                               np.zeros((1, 1), dtype=bool))[0]
+        h1 = np.asarray(h_seed[b])[None]
+        sc, sa = lmhead_conf(h1, W) if w_scale is None else lmhead_conf_fp8(h1, W, w_scale)
+        tokens = np.zeros(B, dtype=np.int64)
+        tokens[0] = sa[0]
+        masked = np.ones(B, dtype=np.uint8)
+        masked[0] = 0
+        o = block_loop(q_steps[b], kc, vc, kv, h_steps[b], W, masked, tokens, tau,
+                       w_scale=w_scale)
+        o.update(seed_attn=seed_attn, seed_conf=float(sc[0]), seed_token=int(sa[0]), P=kv)
+        blocks.append(o)
+        kv += B
+    return {"k_cache": kc, "v_cache": vc, "kv_len": kv, "blocks": blocks}
 
 
 def linear_spec_step(q_draft, kc_draft, vc_draft, q_verify, kc_verify, vc_verify, P,
