@@ -29,6 +29,7 @@ EXPORTS = (
     "bd_lmhead_conf_noalloc",
     "bd_lmhead_conf_fp8_ws_bytes", "bd_lmhead_conf_fp8", "bd_lmhead_conf_commit_fp8",
     "bd_quant_fp8_rows", "bd_block_loop_ws_bytes", "bd_block_loop",
+    "bd_decode_blocks_ws_bytes", "bd_decode_blocks",
     "bd_commit", "bd_spec_accept", "bd_cert_scan",
     "bd_dualstream_attn", "bd_dualstream_attn_seg", "bd_dualstream_attn_fwd",
     "bd_dualstream_attn_bwd_ws_bytes", "bd_dualstream_attn_bwd",
@@ -69,6 +70,10 @@ _SIGS = {
     "bd_block_loop_ws_bytes": ([_I, _I, _I, _I, _I, _I, _I, _I], _SZ),
     "bd_block_loop": ([_I, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _F, _P, _P, _P, _I, _I, _F,
                        _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
+    "bd_decode_blocks_ws_bytes": ([_I] * 9, _SZ),
+    "bd_decode_blocks": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I,
+                          _I, _F, _P, _P, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                          _SZ, _P], _I),
     "bd_block_attn_fp8kv": ([_P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _F, _P, _P, _SZ,
                              _P], _I),
     "bd_kv_quant_fp8": ([_P, _I, _I, _I, _P, _P, _I, _I, _P], _I),
@@ -223,6 +228,25 @@ def bd_block_loop(dt, q_steps, k_cache, v_cache, P, cap, intra_mask, B, Hq, Hkv,
                              _ptr(attn_out), _ptr(conf), _ptr(argmax), _ptr(n_committed),
                              _ptr(n_steps), _ptr(ws), ws_bytes, _stream(stream))
     return _ret("bd_block_loop", st, check)
+
+
+def bd_decode_blocks_ws_bytes(P_max, n_blocks, B, Hq, Hkv, dh, d, V, w_fp8) -> int:
+    return int(lib().bd_decode_blocks_ws_bytes(P_max, n_blocks, B, Hq, Hkv, dh, d, V,
+                                               int(bool(w_fp8))))
+
+
+def bd_decode_blocks(q_seed, h_seed, q_steps, h_steps, k_blk, v_blk, k_cache, v_cache, cap,
+                     kv_len, P_max, intra_mask, n_blocks, B, max_steps, Hq, Hkv, dh, scale, W,
+                     w_scale, d, V, tau, tokens, masked, n_steps, n_committed, seed_attn,
+                     seed_conf, attn_out, conf, argmax, ws, ws_bytes, stream=None,
+                     check=True) -> int:
+    st = lib().bd_decode_blocks(
+        _ptr(q_seed), _ptr(h_seed), _ptr(q_steps), _ptr(h_steps), _ptr(k_blk), _ptr(v_blk),
+        _ptr(k_cache), _ptr(v_cache), cap, _ptr(kv_len), P_max, _ptr(intra_mask), n_blocks, B,
+        max_steps, Hq, Hkv, dh, scale, _ptr(W), _ptr(w_scale), d, V, tau, _ptr(tokens),
+        _ptr(masked), _ptr(n_steps), _ptr(n_committed), _ptr(seed_attn), _ptr(seed_conf),
+        _ptr(attn_out), _ptr(conf), _ptr(argmax), _ptr(ws), ws_bytes, _stream(stream))
+    return _ret("bd_decode_blocks", st, check)
 
 
 def bd_commit(conf, argmax, B, tau, masked, tokens, n_committed, stream=None, check=True) -> int:

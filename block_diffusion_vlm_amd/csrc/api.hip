@@ -375,6 +375,136 @@ bd_status bd_block_loop(bd_dtype dt, const void* q_steps, const void* k_cache,
     return launch_status(e);
 }
 
+namespace {
+
+struct BlocksWs {
+    size_t mask_off, attn_off, lm_off, total;
+};
+
+// Gate word at 0, the all-zero intra-block mask of the seed queries at 8,
+// then one attention workspace (large enough for the last block's steps and
+// every seed) and one LM-head workspace (B rows; the seed uses one).
+BlocksWs blocks_ws(int32_t P_max, int32_t n_blocks, int32_t B, int32_t Hq, int32_t Hkv,
+                   int32_t dh, int32_t d, int32_t V, bool fp8) {
+    BlocksWs L;
+    L.mask_off = 8;
+    L.attn_off = 256;
+    const int32_t P_last = P_max + (n_blocks - 1) * B;
+    const size_t a1 = bd::block_attn_ws_bytes(P_last, B, Hq, Hkv, dh);
+    const size_t a2 = bd::block_attn_ws_bytes(P_last, 1, Hq, Hkv, dh);
+    L.lm_off = L.attn_off + al256(a1 > a2 ? a1 : a2);
+    const size_t l1 = fp8 ? bd::lmhead_fp8_ws_bytes(B, d, V) : bd::lmhead_ws_bytes(B, d, V);
+    const size_t l2 = fp8 ? bd::lmhead_fp8_ws_bytes(1, d, V) : bd::lmhead_ws_bytes(1, d, V);
+    L.total = L.lm_off + al256(l1 > l2 ? l1 : l2);
+    return L;
+}
+
+bool blocks_shape_ok(int32_t P_max, int32_t cap, int32_t n_blocks, int32_t B, int32_t Hq,
+                     int32_t Hkv, int32_t dh, int32_t d, int32_t V) {
+    if (n_blocks < 1 || B < 1 || B > 64 || P_max < 0 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0)
+        return false;
+    if (dh != 128 || d < 128 || d > 16384 || d % 128 != 0 || !vocab_ok(V)) return false;
+    const int64_t end = (int64_t)P_max + (int64_t)n_blocks * B;
+    return end <= cap && end <= 65536;
+}
+
+}  // namespace
+
+size_t bd_decode_blocks_ws_bytes(int32_t P_max, int32_t n_blocks, int32_t B, int32_t Hq,
+                                 int32_t Hkv, int32_t dh, int32_t d, int32_t V, int32_t w_fp8) {
+    if (!blocks_shape_ok(P_max, 1 << 30, n_blocks, B, Hq, Hkv, dh, d, V)) return 0;
+    return blocks_ws(P_max, n_blocks, B, Hq, Hkv, dh, d, V, w_fp8 != 0).total;
+}
+
+bd_status bd_decode_blocks(const void* q_seed, const void* h_seed, const void* q_steps,
+                           const void* h_steps, const void* k_blk, const void* v_blk,
+                           void* k_cache, void* v_cache, int32_t cap, int32_t* kv_len,
+                           int32_t P_max, const uint64_t* intra_mask, int32_t n_blocks, int32_t B,
+                           int32_t max_steps, int32_t Hq, int32_t Hkv, int32_t dh, float scale,
+                           const void* W, const float* w_scale, int32_t d, int32_t V, float tau,
+                           int32_t* tokens, uint8_t* masked, int32_t* n_steps,
+                           int32_t* n_committed, void* seed_attn, float* seed_conf,
+                           void* attn_out, float* conf, int32_t* argmax, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+    if (!q_seed || !h_seed || !q_steps || !h_steps || !k_blk || !v_blk || !k_cache ||
+        !v_cache || !kv_len || !intra_mask || !W || !tokens || !masked || !n_steps ||
+        !n_committed || !seed_attn || !seed_conf || !attn_out || !conf || !argmax)
+        return BD_E_NULL;
+    const bool fp8 = w_scale != nullptr;
+    if (!blocks_shape_ok(P_max, cap, n_blocks, B, Hq, Hkv, dh, d, V)) return BD_E_SHAPE;
+    if (max_steps < 1 || max_steps > 1024) return BD_E_SHAPE;
+    if (!(tau == tau)) return BD_E_SHAPE;
+    if (!(scale >= 0.f) || isinf(scale)) return BD_E_SHAPE;
+    if (!aligned16(q_seed) || !aligned16(h_seed) || !aligned16(q_steps) || !aligned16(h_steps) ||
+        !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        !aligned16(W) || !aligned16(seed_attn) || !aligned16(attn_out) ||
+        (fp8 && !aligned16(w_scale)) || (reinterpret_cast<uintptr_t>(kv_len) & 3u))
+        return BD_E_ALIGN;
+    const BlocksWs L = blocks_ws(P_max, n_blocks, B, Hq, Hkv, dh, d, V, fp8);
+    if (!ws || ws_bytes < L.total) return BD_E_WORKSPACE;
+    if (!aligned16(ws)) return BD_E_ALIGN;
+
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    int32_t* gate = reinterpret_cast<int32_t*>(base);
+    uint64_t* zero_mask = reinterpret_cast<uint64_t*>(base + L.mask_off);
+    void* attn_ws = base + L.attn_off;
+    void* lm_ws = base + L.lm_off;
+    const float sc = default_scale(scale, dh);
+    const size_t row_q = size_t(Hq) * dh * 2;             // one query row, bf16
+    const size_t row_h = size_t(d) * 2;
+    const size_t blk_kv = size_t(B) * Hkv * dh * 2;
+    const size_t step_q = size_t(B) * row_q, step_h = size_t(B) * row_h;
+    auto lm = [&](const void* h, int rows, const bd::Finish& f) {
+        return fp8 ? bd::launch_lmhead_fp8(h, static_cast<const uint8_t*>(W), w_scale, rows, d,
+                                           V, f, lm_ws, stream)
+                   : bd::launch_lmhead_bf16(h, W, rows, d, V, f, lm_ws, stream);
+    };
+    hipError_t e = hipSuccess;
+    for (int b = 0; b < n_blocks && e == hipSuccess; ++b) {
+        const int P_b = P_max + b * B;                    // bound of this block's prefix
+        int32_t* tok_b = tokens + size_t(b) * B;
+        uint8_t* msk_b = masked + size_t(b) * B;
+        int32_t* ncom_b = n_committed + size_t(b) * max_steps;
+        // 1. the previous block joins the prefix; this block's rows go in
+        e = bd::launch_block_begin(static_cast<const uint8_t*>(k_blk) + b * blk_kv,
+                                   static_cast<const uint8_t*>(v_blk) + b * blk_kv, k_cache,
+                                   v_cache, cap, Hkv, B, kv_len, b > 0 ? B : 0, P_b, true,
+                                   n_steps + b, ncom_b, max_steps, zero_mask, stream);
+        if (e != hipSuccess) break;
+        // 2. AR seed: one query over the prefix, the LM head's argmax starts the block
+        e = bd::launch_block_attn_bf16(static_cast<const uint8_t*>(q_seed) + b * row_q, k_cache,
+                                       v_cache, P_b, cap, zero_mask, 1, Hq, Hkv, sc,
+                                       static_cast<uint8_t*>(seed_attn) + b * row_q, attn_ws,
+                                       stream, nullptr, kv_len);
+        if (e != hipSuccess) break;
+        bd::Finish fs{seed_conf + b, tok_b, false, 0.f, nullptr, nullptr, nullptr};
+        fs.gate_out = gate;
+        fs.seed_B = B;
+        fs.seed_masked = msk_b;
+        e = lm(static_cast<const uint8_t*>(h_seed) + b * row_h, 1, fs);
+        // 3. denoising steps, each gated on the positions still masked
+        for (int s = 0; s < max_steps && e == hipSuccess; ++s) {
+            const size_t bs = size_t(b) * max_steps + s;
+            e = bd::launch_block_attn_bf16(static_cast<const uint8_t*>(q_steps) + bs * step_q,
+                                           k_cache, v_cache, P_b, cap, intra_mask, B, Hq, Hkv,
+                                           sc, static_cast<uint8_t*>(attn_out) + bs * step_q,
+                                           attn_ws, stream, gate, kv_len);
+            if (e != hipSuccess) break;
+            bd::Finish f{conf + bs * B, argmax + bs * B, true, tau, msk_b, tok_b, ncom_b + s};
+            f.gate = gate;
+            f.gate_out = gate;
+            f.steps = n_steps + b;
+            e = lm(static_cast<const uint8_t*>(h_steps) + bs * step_h, B, f);
+        }
+    }
+    // 4. the last block joins the prefix
+    if (e == hipSuccess)
+        e = bd::launch_block_begin(nullptr, nullptr, k_cache, v_cache, cap, Hkv, B, kv_len, B,
+                                   P_max + n_blocks * B, false, nullptr, nullptr, 0, nullptr,
+                                   stream);
+    return launch_status(e);
+}
+
 bd_status bd_commit(const float* conf, const int32_t* argmax, int32_t B, float tau,
                     uint8_t* masked, int32_t* tokens, int32_t* n_committed, hipStream_t stream) {
     if (!conf || !argmax || !masked || !tokens || !n_committed) return BD_E_NULL;

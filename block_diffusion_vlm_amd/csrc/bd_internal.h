@@ -80,6 +80,15 @@ hipError_t launch_cert_scan(const float* conf, const int32_t* atok, const int32_
 // counter and the per-step commit counts zeroed.
 hipError_t launch_loop_init(const uint8_t* masked, int B, int32_t* gate, int32_t* steps,
                             int32_t* n_committed, int S, hipStream_t st);
+// Start of a block of the multi-block loop (one workgroup): kv_len advances
+// by `advance` (clamped to [0, len_max]); with `append`, the block's K/V rows
+// k_new, v_new ([B][Hkv][128] bf16) are written into cache rows kv_len ..
+// kv_len + B - 1; steps and n_committed[0 .. S) (if given) are zeroed and
+// *zero_word (if given) cleared.
+hipError_t launch_block_begin(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              int cap, int Hkv, int B, int32_t* kv_len, int advance, int len_max,
+                              bool append, int32_t* steps, int32_t* n_committed, int S,
+                              uint64_t* zero_word, hipStream_t st);
 
 // LM head.  The merge of the per-workgroup partials writes conf/argmax and,
 // when `commit` is set, also applies the threshold commit to the block.
@@ -97,6 +106,13 @@ struct Finish {
     const int32_t* gate = nullptr;
     int32_t* gate_out = nullptr;
     int32_t* steps = nullptr;
+    // AR seed of a block (multi-block loop; 0 otherwise): the merge of a
+    // one-row LM head writes the seed token through `argmax` (pointing at the
+    // block's tokens: position 0), token 0 at positions 1 .. seed_B - 1, marks
+    // those masked and position 0 committed in seed_masked, and sets
+    // *gate_out to seed_B - 1.
+    int seed_B = 0;
+    uint8_t* seed_masked = nullptr;
 };
 int lmhead_grid(int B, int d, int V);           // workgroups used for a shape
 size_t lmhead_ws_bytes(int B, int d, int V);              // either dtype
@@ -120,12 +136,14 @@ hipError_t launch_lmhead_fp8(const void* h, const uint8_t* W, const float* w_sca
 hipError_t launch_quant_fp8_rows(const void* x, int R, int d, uint8_t* q, float* scale,
                                  hipStream_t st);
 
-// Block attention
+// Block attention.  P_dev (nullable): a device-side prefix length, at most P,
+// read by the kernels in place of P (the grid and workspace are sized for P).
 size_t block_attn_ws_bytes(int P, int Bq, int Hq, int Hkv, int dh);
 hipError_t launch_block_attn_bf16(const void* q, const void* kc, const void* vc, int P, int cap,
                                   const uint64_t* mask, int Bq, int Hq, int Hkv, float scale,
                                   void* out, void* ws, hipStream_t st,
-                                  const int32_t* gate = nullptr);
+                                  const int32_t* gate = nullptr,
+                                  const int32_t* P_dev = nullptr);
 // Paged cache: pools [n_pages][Hkv][page_size][128], logical keys from key_lo.
 hipError_t launch_block_attn_paged(const void* q, const void* k_pool, const void* v_pool,
                                    const int32_t* page_table, int page_size, int n_pages, int P,

@@ -87,11 +87,15 @@ struct Fp8Stage {
 template <bool PAGED, bool FP8 = false>
 __global__ __launch_bounds__(256) void block_attn_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ vc, int P, int cap, const uint64_t* __restrict__ mask, int Bq,
-    int Hq, int Hkv, float scale_log2, void* __restrict__ ws, int nsplit, int kt,
-    const int32_t* __restrict__ gate, Paging pg, Fp8Kv f8) {
+    const uint16_t* __restrict__ vc, int P, const int32_t* __restrict__ P_dev, int cap,
+    const uint64_t* __restrict__ mask, int Bq, int Hq, int Hkv, float scale_log2,
+    void* __restrict__ ws, int nsplit, int kt, const int32_t* __restrict__ gate, Paging pg,
+    Fp8Kv f8) {
     static_assert(!(PAGED && FP8), "the FP8 cache is contiguous");
     if (gated_off(gate)) return;
+    // A device-side prefix length (the multi-block loop's kv_len) replaces P;
+    // it never exceeds the host bound the grid and workspace were sized for.
+    if (P_dev != nullptr) P = max(0, min(*P_dev, P));
     __shared__ __align__(16) uint16_t kbuf[2][kTile];
     __shared__ __align__(16) uint16_t vbuf[2][kTile];
     const int split = blockIdx.x;
@@ -106,6 +110,7 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
     const int key_lo = PAGED ? pg.key_lo : 0;
     const int t_beg = split * kt;
     const int ntiles = (Nk - key_lo + kBN - 1) / kBN;
+    if (t_beg >= ntiles) return;                    // past the keys of a shorter prefix
     const int t_end = t_beg + kt < ntiles ? t_beg + kt : ntiles;
     const unsigned koff = dma_lane_offset<false>(kDh);
     const unsigned voff = dma_lane_offset<true>(kDh);
@@ -320,8 +325,15 @@ constexpr int kCombineBatch = 32;
 
 __global__ __launch_bounds__(kCombineThreads) void block_attn_combine_kernel(
     const void* __restrict__ ws, int Bq, int Hq, int Hkv, int nsplit, uint16_t* __restrict__ out,
-    const int32_t* __restrict__ gate) {
+    const int32_t* __restrict__ gate, int P, const int32_t* __restrict__ P_dev, int kt) {
     if (gated_off(gate)) return;
+    // With a device-side prefix length only the splits that hold keys were
+    // written; nsplit stays the row stride of the partials.
+    int nsplit_used = nsplit;
+    if (P_dev != nullptr) {
+        const int Pd = max(0, min(*P_dev, P));
+        nsplit_used = ((Pd + Bq + kBN - 1) / kBN + kt - 1) / kt;
+    }
     const int rg = blockIdx.x;                      // global row = g * R + r
     const int group = Hq / Hkv;
     const int R = Bq * group;
@@ -337,15 +349,16 @@ __global__ __launch_bounds__(kCombineThreads) void block_attn_combine_kernel(
     const float* o = pt.o + size_t(rg) * nsplit * kDh + t;
 
     float M = -INFINITY, L = 0.f, acc = 0.f;
-    for (int s0 = 0; s0 < nsplit; s0 += kCombineBatch) {
+    for (int s0 = 0; s0 < nsplit_used; s0 += kCombineBatch) {
         // Past the last split the last one is read again and dropped.
-        const int su = min(s0 + u_lane, nsplit - 1);
+        const int su = min(s0 + u_lane, nsplit_used - 1);
         float mu = m[su];
         const float lu = l[su];
         float ov[kCombineBatch];
 #pragma unroll
-        for (int u = 0; u < kCombineBatch; ++u) ov[u] = o[size_t(min(s0 + u, nsplit - 1)) * kDh];
-        if (s0 + u_lane >= nsplit) mu = -INFINITY;
+        for (int u = 0; u < kCombineBatch; ++u)
+            ov[u] = o[size_t(min(s0 + u, nsplit_used - 1)) * kDh];
+        if (s0 + u_lane >= nsplit_used) mu = -INFINITY;
         float mb = mu;                              // batch maximum (lanes 32..63 mirror 0..31)
         for (int off = kCombineBatch / 2; off > 0; off >>= 1) mb = fmaxf(mb, __shfl_xor(mb, off));
         // No branch here, so that the output loads stay next to the others.
@@ -451,7 +464,8 @@ int num_splits(int P, int Bq, int Hq, int Hkv) {
 hipError_t launch_block_attn_any(const void* q, const void* kc, const void* vc, int P, int cap,
                                  const uint64_t* mask, int Bq, int Hq, int Hkv, float scale,
                                  void* out, void* ws, hipStream_t st, const int32_t* gate,
-                                 Paging pg, const Fp8Kv* f8 = nullptr) {
+                                 Paging pg, const Fp8Kv* f8 = nullptr,
+                                 const int32_t* P_dev = nullptr) {
     // Splits over the visited keys [key_lo, P + Bq).
     const int kt = tiles_per_split(P - pg.key_lo, Bq, Hq, Hkv);
     const int nsplit = num_splits(P - pg.key_lo, Bq, Hq, Hkv);
@@ -460,22 +474,22 @@ hipError_t launch_block_attn_any(const void* q, const void* kc, const void* vc, 
     if (f8 != nullptr)
         hipLaunchKernelGGL((block_attn_split_kernel<false, true>), grid, dim3(256), 0, st,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
-                           static_cast<const uint16_t*>(vc), P, cap, mask, Bq, Hq, Hkv,
+                           static_cast<const uint16_t*>(vc), P, P_dev, cap, mask, Bq, Hq, Hkv,
                            scale * kLog2e, ws, nsplit, kt, gate, pg, *f8);
     else if (pg.table != nullptr)
         hipLaunchKernelGGL(block_attn_split_kernel<true>, grid, dim3(256), 0, st,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
-                           static_cast<const uint16_t*>(vc), P, cap, mask, Bq, Hq, Hkv,
+                           static_cast<const uint16_t*>(vc), P, P_dev, cap, mask, Bq, Hq, Hkv,
                            scale * kLog2e, ws, nsplit, kt, gate, pg, Fp8Kv{});
     else
         hipLaunchKernelGGL(block_attn_split_kernel<false>, grid, dim3(256), 0, st,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
-                           static_cast<const uint16_t*>(vc), P, cap, mask, Bq, Hq, Hkv,
+                           static_cast<const uint16_t*>(vc), P, P_dev, cap, mask, Bq, Hq, Hkv,
                            scale * kLog2e, ws, nsplit, kt, gate, pg, Fp8Kv{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(block_attn_combine_kernel, dim3(Bq * Hq), dim3(kCombineThreads), 0, st, ws,
-                       Bq, Hq, Hkv, nsplit, static_cast<uint16_t*>(out), gate);
+                       Bq, Hq, Hkv, nsplit, static_cast<uint16_t*>(out), gate, P, P_dev, kt);
     return hipGetLastError();
 }
 
@@ -488,9 +502,10 @@ size_t block_attn_ws_bytes(int P, int Bq, int Hq, int Hkv, int dh) {
 
 hipError_t launch_block_attn_bf16(const void* q, const void* kc, const void* vc, int P, int cap,
                                   const uint64_t* mask, int Bq, int Hq, int Hkv, float scale,
-                                  void* out, void* ws, hipStream_t st, const int32_t* gate) {
+                                  void* out, void* ws, hipStream_t st, const int32_t* gate,
+                                  const int32_t* P_dev) {
     return launch_block_attn_any(q, kc, vc, P, cap, mask, Bq, Hq, Hkv, scale, out, ws, st, gate,
-                                 Paging{nullptr, 1, 1, 0});
+                                 Paging{nullptr, 1, 1, 0}, nullptr, P_dev);
 }
 
 hipError_t launch_block_attn_fp8kv(const void* q, const uint8_t* kc, const uint8_t* vc,

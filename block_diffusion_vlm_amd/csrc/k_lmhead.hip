@@ -63,11 +63,18 @@ __device__ ArgSoft reduce_column(const WsView& w, int G, int col) {
     return st;
 }
 
-// One wave per position: merged confidence and argmax.
+// One wave per position: merged confidence and argmax.  As the AR seed of a
+// block (seed_B > 0, one position), it also starts the block: argmax points
+// at the block's tokens, so position 0 receives the seed token; positions
+// 1 .. seed_B - 1 get token 0 and are masked, and the gate of the block's
+// steps is seed_B - 1.
 __global__ __launch_bounds__(64) void lmhead_combine_kernel(const void* __restrict__ ws, int G,
                                                             int B, float* __restrict__ conf,
                                                             int32_t* __restrict__ argmax,
-                                                            const int32_t* __restrict__ gate) {
+                                                            const int32_t* __restrict__ gate,
+                                                            int seed_B,
+                                                            uint8_t* __restrict__ seed_masked,
+                                                            int32_t* __restrict__ gate_out) {
     if (gated_off(gate)) return;
     const WsView w = ws_view(const_cast<void*>(ws), G, B);
     const int col = blockIdx.x;
@@ -75,6 +82,13 @@ __global__ __launch_bounds__(64) void lmhead_combine_kernel(const void* __restri
     if (threadIdx.x == 0) {
         conf[col] = 1.0f / r.s;
         argmax[col] = r.a;
+    }
+    if (seed_B > 0) {
+        for (int j = threadIdx.x; j < seed_B; j += 64) {
+            seed_masked[j] = j != 0;
+            if (j != 0) argmax[j] = 0;
+        }
+        if (threadIdx.x == 0) *gate_out = seed_B - 1;
     }
 }
 
@@ -121,7 +135,7 @@ hipError_t launch_combine(void* ws, int G, int B, const Finish& f, hipStream_t s
                            f.gate_out, f.steps);
     else
         hipLaunchKernelGGL(lmhead_combine_kernel, dim3(B), dim3(64), 0, st, ws, G, B, f.conf,
-                           f.argmax, f.gate);
+                           f.argmax, f.gate, f.seed_B, f.seed_masked, f.gate_out);
     return hipGetLastError();
 }
 

@@ -92,6 +92,49 @@ __global__ __launch_bounds__(64) void loop_init_kernel(const uint8_t* __restrict
     }
 }
 
+// Start of a block of the multi-block loop (overview §1.2: the earlier
+// blocks stay in the KV cache; §2.2.2: the block's rows join it): one
+// workgroup; every thread reads the old length before thread 0 stores the
+// new one.
+__global__ __launch_bounds__(256) void block_begin_kernel(
+    const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new, u32x4* __restrict__ k_cache,
+    u32x4* __restrict__ v_cache, int cap, int Hkv, int B, int32_t* __restrict__ kv_len,
+    int advance, int len_max, int append, int32_t* __restrict__ steps,
+    int32_t* __restrict__ n_committed, int S, uint64_t* __restrict__ zero_word) {
+    const int len = max(0, min(*kv_len + advance, len_max));
+    if (append) {
+        // 16 pieces of 16 bytes per 128-element row; row i of head g
+        for (int p = threadIdx.x; p < B * Hkv * 16; p += blockDim.x) {
+            const int piece = p & 15;
+            const int ig = p >> 4;                  // i * Hkv + g
+            const int g = ig % Hkv;
+            const int i = ig / Hkv;
+            const size_t dst = (size_t(g) * cap + len + i) * 16 + piece;
+            k_cache[dst] = k_new[size_t(ig) * 16 + piece];
+            v_cache[dst] = v_new[size_t(ig) * 16 + piece];
+        }
+    }
+    for (int s = threadIdx.x; s < S; s += blockDim.x) n_committed[s] = 0;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        *kv_len = len;
+        if (steps != nullptr) *steps = 0;
+        if (zero_word != nullptr) *zero_word = 0;
+    }
+}
+
+hipError_t launch_block_begin(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              int cap, int Hkv, int B, int32_t* kv_len, int advance, int len_max,
+                              bool append, int32_t* steps, int32_t* n_committed, int S,
+                              uint64_t* zero_word, hipStream_t st) {
+    hipLaunchKernelGGL(block_begin_kernel, dim3(1), dim3(256), 0, st,
+                       static_cast<const u32x4*>(k_new), static_cast<const u32x4*>(v_new),
+                       static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), cap, Hkv, B,
+                       kv_len, advance, len_max, append ? 1 : 0, steps, n_committed, S,
+                       zero_word);
+    return hipGetLastError();
+}
+
 hipError_t launch_loop_init(const uint8_t* masked, int B, int32_t* gate, int32_t* steps,
                             int32_t* n_committed, int S, hipStream_t st) {
     hipLaunchKernelGGL(loop_init_kernel, dim3(1), dim3(64), 0, st, masked, B, gate, steps,

@@ -238,6 +238,60 @@ class BlockLoop:
                          self.ws, self.ws_bytes, stream)
 
 
+class DecodeBlocks:
+    """bd_decode_blocks over device buffers from synth.qwen_decode_blocks:
+    several blocks, each seeded by an AR step, denoised on the device and
+    appended to the KV cache, with a device-side kv_len.  ``reset()`` restores
+    the cache and kv_len (two device copies and one fill)."""
+
+    def __init__(self, inp: dict, device="cuda", max_steps=None, w_scale=None):
+        nb, B, S = inp["n_blocks"], inp["B"], inp["S"]
+        self.S = S if max_steps is None else max_steps
+        assert self.S <= S
+        Hq, Hkv, dh, d, V = (inp[k] for k in ("Hq", "Hkv", "dh", "d", "V"))
+        self.inp = inp
+        self.nb, self.B, self.Hq, self.Hkv, self.dh, self.d, self.V = nb, B, Hq, Hkv, dh, d, V
+        self.cap, self.P0, self.tau = inp["cap"], inp["P0"], float(inp["tau"])
+        t = {k: to_dev(inp[k], device) for k in ("q_seed", "h_seed", "k_blk", "v_blk", "W")}
+        # the steps' inputs, cut to max_steps per block (contiguous)
+        t["q_steps"] = to_dev(np.ascontiguousarray(inp["q_steps"][:, :self.S]), device)
+        t["h_steps"] = to_dev(np.ascontiguousarray(inp["h_steps"][:, :self.S]), device)
+        self.t = t
+        self.w_scale = w_scale
+        self.k0 = to_dev(inp["k_cache"], device)
+        self.v0 = to_dev(inp["v_cache"], device)
+        self.k_cache, self.v_cache = self.k0.clone(), self.v0.clone()
+        self.kv_len = torch.full((1,), self.P0, dtype=torch.int32, device=device)
+        self.mask = mask_dev(bd.BD_MASK_BIDIR, B, device)
+        self.tokens = torch.full((nb, B), -1, dtype=torch.int32, device=device)
+        self.masked = torch.full((nb, B), 7, dtype=torch.uint8, device=device)
+        self.n_steps = torch.full((nb,), -1, dtype=torch.int32, device=device)
+        self.n_committed = torch.full((nb, self.S), -1, dtype=torch.int32, device=device)
+        self.seed_attn = torch.zeros((nb, Hq, dh), dtype=torch.bfloat16, device=device)
+        self.seed_conf = torch.full((nb,), -1.0, dtype=torch.float32, device=device)
+        self.attn_out = torch.zeros((nb, self.S, B, Hq, dh), dtype=torch.bfloat16, device=device)
+        self.conf = torch.full((nb, self.S, B), -1.0, dtype=torch.float32, device=device)
+        self.argmax = torch.full((nb, self.S, B), -1, dtype=torch.int32, device=device)
+        self.ws_bytes = bd.bd_decode_blocks_ws_bytes(self.P0, nb, B, Hq, Hkv, dh, d, V,
+                                                     w_scale is not None)
+        self.ws = workspace(self.ws_bytes, device)
+
+    def reset(self):
+        self.k_cache.copy_(self.k0)
+        self.v_cache.copy_(self.v0)
+        self.kv_len.fill_(self.P0)
+
+    def run(self, stream=None):
+        t = self.t
+        bd.bd_decode_blocks(t["q_seed"], t["h_seed"], t["q_steps"], t["h_steps"], t["k_blk"],
+                            t["v_blk"], self.k_cache, self.v_cache, self.cap, self.kv_len,
+                            self.P0, self.mask, self.nb, self.B, self.S, self.Hq, self.Hkv,
+                            self.dh, 0.0, t["W"], self.w_scale, self.d, self.V, self.tau,
+                            self.tokens, self.masked, self.n_steps, self.n_committed,
+                            self.seed_attn, self.seed_conf, self.attn_out, self.conf,
+                            self.argmax, self.ws, self.ws_bytes, stream)
+
+
 class LinearSpecStep:
     """Linear self-speculative step: draft (bidirectional) and verify (causal)
     passes, each block attention + LM head, then bd_spec_accept."""

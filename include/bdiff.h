@@ -304,6 +304,68 @@ bd_status bd_block_loop(bd_dtype dt, const void* q_steps, const void* k_cache,
                         hipStream_t stream);
 
 /*
+ * bd_decode_blocks - the device-resident decode loop over n_blocks blocks of
+ * B positions, generated one after another with the KV cache growing by each
+ * block, and no host round trip.  [OV §1.2: blocks are generated in order,
+ * each denoised in parallel over several steps, the KV cache of the earlier
+ * blocks reused; OV §2.2.2: causal-context decoding, the block's first token
+ * comes from the AR (causal) prediction; OV §4.1: threshold 0.9]
+ * The prefix length lives on the device: *kv_len (the prompt's P0 on entry).
+ * For block b = 0 .. n_blocks-1, in order:
+ *   1. kv_len += B if b > 0 (the previous block joins the prefix); the
+ *      block's own K/V rows k_blk[b], v_blk[b] are written into cache rows
+ *      kv_len .. kv_len + B - 1;
+ *   2. AR seed: q_seed[b] attends the prefix [0, kv_len) (bd_block_attn with
+ *      one query and no block key visible) -> seed_attn[b]; the LM head on
+ *      h_seed[b] gives seed_conf[b] and the seed token tokens[b][0];
+ *      tokens[b][1..B-1] = 0 and masked[b] = [0, 1, ..., 1];
+ *   3. up to max_steps denoising steps while a position of the block is
+ *      masked, exactly as bd_block_loop runs them (bd_block_attn over the
+ *      prefix kv_len and the block's rows under intra_mask, the LM head, the
+ *      threshold commit on tokens[b], masked[b]); a block with max_steps >=
+ *      B - 1 always completes (every step commits at least one position).
+ * Finally kv_len += B for the last block, so *kv_len = P0 + n_blocks B on
+ * exit.  A block that has not completed after max_steps is appended anyway,
+ * with its masked flags left set.  Every kernel is enqueued up front, so the
+ * call can be captured in a HIP graph.  The per-step queries, hidden rows and
+ * block K/V rows stand for what the model's other layers produce.
+ *   q_seed   [n_blocks][Hq][dh] bf16;    h_seed  [n_blocks][d] bf16
+ *   q_steps  [n_blocks][max_steps][B][Hq][dh] bf16
+ *   h_steps  [n_blocks][max_steps][B][d] bf16
+ *   k_blk, v_blk  [n_blocks][B][Hkv][dh] bf16
+ *   k_cache, v_cache [Hkv][cap][dh] bf16, in/out (rows from kv_len on are
+ *            overwritten by the blocks)
+ *   kv_len   [1] int32 (device), in/out; P_max (host) bounds its value on
+ *            entry (larger values are clamped to it)
+ *   intra_mask [B] uint64 (device), as for bd_block_attn
+ *   W        [V][d] bf16, or E4M3 codes when w_scale ([V] float32) is given
+ *   tokens [n_blocks][B] int32 out, masked [n_blocks][B] uint8 out (final state)
+ *   n_steps [n_blocks] int32 out; n_committed [n_blocks][max_steps] int32 out
+ *            (0 for steps not run)
+ *   seed_attn [n_blocks][Hq][dh] bf16 out; seed_conf [n_blocks] float32 out
+ *   attn_out [n_blocks][max_steps][B][Hq][dh] bf16 out; conf, argmax
+ *            [n_blocks][max_steps][B] out (steps not run: left untouched)
+ *   ws       at least bd_decode_blocks_ws_bytes(P_max, n_blocks, B, Hq, Hkv,
+ *            dh, d, V, w_scale != NULL) bytes (no initial contents required)
+ * Limits: dh == 128, 1 <= B <= 64, Hq % Hkv == 0, P_max >= 0,
+ *   P_max + n_blocks B <= min(cap, 65536), 1 <= max_steps <= 1024, LM-head
+ *   limits of bd_lmhead_conf (bf16) or bd_lmhead_conf_fp8.
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_ALIGN, BD_E_WORKSPACE, BD_E_LAUNCH.
+ */
+size_t bd_decode_blocks_ws_bytes(int32_t P_max, int32_t n_blocks, int32_t B, int32_t Hq,
+                                 int32_t Hkv, int32_t dh, int32_t d, int32_t V, int32_t w_fp8);
+bd_status bd_decode_blocks(const void* q_seed, const void* h_seed, const void* q_steps,
+                           const void* h_steps, const void* k_blk, const void* v_blk,
+                           void* k_cache, void* v_cache, int32_t cap, int32_t* kv_len,
+                           int32_t P_max, const uint64_t* intra_mask, int32_t n_blocks, int32_t B,
+                           int32_t max_steps, int32_t Hq, int32_t Hkv, int32_t dh, float scale,
+                           const void* W, const float* w_scale, int32_t d, int32_t V, float tau,
+                           int32_t* tokens, uint8_t* masked, int32_t* n_steps,
+                           int32_t* n_committed, void* seed_attn, float* seed_conf,
+                           void* attn_out, float* conf, int32_t* argmax, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/*
  * bd_commit - threshold unmasking with the always-one rule.
  * [OV §4.1: denoising confidence threshold 0.9; OV §1.2 parallel unmasking]
  * Every position i with masked[i] != 0 and conf[i] > tau is committed.  If

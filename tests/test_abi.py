@@ -422,3 +422,31 @@ def test_probe_stream_read_validation():
     assert f(grid=0) == bd.BD_E_SHAPE
     assert f(grid=65537) == bd.BD_E_SHAPE
     assert f(src=MISALIGNED) == bd.BD_E_ALIGN
+
+
+def test_decode_blocks_validation():
+    base = dict(q_seed=FAKE, h_seed=FAKE, q_steps=FAKE, h_steps=FAKE, k_blk=FAKE, v_blk=FAKE,
+                k_cache=FAKE, v_cache=FAKE, cap=1344, kv_len=FAKE, P_max=1280, intra_mask=FAKE,
+                n_blocks=4, B=16, max_steps=15, Hq=16, Hkv=2, dh=128, scale=0.0, W=FAKE,
+                w_scale=None, d=2048, V=151936, tau=0.9, tokens=FAKE, masked=FAKE, n_steps=FAKE,
+                n_committed=FAKE, seed_attn=FAKE, seed_conf=FAKE, attn_out=FAKE, conf=FAKE,
+                argmax=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=0, check=False)
+    f = lambda **kw: bd.bd_decode_blocks(**{**base, **kw})  # noqa: E731
+    assert f(kv_len=None) == bd.BD_E_NULL
+    assert f(seed_attn=None) == bd.BD_E_NULL
+    assert f(h_seed=None) == bd.BD_E_NULL
+    assert f(cap=1343) == bd.BD_E_SHAPE                 # P_max + n_blocks B > cap
+    assert f(n_blocks=0) == bd.BD_E_SHAPE
+    assert f(B=65) == bd.BD_E_SHAPE
+    assert f(max_steps=0) == bd.BD_E_SHAPE
+    assert f(dh=64) == bd.BD_E_SHAPE
+    assert f(Hq=15) == bd.BD_E_SHAPE
+    assert f(d=1000) == bd.BD_E_SHAPE
+    assert f(tau=float("nan")) == bd.BD_E_SHAPE
+    assert f(P_max=65536 - 63, cap=1 << 20) == bd.BD_E_SHAPE
+    assert f(k_cache=MISALIGNED) == bd.BD_E_ALIGN
+    assert f(kv_len=FAKE + 2) == bd.BD_E_ALIGN
+    need = bd.bd_decode_blocks_ws_bytes(1280, 4, 16, 16, 2, 128, 2048, 151936, False)
+    assert need > bd.bd_block_attn_ws_bytes(1280 + 3 * 16, 16, 16, 2, 128)
+    assert f(ws_bytes=need - 1) == bd.BD_E_WORKSPACE
+    assert bd.bd_decode_blocks_ws_bytes(1280, 0, 16, 16, 2, 128, 2048, 151936, False) == 0
