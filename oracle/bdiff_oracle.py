@@ -83,7 +83,7 @@ __all__ = [
     "intra_block_mask", "masked_attention", "block_attn", "paged_rows", "block_attn_paged",
     "kv_quant_fp8", "kv_dequant_fp8", "block_attn_fp8kv",
     "dualstream_attn",
-    "dualstream_lse", "dualstream_attn_bwd",
+    "dualstream_lse", "dualstream_attn_bwd", "dualstream_attn_bwd_given",
     "lm_logits", "conf_argmax", "lmhead_conf", "E4M3_MAX", "e4m3_decode", "e4m3_encode",
     "quant_fp8_rows", "lm_logits_fp8", "lmhead_conf_fp8", "commit", "spec_accept", "cert_scan",
     "decode_step", "block_loop", "decode_blocks", "linear_spec_step", "fused_spec_step",
@@ -363,6 +363,42 @@ def dualstream_attn_bwd(q, k, v, d_out, n_vis: int, n_txt: int, block: int,
         dv[:, h, :] = p.T @ g[:, h, :]
         dp = g[:, h, :] @ v[:, h, :].T
         ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        dq[:, h, :] = scale * (ds @ k[:, h, :])
+        dk[:, h, :] = scale * (ds.T @ q[:, h, :])
+    return dq, dk, dv
+
+
+def dualstream_attn_bwd_given(q, k, v, out, lse, d_out, n_vis: int, n_txt: int, block: int,
+                              scale: float | None = None, seg_starts=None):
+    """The training backward as a backward pass computes it from what the
+    forward kept: the probabilities from the given row log-sum-exp lse [N][H]
+    (natural log), P = exp(scale Q K^T - lse) on visible pairs, and
+    D = rowsum(dO * out) from the given forward output out [N][H][dh]:
+        dV = P^T dO,   dS = P * (dO V^T - D),   dQ = scale dS K,
+        dK = scale dS^T Q.
+    With the exact out and lse it equals dualstream_attn_bwd; with a rounded
+    out it shows what that rounding does to the gradients.  All float64.
+    [OV §2.2.1; TH §4.1]"""
+    q = widen(q)
+    k = widen(k)
+    v = widen(v)
+    o = widen(out)
+    g = widen(d_out)
+    lse = np.asarray(lse, dtype=np.float64)
+    n, nh, dh = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(dh)
+    allowed = dualstream_mask(n_vis, n_txt, block, seg_starts)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for h in range(nh):
+        s = scale * (q[:, h, :] @ k[:, h, :].T)
+        p = np.where(allowed, np.exp(np.where(allowed, s, 0.0) - lse[:, h:h + 1]), 0.0)
+        dv[:, h, :] = p.T @ g[:, h, :]
+        dp = g[:, h, :] @ v[:, h, :].T
+        d = (g[:, h, :] * o[:, h, :]).sum(axis=1, keepdims=True)
+        ds = p * (dp - d)
         dq[:, h, :] = scale * (ds @ k[:, h, :])
         dk[:, h, :] = scale * (ds.T @ q[:, h, :])
     return dq, dk, dv

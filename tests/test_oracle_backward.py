@@ -79,3 +79,58 @@ def test_backward_identities():
         assert np.abs(dv.sum(axis=0) - g.sum(axis=0)).max() <= 1e-12
         assert np.abs(dk.sum(axis=0)).max() <= 1e-12
         assert np.abs(dq[0]).max() == 0.0
+
+
+# The backward from what the forward kept (dualstream_attn_bwd_given): with
+# the exact output and log-sum-exp it is the gradient above; its response to
+# a changed output or log-sum-exp follows from the formulas in closed form.
+
+def test_given_exact_forward_equals_the_gradient():
+    for n_vis, n_txt, b, seg in CASES:
+        q, k, v, g = _inputs(n_vis, n_txt, seed=3 * n_vis + n_txt)
+        out = oracle.dualstream_attn(q, k, v, n_vis, n_txt, b, seg_starts=seg)
+        lse = oracle.dualstream_lse(q, k, n_vis, n_txt, b, seg_starts=seg)
+        ref = oracle.dualstream_attn_bwd(q, k, v, g, n_vis, n_txt, b, seg_starts=seg)
+        got = oracle.dualstream_attn_bwd_given(q, k, v, out, lse, g, n_vis, n_txt, b,
+                                               seg_starts=seg)
+        for a, r in zip(got, ref):
+            assert np.abs(a - r).max() <= 1e-12 * max(1.0, np.abs(r).max())
+
+
+def test_given_output_enters_through_d_only():
+    # out + delta moves D_i by e_i = dO_i . delta_i, which moves dQ_i by
+    # -scale e_i sum_j P_ij k_j (attention with the keys as values) and dK_j
+    # by -scale sum_i P_ij e_i q_i (the dV of output gradient e * q); dV stays
+    n_vis, n_txt, b, seg = 2, 7, 2, [0, 3]
+    q, k, v, g = _inputs(n_vis, n_txt, seed=11)
+    out = oracle.dualstream_attn(q, k, v, n_vis, n_txt, b, seg_starts=seg)
+    lse = oracle.dualstream_lse(q, k, n_vis, n_txt, b, seg_starts=seg)
+    delta = 1e-3 * np.random.default_rng(12).standard_normal(out.shape)
+    base = oracle.dualstream_attn_bwd_given(q, k, v, out, lse, g, n_vis, n_txt, b, seg_starts=seg)
+    moved = oracle.dualstream_attn_bwd_given(q, k, v, out + delta, lse, g, n_vis, n_txt, b,
+                                             seg_starts=seg)
+    e = (g * delta).sum(axis=2)
+    scale = 1 / np.sqrt(q.shape[2])
+    pk = oracle.dualstream_attn(q, k, k, n_vis, n_txt, b, seg_starts=seg)
+    _, _, pq = oracle.dualstream_attn_bwd(q, k, v, e[:, :, None] * q, n_vis, n_txt, b,
+                                          seg_starts=seg)
+    assert np.abs(moved[0] - base[0] + scale * e[:, :, None] * pk).max() <= 1e-12
+    assert np.abs(moved[1] - base[1] + scale * pq).max() <= 1e-12
+    assert np.array_equal(moved[2], base[2])
+
+
+def test_given_lse_shift_scales_its_row():
+    # lse_i + c multiplies row i of P by exp(-c): dQ_i scales by exp(-c),
+    # every other row of dQ stays
+    n_vis, n_txt, b, seg = 3, 4, 2, None
+    q, k, v, g = _inputs(n_vis, n_txt, seed=5)
+    out = oracle.dualstream_attn(q, k, v, n_vis, n_txt, b)
+    lse = oracle.dualstream_lse(q, k, n_vis, n_txt, b)
+    base = oracle.dualstream_attn_bwd_given(q, k, v, out, lse, g, n_vis, n_txt, b)
+    i, c = 6, 0.37
+    lse2 = lse.copy()
+    lse2[i] += c
+    dq2 = oracle.dualstream_attn_bwd_given(q, k, v, out, lse2, g, n_vis, n_txt, b)[0]
+    assert np.abs(dq2[i] - np.exp(-c) * base[0][i]).max() <= 1e-12
+    rest = np.arange(q.shape[0]) != i
+    assert np.abs(dq2[rest] - base[0][rest]).max() <= 1e-12
