@@ -197,7 +197,8 @@ def mfma(pmc_db: str, trace_db: str | None = None, clock_ghz: float = 2.4) -> st
         busy, act = avg.get("SQ_VALU_MFMA_BUSY_CYCLES"), avg.get("GRBM_GUI_ACTIVE")
         if busy is not None:
             frac = busy / (SIMD_NUM * d * 1e-6 * clock_ghz * 1e9)
-            lines.append(f"    {'MFMA busy % at %.1f GHz' % clock_ghz:34s} {100.0 * frac:18.2f}")
+            label = f"MFMA busy % at {clock_ghz:.1f} GHz"
+            lines.append(f"    {label:34s} {100.0 * frac:18.2f}")
             if act:
                 lines.append(f"    {'MfmaUtil % (per GRBM instance)':34s} "
                              f"{100.0 * busy / (act / grbm_inst * SIMD_NUM):18.2f}")
