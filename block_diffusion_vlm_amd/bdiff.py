@@ -10,11 +10,14 @@ raises BdError unless ``check=False``.  The library must be built
 from __future__ import annotations
 
 import ctypes
+import os
 from pathlib import Path
 
 import numpy as np
 
-LIB_PATH = Path(__file__).resolve().parent / "libbdiff.so"
+# BDIFF_LIB names another build of the same library (the host-only
+# sanitizer build, for argument-validation runs without a GPU).
+LIB_PATH = Path(os.environ.get("BDIFF_LIB") or Path(__file__).resolve().parent / "libbdiff.so")
 
 BD_OK, BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_ALIGN, BD_E_WORKSPACE, BD_E_DEVICE, BD_E_LAUNCH = range(8)
 BD_F32, BD_BF16 = 0, 1

@@ -5,6 +5,13 @@
 Every HIP source under csrc/ is compiled to an object in _build/ (in
 parallel) and linked into block_diffusion_vlm_amd/libbdiff.so.  The build
 always recompiles, so a call after a source change never links stale code.
+
+    python -m block_diffusion_vlm_amd.build host-sanitized
+
+builds the host side alone (no device code) with AddressSanitizer and
+UndefinedBehaviorSanitizer into _build/libbdiff_host_asan.so, for running
+the argument validation of every entry point on a machine without a GPU
+(the library's sanitizer runtime must then be preloaded: host_asan_runtime()).
 """
 from __future__ import annotations
 
@@ -30,6 +37,17 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-function",
     f"-I{ROOT / 'include'}", f"-I{CSRC}",
 ]
+
+
+# Host-only sanitizer build: each -fsanitize= applies to the host pass only.
+HOST_SAN_FLAGS = [
+    "-O1", "-g", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+    f"-I{ROOT / 'include'}", f"-I{CSRC}",
+]
+HOST_SAN_LIB = BUILD / "libbdiff_host_asan.so"
 
 
 def hipcc() -> str:
@@ -69,5 +87,44 @@ def build(verbose: bool = True) -> Path:
     return LIB
 
 
+def host_asan_runtime() -> Path:
+    """The AddressSanitizer runtime of the compiler hipcc drives (it also
+    carries the UndefinedBehaviorSanitizer handlers)."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    p = Path(r.stdout.strip())
+    if r.returncode != 0 or not p.is_absolute() or not p.exists():
+        raise RuntimeError("the compiler's AddressSanitizer runtime was not found")
+    return p
+
+
+def build_host_sanitized(verbose: bool = True) -> Path:
+    """Host code of every source with ASan + UBSan, linked without device code."""
+    san = BUILD / "host_asan"
+    san.mkdir(parents=True, exist_ok=True)
+
+    def one(src: Path) -> Path:
+        obj = san / (src.stem + ".o")
+        r = subprocess.run([hipcc(), *HOST_SAN_FLAGS, "-c", str(src), "-o", str(obj)],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"host sanitizer build failed on {src.name}:\n{r.stderr}")
+        return obj
+
+    srcs = sources()
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
+        objs = list(ex.map(one, srcs))
+    r = subprocess.run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *map(str, objs),
+                        "-o", str(HOST_SAN_LIB)], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"host sanitizer link failed:\n{r.stderr}")
+    if verbose:
+        print(f"built {HOST_SAN_LIB} (host code only, ASan + UBSan)", file=sys.stderr)
+    return HOST_SAN_LIB
+
+
 if __name__ == "__main__":
-    build()
+    if len(sys.argv) > 1 and sys.argv[1] == "host-sanitized":
+        build_host_sanitized()
+    else:
+        build()

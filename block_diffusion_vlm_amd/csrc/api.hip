@@ -39,6 +39,7 @@ const char* bd_status_str(bd_status s) {
         case BD_E_WORKSPACE: return "workspace missing or too small";
         case BD_E_DEVICE: return "device is not gfx950";
         case BD_E_LAUNCH: return "kernel launch failed";
+        default: break;
     }
     return "unknown status";
 }

@@ -37,7 +37,12 @@
 extern "C" {
 #endif
 
+/* Each enum below carries two bound enumerators that are never used as
+ * values: they make its range every int32, so that any int a C caller passes
+ * is a valid value of the type in the C++ implementation, which then
+ * rejects it (BD_E_DTYPE, BD_E_SHAPE) or describes it ("unknown status"). */
 typedef enum {
+    BD_STATUS_INT32_MIN_ = -2147483647 - 1,
     BD_OK = 0,
     BD_E_NULL = 1,       /* a required pointer is NULL                        */
     BD_E_SHAPE = 2,      /* a size is out of range or sizes are inconsistent  */
@@ -45,18 +50,26 @@ typedef enum {
     BD_E_ALIGN = 4,      /* a vector-loaded pointer is not 16-byte aligned    */
     BD_E_WORKSPACE = 5,  /* workspace missing or smaller than *_ws_bytes      */
     BD_E_DEVICE = 6,     /* current device is not gfx950                      */
-    BD_E_LAUNCH = 7      /* the HIP runtime rejected a kernel launch          */
+    BD_E_LAUNCH = 7,     /* the HIP runtime rejected a kernel launch          */
+    BD_STATUS_INT32_MAX_ = 2147483647
 } bd_status;
 
-typedef enum { BD_F32 = 0, BD_BF16 = 1 } bd_dtype;
+typedef enum {
+    BD_DTYPE_INT32_MIN_ = -2147483647 - 1,
+    BD_F32 = 0,
+    BD_BF16 = 1,
+    BD_DTYPE_INT32_MAX_ = 2147483647
+} bd_dtype;
 
 /* Visibility among the Bq block queries (block key j for block query i). */
 typedef enum {
+    BD_MASK_INT32_MIN_ = -2147483647 - 1,
     BD_MASK_BIDIR = 0,      /* all ones: parallel denoising inside a block [OV §1.2] */
     BD_MASK_CAUSAL = 1,     /* j <= i: the AR verify pass [OV §2.3.1]               */
-    BD_MASK_SPEC_FUSED = 2  /* draft+verify in one forward [OV §2.3.1], Bq = 2B:
+    BD_MASK_SPEC_FUSED = 2, /* draft+verify in one forward [OV §2.3.1], Bq = 2B:
                                rows 0..B-1 causal among themselves; rows B..2B-1
                                see row j < B iff j <= i-B, and all of B..2B-1 */
+    BD_MASK_INT32_MAX_ = 2147483647
 } bd_mask_kind;
 
 /* Static description of a status code; never NULL. */
