@@ -42,13 +42,11 @@ __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 
 // D[r] = sum_d dO[r][d] O[r][d] for every (token, head) row r = token * H +
-// head: 16 lanes per row.
+// head: 16 lanes per row (float32 path; the bf16 dQ kernel forms D itself).
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const T* __restrict__ out,
                                                          const T* __restrict__ dout, int rows,
-                                                         int dh, float* __restrict__ D,
-                                                         const float* __restrict__ lse,
-                                                         float* __restrict__ lse2) {
+                                                         int dh, float* __restrict__ D) {
     const int r = blockIdx.x * 16 + (threadIdx.x >> 4);
     const int l = threadIdx.x & 15;
     float acc = 0.f;
@@ -58,12 +56,7 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const T* __restrict__ o
         for (int d = l; d < dh; d += 16) acc = fmaf(to_f32(o[d]), to_f32(g[d]), acc);
     }
     for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
-    if (l == 0 && r < rows) {
-        D[r] = acc;
-        // The row log-sum-exp in log2 units for the dK/dV kernel, which
-        // stages it straight into LDS (no multiply per score there).
-        if (lse2 != nullptr) lse2[r] = lse[r] * kLog2e;
-    }
+    if (l == 0 && r < rows) D[r] = acc;
 }
 
 // Stores a wave's transposed 32 x 128 result (accumulator layout, lane =
@@ -83,14 +76,18 @@ __device__ __forceinline__ void store_rowT(uint16_t* dst, const f32x16 (&acc)[4]
 }
 
 // ---------------------------------------------------------------------------
-// dQ: 128 query rows per workgroup, key tiles of 64.
+// dQ: 128 query rows per workgroup, key tiles of 64.  Each workgroup first
+// forms D = rowsum(dO * O) of its rows from the dO fragments it holds anyway
+// and writes it, with the rows' log-sum-exp in log2 units, for the dK/dV
+// kernel that runs after it.
 // ---------------------------------------------------------------------------
 template <bool SEG>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ D, Geometry G, int H,
-    float scale_log2, float scale, uint16_t* __restrict__ dq, int nqt) {
+    const uint16_t* __restrict__ out, const float* __restrict__ lse, float* __restrict__ D,
+    float* __restrict__ lse2_out, Geometry G, int H, float scale_log2, float scale,
+    uint16_t* __restrict__ dq, int nqt) {
     __shared__ __align__(16) uint16_t kK[kTile];     // K tile, A-operand layout
     __shared__ __align__(16) uint16_t kV[kTile];     // K tile, transposed-read layout
     __shared__ __align__(16) uint16_t vK[kTile];     // V tile, A-operand layout
@@ -119,7 +116,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     load_q(qf, row_ok ? q + size_t(row) * rs + size_t(h) * kDh : nullptr, lane);
     load_q(gf, row_ok ? dout + size_t(row) * rs + size_t(h) * kDh : nullptr, lane);
     const float lse2 = row_ok ? lse[size_t(row) * H + h] * kLog2e : INFINITY;
-    const float Dr = row_ok ? D[size_t(row) * H + h] : 0.f;
+    // D of this lane's row: lanes l and l + 32 hold complementary halves of
+    // dO (load_q's layout), so each adds its half and takes the other's.
+    float Dr;
+    {
+        bf16x8 of[8];
+        load_q(of, row_ok ? out + size_t(row) * rs + size_t(h) * kDh : nullptr, lane);
+        float acc = 0.f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                acc = fmaf(static_cast<float>(of[s][e]), static_cast<float>(gf[s][e]), acc);
+        Dr = acc + other_half(acc);
+    }
+    if (row_ok && lane < 32) {
+        D[size_t(row) * H + h] = Dr;
+        lse2_out[size_t(row) * H + h] = lse2;
+    }
     const RowVis rv = row_ok ? row_vis<SEG>(G, row) : RowVis{-1, 0, 0};
     const ReadOffsets ro = read_offsets(lane);
     const uint16_t* kh = k + size_t(h) * kDh;
@@ -442,9 +456,9 @@ __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(
 
 template <typename T>
 hipError_t launch_rowdot(const T* out, const T* dout, int rows, int dh, float* D,
-                         const float* lse, float* lse2, hipStream_t st) {
+                         hipStream_t st) {
     hipLaunchKernelGGL(bwd_rowdot_kernel<T>, dim3((rows + 15) / 16), dim3(256), 0, st, out, dout,
-                       rows, dh, D, lse, lse2);
+                       rows, dh, D);
     return hipGetLastError();
 }
 
@@ -467,20 +481,18 @@ hipError_t launch_dualstream_bwd_bf16(const void* q, const void* k, const void* 
     const auto* kk = static_cast<const uint16_t*>(k);
     const auto* vv = static_cast<const uint16_t*>(v);
     const auto* gg = static_cast<const uint16_t*>(dout);
-    hipError_t e = launch_rowdot(static_cast<const uint16_t*>(out), gg, G.N * H, kDh, D, lse,
-                                 lse2, st);
-    if (e != hipSuccess) return e;
+    const auto* oo = static_cast<const uint16_t*>(out);
     const int nt = (G.N + kRowsPerWg - 1) / kRowsPerWg;
     const dim3 grid(H, nt), blk(256);
     const float sl = scale * kLog2e;
     if (G.n_seg > 1) {
-        hipLaunchKernelGGL(bwd_dq_kernel<true>, grid, blk, 0, st, qq, kk, vv, gg, lse, D, G, H, sl,
-                           scale, static_cast<uint16_t*>(dq), nt);
+        hipLaunchKernelGGL(bwd_dq_kernel<true>, grid, blk, 0, st, qq, kk, vv, gg, oo, lse, D, lse2,
+                           G, H, sl, scale, static_cast<uint16_t*>(dq), nt);
         hipLaunchKernelGGL(bwd_dkdv_kernel<true>, grid, blk, 0, st, qq, kk, vv, gg, lse2, D, G, H,
                            sl, scale, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
     } else {
-        hipLaunchKernelGGL(bwd_dq_kernel<false>, grid, blk, 0, st, qq, kk, vv, gg, lse, D, G, H,
-                           sl, scale, static_cast<uint16_t*>(dq), nt);
+        hipLaunchKernelGGL(bwd_dq_kernel<false>, grid, blk, 0, st, qq, kk, vv, gg, oo, lse, D,
+                           lse2, G, H, sl, scale, static_cast<uint16_t*>(dq), nt);
         hipLaunchKernelGGL(bwd_dkdv_kernel<false>, grid, blk, 0, st, qq, kk, vv, gg, lse2, D, G, H,
                            sl, scale, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
     }
@@ -494,7 +506,7 @@ hipError_t launch_dualstream_bwd_f32(const float* q, const float* k, const float
                                      float* dv, void* ws, hipStream_t st) {
     const Geometry G = make_geometry(n_vis, n_txt, block, seg, n_seg);
     float* D = static_cast<float*>(ws);
-    hipError_t e = launch_rowdot(out, dout, G.N * H, dh, D, nullptr, nullptr, st);
+    hipError_t e = launch_rowdot(out, dout, G.N * H, dh, D, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_dq_f32_kernel, dim3(G.N * H), dim3(64), 0, st, q, k, v, dout, lse, D,
                        G, H, dh, scale, dq);
