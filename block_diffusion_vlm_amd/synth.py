@@ -23,7 +23,7 @@ from __future__ import annotations
 import numpy as np
 
 BASE_SEED = 20261203
-N_CONFIGS = 10
+N_CONFIGS = 11
 
 
 # ---------------------------------------------------------------------------
@@ -31,7 +31,7 @@ N_CONFIGS = 10
 # ---------------------------------------------------------------------------
 
 def config_rng(cfg: int, seed: int | None = None) -> np.random.Generator:
-    """PCG64 stream for workload ``cfg`` (1..10): child ``cfg-1`` of
+    """PCG64 stream for workload ``cfg`` (1..11): child ``cfg-1`` of
     SeedSequence(seed or BASE_SEED) (a child's stream does not depend on how
     many children are spawned)."""
     ss = np.random.SeedSequence(BASE_SEED if seed is None else seed)
@@ -420,7 +420,7 @@ def qwen_block_loop(seed: int | None = None, B=16, S=16, T=8, n_vis=1024, n_prom
 
 def qwen_decode_blocks(seed: int | None = None, n_blocks=4, B=16, S=15, T=8, n_vis=1024,
                        n_prompt=256, Hq=16, Hkv=2, dh=128, d=2048, V=151936, sigma_w=0.02,
-                       guard=None) -> dict:
+                       fp8=False, guard=None) -> dict:
     """Several consecutive blocks of the Qwen-shaped decode, bf16, each
     started by an AR seed step and appended to the KV cache before the next
     (causal-context decoding, Fast-dVLM overview §2.2.2; blocks in order,
@@ -432,27 +432,37 @@ def qwen_decode_blocks(seed: int | None = None, n_blocks=4, B=16, S=15, T=8, n_v
     first token), and S >= T denoising steps planted as in qwen_block_loop
     (every masked position committed by threshold within T steps; S = B - 1
     steps always suffice, as every step commits at least one position).
+    With ``fp8`` the LM head's W is stored as E4M3 codes with one float32
+    scale per row, as in qwen_decode_fp8, and the rows are planted against the
+    stored weights (its own random stream).
     ``guard`` as in qwen_decode, applied to every planted row."""
-    rng = config_rng(10, seed)
+    rng = config_rng(11 if fp8 else 10, seed)
     P0 = n_vis + n_prompt
     cap = P0 + n_blocks * B
-    W = normal_bf16(rng, (V, d), std=sigma_w)
+    if fp8:
+        W = normal_e4m3(rng, (V, d))
+        w_scale = (np.float32(sigma_w / E4M3_CODE_STD)
+                   * rng.uniform(0.9, 1.1, V).astype(np.float32))
+        row = lambda v: e4m3_row_values(W[v]) * float(w_scale[v])  # noqa: E731
+    else:
+        W = normal_bf16(rng, (V, d), std=sigma_w)
+        w_scale, row = None, None
     k_cache = np.zeros((Hkv, cap, dh), np.uint16)
     v_cache = np.zeros((Hkv, cap, dh), np.uint16)
     k_cache[:, :P0] = normal_bf16(rng, (Hkv * P0, dh)).reshape(Hkv, P0, dh)
     v_cache[:, :P0] = normal_bf16(rng, (Hkv * P0, dh), trunc=4.0).reshape(Hkv, P0, dh)
     seed_t = rng.integers(0, V, n_blocks)
     seed_c = rng.uniform(0.92, 0.999, n_blocks)
-    h_seed, _ = planted_bits(rng, W, seed_t, seed_c, sigma_w, guard=guard,
-                             redraw_conf=_uniform_redraw(0.92, 0.999))
+    h_seed, _ = planted_bits(rng, W, seed_t, seed_c, sigma_w, row=row, guard=guard,
+                             w_scale=w_scale, redraw_conf=_uniform_redraw(0.92, 0.999))
     h_steps = np.empty((n_blocks, S, B, d), np.uint16)
     final = np.empty((n_blocks, B), np.int32)
     commit_step = np.empty((n_blocks, B), np.int64)
     for b in range(n_blocks):
-        f, c, h = _plant_trajectory(rng, W, None, None, B, S, T, V, sigma_w, guard)
+        f, c, h = _plant_trajectory(rng, W, row, w_scale, B, S, T, V, sigma_w, guard)
         final[b], commit_step[b], h_steps[b] = f, c, h
-    return {
-        "dtype": "bf16", "n_blocks": n_blocks, "B": B, "S": S, "T": T, "P0": P0, "cap": cap,
+    r = {
+        "dtype": "fp8" if fp8 else "bf16", "n_blocks": n_blocks, "B": B, "S": S, "T": T, "P0": P0, "cap": cap,
         "n_vis": n_vis, "n_prompt": n_prompt, "Hq": Hq, "Hkv": Hkv, "dh": dh, "d": d, "V": V,
         "tau": 0.9, "W": W, "k_cache": k_cache, "v_cache": v_cache,
         "k_blk": normal_bf16(rng, (n_blocks * B * Hkv, dh)).reshape(n_blocks, B, Hkv, dh),
@@ -463,6 +473,9 @@ def qwen_decode_blocks(seed: int | None = None, n_blocks=4, B=16, S=15, T=8, n_v
         "q_steps": normal_bf16(rng, (n_blocks * S * B * Hq, dh)).reshape(n_blocks, S, B, Hq, dh),
         "h_steps": h_steps, "final_tokens": final, "commit_step": commit_step,
     }
+    if fp8:
+        r["w_scale"] = w_scale
+    return r
 
 
 def linear_spec(seed: int | None = None, B=32, n_vis=1024, n_prompt=256, Hq=16, Hkv=2,

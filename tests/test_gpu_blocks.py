@@ -31,7 +31,15 @@ def gfx950():
 def _oracle(r, S):
     return oracle.decode_blocks(r["q_seed"], r["h_seed"], r["q_steps"][:, :S],
                                 r["h_steps"][:, :S], r["k_blk"], r["v_blk"], r["k_cache"],
-                                r["v_cache"], r["P0"], r["W"], TAU32)
+                                r["v_cache"], r["P0"], r["W"], TAU32, w_scale=r.get("w_scale"))
+
+
+def _run(r, **kw):
+    ws = r.get("w_scale")
+    run = runner.DecodeBlocks(r, w_scale=None if ws is None else runner.to_dev(ws), **kw)
+    run.run()
+    torch.cuda.synchronize()
+    return run
 
 
 def _check(run, r, o, guards=True):
@@ -41,8 +49,8 @@ def _check(run, r, o, guards=True):
         d = r["h_steps"].shape[-1]
         rows = [r["h_seed"]] + [r["h_steps"][b, :o["blocks"][b]["n_steps"]].reshape(-1, d)
                                 for b in range(nb)]
-        gap, dist = lmhead_margins(np.concatenate(rows), r["W"], TAU32)
-        assert gap.min() > 1e-2 and dist[nb:].min() >= 1e-3
+        gap, dist = lmhead_margins(np.concatenate(rows), r["W"], TAU32, r.get("w_scale"))
+        assert gap.min() > 1e-2 and (dist[nb:].size == 0 or dist[nb:].min() >= 1e-3)
     assert int(run.kv_len.item()) == o["kv_len"] == r["P0"] + nb * B
     assert np.array_equal(runner.to_host(run.k_cache), o["k_cache"])
     assert np.array_equal(runner.to_host(run.v_cache), o["v_cache"])
@@ -167,3 +175,31 @@ def test_decode_blocks_full_size():
     for b, blk in enumerate(o["blocks"]):
         assert blk["n_steps"] == r["T"] and blk["seed_token"] == r["seed_targets"][b]
     _check(run, r, o)
+
+
+@pytest.mark.parametrize("B,S,T,n_vis,n_prompt,Hq,Hkv,d,V", [
+    (5, 4, 3, 37, 11, 4, 1, 256, 3001),       # ragged block, prefix off the tile grid
+    (1, 1, 1, 20, 3, 2, 1, 128, 1000),        # the seed is the whole block: no steps run
+    (64, 8, 6, 100, 20, 2, 2, 128, 1000),     # the largest block (one mask word)
+])
+def test_decode_blocks_ragged_shapes(B, S, T, n_vis, n_prompt, Hq, Hkv, d, V):
+    r = synth.qwen_decode_blocks(n_blocks=3, B=B, S=S, T=T, n_vis=n_vis, n_prompt=n_prompt,
+                                 Hq=Hq, Hkv=Hkv, d=d, V=V, guard=row_guard(TAU32))
+    print(f"decode_blocks B={B} S={S} P0={n_vis + n_prompt} Hq={Hq} Hkv={Hkv} d={d} V={V}",
+          flush=True)
+    run = _run(r)
+    o = _oracle(r, run.S)
+    for b, blk in enumerate(o["blocks"]):
+        assert blk["n_steps"] == (T if B > 1 else 0) and blk["seed_token"] == r["seed_targets"][b]
+    _check(run, r, o)
+
+
+def test_decode_blocks_fp8_lm_head_matches_oracle():
+    r = synth.qwen_decode_blocks(n_blocks=3, V=30011, fp8=True, guard=row_guard(TAU32))
+    print("decode_blocks FP8 LM head, 3 blocks V=30011", flush=True)
+    run = _run(r)
+    o = _oracle(r, run.S)
+    for b, blk in enumerate(o["blocks"]):
+        assert blk["n_steps"] == r["T"] and blk["seed_token"] == r["seed_targets"][b]
+    _check(run, r, o)
+

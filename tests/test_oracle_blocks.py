@@ -114,3 +114,20 @@ def test_one_block_with_too_few_steps_stays_masked_and_is_still_appended():
     for blk in o["blocks"]:
         assert blk["n_steps"] == 3 and blk["masked"].any()
         assert int(blk["masked"].sum()) == r["B"] - 1 - int(blk["n_committed"].sum())
+
+
+def test_planted_fp8_blocks_commit_seed_and_positions_at_their_steps():
+    # the same trajectories with an E4M3 weight matrix (one scale per row):
+    # the W8A8 logits recover every planted token at its planted step
+    r = synth.qwen_decode_blocks(n_blocks=2, B=6, S=5, T=4, V=2000, d=256, n_vis=24, n_prompt=8,
+                                 Hq=2, Hkv=1, dh=16, fp8=True)
+    o = oracle.decode_blocks(r["q_seed"], r["h_seed"], r["q_steps"], r["h_steps"], r["k_blk"],
+                             r["v_blk"], r["k_cache"], r["v_cache"], r["P0"], r["W"], TAU,
+                             w_scale=r["w_scale"])
+    T = r["T"]
+    for b, blk in enumerate(o["blocks"]):
+        assert blk["seed_token"] == r["seed_targets"][b]
+        assert np.array_equal(blk["tokens"][1:], r["final_tokens"][b][1:])
+        assert not blk["masked"].any() and blk["n_steps"] == T
+        assert np.array_equal(blk["n_committed"][:T], np.bincount(r["commit_step"][b][1:],
+                                                                  minlength=T))
