@@ -472,42 +472,46 @@ def secondary(args, stream, others):
         # Several blocks in a row (bd_decode_blocks): each block's K/V rows
         # join the cache at a device-side kv_len, an AR seed step gives its
         # first token, and up to B - 1 = 15 denoising steps (enough for any
-        # block) are enqueued; one graph per call.
-        note("decode_blocks")
-        rb = synth.qwen_decode_blocks()
-        run = runner.DecodeBlocks(rb)
-        run.reset()
-        run.run()
-        torch.cuda.synchronize()
-        steps_run = run.n_steps.cpu().numpy().tolist()
-        tok_ref = run.tokens.clone()
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
+        # block) are enqueued; one graph per call.  With the bf16 and with
+        # the FP8 (E4M3 W8A8) LM head.
+        for key, fp8 in (("decode_blocks", False), ("decode_blocks_fp8", True)):
+            note(key)
+            rb = synth.qwen_decode_blocks(fp8=fp8)
+            wsc = runner.to_dev(rb["w_scale"]) if fp8 else None
+            run = runner.DecodeBlocks(rb, w_scale=wsc)
             run.reset()
             run.run()
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            run.reset()
-            run.run()
-        torch.cuda.synchronize()
-        ms = timed(g.replay, max(3, iters // 32), 1, stream)
-        torch.cuda.synchronize()
-        assert torch.equal(run.tokens, tok_ref)
-        assert int(run.kv_len.item()) == rb["P0"] + rb["n_blocks"] * rb["B"]
-        nb = rb["n_blocks"]
-        toks = nb * rb["B"]                      # the seed and 15 commits per block
-        res["decode_blocks"] = {
-            "us_per_call": round(ms * 1e3, 2), "blocks": nb,
-            "us_per_block": round(ms * 1e3 / nb, 2), "steps_per_block": steps_run,
-            "max_steps": run.S, "tokens": toks,
-            "committed_tok_per_s": round(toks / (ms * 1e-3), 1),
-            "shape": "4 blocks of 16 after a 1024 + 256 token prefix, each seeded by an AR step "
-                     "(one query over the prefix + the LM head) and planted to finish in 8 "
-                     "steps; KV rows appended at a device-side kv_len"}
-        del run, rb, g
+            torch.cuda.synchronize()
+            steps_run = run.n_steps.cpu().numpy().tolist()
+            tok_ref = run.tokens.clone()
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                run.reset()
+                run.run()
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run.reset()
+                run.run()
+            torch.cuda.synchronize()
+            ms = timed(g.replay, max(3, iters // 32), 1, stream)
+            torch.cuda.synchronize()
+            assert torch.equal(run.tokens, tok_ref)
+            assert int(run.kv_len.item()) == rb["P0"] + rb["n_blocks"] * rb["B"]
+            nb = rb["n_blocks"]
+            toks = nb * rb["B"]                  # the seed and 15 commits per block
+            res[key] = {
+                "us_per_call": round(ms * 1e3, 2), "blocks": nb,
+                "us_per_block": round(ms * 1e3 / nb, 2), "steps_per_block": steps_run,
+                "max_steps": run.S, "tokens": toks,
+                "committed_tok_per_s": round(toks / (ms * 1e-3), 1),
+                "shape": "4 blocks of 16 after a 1024 + 256 token prefix, each seeded by an AR "
+                         "step (one query over the prefix + the LM head) and planted to finish "
+                         "in 8 steps; KV rows appended at a device-side kv_len"
+                         + ("; E4M3 LM-head weights with one scale per row" if fp8 else "")}
+            del run, rb, g, wsc
 
     if "train" in args.sections:
         # The training attention is compute-bound: its clock settles only
