@@ -157,18 +157,18 @@ namespace {
 // banks.  The next tile's loads are in flight while the current tile is
 // multiplied.
 // ---------------------------------------------------------------------------
-template <int NB, int NCH>
-__global__ __launch_bounds__(256) void lmhead_bf16_kernel(const uint16_t* __restrict__ h,
-                                                          const uint16_t* __restrict__ W,
-                                                          int B, int d, int V, int ntiles,
-                                                          void* __restrict__ ws,
-                                                          const int32_t* __restrict__ gate) {
+template <int NB, int NCH, int KS = 4>
+__global__ __launch_bounds__(64 * KS) void lmhead_bf16_kernel(const uint16_t* __restrict__ h,
+                                                              const uint16_t* __restrict__ W,
+                                                              int B, int d, int V, int ntiles,
+                                                              void* __restrict__ ws,
+                                                              const int32_t* __restrict__ gate) {
     if (gated_off(gate)) return;
     constexpr int NL = NCH * 4;                       // 16-byte loads per lane per tile
     constexpr int PIECES = NCH * 16;                  // 16-byte pieces per row segment
-    __shared__ f32x4 red[2][4][NB][64];               // per-wave partial logits, 2 buffers
-    __shared__ ArgSoft fin[4][NB][16];
-    __shared__ __align__(16) u32x4 stage[4][16 * PIECES];
+    __shared__ f32x4 red[2][KS][NB][64];              // per-wave partial logits, 2 buffers
+    __shared__ ArgSoft fin[KS][NB][16];
+    __shared__ __align__(16) u32x4 stage[KS][16 * PIECES];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -363,13 +363,18 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(const float* __restrict
 // Host-side plan for the bf16 kernel: waves per workgroup (K split) and
 // chunks per wave.  Returns false when the register-resident variant does not
 // apply (then the generic kernel runs).
+// Waves per workgroup (ks, splitting K) and 128-element chunks per wave
+// (nch) of the streaming kernel: four waves when h's fragments fit, else
+// eight with at most two chunks each (the LDS holds eight waves' stages only
+// then), which covers 33 to 64 positions at d = 2048 (two waves per SIMD).
 bool plan_bf16(int B, int d, int* ks, int* nch) {
     const int NB = (B + 15) / 16;
     const int c = d / 128;
     const int max_nch = 8 / NB;       // h fragments: 16 * NCH * NB VGPRs <= 128
-    const int order[3] = {4, 2, 1};
-    for (int i = 0; i < 3; ++i) {
+    const int order[4] = {4, 2, 1, 8};
+    for (int i = 0; i < 4; ++i) {
         const int k = order[i];
+        if (k == 8 && c / k > 2) continue;
         if (c % k == 0 && c / k <= max_nch) {
             *ks = k;
             *nch = c / k;
@@ -395,11 +400,18 @@ hipError_t launch_nb(const void* h, const void* W, int B, int d, int V, const Fi
     }
 #define BD_LMH_CASE(N)                                                                     \
     case N:                                                                                \
-        if constexpr (N * NB <= 8) {                                                       \
+        if constexpr (N * NB > 8) {                                                        \
+            return hipErrorInvalidValue;                                                   \
+        } else if constexpr (N <= 2) {                                                     \
+            if (ks == 8)                                                                   \
+                hipLaunchKernelGGL((lmhead_bf16_kernel<NB, N, 8>), dim3(G), dim3(512), 0,  \
+                                   st, hh, ww, B, d, V, ntiles, ws, f.gate);               \
+            else                                                                           \
+                hipLaunchKernelGGL((lmhead_bf16_kernel<NB, N>), dim3(G), dim3(64 * ks), 0, \
+                                   st, hh, ww, B, d, V, ntiles, ws, f.gate);               \
+        } else {                                                                           \
             hipLaunchKernelGGL((lmhead_bf16_kernel<NB, N>), dim3(G), dim3(64 * ks), 0, st, \
                                hh, ww, B, d, V, ntiles, ws, f.gate);                       \
-        } else {                                                                           \
-            return hipErrorInvalidValue;                                                   \
         }                                                                                  \
         break;
     switch (nch) {

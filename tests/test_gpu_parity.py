@@ -128,7 +128,8 @@ def _lmhead_case(B, d, V, seed):
 
 @pytest.mark.parametrize("B,d,V", [
     (1, 128, 17), (4, 256, 1000), (16, 512, 4099), (16, 640, 777), (16, 1024, 5000),
-    (32, 2048, 20011), (33, 384, 999), (64, 2048, 3001), (16, 2048, 151936),
+    (32, 2048, 20011), (33, 384, 999), (48, 2048, 7001), (64, 2048, 3001),
+    (16, 2048, 151936),
 ])
 def test_lmhead_bf16_matches_oracle(B, d, V):
     r = _lmhead_case(B, d, V, seed=B * 7 + d + V)
