@@ -113,7 +113,8 @@ def _case(B, d, V, seed, tau=None):
 
 SHAPES = [
     (1, 128, 17), (4, 256, 1000), (16, 512, 4099), (16, 640, 777), (16, 1024, 5000),
-    (32, 2048, 20011), (33, 384, 999), (64, 2048, 3001), (16, 2048, 151936),
+    (17, 1024, 3001), (32, 2048, 20011), (33, 384, 999), (64, 2048, 3001),
+    (16, 2048, 151936),
     # shapes outside the streaming kernel's register/LDS plan (generic path)
     (16, 8192, 3000), (48, 4096, 2001), (2, 16384, 333),
 ]
@@ -138,8 +139,8 @@ def test_lmhead_fp8_matches_oracle(B, d, V):
     assert np.array_equal(lm.argmax.cpu().numpy(), a0)
 
 
-@pytest.mark.parametrize("B,d,V", [(1, 128, 1000), (16, 2048, 30011), (33, 384, 999),
-                                   (20, 8192, 700)])
+@pytest.mark.parametrize("B,d,V", [(1, 128, 1000), (16, 2048, 30011), (32, 2048, 3001),
+                                   (33, 384, 999), (20, 8192, 700)])
 def test_lmhead_fp8_conf_commit_equals_separate_calls(B, d, V):
     r = _case(B, d, V, seed=B + V, tau=TAU32)
     h, W, ws = runner.to_dev(r["h"]), runner.to_dev(r["W"]), runner.to_dev(r["w_scale"])
