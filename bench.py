@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=400,
                     help="untimed steps first (~43 ms of work: the clocks settle)")
-    ap.add_argument("--graph-steps", type=int, default=8,
+    ap.add_argument("--graph-steps", type=int, default=25,
                     help="at most this many decode steps per HIP graph (a divisor of --steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workloads", default="all",
