@@ -258,11 +258,12 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
             tile_barrier();
         }
     };
-    for (int t = t_beg; t < t_end; t += 2) {
-        step(t, kbuf[0], vbuf[0], kbuf[1], vbuf[1]);
-        sync();
-        if (t + 1 == t_end) break;
-        step(t + 1, kbuf[1], vbuf[1], kbuf[0], vbuf[0]);
+    // One copy of the step in the code (the buffers alternate at run time):
+    // short calls run one tile per split, on CUs whose instruction cache may
+    // not hold this kernel, so its size shows in their latency.
+    for (int t = t_beg; t < t_end; ++t) {
+        const int cur = (t - t_beg) & 1;
+        step(t, kbuf[cur], vbuf[cur], kbuf[cur ^ 1], vbuf[cur ^ 1]);
         sync();
     }
     if constexpr (FP8) {
