@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
 // maxima (lane groups by shuffles, waves through LDS), and each lane keeps
 // the E4M3 B operands of its rows for the whole kernel.
 // ---------------------------------------------------------------------------
-template <int NB, int NCH>
+template <int NB, int NCH, int DEPTH = 2>
 __global__ __launch_bounds__(256) void lmhead_fp8_kernel(const uint16_t* __restrict__ h,
                                                          const uint8_t* __restrict__ W,
                                                          const float* __restrict__ wscale, int B,
@@ -175,16 +175,18 @@ __global__ __launch_bounds__(256) void lmhead_fp8_kernel(const uint16_t* __restr
 
     const int t_beg = int(int64_t(ntiles) * blockIdx.x / G);
     const int t_end = int(int64_t(ntiles) * (blockIdx.x + 1) / G);
-    u32x4 bufA[NL], bufB[NL];                      // two tiles in flight
+    u32x4 bufA[NL], bufB[NL];                      // DEPTH (1 or 2) tiles in flight
     f32x4 scA[RT], scB[RT];
     auto issue_first_tiles = [&]() {
         if (t_beg < t_end) {
             load_tile(bufA, t_beg);
             load_scales(scA, t_beg);
         }
-        if (t_beg + 1 < t_end) {
-            load_tile(bufB, t_beg + 1);
-            load_scales(scB, t_beg + 1);
+        if constexpr (DEPTH == 2) {
+            if (t_beg + 1 < t_end) {
+                load_tile(bufB, t_beg + 1);
+                load_scales(scB, t_beg + 1);
+            }
         }
     };
 
@@ -285,9 +287,9 @@ __global__ __launch_bounds__(256) void lmhead_fp8_kernel(const uint16_t* __restr
         f32x4 sc[RT];
 #pragma unroll
         for (int s = 0; s < RT; ++s) sc[s] = scb[s];
-        if (tile + 2 < t_end) {
-            load_tile(buf, tile + 2);
-            load_scales(scb, tile + 2);
+        if (tile + DEPTH < t_end) {
+            load_tile(buf, tile + DEPTH);
+            load_scales(scb, tile + DEPTH);
         }
 
         f32x4 acc[RT][NB];
@@ -346,9 +348,13 @@ __global__ __launch_bounds__(256) void lmhead_fp8_kernel(const uint16_t* __restr
         }
         ++it;
     };
-    for (int tile = t_beg; tile < t_end; tile += 2) {
-        step(bufA, scA, tile);
-        if (tile + 1 < t_end) step(bufB, scB, tile + 1);
+    if constexpr (DEPTH == 2) {
+        for (int tile = t_beg; tile < t_end; tile += 2) {
+            step(bufA, scA, tile);
+            if (tile + 1 < t_end) step(bufB, scB, tile + 1);
+        }
+    } else {
+        for (int tile = t_beg; tile < t_end; ++tile) step(bufA, scA, tile);
     }
 
     store_workgroup_partials<NB>(st, fin, ws, B);
@@ -469,8 +475,12 @@ template <int NB, int NCH>
 void launch_fp8_stream(int G, int ks, const uint16_t* h, const uint8_t* W, const float* wsc,
                        int B, int d, int V, int ntiles, void* ws, hipStream_t st,
                        const int32_t* gate) {
-    hipLaunchKernelGGL((lmhead_fp8_kernel<NB, NCH>), dim3(G), dim3(64 * ks), 0, st, h, W, wsc, B,
-                       d, V, ntiles, ws, gate);
+    // Two tiles in flight for one position block; one for more, whose
+    // hidden codes and accumulators would otherwise push the second tile's
+    // registers out to the accumulation registers.
+    constexpr int kDepth = NB == 1 ? 2 : 1;
+    hipLaunchKernelGGL((lmhead_fp8_kernel<NB, NCH, kDepth>), dim3(G), dim3(64 * ks), 0, st, h, W,
+                       wsc, B, d, V, ntiles, ws, gate);
 }
 
 template <int NB>
