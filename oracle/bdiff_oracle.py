@@ -43,7 +43,7 @@ design notes of the repository):
   R7  Attention scale is 1/sqrt(dh); queries/keys are taken post-RoPE.
   R8  A query row with no visible key produces a zero output row.
   R9  Speculative accept compares index-aligned draft and verify arrays and
-      accepts exactly L tokens (no bonus token).
+      accepts exactly L tokens (no bonus token) unless asked for R20's.
   R10 SPEC_FUSED (the quadratic variant's one-forward mask, whose layout the
       pages do not print) is the dual-stream mask restricted to one block:
       rows 0..B-1 (verify half, draft tokens as input) are causal among
@@ -67,6 +67,13 @@ design notes of the repository):
       decode(code) * scale.  New rows are quantized as code = E4M3 rounding of
       fl32(x * fl32(1 / scale)), clamped to [-448, 448] first (float32 steps,
       as in R16).
+  R20 Bonus token (optional; the pages do not state one): at the first
+      disagreement L < B the verify pass's own token verify[L] is taken as
+      well, as greedy speculative decoding does (Leviathan et al. 2023, "Fast
+      Inference from Transformers via Speculative Decoding", and Chen et al.
+      2023, speculative sampling, both with a greedy target); L + 1 tokens
+      are appended and kv_len stays P + L (the K/V row of position L was
+      computed from the rejected draft token).  With L = B nothing is added.
 
 Every function below takes float64 (or integer) arrays and returns new arrays;
 bfloat16 inputs are passed as raw uint16 bit patterns and widened exactly.
@@ -561,16 +568,21 @@ def commit(conf, argmax, masked, tokens, tau: float):
     return masked, tokens, len(chosen)
 
 
-def spec_accept(draft, verify, P: int):
+def spec_accept(draft, verify, P: int, bonus: bool = False):
     """Longest prefix where the diffusion draft equals the causal verify pass;
     the KV cache is truncated to P + L and the L accepted tokens are appended.
-    [OV §2.3.1]  Returns (L, kv_len, accepted_tokens)."""
+    [OV §2.3.1]  With bonus (R20), a first disagreement at L < B also appends
+    the verify pass's token there.  Returns (number of tokens appended,
+    kv_len, appended tokens)."""
     draft = np.asarray(draft).astype(np.int64)
     verify = np.asarray(verify).astype(np.int64)
     L = 0
     while L < draft.shape[0] and draft[L] == verify[L]:
         L += 1
-    return L, P + L, draft[:L].copy()
+    tokens = draft[:L].copy()
+    if bonus and L < draft.shape[0]:
+        tokens = np.append(tokens, verify[L])
+    return tokens.shape[0], P + L, tokens
 
 
 def cert_scan(anchor_conf, anchor_tok, text_tok, k: int):

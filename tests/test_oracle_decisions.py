@@ -90,6 +90,54 @@ def test_accept_brute_force(b):
             # largest l such that the first l entries agree, by checking every l
             best = max(l for l in range(b + 1) if tuple(d[:l]) == tuple(v[:l]))
             assert L == best and kv == P + best and tuple(acc) == tuple(d[:best])
+            # with the bonus token the appended tokens are the verify pass's
+            # own first min(best + 1, b) tokens (the draft agrees before best)
+            n, kv2, acc2 = oracle.spec_accept(np.array(d, int), np.array(v, int), P, bonus=True)
+            assert kv2 == P + best and n == min(best + 1, b) == len(acc2)
+            assert tuple(acc2) == tuple(v[:n])
+
+
+def _greedy_target(vocab, salt):
+    """A deterministic stand-in for the verifier's greedy next token: a hash
+    of the whole context."""
+    def nxt(ctx):
+        return hash((salt,) + tuple(ctx)) % vocab
+    return nxt
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_accept_with_bonus_reproduces_greedy_decoding(seed):
+    """Greedy speculative decoding is lossless: the tokens appended per step,
+    bonus included, are exactly what greedy decoding with the verifier alone
+    produces, and after enough steps the two sequences coincide.  The verify
+    pass is the verifier run on the draft under teacher forcing (position i
+    sees the context and draft[:i]); the draft agrees with greedy decoding
+    for a random number of positions and is random after that.  Only the
+    first kv_len - P appended tokens were inputs of the verify pass, which is
+    why the cache keeps exactly those."""
+    rng = np.random.default_rng(seed)
+    vocab, B = 5, 8
+    nxt = _greedy_target(vocab, seed)
+    ctx = list(rng.integers(0, vocab, 3))
+    greedy = list(ctx)
+    for _ in range(60):
+        greedy.append(nxt(greedy))
+    out = list(ctx)
+    kv = len(ctx)
+    steps = 0
+    while len(out) < len(greedy) - B:
+        ref = greedy[len(out):len(out) + B]
+        agree = int(rng.integers(0, B + 1))
+        draft = ref[:agree] + list((np.array(ref[agree:]) + rng.integers(1, vocab, B - agree))
+                                   % vocab)
+        verify = [nxt(out + draft[:i]) for i in range(B)]
+        n, kv_len, toks = oracle.spec_accept(np.array(draft), np.array(verify), kv, bonus=True)
+        assert kv_len - kv == min(agree, B) and n == min(agree + 1, B)
+        out += list(toks)
+        kv = len(out)                         # the next step computes the bonus row
+        assert out == greedy[:len(out)]
+        steps += 1
+    assert steps > 1
 
 
 # --- certificate scan (LOWN 'method step details' (2)-(3))
