@@ -33,7 +33,7 @@ EXPORTS = (
     "bd_lmhead_conf_fp8_ws_bytes", "bd_lmhead_conf_fp8", "bd_lmhead_conf_commit_fp8",
     "bd_quant_fp8_rows", "bd_block_loop_ws_bytes", "bd_block_loop",
     "bd_decode_blocks_ws_bytes", "bd_decode_blocks",
-    "bd_commit", "bd_spec_accept", "bd_cert_scan",
+    "bd_commit", "bd_spec_accept", "bd_spec_accept_bonus", "bd_cert_scan",
     "bd_dualstream_attn", "bd_dualstream_attn_seg", "bd_dualstream_attn_fwd",
     "bd_dualstream_attn_bwd_ws_bytes", "bd_dualstream_attn_bwd",
     "bd_probe_stream_read",
@@ -82,6 +82,7 @@ _SIGS = {
     "bd_kv_quant_fp8": ([_P, _I, _I, _I, _P, _P, _I, _I, _P], _I),
     "bd_commit": ([_P, _P, _I, _F, _P, _P, _P, _P], _I),
     "bd_spec_accept": ([_P, _P, _I, _I, _P, _P, _P, _P], _I),
+    "bd_spec_accept_bonus": ([_P, _P, _I, _I, _P, _P, _P, _P], _I),
     "bd_cert_scan": ([_P, _P, _P, _I, _I, _P, _P, _P, _P], _I),
     "bd_dualstream_attn": ([_I, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P], _I),
     "bd_dualstream_attn_seg": ([_I, _P, _P, _P, _I, _I, _I, _P, _I, _I, _I, _F, _P, _P], _I),
@@ -263,6 +264,13 @@ def bd_spec_accept(draft, verify, B, P, accepted, kv_len, out_tokens, stream=Non
     st = lib().bd_spec_accept(_ptr(draft), _ptr(verify), B, P, _ptr(accepted), _ptr(kv_len),
                               _ptr(out_tokens), _stream(stream))
     return _ret("bd_spec_accept", st, check)
+
+
+def bd_spec_accept_bonus(draft, verify, B, P, accepted, kv_len, out_tokens, stream=None,
+                         check=True) -> int:
+    st = lib().bd_spec_accept_bonus(_ptr(draft), _ptr(verify), B, P, _ptr(accepted),
+                                    _ptr(kv_len), _ptr(out_tokens), _stream(stream))
+    return _ret("bd_spec_accept_bonus", st, check)
 
 
 def bd_block_attn_fp8kv(q, k_cache, v_cache, k_scale, v_scale, P, cap, intra_mask, Bq, Hq, Hkv,

@@ -524,6 +524,15 @@ bd_status bd_spec_accept(const int32_t* draft, const int32_t* verify, int32_t B,
         bd::launch_spec_accept(draft, verify, B, P, accepted, kv_len, out_tokens, stream));
 }
 
+bd_status bd_spec_accept_bonus(const int32_t* draft, const int32_t* verify, int32_t B, int32_t P,
+                               int32_t* accepted, int32_t* kv_len, int32_t* out_tokens,
+                               hipStream_t stream) {
+    if (!draft || !verify || !accepted || !kv_len || !out_tokens) return BD_E_NULL;
+    if (B < 0 || B > 64 || P < 0 || (int64_t)P + B > INT32_MAX) return BD_E_SHAPE;
+    return launch_status(bd::launch_spec_accept(draft, verify, B, P, accepted, kv_len, out_tokens,
+                                                stream, true));
+}
+
 bd_status bd_cert_scan(const float* anchor_conf, const int32_t* anchor_tok,
                        const int32_t* text_tok, int32_t n, int32_t k, int32_t* order,
                        int32_t* accepted, int32_t* skip_full, hipStream_t stream) {

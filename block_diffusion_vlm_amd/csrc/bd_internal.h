@@ -72,7 +72,7 @@ hipError_t launch_commit(const float* conf, const int32_t* argmax, int B, float 
                          uint8_t* masked, int32_t* tokens, int32_t* n_committed, hipStream_t st);
 hipError_t launch_spec_accept(const int32_t* draft, const int32_t* verify, int B, int P,
                               int32_t* accepted, int32_t* kv_len, int32_t* out_tokens,
-                              hipStream_t st);
+                              hipStream_t st, bool bonus = false);
 hipError_t launch_cert_scan(const float* conf, const int32_t* atok, const int32_t* ttok, int n,
                             int k, int32_t* order, int32_t* accepted, int32_t* skip,
                             hipStream_t st);

@@ -20,7 +20,10 @@ __global__ __launch_bounds__(64) void commit_kernel(const float* __restrict__ co
 }
 
 // Longest verified prefix (overview §2.3.1): the first disagreement is the
-// lowest set bit of a ballot.
+// lowest set bit of a ballot.  With BONUS the verify token at the first
+// disagreement is appended too (greedy speculative decoding's correction
+// token); the cache keeps P + L rows either way.
+template <bool BONUS>
 __global__ __launch_bounds__(64) void spec_accept_kernel(const int32_t* __restrict__ draft,
                                                          const int32_t* __restrict__ verify,
                                                          int B, int P,
@@ -29,12 +32,14 @@ __global__ __launch_bounds__(64) void spec_accept_kernel(const int32_t* __restri
                                                          int32_t* __restrict__ out_tokens) {
     const int i = threadIdx.x;
     const int32_t d = i < B ? draft[i] : 0;
-    const bool differ = i < B && d != verify[i];
+    const int32_t v = i < B ? verify[i] : 0;
+    const bool differ = i < B && d != v;
     const uint64_t bits = __ballot(differ);
     const int L = bits ? __builtin_ctzll(bits) : B;
     if (i < L) out_tokens[i] = d;
+    if (BONUS && i == L && L < B) out_tokens[i] = v;
     if (i == 0) {
-        *accepted = L;
+        *accepted = BONUS && L < B ? L + 1 : L;
         *kv_len = P + L;
     }
 }
@@ -151,9 +156,13 @@ hipError_t launch_commit(const float* conf, const int32_t* argmax, int B, float 
 
 hipError_t launch_spec_accept(const int32_t* draft, const int32_t* verify, int B, int P,
                               int32_t* accepted, int32_t* kv_len, int32_t* out_tokens,
-                              hipStream_t st) {
-    hipLaunchKernelGGL(spec_accept_kernel, dim3(1), dim3(64), 0, st, draft, verify, B, P,
-                       accepted, kv_len, out_tokens);
+                              hipStream_t st, bool bonus) {
+    if (bonus)
+        hipLaunchKernelGGL(spec_accept_kernel<true>, dim3(1), dim3(64), 0, st, draft, verify, B,
+                           P, accepted, kv_len, out_tokens);
+    else
+        hipLaunchKernelGGL(spec_accept_kernel<false>, dim3(1), dim3(64), 0, st, draft, verify, B,
+                           P, accepted, kv_len, out_tokens);
     return hipGetLastError();
 }
 

@@ -415,6 +415,24 @@ bd_status bd_spec_accept(const int32_t* draft, const int32_t* verify, int32_t B,
                          hipStream_t stream);
 
 /*
+ * bd_spec_accept_bonus - bd_spec_accept that also takes the verify pass's
+ * own token at the first disagreement.  The pages state no such token [OV
+ * §2.3.1]; it is the correction token of greedy speculative decoding
+ * (Leviathan et al. 2023; Chen et al. 2023), with which the tokens appended
+ * over the steps are exactly those of greedy decoding with the verifier.
+ *   L as in bd_spec_accept.  If L < B:  accepted[0] = L + 1,
+ *   out_tokens[0..L) = draft[0..L), out_tokens[L] = verify[L];
+ *   otherwise as bd_spec_accept.  kv_len[0] = P + L in both cases: the K/V
+ *   row of position L was computed from the rejected draft token, so the
+ *   caller's next step computes the appended token's row.
+ *   out_tokens[accepted..B) are left untouched.
+ *   Arguments, limits and errors as bd_spec_accept.
+ */
+bd_status bd_spec_accept_bonus(const int32_t* draft, const int32_t* verify, int32_t B, int32_t P,
+                               int32_t* accepted, int32_t* kv_len, int32_t* out_tokens,
+                               hipStream_t stream);
+
+/*
  * bd_cert_scan - LOWN certificate over n masked positions.
  * [LOWN 'method step details' (2)-(3)]  order = the positions sorted by
  * anchor_conf descending (stable: lower index first on ties);

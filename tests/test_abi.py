@@ -308,13 +308,16 @@ def test_small_calls_validation():
     assert c(B=-1) == bd.BD_E_SHAPE
     assert c(B=65) == bd.BD_E_SHAPE
     assert c(tau=float("nan")) == bd.BD_E_SHAPE
-    a = lambda **kw: bd.bd_spec_accept(**{**dict(draft=FAKE, verify=FAKE, B=16, P=10,
-                                                 accepted=FAKE, kv_len=FAKE, out_tokens=FAKE,
-                                                 stream=0, check=False), **kw})
-    assert a(verify=None) == bd.BD_E_NULL
-    assert a(B=65) == bd.BD_E_SHAPE
-    assert a(P=-3) == bd.BD_E_SHAPE
-    assert a(P=2 ** 31 - 5) == bd.BD_E_SHAPE
+    for fn in (bd.bd_spec_accept, bd.bd_spec_accept_bonus):
+        a = lambda **kw: fn(**{**dict(draft=FAKE, verify=FAKE, B=16, P=10, accepted=FAKE,
+                                      kv_len=FAKE, out_tokens=FAKE, stream=0, check=False),
+                               **kw})
+        assert a(verify=None) == bd.BD_E_NULL
+        assert a(out_tokens=None) == bd.BD_E_NULL
+        assert a(B=65) == bd.BD_E_SHAPE
+        assert a(B=-1) == bd.BD_E_SHAPE
+        assert a(P=-3) == bd.BD_E_SHAPE
+        assert a(P=2 ** 31 - 5) == bd.BD_E_SHAPE
     s = lambda **kw: bd.bd_cert_scan(**{**dict(anchor_conf=FAKE, anchor_tok=FAKE, text_tok=FAKE,
                                                n=64, k=4, order=FAKE, accepted=FAKE,
                                                skip_full=FAKE, stream=0, check=False), **kw})

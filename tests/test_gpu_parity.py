@@ -67,9 +67,11 @@ def test_commit_matches_oracle(B):
             assert np.array_equal(runner.to_host(d["tokens"]), t2)
 
 
+@pytest.mark.parametrize("bonus", [False, True])
 @pytest.mark.parametrize("B", [0, 1, 7, 16, 32, 64])
-def test_spec_accept_matches_oracle(B):
+def test_spec_accept_matches_oracle(B, bonus):
     rng = np.random.default_rng(200 + B)
+    call = bd.bd_spec_accept_bonus if bonus else bd.bd_spec_accept
     for trial in range(30):
         draft = rng.integers(0, 5 if trial % 2 else 151936, B).astype(np.int32)
         verify = draft.copy()
@@ -82,12 +84,12 @@ def test_spec_accept_matches_oracle(B):
         acc = torch.full((1,), -1, dtype=torch.int32, device="cuda")
         kv = torch.full((1,), -1, dtype=torch.int32, device="cuda")
         out = torch.full((max(B, 1),), -99, dtype=torch.int32, device="cuda")
-        bd.bd_spec_accept(dd, vv, B, P, acc, kv, out)
+        call(dd, vv, B, P, acc, kv, out)
         torch.cuda.synchronize()
-        L, kvl, toks = oracle.spec_accept(draft, verify, P)
-        assert int(acc.item()) == L and int(kv.item()) == kvl
+        n, kvl, toks = oracle.spec_accept(draft, verify, P, bonus=bonus)
+        assert int(acc.item()) == n and int(kv.item()) == kvl
         o = runner.to_host(out)
-        assert np.array_equal(o[:L], toks) and (o[L:] == -99).all()
+        assert np.array_equal(o[:n], toks) and (o[n:] == -99).all()
 
 
 @pytest.mark.parametrize("n", [0, 1, 7, 64, 200, 1024])
