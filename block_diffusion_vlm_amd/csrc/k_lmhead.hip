@@ -13,8 +13,9 @@
 // ready-made B fragments for the wave's K range.
 //
 // A workgroup has `ks` waves that split K; per 16-row vocabulary tile they
-// add their partial logits through LDS and one wave (rotating) folds the 16
-// rows into running (max, sum, argmax) states in the log2 domain.  Each
+// add their partial logits through LDS and one wave (rotating; a different
+// wave for each 16-position block) folds the 16 rows into running (max, sum,
+// argmax) states in the log2 domain.  Each
 // workgroup of a persistent grid streams one contiguous range of tiles (the
 // ranges differ by at most one tile).  Each workgroup writes one partial state per position;
 // a second, small kernel (one wave per position) merges the partials in a
@@ -244,27 +245,25 @@ __global__ __launch_bounds__(64 * KS) void lmhead_bf16_kernel(const uint16_t* __
                                                                       0, 0, 0);
             }
 
-        bool mine = true;
         if (nwave > 1) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) red[it & 1][wave][nb][lane] = acc[nb];
             __syncthreads();
-            mine = (wave == it % nwave);
-            if (mine) {
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    f32x4 t = red[it & 1][0][nb][lane];
-                    for (int w = 1; w < nwave; ++w) t += red[it & 1][w][nb][lane];
-                    acc[nb] = t;
-                }
-            }
         }
-        if (mine) {
-            const int row0 = tile * 16 + g * 4;
+        // Position block nb of this tile is added up and folded by wave
+        // (it + nb * nwave / NB) % nwave, so with several blocks different
+        // waves fold them side by side.
+        const int row0 = tile * 16 + g * 4;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const float x[4] = {acc[nb][0] * kLog2e, acc[nb][1] * kLog2e,
-                                    acc[nb][2] * kLog2e, acc[nb][3] * kLog2e};
+        for (int nb = 0; nb < NB; ++nb) {
+            const int folder = (it + nb * (nwave >= NB ? nwave / NB : 1)) % nwave;
+            if (wave == folder) {
+                f32x4 t = acc[nb];
+                if (nwave > 1) {
+                    t = red[it & 1][0][nb][lane];
+                    for (int w = 1; w < nwave; ++w) t += red[it & 1][w][nb][lane];
+                }
+                const float x[4] = {t[0] * kLog2e, t[1] * kLog2e, t[2] * kLog2e, t[3] * kLog2e};
                 fold4(st[nb], x, row0, V);
             }
         }

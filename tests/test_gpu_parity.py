@@ -132,6 +132,10 @@ def _lmhead_case(B, d, V, seed):
     (1, 128, 17), (4, 256, 1000), (16, 512, 4099), (16, 640, 777), (16, 1024, 5000),
     (32, 2048, 20011), (33, 384, 999), (48, 2048, 7001), (64, 2048, 3001),
     (16, 2048, 151936),
+    # 17 to 32 positions (two position blocks, folded by different waves)
+    # with d = 512 .. 2048: one tile per workgroup (V = 1001), one or two
+    # (V = 4097), a ragged vocabulary tail
+    (17, 512, 1001), (20, 1536, 4097), (25, 1024, 3000), (31, 2048, 151936),
 ])
 def test_lmhead_bf16_matches_oracle(B, d, V):
     r = _lmhead_case(B, d, V, seed=B * 7 + d + V)
@@ -382,8 +386,8 @@ def test_decode_step_full_size():
     assert np.array_equal(runner.to_host(step.tokens), o["tokens"])
 
 
-@pytest.mark.parametrize("B,d,V", [(1, 128, 1000), (16, 2048, 30011), (33, 384, 999),
-                                   (64, 2048, 3001)])
+@pytest.mark.parametrize("B,d,V", [(1, 128, 1000), (16, 2048, 30011), (24, 2048, 9001),
+                                   (33, 384, 999), (64, 2048, 3001)])
 def test_lmhead_conf_commit_equals_separate_calls(B, d, V):
     r = synth.qwen_decode(seed=B + V, B=B, d=d, V=V, n_vis=4, n_prompt=4, Hq=2, Hkv=1,
                           guard=row_guard(TAU32))
