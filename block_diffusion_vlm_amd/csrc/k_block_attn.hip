@@ -442,18 +442,25 @@ __global__ __launch_bounds__(64) void block_attn_f32_kernel(
     if (lane + 64 < dh) orow[lane + 64] = o1 * inv;
 }
 
-// Key tiles per workgroup.  A split writes a partial output row of 128 floats
-// for each of the R = Bq * Hq / Hkv query rows of its KV head, while it reads
-// 64 keys x 512 bytes of K and V per tile; grouping tiles keeps the partial
-// traffic near the KV traffic when R is large (R / 128 tiles per split), and
-// one tile per split keeps the most workgroups busy when R is small.
-int tiles_per_split(int P, int Bq, int Hq, int Hkv) {
+// Key tiles per workgroup.  A decode-sized call is bound by latency: each
+// split runs a chain of dependent steps per tile, so the fewest tiles per
+// split win as long as the grid (splits x KV heads x 128-row blocks) fits on
+// the chip in one round, one workgroup per CU.  Past that, splits take
+// ceil(ntiles / max_splits) tiles each, which also bounds the partial
+// outputs (a 512-byte row per query row and split) when the prefix is long.
+constexpr int kSplitCUs = 256;                       // compute units of the chip
+
+int max_splits(int Bq, int Hq, int Hkv) {
     const int R = Bq * (Hq / Hkv);
+    const int per_split = Hkv * ((R + kRowsPerWg - 1) / kRowsPerWg);   // workgroups
+    const int m = kSplitCUs / per_split;
+    return m > 1 ? m : 1;
+}
+
+int tiles_per_split(int P, int Bq, int Hq, int Hkv) {
     const int ntiles = (P + Bq + kBN - 1) / kBN;
-    int kt = (R + 127) / 128;
-    if (kt < 1) kt = 1;
-    if (kt > ntiles) kt = ntiles;
-    return kt;
+    const int m = max_splits(Bq, Hq, Hkv);
+    return ntiles > m ? (ntiles + m - 1) / m : 1;
 }
 
 int num_splits(int P, int Bq, int Hq, int Hkv) {
@@ -496,9 +503,15 @@ hipError_t launch_block_attn_any(const void* q, const void* kc, const void* vc, 
 
 }  // namespace
 
+// Sized for min(ntiles, max_splits) splits, an upper bound of num_splits
+// that never decreases with P, so a workspace sized for one prefix length
+// serves every shorter one (the multi-block loop sizes it for its last
+// block).
 size_t block_attn_ws_bytes(int P, int Bq, int Hq, int Hkv, int dh) {
     (void)dh;
-    return partials_bytes(Bq * Hq, num_splits(P, Bq, Hq, Hkv));
+    const int ntiles = (P + Bq + kBN - 1) / kBN;
+    const int m = max_splits(Bq, Hq, Hkv);
+    return partials_bytes(Bq * Hq, ntiles < m ? ntiles : m);
 }
 
 hipError_t launch_block_attn_bf16(const void* q, const void* kc, const void* vc, int P, int cap,
