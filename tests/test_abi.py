@@ -79,6 +79,20 @@ def test_workspace_queries():
     assert bd.bd_lmhead_conf_ws_bytes(65, 2048, 151936) == 0
 
 
+@pytest.mark.parametrize("Bq,Hq,Hkv", [(1, 16, 2), (16, 16, 2), (32, 16, 2), (64, 16, 2),
+                                       (33, 32, 4), (8, 64, 64)])
+def test_block_attn_workspace_never_shrinks_with_the_prefix(Bq, Hq, Hkv):
+    # A workspace sized for one prefix length must serve every shorter one
+    # (the multi-block loop sizes it for its last block), and it must hold at
+    # least one 512-byte partial row (plus max and sum) per query row.
+    prev = 0
+    for P in range(0, 65536 - Bq + 1, 61):
+        w = bd.bd_block_attn_ws_bytes(P, Bq, Hq, Hkv, 128)
+        assert w >= prev, P
+        assert w >= Bq * Hq * (128 + 2) * 4
+        prev = w
+
+
 def _attn(**kw):
     a = dict(dt=bd.BD_BF16, q=FAKE, k_cache=FAKE, v_cache=FAKE, P=32, cap=64, intra_mask=FAKE,
              Bq=16, Hq=16, Hkv=2, dh=128, scale=0.0, out=FAKE, ws=FAKE, ws_bytes=1 << 30,
