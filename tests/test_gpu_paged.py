@@ -45,6 +45,9 @@ CASES = [
     (5, 30, 7, 4, 2, 3, 37),              # key_lo = P: the block's own keys only
     (33, 60, 40, 8, 1, 7, 13),
     (64, 100, 28, 2, 2, 32, 64),
+    # long prefixes: two key tiles per split (145 and 129 tiles visited)
+    (16, 8192, 1024, 16, 2, 16, 0),
+    (16, 8192, 1024, 16, 2, 64, 1000),
 ]
 
 
