@@ -74,8 +74,6 @@ def graph_divisor(K, cap):
     return 1
 
 
-
-
 def timed(fn, iters, warmup, stream):
     """Average ms per call of fn() (launching on `stream`), HIP events on it."""
     import torch
