@@ -103,7 +103,10 @@ bd_status bd_make_intra_mask(bd_mask_kind kind, int32_t Bq, uint64_t* host_rows)
  *   intra_mask  [Bq] uint64 (device), e.g. from bd_make_intra_mask
  *   out         [Bq][Hq][dh]   dtype dt
  *   scale       softmax scale, > 0; 0 selects 1/sqrt(dh)
- *   ws          workspace of at least bd_block_attn_ws_bytes(...) bytes
+ *   ws          workspace of at least bd_block_attn_ws_bytes(...) bytes; the
+ *               size never decreases as P grows (other arguments fixed), so
+ *               a workspace sized for the longest prefix serves every call
+ *               with a shorter one
  * Limits: 1 <= Bq <= 64, 0 <= P, P + Bq <= cap, Hkv >= 1, Hq % Hkv == 0,
  *   BD_BF16: dh == 128 and P + Bq <= 65536;  BD_F32: dh % 4 == 0 and
  *   4 <= dh <= 128.
