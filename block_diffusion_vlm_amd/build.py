@@ -30,10 +30,17 @@ LIB = PKG / "libbdiff.so"
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are switched off for all device code: hipcc would
-# otherwise emit v_pk_* float ops from ordinary float code.
+# otherwise emit v_pk_* float ops from ordinary float code.  MFMA results are
+# kept in architectural registers (the compiler's VGPR form of the MFMA
+# instructions): by default it places them in accumulation registers and
+# copies them to and fro, about 900 copies in the block-attention split kernel
+# (304 registers, one wave per SIMD; 200 and two waves in this form) and 1,000
+# in the dual-stream backward.  Measured A/B on one box: backward 319-320
+# against 332-334 us, the decode step +0.4-0.5%, the rest unchanged.
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function",
     f"-I{ROOT / 'include'}", f"-I{CSRC}",
 ]
