@@ -36,7 +36,10 @@ ARCH = "gfx950"
 # copies them to and fro, about 900 copies in the block-attention split kernel
 # (304 registers, one wave per SIMD; 200 and two waves in this form) and 1,000
 # in the dual-stream backward.  Measured A/B on one box: backward 319-320
-# against 332-334 us, the decode step +0.4-0.5%, the rest unchanged.
+# against 332-334 us, the decode step +0.4-0.5%, the rest unchanged.  The
+# compiler's other scheduling strategies (max-ilp, iterative-ilp,
+# max-memory-clause) and its automatic wave priorities measured slower on
+# the backward (322-329 us) and no better elsewhere.
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
