@@ -225,11 +225,20 @@ __device__ __forceinline__ void dma_tile_full1(unsigned lofs, const uint16_t* g,
 }
 
 // Waits until at most N of this wave's global memory loads (global -> LDS
-// included) are outstanding; they complete in issue order.
+// included) are outstanding; they complete in issue order.  The asm statement
+// orders the LDS reads that follow (its memory clobber); the same wait is then
+// issued as a builtin, which the compiler's own wait insertion sees.  The
+// compiler does not count the global -> LDS loads (they are asm), so without
+// it, it took the ordinary loads issued before this point (the query
+// fragments) as still outstanding at their first use inside a tile loop, and
+// waited there for every load in flight, the next tile's included.  The
+// builtin's operand: vmcnt in bits 3:0 and 15:14, expcnt (7 = no wait) in
+// bits 6:4, lgkmcnt (15 = no wait) in bits 11:8.
 template <int N = 0>
 __device__ __forceinline__ void dma_wait() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // Workgroup barrier without the memory fence of __syncthreads(), whose

@@ -176,6 +176,10 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
     const ReadOffsets ro = read_offsets(lane);
 
     if constexpr (FP8) {
+        // The query fragments are in before the loop: waited for at their
+        // first use inside it, they would hold the MFMAs up behind the next
+        // tile's code loads issued just before.
+        dma_wait<0>();
         __syncthreads();
         scale_log2 *= f8.k_scale[g];
     } else {
