@@ -8,11 +8,12 @@ workload: bd_block_attn (16 block queries, bidirectional block, over a
 bd_lmhead_conf (hidden 2048 x vocabulary 151936, bf16) -> bd_commit
 (threshold 0.9), plus the restore of the block state so that every step does
 the same work.  Inputs are seeded synthetic tensors already resident in HBM;
-S consecutive steps (default 8) are captured as one HIP graph, which is
-replayed K/S times between HIP events (S is the largest divisor of K up to
-8, so that exactly K steps are timed).  Each of the S steps of a graph works
-on its own copy of the block state, and one device copy at the head of the
-graph restores all S copies, so that every step starts from the same state.
+S consecutive steps (at most 25 by default) are captured as one HIP graph,
+which is replayed K/S times between HIP events (S is the largest divisor of
+K up to --graph-steps, so that exactly K steps are timed).  Each of the S
+steps of a graph works on its own copy of the block state, and one device
+copy at the head of the graph restores all S copies, so that every step
+starts from the same state.
 One JSON line is printed.  ``--workloads`` selects the secondary workloads
 (comma-separated among fp8, loop, train, attn, spec; "all" or "none"), so
 that a profiled run can be cut to the kernels it is about.
