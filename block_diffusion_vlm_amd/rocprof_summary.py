@@ -1,7 +1,10 @@
 """Summaries of rocprofv3 result databases (SQLite, the tool's default output).
 
-    python -m block_diffusion_vlm_amd.rocprof_summary trace <results.db>
-        per-kernel dispatch count and average / min / max duration (us)
+    python -m block_diffusion_vlm_amd.rocprof_summary trace <results.db> [--by-grid]
+        per-kernel dispatch count and average / median / min / max duration
+        (us); with --by-grid, one line per kernel and grid size (a kernel
+        launched at several shapes, such as the block attention of the
+        linear and the fused speculation steps, then gets a line per shape)
     python -m block_diffusion_vlm_amd.rocprof_summary pmc <results.db> <COUNTER>
         per-kernel dispatch count and average counter value per dispatch
     python -m block_diffusion_vlm_amd.rocprof_summary traffic <fetch.db> <write.db> <out.json> [bf16|fp8|attn]
@@ -44,21 +47,24 @@ def kernel_rows(db: str):
                        "order by start").fetchall()
 
 
-def trace(db: str) -> str:
-    """Per kernel: calls, average, median, min and max duration, share of the
-    total.  The median is the figure to compare with event timings when some
-    dispatches of a kernel return at once (the skipped steps of the block
-    loop)."""
+def trace(db: str, by_grid: bool = False) -> str:
+    """Per kernel (and grid size, with by_grid): calls, average, median, min
+    and max duration, share of the total.  The median is the figure to
+    compare with event timings when some dispatches of a kernel return at
+    once (the skipped steps of the block loop)."""
     agg = collections.OrderedDict()
-    for _, n, s, e, *_ in kernel_rows(db):
-        agg.setdefault(_short(n), []).append((e - s) / 1000.0)
+    for _, n, s, e, gx, gy, gz in kernel_rows(db):
+        key = (_short(n), (gx, gy, gz) if by_grid else None)
+        agg.setdefault(key, []).append((e - s) / 1000.0)
     tot = sum(sum(v) for v in agg.values())
-    out = [f"{'kernel':58s} {'calls':>6s} {'avg_us':>8s} {'med_us':>8s} {'min_us':>8s} "
+    gcol = f" {'grid':>20s}" if by_grid else ""
+    out = [f"{'kernel':58s}{gcol} {'calls':>6s} {'avg_us':>8s} {'med_us':>8s} {'min_us':>8s} "
            f"{'max_us':>8s} {'time%':>6s}"]
-    for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+    for (k, grid), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
         med = sorted(v)[len(v) // 2]
-        out.append(f"{k[:58]:58s} {len(v):6d} {sum(v) / len(v):8.2f} {med:8.2f} {min(v):8.2f} "
-                   f"{max(v):8.2f} {100 * sum(v) / tot:6.2f}")
+        g = f" {str(grid):>20s}" if by_grid else ""
+        out.append(f"{k[:58]:58s}{g} {len(v):6d} {sum(v) / len(v):8.2f} {med:8.2f} "
+                   f"{min(v):8.2f} {max(v):8.2f} {100 * sum(v) / tot:6.2f}")
     return "\n".join(out)
 
 
@@ -214,7 +220,7 @@ def mfma(pmc_db: str, trace_db: str | None = None, clock_ghz: float = 2.4) -> st
 
 def main(argv):
     if len(argv) >= 2 and argv[0] == "trace":
-        print(trace(argv[1]))
+        print(trace(argv[1], by_grid="--by-grid" in argv[2:]))
     elif len(argv) >= 3 and argv[0] == "pmc":
         print(pmc(argv[1], argv[2]))
     elif len(argv) >= 2 and argv[0] == "mfma":

@@ -44,6 +44,25 @@ def test_trace_reports_calls_and_durations(tmp_path):
     assert "(anonymous namespace)" not in out[1]
 
 
+def test_trace_by_grid_separates_shapes(tmp_path):
+    db = str(tmp_path / "g.db")
+    con = sqlite3.connect(db)
+    con.execute("create table kernels (id, name, start, end, grid_x, grid_y, grid_z)")
+    con.executemany("insert into kernels values (?, ?, ?, ?, ?, ?, ?)",
+                    [(1, KNAME, 0, 10_000, 21, 2, 1), (2, KNAME, 0, 30_000, 37, 2, 2),
+                     (3, KNAME, 0, 12_000, 21, 2, 1)])
+    con.commit()
+    con.close()
+    lines = [x for x in rs.trace(db, by_grid=True).splitlines() if "dualstream" in x]
+    assert len(lines) == 2
+    small = next(x for x in lines if "(21, 2, 1)" in x).split()
+    assert small[-6:-1] == ["2", "11.00", "12.00", "10.00", "12.00"]
+    big = next(x for x in lines if "(37, 2, 2)" in x).split()
+    assert big[-6:-1] == ["1", "30.00", "30.00", "30.00", "30.00"]
+    # without grouping by grid the three dispatches share one line
+    assert [x.split()[-6] for x in rs.trace(db).splitlines() if "dualstream" in x] == ["3"]
+
+
 def test_mfma_summary_fractions(tmp_path):
     pmc, tr = str(tmp_path / "p.db"), str(tmp_path / "t.db")
     busy = 0.25 * rs.SIMD_NUM * 100e-6 * 2.4e9        # a quarter of the pipes' cycles in 100 us
