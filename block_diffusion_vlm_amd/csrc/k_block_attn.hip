@@ -7,8 +7,11 @@
 // bf16 path: split-K over the keys (flash-decoding).  Grouped-query heads are
 // packed so that all Bq x (Hq/Hkv) query rows of one KV head form the rows of
 // one tile; workgroup (split, kv head, row block) handles 64 keys for up to
-// 128 rows (4 waves x 32 rows) and writes an unnormalised partial
-// (max, sum, O) per row; a second kernel merges the splits in a fixed order.
+// 128 rows (4 waves x 32 rows) and writes a partial per row: its maximum and
+// sum in float32 and its output normalised by that sum, O / l, in bfloat16
+// (each value a convex combination of V rows, so bfloat16 keeps its range
+// and costs the output at most about one more rounding of its own format);
+// a second kernel merges the splits in a fixed order.
 //
 // FP8 KV cache (the fastest configuration of the overview runs FP8, §2.3.2):
 // K and V hold OCP E4M3 codes with one float32 scale per KV head for each.
@@ -29,9 +32,9 @@ using namespace attn;
 constexpr int kRowsPerWg = 128;
 
 struct Partials {
-    float* m;   // [rows][nsplit]
-    float* l;   // [rows][nsplit]
-    float* o;   // [rows][nsplit][128]
+    float* m;      // [rows][nsplit]
+    float* l;      // [rows][nsplit]
+    uint16_t* o;   // [rows][nsplit][128] bfloat16, O / l
 };
 
 __host__ __device__ inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -43,12 +46,12 @@ __host__ __device__ inline Partials partials(void* ws, int rows, int nsplit) {
     size_t off = al256(size_t(rows) * nsplit * 4);
     r.l = reinterpret_cast<float*>(p + off);
     off += al256(size_t(rows) * nsplit * 4);
-    r.o = reinterpret_cast<float*>(p + off);
+    r.o = reinterpret_cast<uint16_t*>(p + off);
     return r;
 }
 
 inline size_t partials_bytes(int rows, int nsplit) {
-    return 2 * al256(size_t(rows) * nsplit * 4) + al256(size_t(rows) * nsplit * kDh * 4);
+    return 2 * al256(size_t(rows) * nsplit * 4) + al256(size_t(rows) * nsplit * kDh * 2);
 }
 
 // Paged cache: kc/vc are the page pools ([n_pages][Hkv][page_size][128]),
@@ -282,38 +285,46 @@ __global__ __launch_bounds__(256) void block_attn_split_kernel(
         pt.m[rg * nsplit + split] = m;
         pt.l[rg * nsplit + split] = l;
     }
-    // The partial output leaves through LDS.  A lane holds 16-byte pieces of
-    // its own row only, so stores straight from the accumulators would write
-    // 32 rows x 32 bytes per instruction.  Each wave instead writes its
-    // 32 x 128 block into one of the four tile buffers (free after the last
-    // barrier of the loop), row-major with 16-byte piece c of row rr at slot
-    // c ^ rr, and reads it back so that each store instruction writes two
-    // whole 512-byte rows.
-    uint16_t* const region = wave < 2 ? kbuf[wave] : vbuf[wave - 2];
-    f32x4* const sl = reinterpret_cast<f32x4*>(region);
+    // The partial output leaves through LDS.  A lane holds pieces of its own
+    // row only (four consecutive dims per accumulator group), so stores
+    // straight from the accumulators would write 32 rows x 8 bytes per
+    // instruction.  Each wave instead writes its 32 x 128 block of O / l, as
+    // bfloat16, into one of the four tile buffers (free after the last
+    // barrier of the loop), row-major: row rr holds sixteen 16-byte pieces
+    // (8 dims each), piece c at slot c ^ (rr % 16), and a lane's four dims
+    // fill one 8-byte half of a piece.  Read back as whole pieces, each
+    // store instruction then writes four whole 256-byte rows.
+    uint8_t* const region =
+        reinterpret_cast<uint8_t*>(wave < 2 ? kbuf[wave] : vbuf[wave - 2]);
     const int rr = lane & 31;
+    const float inv_l = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
-            const int c = (32 * db + acc_row(4 * e4, lane)) >> 2;
-            sl[rr * 32 + (c ^ rr)] = f32x4{oacc[db][4 * e4], oacc[db][4 * e4 + 1],
-                                           oacc[db][4 * e4 + 2], oacc[db][4 * e4 + 3]};
+            // dims 32 db + 8 e4 + 4 (lane / 32) .. + 3: piece 4 db + e4, half lane / 32
+            const int c = 4 * db + e4;
+            const bf16x4 w = {static_cast<__bf16>(oacc[db][4 * e4] * inv_l),
+                              static_cast<__bf16>(oacc[db][4 * e4 + 1] * inv_l),
+                              static_cast<__bf16>(oacc[db][4 * e4 + 2] * inv_l),
+                              static_cast<__bf16>(oacc[db][4 * e4 + 3] * inv_l)};
+            *reinterpret_cast<bf16x4*>(region + rr * 256 + 16 * (c ^ (rr & 15)) +
+                                       8 * (lane >> 5)) = w;
         }
     const int r0 = blockIdx.z * kRowsPerWg + wave * 32;  // first query row of this wave
-    const int c = lane & 31;
-    f32x4 val[16];
+    const int c = lane & 15;
+    u32x4 val[8];
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-        const int row = 2 * it + (lane >> 5);
-        val[it] = sl[row * 32 + (c ^ row)];
+    for (int it = 0; it < 8; ++it) {
+        const int row = 4 * it + (lane >> 4);
+        val[it] = *reinterpret_cast<const u32x4*>(region + row * 256 + 16 * (c ^ (row & 15)));
     }
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-        const int row = 2 * it + (lane >> 5);
+    for (int it = 0; it < 8; ++it) {
+        const int row = 4 * it + (lane >> 4);
         if (r0 + row < R) {
             const size_t rg = size_t(g) * R + r0 + row;
-            *reinterpret_cast<f32x4*>(pt.o + (rg * nsplit + split) * kDh + 4 * c) = val[it];
+            *reinterpret_cast<u32x4*>(pt.o + (rg * nsplit + split) * kDh + 8 * c) = val[it];
         }
     }
 }
@@ -351,7 +362,7 @@ __global__ __launch_bounds__(kCombineThreads) void block_attn_combine_kernel(
     const Partials pt = partials(const_cast<void*>(ws), Hkv * R, nsplit);
     const float* m = pt.m + size_t(rg) * nsplit;
     const float* l = pt.l + size_t(rg) * nsplit;
-    const float* o = pt.o + size_t(rg) * nsplit * kDh + t;
+    const uint16_t* o = pt.o + size_t(rg) * nsplit * kDh + t;
 
     float M = -INFINITY, L = 0.f, acc = 0.f;
     for (int s0 = 0; s0 < nsplit_used; s0 += kCombineBatch) {
@@ -362,7 +373,7 @@ __global__ __launch_bounds__(kCombineThreads) void block_attn_combine_kernel(
         float ov[kCombineBatch];
 #pragma unroll
         for (int u = 0; u < kCombineBatch; ++u)
-            ov[u] = o[size_t(min(s0 + u, nsplit_used - 1)) * kDh];
+            ov[u] = bf16_to_f32(o[size_t(min(s0 + u, nsplit_used - 1)) * kDh]);
         if (s0 + u_lane >= nsplit_used) mu = -INFINITY;
         float mb = mu;                              // batch maximum (lanes 32..63 mirror 0..31)
         for (int off = kCombineBatch / 2; off > 0; off >>= 1) mb = fmaxf(mb, __shfl_xor(mb, off));
@@ -376,8 +387,9 @@ __global__ __launch_bounds__(kCombineThreads) void block_attn_combine_kernel(
         for (int u = 0; u < kCombineBatch; ++u) {
             const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wu), u));
             const float lw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lu), u));
-            L += w * lw;
-            acc += w * ov[u];
+            const float wl = w * lw;                // split weight of its O / l
+            L += wl;
+            acc += wl * ov[u];
         }
         M = Mn;
     }
