@@ -84,12 +84,13 @@ def test_workspace_queries():
 def test_block_attn_workspace_never_shrinks_with_the_prefix(Bq, Hq, Hkv):
     # A workspace sized for one prefix length must serve every shorter one
     # (the multi-block loop sizes it for its last block), and it must hold at
-    # least one 512-byte partial row (plus max and sum) per query row.
+    # least one partial row per query row: 128 bf16 values plus a float32
+    # maximum and sum.
     prev = 0
     for P in range(0, 65536 - Bq + 1, 61):
         w = bd.bd_block_attn_ws_bytes(P, Bq, Hq, Hkv, 128)
         assert w >= prev, P
-        assert w >= Bq * Hq * (128 + 2) * 4
+        assert w >= Bq * Hq * (128 * 2 + 2 * 4)
         prev = w
 
 
