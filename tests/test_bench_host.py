@@ -41,6 +41,17 @@ def test_dualstream_pairs_of_the_training_config():
     assert abs(n * 16 * 4 * 128 / 1e9 - 73.57) < 0.01
 
 
+def test_headline_steps_per_graph():
+    # long runs keep 25 steps per replay; short ones time at least 4 replays
+    assert bench.headline_steps_per_graph(500, 25) == 25
+    assert bench.headline_steps_per_graph(20, 25) == 5
+    assert bench.headline_steps_per_graph(24, 25) == 6
+    assert bench.headline_steps_per_graph(3, 25) == 1
+    for K in range(1, 300):
+        S = bench.headline_steps_per_graph(K, 25)
+        assert K % S == 0 and 1 <= S <= 25 and (S == 1 or K // S >= 4)
+
+
 def test_graph_divisor():
     assert bench.graph_divisor(500, 25) == 25
     assert bench.graph_divisor(20, 25) == 20
