@@ -28,7 +28,7 @@ EXPORTS = (
     "bd_status_str", "bd_device_check", "bd_make_intra_mask",
     "bd_block_attn_ws_bytes", "bd_block_attn", "bd_block_attn_paged", "bd_block_attn_fp8kv",
     "bd_kv_quant_fp8",
-    "bd_lmhead_conf_ws_bytes", "bd_lmhead_conf", "bd_lmhead_conf_commit",
+    "bd_lmhead_conf_ws_bytes", "bd_lmhead_conf", "bd_lmhead_conf_commit", "bd_lmhead_conf_accept",
     "bd_lmhead_conf_noalloc",
     "bd_lmhead_conf_fp8_ws_bytes", "bd_lmhead_conf_fp8", "bd_lmhead_conf_commit_fp8",
     "bd_quant_fp8_rows", "bd_block_loop_ws_bytes", "bd_block_loop",
@@ -64,6 +64,8 @@ _SIGS = {
     "bd_lmhead_conf_ws_bytes": ([_I, _I, _I], _SZ),
     "bd_lmhead_conf": ([_I, _P, _P, _I, _I, _I, _P, _P, _P, _SZ, _P], _I),
     "bd_lmhead_conf_commit": ([_I, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
+    "bd_lmhead_conf_accept": ([_I, _P, _P, _I, _I, _I, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P,
+                               _SZ, _P], _I),
     "bd_lmhead_conf_noalloc": ([_I, _P, _P, _I, _I, _I, _P, _P, _P], _I),
     "bd_lmhead_conf_fp8_ws_bytes": ([_I, _I, _I], _SZ),
     "bd_lmhead_conf_fp8": ([_P, _P, _P, _I, _I, _I, _P, _P, _P, _SZ, _P], _I),
@@ -187,6 +189,15 @@ def bd_lmhead_conf_commit(dt, h, W, B, d, V, tau, conf, argmax, masked, tokens, 
                                      _ptr(masked), _ptr(tokens), _ptr(n_committed), _ptr(ws),
                                      ws_bytes, _stream(stream))
     return _ret("bd_lmhead_conf_commit", st, check)
+
+
+def bd_lmhead_conf_accept(dt, h, W, B, d, V, conf, argmax, draft, B_acc, P, bonus, accepted,
+                          kv_len, out_tokens, ws, ws_bytes, stream=None, check=True) -> int:
+    st = lib().bd_lmhead_conf_accept(dt, _ptr(h), _ptr(W), B, d, V, _ptr(conf), _ptr(argmax),
+                                     _ptr(draft), B_acc, P, int(bonus), _ptr(accepted),
+                                     _ptr(kv_len), _ptr(out_tokens), _ptr(ws), ws_bytes,
+                                     _stream(stream))
+    return _ret("bd_lmhead_conf_accept", st, check)
 
 
 def bd_lmhead_conf_noalloc(dt, h, W, B, d, V, conf, argmax, stream=None, check=True) -> int:

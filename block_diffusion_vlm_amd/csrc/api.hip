@@ -230,6 +230,26 @@ bd_status bd_lmhead_conf_commit(bd_dtype dt, const void* h, const void* W, int32
     return lmhead_common(dt, h, W, B, d, V, f, ws, ws_bytes, stream);
 }
 
+bd_status bd_lmhead_conf_accept(bd_dtype dt, const void* h, const void* W, int32_t B, int32_t d,
+                                int32_t V, float* conf, int32_t* argmax, const int32_t* draft,
+                                int32_t B_acc, int32_t P, int32_t bonus, int32_t* accepted,
+                                int32_t* kv_len, int32_t* out_tokens, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+    if (!draft || !accepted || !kv_len || !out_tokens) return BD_E_NULL;
+    bd::Finish f{conf, argmax, false, 0.f, nullptr, nullptr, nullptr};
+    const bd_status s = bd::lmhead_args_status(dt, h, W, B, d, V, f);
+    if (s != BD_OK) return s;
+    if (B_acc < 1 || B_acc > B || P < 0 || (int64_t)P + B_acc > INT32_MAX) return BD_E_SHAPE;
+    f.accept_draft = draft;
+    f.accept_B = B_acc;
+    f.accept_P = P;
+    f.accept_bonus = bonus != 0;
+    f.accepted = accepted;
+    f.kv_len = kv_len;
+    f.out_tokens = out_tokens;
+    return lmhead_common(dt, h, W, B, d, V, f, ws, ws_bytes, stream);
+}
+
 size_t bd_lmhead_conf_fp8_ws_bytes(int32_t B, int32_t d, int32_t V) {
     if (B < 1 || B > 64 || d < 128 || d > 16384 || d % 128 != 0 || !vocab_ok(V)) return 0;
     return bd::lmhead_fp8_ws_bytes(B, d, V);

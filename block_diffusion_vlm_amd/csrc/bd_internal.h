@@ -113,6 +113,16 @@ struct Finish {
     // *gate_out to seed_B - 1.
     int seed_B = 0;
     uint8_t* seed_masked = nullptr;
+    // Speculative accept after the merge (null accept_draft otherwise): the
+    // verify tokens are this call's argmax at positions 0 .. accept_B - 1,
+    // compared with accept_draft[0 .. accept_B) as bd_spec_accept(_bonus) does.
+    const int32_t* accept_draft = nullptr;
+    int accept_B = 0;
+    int accept_P = 0;
+    bool accept_bonus = false;
+    int32_t* accepted = nullptr;
+    int32_t* kv_len = nullptr;
+    int32_t* out_tokens = nullptr;
 };
 int lmhead_grid(int B, int d, int V);           // workgroups used for a shape
 size_t lmhead_ws_bytes(int B, int d, int V);              // either dtype

@@ -55,6 +55,30 @@ __device__ __forceinline__ void commit_wave_flag(bool was_masked, float c, int32
     }
 }
 
+// Longest verified prefix (Fast-dVLM overview §2.3.1), executed by one full
+// wavefront: lane i holds draft token d and verify token v of position i
+// (ignored for i >= B).  The first disagreement is the lowest set bit of a
+// ballot.  out_tokens[0 .. L) = draft, accepted = L and kv_len = P + L; with
+// `bonus` the verify token at the first disagreement is appended too
+// (accepted = L + 1 when L < B), the cache still keeping P + L rows.  Shared
+// by the standalone accept kernel and the LM-head merge that accepts right
+// after it.
+__device__ __forceinline__ void accept_wave(bool bonus, int32_t d, int32_t v, int B, int P,
+                                            int32_t* __restrict__ accepted,
+                                            int32_t* __restrict__ kv_len,
+                                            int32_t* __restrict__ out_tokens) {
+    const int i = threadIdx.x & 63;
+    const bool differ = i < B && d != v;
+    const uint64_t bits = __ballot(differ);
+    const int L = bits ? __builtin_ctzll(bits) : B;
+    if (i < L) out_tokens[i] = d;
+    if (bonus && i == L && L < B) out_tokens[i] = v;
+    if (i == 0) {
+        *accepted = bonus && L < B ? L + 1 : L;
+        *kv_len = P + L;
+    }
+}
+
 __device__ __forceinline__ void commit_wave(float c, int32_t a, int B, float tau,
                                             uint8_t* __restrict__ masked,
                                             int32_t* __restrict__ tokens,

@@ -64,6 +64,74 @@ __device__ ArgSoft reduce_column(const WsView& w, int G, int col) {
     return st;
 }
 
+// reduce_column for a group of LANES lanes (64, 32 or 16) of a wave, so that
+// the 64 / LANES groups of a wave merge as many positions side by side: lane
+// l of the group folds partials l, l + LANES, ..., eight per batch with every
+// load of a batch issued first, then a fixed xor-shuffle tree inside the
+// group (offsets below LANES never leave it).  The result is valid in every
+// lane of the group; with LANES = 64 it is reduce_column, bit for bit.
+template <int LANES>
+__device__ ArgSoft reduce_column_lanes(const WsView& w, int G, int col) {
+    const int gl = threadIdx.x & (LANES - 1);
+    const float* m = w.m + size_t(col) * G;
+    const float* s = w.s + size_t(col) * G;
+    const int* a = w.a + size_t(col) * G;
+    ArgSoft st{-INFINITY, 0.f, 0x7fffffff};
+    for (int p0 = 0; p0 < G; p0 += 8 * LANES) {
+        float mm[8], ss[8];
+        int aa[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            // Past the last partial: reload the last one and drop it below.
+            const int p = min(p0 + LANES * u + gl, G - 1);
+            mm[u] = m[p];
+            ss[u] = s[p];
+            aa[u] = a[p];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (p0 + LANES * u + gl >= G) mm[u] = -INFINITY, ss[u] = 0.f, aa[u] = 0x7fffffff;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) st = merge(st, ArgSoft{mm[u], ss[u], aa[u]});
+    }
+    for (int off = 1; off < LANES; off <<= 1) st = merge(st, shfl_xor_state(st, off));
+    return st;
+}
+
+// One workgroup of 16 waves merges every position, 16 x 64 / LANES at a time
+// (LANES = 64 up to 16 positions, 32 up to 32, 16 up to 64: a single round
+// for any B), then wave 0 runs the speculative accept of the first accept_B
+// positions against the draft tokens (Fast-dVLM overview §2.3.1), so the
+// accept needs no dispatch of its own.
+template <int LANES>
+__global__ __launch_bounds__(1024) void lmhead_combine_accept_kernel(
+    const void* __restrict__ ws, int G, int B, float* __restrict__ conf,
+    int32_t* __restrict__ argmax, const int32_t* __restrict__ draft, int B_acc, int P,
+    int bonus, int32_t* __restrict__ accepted, int32_t* __restrict__ kv_len,
+    int32_t* __restrict__ out_tokens) {
+    constexpr int kPerWave = 64 / LANES;
+    __shared__ int sarg[64];
+    const WsView w = ws_view(const_cast<void*>(ws), G, B);
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    // The draft tokens are read now, with the partials (every wave reads
+    // them, unconditionally, so no branch waits on them).
+    const int32_t d = draft[min(lane, B_acc - 1)];
+    for (int c0 = wave * kPerWave; c0 < B; c0 += 16 * kPerWave) {
+        const int col = c0 + lane / LANES;
+        const ArgSoft r = reduce_column_lanes<LANES>(w, G, min(col, B - 1));
+        if ((lane & (LANES - 1)) == 0 && col < B) {
+            conf[col] = 1.0f / r.s;
+            argmax[col] = r.a;
+            sarg[col] = r.a;
+        }
+    }
+    __syncthreads();
+    if (wave == 0)
+        accept_wave(bonus != 0, d, lane < B_acc ? sarg[lane] : 0, B_acc, P, accepted, kv_len,
+                    out_tokens);
+}
+
 // One wave per position: merged confidence and argmax.  As the AR seed of a
 // block (seed_B > 0, one position), it also starts the block: argmax points
 // at the block's tokens, so position 0 receives the seed token; positions
@@ -130,7 +198,14 @@ __global__ __launch_bounds__(1024) void lmhead_combine_commit_kernel(
 }  // namespace
 
 hipError_t launch_combine(void* ws, int G, int B, const Finish& f, hipStream_t st) {
-    if (f.commit)
+    if (f.accept_draft != nullptr) {
+        auto k = B <= 16 ? lmhead_combine_accept_kernel<64>
+                         : (B <= 32 ? lmhead_combine_accept_kernel<32>
+                                    : lmhead_combine_accept_kernel<16>);
+        hipLaunchKernelGGL(k, dim3(1), dim3(1024), 0, st, ws, G, B, f.conf, f.argmax,
+                           f.accept_draft, f.accept_B, f.accept_P, int(f.accept_bonus),
+                           f.accepted, f.kv_len, f.out_tokens);
+    } else if (f.commit)
         hipLaunchKernelGGL(lmhead_combine_commit_kernel, dim3(1), dim3(1024), 0, st, ws, G, B,
                            f.conf, f.argmax, f.tau, f.masked, f.tokens, f.n_committed, f.gate,
                            f.gate_out, f.steps);

@@ -19,10 +19,9 @@ __global__ __launch_bounds__(64) void commit_kernel(const float* __restrict__ co
     commit_wave(c, a, B, tau, masked, tokens, n_committed);
 }
 
-// Longest verified prefix (overview §2.3.1): the first disagreement is the
-// lowest set bit of a ballot.  With BONUS the verify token at the first
-// disagreement is appended too (greedy speculative decoding's correction
-// token); the cache keeps P + L rows either way.
+// Longest verified prefix (overview §2.3.1; accept_wave).  With BONUS the
+// verify token at the first disagreement is appended too (greedy speculative
+// decoding's correction token); the cache keeps P + L rows either way.
 template <bool BONUS>
 __global__ __launch_bounds__(64) void spec_accept_kernel(const int32_t* __restrict__ draft,
                                                          const int32_t* __restrict__ verify,
@@ -33,15 +32,7 @@ __global__ __launch_bounds__(64) void spec_accept_kernel(const int32_t* __restri
     const int i = threadIdx.x;
     const int32_t d = i < B ? draft[i] : 0;
     const int32_t v = i < B ? verify[i] : 0;
-    const bool differ = i < B && d != v;
-    const uint64_t bits = __ballot(differ);
-    const int L = bits ? __builtin_ctzll(bits) : B;
-    if (i < L) out_tokens[i] = d;
-    if (BONUS && i == L && L < B) out_tokens[i] = v;
-    if (i == 0) {
-        *accepted = BONUS && L < B ? L + 1 : L;
-        *kv_len = P + L;
-    }
+    accept_wave(BONUS, d, v, B, P, accepted, kv_len, out_tokens);
 }
 
 // LOWN certificate (method step details (2)-(3)).  Thread i computes the

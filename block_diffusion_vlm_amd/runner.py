@@ -65,6 +65,12 @@ class LMHead:
                                  self.argmax, masked, tokens, n_committed, self.ws,
                                  self.ws_bytes, stream)
 
+    def conf_accept(self, h, draft, B_acc, P, accepted, kv_len, out_tokens, bonus=False,
+                    stream=None):
+        bd.bd_lmhead_conf_accept(self.dt, h, self.W, self.B, self.d, self.V, self.conf,
+                                 self.argmax, draft, B_acc, P, int(bonus), accepted, kv_len,
+                                 out_tokens, self.ws, self.ws_bytes, stream)
+
 
 class LMHeadFP8:
     """bd_lmhead_conf_fp8 over fixed device buffers: W holds E4M3 codes
@@ -294,9 +300,12 @@ class DecodeBlocks:
 
 class LinearSpecStep:
     """Linear self-speculative step: draft (bidirectional) and verify (causal)
-    passes, each block attention + LM head, then bd_spec_accept."""
+    passes, each block attention + LM head, then the accept.  With
+    ``fused_accept`` (the default) the verify pass's LM head and the accept
+    are one call, bd_lmhead_conf_accept; otherwise bd_lmhead_conf and
+    bd_spec_accept."""
 
-    def __init__(self, inp: dict, device="cuda"):
+    def __init__(self, inp: dict, device="cuda", fused_accept=True):
         self.inp = inp
         B, P = inp["B"], inp["P"]
         dh = inp["q_draft"].shape[-1]
@@ -313,12 +322,17 @@ class LinearSpecStep:
         self.kv_len = torch.zeros(1, dtype=torch.int32, device=device)
         self.out_tokens = torch.full((B,), -1, dtype=torch.int32, device=device)
         self.B, self.P = B, P
+        self.fused_accept = fused_accept
 
     def run(self, stream=None):
         t = self.t
         self.attn_d(t["q_draft"], t["k_draft"], t["v_draft"], stream)
         self.lm_d(t["h_draft"], stream)
         self.attn_v(t["q_verify"], t["k_verify"], t["v_verify"], stream)
+        if self.fused_accept:
+            self.lm_v.conf_accept(t["h_verify"], self.lm_d.argmax, self.B, self.P, self.accepted,
+                                  self.kv_len, self.out_tokens, stream=stream)
+            return
         self.lm_v(t["h_verify"], stream)
         bd.bd_spec_accept(self.lm_d.argmax, self.lm_v.argmax, self.B, self.P, self.accepted,
                           self.kv_len, self.out_tokens, stream)
@@ -326,10 +340,12 @@ class LinearSpecStep:
 
 class FusedSpecStep:
     """Fused (quadratic) speculative step: one block attention over 2B rows
-    under the SPEC_FUSED mask, one LM head over the 2B rows, bd_spec_accept on
-    the verify half; plus the LOWN certificate scan."""
+    under the SPEC_FUSED mask, one LM head over the 2B rows, the accept on
+    the verify half; plus the LOWN certificate scan.  With ``fused_accept``
+    (the default) the LM head and the accept are one call,
+    bd_lmhead_conf_accept; otherwise bd_lmhead_conf and bd_spec_accept."""
 
-    def __init__(self, inp: dict, device="cuda"):
+    def __init__(self, inp: dict, device="cuda", fused_accept=True):
         self.inp = inp
         B, bq, P = inp["B"], inp["Bq"], inp["P"]
         dh = inp["q"].shape[-1]
@@ -347,13 +363,18 @@ class FusedSpecStep:
         self.cert_L = torch.zeros(1, dtype=torch.int32, device=device)
         self.skip = torch.zeros(1, dtype=torch.int32, device=device)
         self.B, self.P, self.n, self.k = B, P, n, int(inp["k_cert"])
+        self.fused_accept = fused_accept
 
     def run(self, stream=None):
         t = self.t
         self.attn(t["q"], t["k_cache"], t["v_cache"], stream)
-        self.lm(t["h"], stream)
-        bd.bd_spec_accept(t["draft_in"], self.lm.argmax, self.B, self.P, self.accepted,
-                          self.kv_len, self.out_tokens, stream)
+        if self.fused_accept:
+            self.lm.conf_accept(t["h"], t["draft_in"], self.B, self.P, self.accepted,
+                                self.kv_len, self.out_tokens, stream=stream)
+        else:
+            self.lm(t["h"], stream)
+            bd.bd_spec_accept(t["draft_in"], self.lm.argmax, self.B, self.P, self.accepted,
+                              self.kv_len, self.out_tokens, stream)
         bd.bd_cert_scan(t["anchor_conf"], t["anchor_tok"], t["text_tok"], self.n, self.k,
                         self.order, self.cert_L, self.skip, stream)
 

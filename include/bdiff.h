@@ -436,6 +436,34 @@ bd_status bd_spec_accept_bonus(const int32_t* draft, const int32_t* verify, int3
                                hipStream_t stream);
 
 /*
+ * bd_lmhead_conf_accept - the verify pass's LM head followed by the
+ * speculative accept, as one call: bd_lmhead_conf on h, then
+ * bd_spec_accept (bd_spec_accept_bonus when bonus != 0) with verify = this
+ * call's argmax[0..B_acc) against draft[0..B_acc).  The merge of the LM-head
+ * partials and the accept run in the same small kernel, saving the accept's
+ * launch per speculative step.  [OV §2.3.1 the linear (two forwards) and
+ * quadratic (one forward; rows 0..B_acc-1 of the fused block are the verify
+ * half) self-speculative steps; LOWN 'method step details' (1) for conf]
+ *   h, W, B, d, V, conf, argmax, ws, ws_bytes  as in bd_lmhead_conf
+ *   draft     [B_acc] int32 (device; read only)
+ *   B_acc     positions verified, 1 <= B_acc <= B
+ *   P, accepted, kv_len, out_tokens  as in bd_spec_accept
+ * argmax is bit-identical to bd_lmhead_conf's; conf is too for B <= 16 and
+ * otherwise within float32 rounding of it (the merge sums the partials of
+ * several positions side by side, in another fixed order).  accepted, kv_len
+ * and out_tokens are exactly those of the two separate calls.
+ * Errors: those of bd_lmhead_conf, plus BD_E_NULL for draft, accepted, kv_len
+ *   or out_tokens, and BD_E_SHAPE unless 1 <= B_acc <= B, P >= 0 and
+ *   P + B_acc fits in int32.
+ */
+bd_status bd_lmhead_conf_accept(bd_dtype dt, const void* h, const void* W,
+                                int32_t B, int32_t d, int32_t V,
+                                float* conf, int32_t* argmax,
+                                const int32_t* draft, int32_t B_acc, int32_t P, int32_t bonus,
+                                int32_t* accepted, int32_t* kv_len, int32_t* out_tokens,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * bd_cert_scan - LOWN certificate over n masked positions.
  * [LOWN 'method step details' (2)-(3)]  order = the positions sorted by
  * anchor_conf descending (stable: lower index first on ties);

@@ -203,6 +203,24 @@ def test_lmhead_validation():
     assert _lm(ws_bytes=bd.bd_lmhead_conf_ws_bytes(16, 2048, 151936) - 1) == bd.BD_E_WORKSPACE
 
 
+def test_lmhead_conf_accept_validation():
+    f = lambda **kw: bd.bd_lmhead_conf_accept(**{**dict(  # noqa: E731
+        dt=bd.BD_BF16, h=FAKE, W=FAKE, B=32, d=2048, V=151936, conf=FAKE, argmax=FAKE,
+        draft=FAKE, B_acc=16, P=4608, bonus=0, accepted=FAKE, kv_len=FAKE, out_tokens=FAKE,
+        ws=FAKE, ws_bytes=1 << 30, stream=0, check=False), **kw})
+    for name in ("draft", "accepted", "kv_len", "out_tokens", "conf", "argmax", "h", "W"):
+        assert f(**{name: None}) == bd.BD_E_NULL, name
+    assert f(dt=9) == bd.BD_E_DTYPE
+    assert f(B_acc=0) == bd.BD_E_SHAPE
+    assert f(B_acc=33) == bd.BD_E_SHAPE            # more verified positions than rows
+    assert f(B=65, B_acc=16) == bd.BD_E_SHAPE
+    assert f(P=-1) == bd.BD_E_SHAPE
+    assert f(P=2 ** 31 - 16) == bd.BD_E_SHAPE      # P + B_acc must fit in int32
+    assert f(h=MISALIGNED) == bd.BD_E_ALIGN
+    assert f(ws=None) == bd.BD_E_WORKSPACE
+    assert f(ws_bytes=bd.bd_lmhead_conf_ws_bytes(32, 2048, 151936) - 1) == bd.BD_E_WORKSPACE
+
+
 def test_lmhead_conf_commit_validation():
     f = lambda **kw: bd.bd_lmhead_conf_commit(**{**dict(
         dt=bd.BD_BF16, h=FAKE, W=FAKE, B=16, d=2048, V=151936, tau=0.9, conf=FAKE, argmax=FAKE,

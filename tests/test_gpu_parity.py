@@ -417,6 +417,60 @@ def test_lmhead_conf_commit_equals_separate_calls(B, d, V):
     assert out[True][4] == nc
 
 
+@pytest.mark.parametrize("B,d,V,B_acc,bonus", [
+    (1, 128, 1000, 1, False), (16, 2048, 30011, 16, False), (16, 1024, 5000, 9, True),
+    (17, 512, 4097, 17, True), (32, 2048, 30011, 16, False), (32, 2048, 9001, 32, True),
+    (33, 384, 999, 20, False), (48, 1024, 3001, 48, True), (64, 2048, 3001, 64, False),
+    (32, 2048, 151936, 16, True)])
+def test_lmhead_conf_accept_equals_separate_calls_and_oracle(B, d, V, B_acc, bonus):
+    """bd_lmhead_conf_accept = bd_lmhead_conf + bd_spec_accept(_bonus) on its
+    argmax: argmax and the accept outputs bit-exact (against the separate
+    calls and the oracle), conf equal bit for bit up to 16 positions and
+    within float32 rounding above (the merge order differs there)."""
+    r = _lmhead_case(B, d, V, seed=3 * B + d + V)
+    h, W = runner.to_dev(r["h"]), runner.to_dev(r["W"])
+    oc, oa = oracle.lmhead_conf(r["h"], r["W"])
+    rng = np.random.default_rng(B * 31 + B_acc)
+    call = bd.bd_spec_accept_bonus if bonus else bd.bd_spec_accept
+    for trial in range(4):
+        # drafts that agree with the verify argmax up to a planted cut (or all)
+        draft = oa[:B_acc].astype(np.int32).copy()
+        if trial:
+            cut = int(rng.integers(0, B_acc))
+            draft[cut:] = (draft[cut:] + 1 + rng.integers(0, 5, B_acc - cut)) % V
+        P = int(rng.integers(0, 5000))
+        dd = runner.to_dev(draft)
+        out = {}
+        for fused in (False, True):
+            lm = runner.LMHead(bd.BD_BF16, W, B, d, V)
+            acc = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+            kv = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+            toks = torch.full((B_acc,), -99, dtype=torch.int32, device="cuda")
+            if fused:
+                lm.conf_accept(h, dd, B_acc, P, acc, kv, toks, bonus=bonus)
+            else:
+                lm(h)
+                call(dd, lm.argmax, B_acc, P, acc, kv, toks)
+            torch.cuda.synchronize()
+            out[fused] = (lm.conf.cpu().numpy(), lm.argmax.cpu().numpy(), int(acc.item()),
+                          int(kv.item()), runner.to_host(toks))
+        c0, a0, n0, k0, t0 = out[False]
+        c1, a1, n1, k1, t1 = out[True]
+        assert np.array_equal(a1, a0) and np.array_equal(a1, oa)
+        if B <= 16:
+            assert np.array_equal(c1, c0)
+        else:
+            # Two fixed-order merges of at most 256 positive partials, each
+            # within about (256 + 32) float32 roundings (the sums and the
+            # exp2 rescales on a tree of depth 8) of the exact value.
+            assert np.abs(c1 / c0 - 1).max() <= 2 * (256 + 32) * 2.0 ** -24
+        assert rel_err(c1, oc) <= 1e-4 or np.abs(c1 / oc - 1).max() <= 1e-4
+        assert (n1, k1) == (n0, k0) and np.array_equal(t1, t0)
+        n, kvl, ref = oracle.spec_accept(draft, oa[:B_acc].astype(np.int32), P, bonus=bonus)
+        assert n1 == n and k1 == kvl
+        assert np.array_equal(t1[:n], ref) and (t1[n:] == -99).all()
+
+
 def test_decode_step_full_size_separate_calls():
     r = synth.qwen_decode(guard=row_guard(TAU32))
     _assert_guards(r["h"], r["W"], TAU32)
@@ -445,35 +499,43 @@ def test_tiny_decode_step_f32():
 
 
 def test_linear_spec_step_full_size():
+    """Both compositions: the verify LM head and the accept as one call
+    (bd_lmhead_conf_accept, the default) and as two."""
     r = synth.linear_spec(guard=row_guard())
     _assert_guards(r["h_draft"], r["W"])
     _assert_guards(r["h_verify"], r["W"])
-    step = runner.LinearSpecStep(r)
-    step.run()
-    torch.cuda.synchronize()
     o = oracle.linear_spec_step(r["q_draft"], r["k_draft"], r["v_draft"], r["q_verify"],
                                 r["k_verify"], r["v_verify"], r["P"], r["h_draft"],
                                 r["h_verify"], r["W"])
-    assert int(step.accepted.item()) == o["accepted"] == r["L_true"]
-    assert int(step.kv_len.item()) == o["kv_len"]
-    assert np.array_equal(runner.to_host(step.out_tokens)[:o["accepted"]], o["out_tokens"])
-    assert np.abs(bf16_host(step.attn_d.out) - o["attn_draft"]).max() <= 2e-2
-    assert np.abs(bf16_host(step.attn_v.out) - o["attn_verify"]).max() <= 2e-2
+    for fused_accept in (True, False):
+        step = runner.LinearSpecStep(r, fused_accept=fused_accept)
+        step.run()
+        torch.cuda.synchronize()
+        assert int(step.accepted.item()) == o["accepted"] == r["L_true"]
+        assert int(step.kv_len.item()) == o["kv_len"]
+        assert np.array_equal(runner.to_host(step.out_tokens)[:o["accepted"]], o["out_tokens"])
+        assert np.abs(bf16_host(step.attn_d.out) - o["attn_draft"]).max() <= 2e-2
+        assert np.abs(bf16_host(step.attn_v.out) - o["attn_verify"]).max() <= 2e-2
+        del step
 
 
 def test_fused_spec_step_full_size():
+    """Both compositions: the LM head and the accept as one call
+    (bd_lmhead_conf_accept, the default) and as two."""
     r = synth.fused_spec(guard=row_guard())
     _assert_guards(r["h"], r["W"])
-    step = runner.FusedSpecStep(r)
-    step.run()
-    torch.cuda.synchronize()
     o = oracle.fused_spec_step(r["q"], r["k_cache"], r["v_cache"], r["P"], r["h"], r["W"],
                                r["draft_in"])
-    assert np.array_equal(step.lm.argmax.cpu().numpy(), o["argmax"])
-    assert int(step.accepted.item()) == o["accepted"] == r["L_true"]
-    assert int(step.kv_len.item()) == o["kv_len"]
-    assert np.abs(bf16_host(step.attn.out) - o["attn"]).max() <= 2e-2
     order, L, skip = oracle.cert_scan(r["anchor_conf"], r["anchor_tok"], r["text_tok"],
                                       r["k_cert"])
-    assert np.array_equal(runner.to_host(step.order), order)
-    assert int(step.cert_L.item()) == L and int(step.skip.item()) == skip
+    for fused_accept in (True, False):
+        step = runner.FusedSpecStep(r, fused_accept=fused_accept)
+        step.run()
+        torch.cuda.synchronize()
+        assert np.array_equal(step.lm.argmax.cpu().numpy(), o["argmax"])
+        assert int(step.accepted.item()) == o["accepted"] == r["L_true"]
+        assert int(step.kv_len.item()) == o["kv_len"]
+        assert np.abs(bf16_host(step.attn.out) - o["attn"]).max() <= 2e-2
+        assert np.array_equal(runner.to_host(step.order), order)
+        assert int(step.cert_L.item()) == L and int(step.skip.item()) == skip
+        del step
