@@ -197,6 +197,34 @@ def test_lmhead_f32_ragged(B, d, V):
     assert rel_err(lm.conf.cpu().numpy(), oc) <= 1e-5
 
 
+@pytest.mark.parametrize("B,d,V,B_acc", [(4, 16, 64, 4), (33, 40, 1000, 17), (64, 16, 700, 64)])
+def test_lmhead_conf_accept_f32(B, d, V, B_acc):
+    """The float32 LM head with the accept in its merge: argmax and the accept
+    bit-exact against the oracle on rows whose top-2 gap exceeds 1e-4."""
+    rng = np.random.default_rng(B * 5 + V)
+    h = rng.standard_normal((B, d)).astype(np.float32)
+    W = rng.standard_normal((V, d)).astype(np.float32)
+    oc, oa = oracle.lmhead_conf(h, W)
+    gap, _ = lmhead_margins(h, W)
+    assert (gap[:B_acc] > 1e-4).all()
+    draft = oa[:B_acc].astype(np.int32).copy()
+    cut = B_acc // 2
+    draft[cut] = (draft[cut] + 1) % V
+    lm = runner.LMHead(bd.BD_F32, runner.to_dev(W), B, d, V)
+    acc = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    kv = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    toks = torch.full((B_acc,), -99, dtype=torch.int32, device="cuda")
+    lm.conf_accept(runner.to_dev(h), runner.to_dev(draft), B_acc, 77, acc, kv, toks, bonus=True)
+    torch.cuda.synchronize()
+    ok = gap > 1e-4
+    assert np.array_equal(lm.argmax.cpu().numpy()[ok], oa[ok])
+    assert rel_err(lm.conf.cpu().numpy(), oc) <= 1e-5
+    n, kvl, ref = oracle.spec_accept(draft, oa[:B_acc].astype(np.int32), 77, bonus=True)
+    assert (int(acc.item()), int(kv.item())) == (n, kvl) == (cut + 1, 77 + cut)
+    t = runner.to_host(toks)
+    assert np.array_equal(t[:n], ref) and (t[n:] == -99).all()
+
+
 # ---------------------------------------------------------------------------
 # Block attention
 # ---------------------------------------------------------------------------
