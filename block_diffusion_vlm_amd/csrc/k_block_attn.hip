@@ -460,21 +460,36 @@ __global__ __launch_bounds__(64) void block_attn_f32_kernel(
 
 // Key tiles per workgroup.  A decode-sized call is bound by latency: each
 // split runs a chain of dependent steps per tile, so the fewest tiles per
-// split win as long as the grid (splits x KV heads x 128-row blocks) fits on
-// the chip in one round, one workgroup per CU.  Past that, splits take
-// ceil(ntiles / max_splits) tiles each, which also bounds the partial
-// outputs (a 512-byte row per query row and split) when the prefix is long.
+// split win while the grid (splits x KV heads x 128-row blocks) is small;
+// every split also writes a partial row per query row, which the merge
+// reads back.  A split takes the fewest tiles that keep the grid within half
+// the chip (one workgroup per CU) as long as that is at most
+// kMaxTilesHalf tiles, and otherwise the fewest that keep it within the
+// whole chip, which also bounds the partial outputs when the prefix is long.
+// (Measured against the whole-chip rule alone: 0.65 us less at 2 x 16
+// queries over 4,608 keys (3 tiles per split instead of 2) and at 16 over
+// 20,016 (5 instead of 3); 17 tiles instead of 9 at 65,536 keys took 8 us
+// more, hence the bound.)
 constexpr int kSplitCUs = 256;                       // compute units of the chip
+constexpr int kMaxTilesHalf = 6;
+
+int workgroups_per_split(int Bq, int Hq, int Hkv) {
+    const int R = Bq * (Hq / Hkv);
+    return Hkv * ((R + kRowsPerWg - 1) / kRowsPerWg);
+}
 
 int max_splits(int Bq, int Hq, int Hkv) {
-    const int R = Bq * (Hq / Hkv);
-    const int per_split = Hkv * ((R + kRowsPerWg - 1) / kRowsPerWg);   // workgroups
-    const int m = kSplitCUs / per_split;
+    const int m = kSplitCUs / workgroups_per_split(Bq, Hq, Hkv);
     return m > 1 ? m : 1;
 }
 
 int tiles_per_split(int P, int Bq, int Hq, int Hkv) {
     const int ntiles = (P + Bq + kBN - 1) / kBN;
+    const int mh = kSplitCUs / 2 / workgroups_per_split(Bq, Hq, Hkv);
+    if (mh >= 1) {
+        const int kt = ntiles > mh ? (ntiles + mh - 1) / mh : 1;
+        if (kt <= kMaxTilesHalf) return kt;
+    }
     const int m = max_splits(Bq, Hq, Hkv);
     return ntiles > m ? (ntiles + m - 1) / m : 1;
 }
