@@ -468,7 +468,7 @@ __global__ __launch_bounds__(64) void block_attn_f32_kernel(
 // whole chip, which also bounds the partial outputs when the prefix is long.
 // (Measured against the whole-chip rule alone: 0.65 us less at 2 x 16
 // queries over 4,608 keys (3 tiles per split instead of 2) and at 16 over
-// 20,016 (5 instead of 3); 17 tiles instead of 9 at 65,536 keys took 8 us
+// 20,016 (5 instead of 3); 16 tiles instead of 8 at 65,536 keys took 8 us
 // more, hence the bound.)
 constexpr int kSplitCUs = 256;                       // compute units of the chip
 constexpr int kMaxTilesHalf = 6;
